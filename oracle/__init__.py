@@ -1,0 +1,205 @@
+"""TEST INFRASTRUCTURE: float64 CPU oracle for unified-max split-KV decode attention.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library neither imports nor links it, and the two share
+no source.  The arithmetic lives in ``fd_oracle.c`` (plain C, float64, one
+OpenMP loop over rows); this module only marshals numpy arrays.
+
+Functions follow the FlashDecoding++ theory page: ``decode_exact`` is the plain
+max-subtracted softmax attention plus the safe-band test (section 3, first
+formula and the fallback rule); ``decode_unified`` walks the method's steps --
+per-chunk sums against the preset constant phi, online-softmax recompute of a
+chunk whose scores leave the band, plain-sum merge (section 3, second formula
+and the fallback rule; the split-KV figure of section 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libfd_oracle.so")
+
+_DT = {"f32": 0, "bf16": 1, "e4m3fn": 2}
+_NP_DT = {"f32": np.float32, "bf16": np.uint16, "e4m3fn": np.uint8}
+
+
+def build(force: bool = False) -> str:
+    """Compile fd_oracle.c with gcc (float64, OpenMP).  Returns the library path."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                        "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_double)]
+
+
+class _Inputs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P, I = ctypes.POINTER(_Problem), ctypes.POINTER(_Inputs)
+        lib.orc_decode_exact.argtypes = [P, I, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_decode_exact.restype = ctypes.c_int
+        lib.orc_decode_unified.argtypes = [P, I, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_decode_unified.restype = ctypes.c_int
+        lib.orc_scores.argtypes = [P, I, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.orc_scores.restype = ctypes.c_int
+        lib.orc_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.orc_decode_bf16.restype = ctypes.c_double
+        lib.orc_decode_e4m3fn.argtypes = [ctypes.c_uint8]
+        lib.orc_decode_e4m3fn.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _marshal(q, k_cache, v_cache, seq_lens, block_table, num_kv_heads, max_seq_len, page_size,
+             q_dtype, kv_dtype, scale, k_scale, v_scale):
+    q = np.ascontiguousarray(q, dtype=_NP_DT[q_dtype])
+    k_cache = np.ascontiguousarray(k_cache, dtype=_NP_DT[kv_dtype])
+    v_cache = np.ascontiguousarray(v_cache, dtype=_NP_DT[kv_dtype])
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    if Hq % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if seq_lens.shape != (B,):
+        raise ValueError("seq_lens must have shape [batch]")
+    if page_size:
+        if block_table is None:
+            raise ValueError("paged cache needs a block table")
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        if block_table.ndim != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [batch][max_blocks]")
+        if block_table.shape[1] * page_size < min(max_seq_len, int(seq_lens.max(initial=0))):
+            raise ValueError("block_table too narrow for the sequence lengths")
+        if k_cache.shape[1:] != (num_kv_heads, page_size, D):
+            raise ValueError("paged cache must be [pages][Hkv][page_size][D]")
+        max_blocks = block_table.shape[1]
+    else:
+        block_table = None
+        if k_cache.shape != (B, num_kv_heads, max_seq_len, D):
+            raise ValueError("contiguous cache must be [B][Hkv][max_seq_len][D]")
+        max_blocks = 0
+    if kv_dtype == "e4m3fn":
+        k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+        v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+        if k_scale.shape != (num_kv_heads,) or v_scale.shape != (num_kv_heads,):
+            raise ValueError("k_scale/v_scale must be [num_kv_heads]")
+    else:
+        k_scale = v_scale = None
+    prob = _Problem(B, Hq, num_kv_heads, D, max_seq_len, page_size, max_blocks,
+                    _DT[q_dtype], _DT[kv_dtype], float(scale))
+    keep = (q, k_cache, v_cache, seq_lens, block_table, k_scale, v_scale)
+    ins = _Inputs(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+                  _ptr(k_scale), _ptr(v_scale))
+    return prob, ins, keep
+
+
+def _rows(rows, B, Hq):
+    if rows is None:
+        return None, B * Hq
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if rows.size and (rows.min() < 0 or rows.max() >= B * Hq):
+        raise ValueError("row id out of range")
+    return rows, rows.size
+
+
+def decode_exact(q, k_cache, v_cache, seq_lens, block_table=None, *, num_kv_heads, max_seq_len,
+                 page_size=0, q_dtype="bf16", kv_dtype="bf16", scale, phi, a, b, k_scale=None,
+                 v_scale=None, rows=None, with_threads=False):
+    """Exact softmax decode attention + band flags, float64.
+
+    Returns (out [nrows][D] float64, flags [nrows] uint8, margin [nrows] float64);
+    rows are ids b * Hq + h (default: all, in order).  margin is the smallest
+    distance of any valid score to a band edge.  With with_threads=True the
+    number of OpenMP threads used is appended.
+    """
+    prob, ins, keep = _marshal(q, k_cache, v_cache, seq_lens, block_table, num_kv_heads,
+                               max_seq_len, page_size, q_dtype, kv_dtype, scale, k_scale, v_scale)
+    B, Hq, D = keep[0].shape
+    rows, n = _rows(rows, B, Hq)
+    out = np.zeros((n, D), dtype=np.float64)
+    flags = np.zeros(n, dtype=np.uint8)
+    margin = np.zeros(n, dtype=np.float64)
+    th = _load().orc_decode_exact(ctypes.byref(prob), ctypes.byref(ins), phi, a, b, n, _ptr(rows),
+                                  _ptr(out), _ptr(flags), _ptr(margin))
+    return (out, flags, margin, th) if with_threads else (out, flags, margin)
+
+
+def decode_unified(q, k_cache, v_cache, seq_lens, block_table=None, *, num_kv_heads, max_seq_len,
+                   page_size=0, q_dtype="bf16", kv_dtype="bf16", scale, phi, a, b, chunk_size,
+                   k_scale=None, v_scale=None, rows=None):
+    """The method's steps in float64 (unified-max chunk partials, band test,
+    online-softmax recompute of flagged chunks, merge).
+
+    Returns (out [nrows][D] float64, flags [nrows] uint8, recomputed chunks [nrows] int32).
+    """
+    prob, ins, keep = _marshal(q, k_cache, v_cache, seq_lens, block_table, num_kv_heads,
+                               max_seq_len, page_size, q_dtype, kv_dtype, scale, k_scale, v_scale)
+    B, Hq, D = keep[0].shape
+    rows, n = _rows(rows, B, Hq)
+    out = np.zeros((n, D), dtype=np.float64)
+    flags = np.zeros(n, dtype=np.uint8)
+    rec = np.zeros(n, dtype=np.int32)
+    rc = _load().orc_decode_unified(ctypes.byref(prob), ctypes.byref(ins), int(chunk_size), phi, a,
+                                    b, n, _ptr(rows), _ptr(out), _ptr(flags), _ptr(rec))
+    if rc < 0:
+        raise ValueError("chunk_size must be positive")
+    return out, flags, rec
+
+
+def scores(q, k_cache, v_cache, seq_lens, block_table=None, *, num_kv_heads, max_seq_len,
+           page_size=0, q_dtype="bf16", kv_dtype="bf16", scale, batch_index, head,
+           k_scale=None, v_scale=None, **_ignored):
+    """float64 scores s_t = scale * q . k_t of one row, t < seq_lens[b]."""
+    prob, ins, keep = _marshal(q, k_cache, v_cache, seq_lens, block_table, num_kv_heads,
+                               max_seq_len, page_size, q_dtype, kv_dtype, scale, k_scale, v_scale)
+    L = int(np.clip(keep[3][batch_index], 0, max_seq_len))
+    s = np.zeros(max(L, 1), dtype=np.float64)
+    n = _load().orc_scores(ctypes.byref(prob), ctypes.byref(ins), int(batch_index), int(head),
+                           _ptr(s))
+    return s[:n]
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """E4M3FN codes -> float64 values, through the oracle's own decoder."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.orc_decode_e4m3fn(int(x)) for x in c], dtype=np.float64)
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 values, through the oracle's own decoder."""
+    lib = _load()
+    c = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.orc_decode_bf16(int(x)) for x in c], dtype=np.float64)

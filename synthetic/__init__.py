@@ -1,0 +1,340 @@
+"""Seeded synthetic inputs for unified-max split-KV decode attention.
+
+The pages measure no public benchmark; these generators stand in for the
+workloads they describe: a single decode query per (batch, head) against a
+long, optionally ragged and optionally paged KV cache (FlashDecoding++ theory
+page, section 1; export-strategy page, section 2).
+
+This module draws numbers and stores them in the caller-visible storage
+formats (fp32, bf16 bit patterns, OCP E4M3FN codes).  It holds none of the
+attention arithmetic: no scores, exponentials, band tests or merges.  Both the
+float64 oracle and the GPU library consume what it returns.
+
+Recipe (also stated in the design doc):
+  * every value ~ N(0, 1), drawn as float32 from numpy's PCG64 stream keyed by
+    (seed, tensor id, batch, kv head), so any subset of rows can be drawn
+    alone and is identical to the same rows of a full draw;
+  * bf16 storage: float32 rounded to nearest-even on the upper 16 bits;
+  * E4M3FN storage: per-KV-head scale = max|x| / 448 over that head's draws,
+    code = nearest-even E4M3FN of x / scale (saturating at +-448);
+  * ragged lengths ~ U{lo..hi} inclusive; paged caches place tokens in
+    16-token pages whose physical ids are a seeded permutation of the pool,
+    assigned in (batch, token) order, unused table slots = -1.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Problem", "CONFIGS", "make_config", "make_problem", "bf16_round",
+           "bf16_to_f32", "e4m3fn_encode", "e4m3fn_values"]
+
+HEAD_DIM = 128
+SEED_BASE = 0x5EED0000
+
+# stream ids (second word of the numpy seed sequence)
+_S_Q, _S_K, _S_V, _S_LENS, _S_PERM, _S_PAIRS = 1, 2, 3, 4, 5, 6
+
+# The five workloads.  Field names match the arguments of the library and of
+# the oracle.  "lens" is ("fixed", L) or ("uniform", lo, hi).
+CONFIGS = {
+    1: dict(workload="mha1x1-L4096-f32", batch=1, num_q_heads=1, num_kv_heads=1,
+            lens=("fixed", 4096), max_seq_len=4096, q_dtype="f32", kv_dtype="f32",
+            page_size=0, chunk_size=1024, phi=3.0, a=20.0, b=8.0),
+    2: dict(workload="mha8x32-L8192-bf16", batch=8, num_q_heads=32, num_kv_heads=32,
+            lens=("fixed", 8192), max_seq_len=8192, q_dtype="bf16", kv_dtype="bf16",
+            page_size=0, chunk_size=512, phi=4.0, a=20.0, b=6.0),
+    3: dict(workload="gqa32x64/8-L1k..32k-bf16", batch=32, num_q_heads=64, num_kv_heads=8,
+            lens=("uniform", 1024, 32768), max_seq_len=32768, q_dtype="bf16", kv_dtype="bf16",
+            page_size=0, chunk_size=1024, phi=4.0, a=20.0, b=6.0),
+    4: dict(workload="mha1x32-L131072-bf16-1pct-fallback", batch=1, num_q_heads=32,
+            num_kv_heads=32, lens=("fixed", 131072), max_seq_len=131072, q_dtype="bf16",
+            kv_dtype="bf16", page_size=0, chunk_size=1024, phi=4.0, a=20.0, b=6.0,
+            perturb_fraction=0.01, perturb_factor=8.0),
+    5: dict(workload="paged16-gqa64x32/8-L512..16k-fp8e4m3", batch=64, num_q_heads=32,
+            num_kv_heads=8, lens=("uniform", 512, 16384), max_seq_len=16384, q_dtype="bf16",
+            kv_dtype="e4m3fn", page_size=16, chunk_size=512, phi=4.0, a=16.0, b=6.0),
+}
+
+_PLAN_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "tests", "golden", "config4_perturbation.txt")
+
+
+@dataclasses.dataclass
+class Problem:
+    """One decode-attention call's inputs, in storage format (host arrays)."""
+    q: np.ndarray                 # [B][Hq][D]; float32 or uint16 (bf16 bits)
+    k_cache: np.ndarray           # contiguous [B][Hkv][Lmax][D] or paged [pages][Hkv][P][D]
+    v_cache: np.ndarray
+    seq_lens: np.ndarray          # int32 [B]
+    block_table: Optional[np.ndarray]  # int32 [B][max_blocks] or None
+    num_kv_heads: int
+    max_seq_len: int
+    page_size: int
+    q_dtype: str                  # "f32" | "bf16"
+    kv_dtype: str                 # "f32" | "bf16" | "e4m3fn"
+    scale: float
+    phi: float
+    a: float
+    b: float
+    chunk_size: int
+    k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (E4M3FN only)
+    v_scale: Optional[np.ndarray] = None
+    workload: str = "custom"
+    perturbed: Optional[np.ndarray] = None  # int32 [n][3] (head, chunk, token), batch 0
+
+    @property
+    def batch(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.q.shape[2]
+
+    def kv_bytes(self) -> int:
+        """Bytes of valid K and V elements (each read once by the method)."""
+        elt = {"f32": 4, "bf16": 2, "e4m3fn": 1}[self.kv_dtype]
+        return int(np.clip(self.seq_lens, 0, self.max_seq_len).astype(np.int64).sum()) \
+            * self.num_kv_heads * self.head_dim * 2 * elt
+
+    def args(self) -> dict:
+        """Keyword arguments shared by the oracle and the library binding."""
+        return dict(q=self.q, k_cache=self.k_cache, v_cache=self.v_cache,
+                    seq_lens=self.seq_lens, block_table=self.block_table,
+                    num_kv_heads=self.num_kv_heads, max_seq_len=self.max_seq_len,
+                    page_size=self.page_size, q_dtype=self.q_dtype,
+                    kv_dtype=self.kv_dtype, scale=self.scale, phi=self.phi,
+                    a=self.a, b=self.b, k_scale=self.k_scale, v_scale=self.v_scale)
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+# ----------------------------------------------------------------------------
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    return ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))))
+            >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def e4m3fn_values() -> np.ndarray:
+    """The 127 finite non-negative OCP E4M3FN values, codes 0x00..0x7E, ascending.
+
+    Used only for encoding: exponent bias 7, 3 mantissa bits, codes with
+    exponent field 0 are subnormal (m * 2^-9), 0x7F is NaN, no infinities.
+    """
+    vals = np.empty(127, dtype=np.float64)
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        vals[c] = m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3_VALS = e4m3fn_values()
+_E4M3_MID = (_E4M3_VALS[:-1] + _E4M3_VALS[1:]) / 2.0   # rounding thresholds
+
+
+def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
+    """float -> E4M3FN codes (uint8): nearest, ties to even code, saturating at 448."""
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.minimum(np.abs(y), 448.0)
+    idx = np.searchsorted(_E4M3_MID, mag, side="left")      # first midpoint >= mag
+    # exactly on a midpoint: searchsorted(left) picked the lower code; ties go to the even one
+    on_mid = (idx < _E4M3_MID.size) & (mag == _E4M3_MID[np.minimum(idx, _E4M3_MID.size - 1)])
+    idx = np.where(on_mid & (idx % 2 == 1), idx + 1, idx)
+    code = idx.astype(np.uint8)
+    sign = np.signbit(y).astype(np.uint8) << np.uint8(7)
+    return code | sign
+
+
+# ----------------------------------------------------------------------------
+# drawing
+# ----------------------------------------------------------------------------
+
+def _rng(seed: int, stream: int, *keys: int) -> np.random.Generator:
+    return np.random.default_rng([seed & 0xFFFFFFFF, stream, *[int(k) for k in keys]])
+
+
+def _draw_kv_rows(seed: int, stream: int, b: int, kvh: int, n: int, d: int) -> np.ndarray:
+    return _rng(seed, stream, b, kvh).standard_normal((n, d), dtype=np.float32)
+
+
+def _draw_lens(spec, batch: int, seed: int) -> np.ndarray:
+    if spec[0] == "fixed":
+        return np.full(batch, spec[1], dtype=np.int32)
+    lo, hi = spec[1], spec[2]
+    return _rng(seed, _S_LENS).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def make_problem(*, batch: int, num_q_heads: int, num_kv_heads: int, seq_lens,
+                 q_dtype: str = "bf16", kv_dtype: str = "bf16", page_size: int = 0,
+                 chunk_size: int = 512, phi: float = 4.0, a: float = 20.0, b: float = 6.0,
+                 max_seq_len: Optional[int] = None, scale: Optional[float] = None,
+                 head_dim: int = HEAD_DIM, seed: int = SEED_BASE, workload: str = "custom",
+                 value_sigma: float = 1.0, extra_pages: int = 0) -> Problem:
+    """Draw one problem.  seq_lens: int or sequence of ints (may include 0)."""
+    if np.isscalar(seq_lens):
+        seq_lens = np.full(batch, int(seq_lens), dtype=np.int32)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (batch,)
+    if max_seq_len is None:
+        max_seq_len = max(1, int(seq_lens.max(initial=0)))
+    if page_size:
+        max_seq_len = -(-max_seq_len // page_size) * page_size
+    assert num_q_heads % num_kv_heads == 0
+    D = head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+
+    # query
+    qf = _rng(seed, _S_Q).standard_normal((batch, num_q_heads, D), dtype=np.float32) * value_sigma
+    q = qf if q_dtype == "f32" else bf16_round(qf)
+
+    # K/V draws per (batch, kv head), only valid tokens
+    lens = np.clip(seq_lens, 0, max_seq_len)
+    jobs = [(b_, h) for b_ in range(batch) for h in range(num_kv_heads)]
+
+    def draw(job, stream):
+        b_, h = job
+        return _draw_kv_rows(seed, stream, b_, h, int(lens[b_]), D) * np.float32(value_sigma)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        kf = list(ex.map(lambda j: draw(j, _S_K), jobs))
+        vf = list(ex.map(lambda j: draw(j, _S_V), jobs))
+
+    k_scale = v_scale = None
+    if kv_dtype == "e4m3fn":
+        k_scale = np.zeros(num_kv_heads, dtype=np.float32)
+        v_scale = np.zeros(num_kv_heads, dtype=np.float32)
+        for h in range(num_kv_heads):
+            mk = max([float(np.abs(kf[i]).max(initial=0.0)) for i, j in enumerate(jobs) if j[1] == h])
+            mv = max([float(np.abs(vf[i]).max(initial=0.0)) for i, j in enumerate(jobs) if j[1] == h])
+            k_scale[h] = np.float32(mk / 448.0) if mk > 0 else np.float32(1.0)
+            v_scale[h] = np.float32(mv / 448.0) if mv > 0 else np.float32(1.0)
+
+    def store(i, arrs, sc):
+        x = arrs[i]
+        if kv_dtype == "f32":
+            return x
+        if kv_dtype == "bf16":
+            return bf16_round(x)
+        return e4m3fn_encode(x / sc[jobs[i][1]])
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        ks = list(ex.map(lambda i: store(i, kf, k_scale), range(len(jobs))))
+        vs = list(ex.map(lambda i: store(i, vf, v_scale), range(len(jobs))))
+    del kf, vf
+
+    sdt = {"f32": np.float32, "bf16": np.uint16, "e4m3fn": np.uint8}[kv_dtype]
+    block_table = None
+    if page_size == 0:
+        k_cache = np.zeros((batch, num_kv_heads, max_seq_len, D), dtype=sdt)
+        v_cache = np.zeros_like(k_cache)
+        for i, (b_, h) in enumerate(jobs):
+            n = int(lens[b_])
+            k_cache[b_, h, :n] = ks[i]
+            v_cache[b_, h, :n] = vs[i]
+    else:
+        P = page_size
+        max_blocks = max_seq_len // P
+        pages_per_seq = [-(-int(n) // P) for n in lens]
+        pool = int(sum(pages_per_seq)) + int(extra_pages)
+        perm = _rng(seed, _S_PERM).permutation(pool).astype(np.int32)
+        block_table = np.full((batch, max(1, max_blocks)), -1, dtype=np.int32)
+        k_cache = np.zeros((max(1, pool), num_kv_heads, P, D), dtype=sdt)
+        v_cache = np.zeros_like(k_cache)
+        nxt = 0
+        for b_ in range(batch):
+            for blk in range(pages_per_seq[b_]):
+                block_table[b_, blk] = perm[nxt]
+                nxt += 1
+        for i, (b_, h) in enumerate(jobs):
+            n = int(lens[b_])
+            for blk in range(pages_per_seq[b_]):
+                t0, t1 = blk * P, min(n, (blk + 1) * P)
+                pg = block_table[b_, blk]
+                k_cache[pg, h, :t1 - t0] = ks[i][t0:t1]
+                v_cache[pg, h, :t1 - t0] = vs[i][t0:t1]
+    return Problem(q=q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens,
+                   block_table=block_table, num_kv_heads=num_kv_heads,
+                   max_seq_len=max_seq_len, page_size=page_size, q_dtype=q_dtype,
+                   kv_dtype=kv_dtype, scale=float(scale), phi=float(phi), a=float(a),
+                   b=float(b), chunk_size=chunk_size, k_scale=k_scale, v_scale=v_scale,
+                   workload=workload)
+
+
+def perturbation_pairs(num_heads: int, num_chunks: int, fraction: float, seed: int) -> np.ndarray:
+    """(head, chunk) pairs, round(fraction * H * C) of them, uniform without replacement."""
+    n = int(round(fraction * num_heads * num_chunks))
+    flat = _rng(seed, _S_PAIRS).choice(num_heads * num_chunks, size=n, replace=False)
+    flat.sort()
+    return np.stack([flat // num_chunks, flat % num_chunks], axis=1).astype(np.int32)
+
+
+def load_perturbation_plan(path: str = _PLAN_FILE) -> np.ndarray:
+    """Rows (head, chunk, token) of the stored config-4 plan (batch 0)."""
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return np.asarray(rows, dtype=np.int32).reshape(-1, 3)
+
+
+def apply_key_scaling(prob: Problem, plan: np.ndarray, factor: float) -> None:
+    """Multiply the listed keys (batch 0) by `factor` in place (exact for a power of two)."""
+    for h, _c, t in plan:
+        row = prob.k_cache[0, h, t]
+        if prob.kv_dtype == "bf16":
+            prob.k_cache[0, h, t] = bf16_round(bf16_to_f32(row) * np.float32(factor))
+        elif prob.kv_dtype == "f32":
+            prob.k_cache[0, h, t] = row * np.float32(factor)
+        else:
+            raise ValueError("key scaling is defined for f32/bf16 caches")
+    prob.perturbed = np.asarray(plan, dtype=np.int32)
+
+
+def make_config(cfg: int, *, batch: Optional[int] = None, length: Optional[int] = None,
+                lens: Optional[tuple] = None, seed: Optional[int] = None,
+                perturb: bool = True) -> Problem:
+    """The numbered workload, optionally shrunk (batch, fixed length or length range)."""
+    c = dict(CONFIGS[cfg])
+    seed = SEED_BASE + cfg if seed is None else seed
+    B = batch or c["batch"]
+    spec = c["lens"]
+    if length is not None:
+        spec = ("fixed", length)
+    elif lens is not None:
+        spec = ("uniform", lens[0], lens[1])
+    seq = _draw_lens(spec, B, seed)
+    max_len = c["max_seq_len"] if (batch is None and length is None and lens is None) else int(
+        spec[1] if spec[0] == "fixed" else spec[2])
+    prob = make_problem(batch=B, num_q_heads=c["num_q_heads"], num_kv_heads=c["num_kv_heads"],
+                        seq_lens=seq, q_dtype=c["q_dtype"], kv_dtype=c["kv_dtype"],
+                        page_size=c["page_size"], chunk_size=c["chunk_size"], phi=c["phi"],
+                        a=c["a"], b=c["b"], max_seq_len=max_len, seed=seed,
+                        workload=c["workload"])
+    if cfg == 4 and perturb and batch is None and length is None:
+        apply_key_scaling(prob, load_perturbation_plan(), c["perturb_factor"])
+    return prob
