@@ -1,0 +1,182 @@
+"""Benchmark: unified-max split-KV decode attention on one MI355X.
+
+A step is one fd_attn_decode call (chunk kernel + fallback pass + merge) over
+the 32K-context grouped-query workload (batch 32, 64 query / 8 KV heads,
+head_dim 128, ragged lengths U{1024..32768}, bf16 cache, chunk 1024), inputs
+resident in HBM.  Prints one JSON line: KV GB/s (valid K and V bytes / time
+per call), calls/s, the chunk kernel's roofline (algorithmic bytes / its
+average duration from HIP events recorded around it on its stream), and the
+float64 CPU oracle timed on a bounded sample as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--config N]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s and % of HBM peak; calls/sec at GQA 32K ctx"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = 3
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "split_kv_asynchronous_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def partial_kernel_bytes(prob) -> int:
+    """Algorithmic bytes the chunk kernel must move: every valid K and V
+    element once, the queries, the lengths and the used block-table entries."""
+    qb = prob.q.nbytes
+    lens = np.clip(prob.seq_lens, 0, prob.max_seq_len).astype(np.int64)
+    extra = prob.seq_lens.nbytes
+    if prob.page_size:
+        extra += int((-(-lens // prob.page_size)).sum()) * 4
+    return prob.kv_bytes() + qb + extra
+
+
+def cpu_baseline(prob, budget_rows=None):
+    """The oracle, untouched, on the first batch entries of the same workload."""
+    import oracle
+    B, Hq = prob.batch, prob.num_q_heads
+    nb = budget_rows or max(1, min(B, 8))
+    rows = np.arange(nb * Hq, dtype=np.int32)
+    t = time.perf_counter()
+    _, _, _, threads = oracle.decode_exact(**prob.args(), rows=rows, with_threads=True)
+    dt = time.perf_counter() - t
+    elt = {"f32": 4, "bf16": 2, "e4m3fn": 1}[prob.kv_dtype]
+    lens = np.clip(prob.seq_lens[:nb], 0, prob.max_seq_len).astype(np.int64)
+    sample_bytes = int(lens.sum()) * prob.num_kv_heads * prob.head_dim * 2 * elt
+    gbs = sample_bytes / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "batch entries 0..%d (all %d query heads, %d tokens), float64, %.1f s; "
+                      "calls/s equivalent %.4f" % (nb - 1, Hq, int(lens.sum()), dt,
+                                                   gbs * 1e9 / prob.kv_bytes())}
+
+
+def load_traffic(workload: str):
+    """HBM bytes per chunk-kernel launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode-attention path is built and timed on a "
+              "single MI355X; multi-GPU runs are not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import split_kv_asynchronous_amd as fd
+    import synthetic
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_device import DeviceProblem
+
+    t_gen = time.perf_counter()
+    prob = synthetic.make_config(args.config)
+    print("generated %s in %.1f s" % (prob.workload, time.perf_counter() - t_gen),
+          file=sys.stderr, flush=True)
+    dp = DeviceProblem(prob)
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+
+    for _ in range(W):
+        dp.run()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back calls; every call records its stage events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for row in evs:            # create the HIP events before the timed region
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        dp.run(stage_events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_call = elapsed / K
+    chunk_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
+    fb_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
+    merge_ms = [evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]
+    call_ms = [evs[i][0].elapsed_time(evs[i][3]) for i in range(K)]
+
+    kv = prob.kv_bytes()
+    value = kv / per_call / 1e9
+    chunk_s = float(np.mean(chunk_ms)) / 1e3
+    achieved = partial_kernel_bytes(prob) / chunk_s / 1e9
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(per_call * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3fn": "fp8e4m3"}[prob.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": prob.workload, "batch": prob.batch,
+                   "num_q_heads": prob.num_q_heads, "num_kv_heads": prob.num_kv_heads,
+                   "head_dim": prob.head_dim, "sum_seq_len": int(prob.seq_lens.sum()),
+                   "max_seq_len": prob.max_seq_len, "chunk_size": prob.chunk_size,
+                   "page_size": prob.page_size, "kv_bytes_per_call": kv,
+                   "phi": prob.phi, "band": [prob.phi - prob.a, prob.phi + prob.b]},
+        "calls_per_s": round(1.0 / per_call, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "stage_ms": {"chunk": round(float(np.mean(chunk_ms)), 5),
+                     "fallback": round(float(np.mean(fb_ms)), 5),
+                     "merge": round(float(np.mean(merge_ms)), 5),
+                     "call_events": round(float(np.mean(call_ms)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(prob.workload),
+                     "kernel": "partial (chunk) kernel",
+                     "bytes_per_launch": partial_kernel_bytes(prob)},
+        "source_hash": source_hash(),
+    }
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(prob)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * fd_attn.h -- C ABI of the unified-max split-KV decode-attention library for
+ * AMD MI355X (gfx950).
+ *
+ * The operation (FlashDecoding++ theory page, sections 1 and 3; the split-KV
+ * figure credited there to the Flash-Decoding post): one decode step of
+ * attention.  For every batch entry b and query head h, a single query vector
+ * q[b][h] is scored against the first seq_lens[b] keys of its KV head
+ * (kvh = h / (Hq / Hkv)), and the output is the softmax-weighted sum of the
+ * matching values:
+ *
+ *     s_t = scale * <q, k_t>             (fp8 caches: k_t = k_scale[kvh] * code)
+ *     out = sum_t exp(s_t - phi) v_t / sum_t exp(s_t - phi)
+ *
+ * The cache is cut into chunks of chunk_size tokens.  Each chunk is reduced on
+ * its own against the caller's constant phi -- no chunk waits for another's
+ * maximum -- and the chunk sums are merged by a plain addition (theory page,
+ * section 3, the unified-max formula).  A (b, h) row in which any score leaves
+ * the safe band [phi - a, phi + b] is reported in fallback_flags and its
+ * out-of-band chunks are recomputed with the ordinary running-max online
+ * softmax, then merged with the usual max rescale (same section, the fallback
+ * rule).  With or without fallback the result equals exact softmax attention
+ * up to fp32 rounding.
+ *
+ * Ownership and threading: every pointer is device memory owned by the
+ * caller.  The library never allocates, frees or synchronises and keeps no
+ * global state; a call only enqueues kernels on `stream` and returns.  out,
+ * fallback_flags and the workspace are valid once the stream has completed
+ * the call.  Calls may run concurrently on different streams as long as each
+ * has its own workspace and outputs.
+ *
+ * Errors: a call returns FD_OK (0) or a negative FD_ERR_* code.  On any
+ * host-detected error nothing is enqueued.  Device-resident data cannot be
+ * checked without a synchronisation: seq_lens[b] is clamped to
+ * [0, max_seq_len]; a block_table entry outside [0, num_pages) that a valid
+ * token needs is undefined behaviour (it addresses memory outside the cache).
+ */
+#ifndef FD_ATTN_H
+#define FD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage formats.  FD_FP8_E4M3FN is the OCP 8-bit float with 4 exponent
+ * bits (bias 7) and 3 mantissa bits, max +-448, no infinities, S.1111.111 =
+ * NaN; a cached value is code * per-KV-head fp32 scale (the symmetric scale of
+ * the quantisation background page). */
+typedef enum {
+    FD_F32 = 0,
+    FD_BF16 = 1,
+    FD_FP8_E4M3FN = 2
+} fd_dtype_t;
+
+enum {
+    FD_OK = 0,
+    FD_ERR_NULL = -1,         /* a required pointer is NULL */
+    FD_ERR_SHAPE = -2,        /* a size is out of range or inconsistent */
+    FD_ERR_DTYPE = -3,        /* unsupported storage format combination */
+    FD_ERR_ALIGN = -4,        /* q, caches or out not 16-byte aligned */
+    FD_ERR_BAND = -5,         /* phi, a or b not finite, a or b outside [0, 64] */
+    FD_ERR_WORKSPACE = -6,    /* workspace NULL, unaligned or smaller than required */
+    FD_ERR_LAUNCH = -7        /* the HIP runtime rejected a launch */
+};
+
+/*
+ * Problem descriptor.  Shapes and layouts (all dense, row-major):
+ *   q               [batch][num_q_heads][head_dim]          q_dtype (F32 or BF16)
+ *   contiguous K/V  [batch][num_kv_heads][max_seq_len][head_dim]       (page_size == 0)
+ *   paged K/V       [num_pages][num_kv_heads][page_size][head_dim]     (page_size  > 0)
+ *                   token t of sequence b is in page block_table[b][t / page_size],
+ *                   slot t % page_size
+ *   block_table     int32 [batch][max_blocks_per_seq]           (paged only)
+ *   seq_lens        int32 [batch]
+ *   out             [batch][num_q_heads][head_dim]          out_dtype (F32 or BF16)
+ *   fallback_flags  uint8 [batch][num_q_heads]: 1 if any score of the row left the band
+ */
+typedef struct {
+    int32_t batch;              /* >= 1 */
+    int32_t num_q_heads;        /* >= 1, a multiple of num_kv_heads */
+    int32_t num_kv_heads;       /* >= 1 */
+    int32_t head_dim;           /* must be 128 */
+    int32_t max_seq_len;        /* >= 1: contiguous capacity; seq_lens are clamped to it */
+    int32_t chunk_size;         /* split size: a multiple of 32 (and of page_size), >= 32 */
+    int32_t page_size;          /* 0 = contiguous; else a power of two in [16, 256] */
+    int32_t max_blocks_per_seq; /* paged: >= ceil(max_seq_len / page_size) */
+    int32_t num_pages;          /* paged: number of pages in the K/V pool (>= 1) */
+    float scale;                /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+    fd_dtype_t q_dtype;         /* FD_F32 or FD_BF16 */
+    fd_dtype_t kv_dtype;        /* FD_F32, FD_BF16 or FD_FP8_E4M3FN */
+    fd_dtype_t out_dtype;       /* FD_F32 or FD_BF16 */
+    const float *k_scale;       /* [num_kv_heads] device fp32, required iff kv_dtype is fp8 */
+    const float *v_scale;       /* [num_kv_heads] device fp32, required iff kv_dtype is fp8 */
+    void *workspace;            /* device, 256-byte aligned, >= fd_attn_workspace_size() bytes */
+    size_t workspace_bytes;
+    /* Optional instrumentation: NULL, or 4 events the call records on `stream`
+     * before the chunk kernel, after it, after the fallback kernel and after
+     * the merge kernel, so a caller can time each stage. */
+    hipEvent_t *stage_events;
+} fd_attn_desc_t;
+
+/* Bytes of workspace a call with this descriptor needs (0 if desc is NULL or
+ * its sizes are invalid).  The workspace holds per-(row, chunk) partial sums;
+ * its first 4 bytes hold, after a call completes, the int32 number of
+ * (row, chunk) pairs that were recomputed with online softmax. */
+size_t fd_attn_workspace_size(const fd_attn_desc_t *desc);
+
+/* One decode-attention call (see the top of this file).  phi is the preset
+ * unified maximum; [phi - a, phi + b] the safe band (closed; a NaN score is
+ * outside it).  Returns FD_OK or an FD_ERR_* code; asynchronous on `stream`. */
+int fd_attn_decode(const fd_attn_desc_t *desc, const void *q, const void *k_cache,
+                   const void *v_cache, const int32_t *seq_lens, const int32_t *block_table,
+                   float phi, float a, float b, void *out, uint8_t *fallback_flags,
+                   hipStream_t stream);
+
+/* Static text for a status code. */
+const char *fd_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_ATTN_H */

@@ -1,0 +1,179 @@
+"""Python binding of the unified-max split-KV decode-attention library (gfx950).
+
+The binding only marshals arguments: torch tensors give the device pointers
+and the current HIP stream, every step of the computation runs in the HIP
+kernels of ``libfd_attn.so`` (declared in ``include/fd_attn.h``).  The
+function names are those of the C ABI.  If the shared library is missing the
+import of the first function raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+__all__ = ["fd_attn_decode", "fd_attn_workspace_size", "fd_attn_status_string", "FdAttnError",
+           "make_desc", "library_path", "FD_F32", "FD_BF16", "FD_FP8_E4M3FN"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfd_attn.so")
+
+FD_F32, FD_BF16, FD_FP8_E4M3FN = 0, 1, 2
+_DTYPE_CODE = {"f32": FD_F32, "bf16": FD_BF16, "e4m3fn": FD_FP8_E4M3FN}
+
+
+class FdAttnError(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__("fd_attn status %d: %s" % (status, msg))
+        self.status = status
+
+
+class FdAttnDesc(ctypes.Structure):
+    """Mirror of fd_attn_desc_t."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stage_events", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libfd_attn.so is not built; run __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        D = ctypes.POINTER(FdAttnDesc)
+        lib.fd_attn_workspace_size.argtypes = [D]
+        lib.fd_attn_workspace_size.restype = ctypes.c_size_t
+        lib.fd_attn_decode.argtypes = [D, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        lib.fd_attn_decode.restype = ctypes.c_int
+        lib.fd_attn_status_string.argtypes = [ctypes.c_int]
+        lib.fd_attn_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def fd_attn_status_string(status: int) -> str:
+    return _load().fd_attn_status_string(int(status)).decode()
+
+
+def make_desc(*, batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+              chunk_size: int, page_size: int = 0, max_blocks_per_seq: int = 0,
+              num_pages: int = 0, scale: Optional[float] = None, q_dtype: str = "bf16",
+              kv_dtype: str = "bf16", out_dtype: str = "f32", head_dim: int = 128,
+              k_scale_ptr: int = 0, v_scale_ptr: int = 0, workspace_ptr: int = 0,
+              workspace_bytes: int = 0, stage_events_ptr: int = 0) -> FdAttnDesc:
+    return FdAttnDesc(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, chunk_size,
+                      page_size, max_blocks_per_seq, num_pages,
+                      -1.0 if scale is None else float(scale), _DTYPE_CODE[q_dtype],
+                      _DTYPE_CODE[kv_dtype], _DTYPE_CODE[out_dtype], k_scale_ptr or None,
+                      v_scale_ptr or None, workspace_ptr or None, workspace_bytes,
+                      stage_events_ptr or None)
+
+
+def fd_attn_workspace_size(desc: FdAttnDesc) -> int:
+    return int(_load().fd_attn_workspace_size(ctypes.byref(desc)))
+
+
+def _torch_code(t) -> str:
+    import torch
+    return {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "e4m3fn",
+            torch.int16: "bf16", torch.uint16: "bf16", torch.uint8: "e4m3fn"}[t.dtype]
+
+
+def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,
+                   out=None, fallback_flags=None, *, chunk_size: int, max_seq_len: int,
+                   num_kv_heads: Optional[int] = None, page_size: int = 0,
+                   scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
+                   q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
+                   out_dtype: str = "f32", stream=None, stage_events: Optional[Sequence] = None):
+    """One decode-attention call on device tensors; returns (out, fallback_flags).
+
+    Tensors must live on the same GPU.  Layouts as in include/fd_attn.h:
+    q [B][Hq][128]; contiguous caches [B][Hkv][max_seq_len][128] or paged
+    caches [pages][Hkv][page_size][128]; seq_lens int32 [B]; block_table
+    int32 [B][max_blocks] (paged) or None.  bf16 data may be passed as
+    torch.bfloat16 or as 16-bit integer bit patterns, E4M3FN as
+    torch.float8_e4m3fn or uint8 codes.  ``workspace`` is a uint8 device
+    tensor of at least fd_attn_workspace_size() bytes (allocated here if None).
+    """
+    import torch
+    dev = q.device
+    B, Hq, D = q.shape
+    qd = q_dtype or _torch_code(q)
+    kd = kv_dtype or _torch_code(k_cache)
+    if num_kv_heads is None:
+        num_kv_heads = k_cache.shape[1]
+    for t in (q, k_cache, v_cache, seq_lens):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on the same device")
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    max_blocks = num_pages = 0
+    if page_size:
+        if block_table is None or block_table.dtype != torch.int32 or not block_table.is_contiguous():
+            raise ValueError("paged caches need a contiguous int32 block_table")
+        max_blocks = block_table.shape[1]
+        num_pages = k_cache.shape[0]
+    ks = vs = 0
+    if kd == "e4m3fn":
+        if k_scale is None or v_scale is None:
+            raise ValueError("fp8 caches need k_scale and v_scale")
+        k_scale = k_scale.contiguous()
+        v_scale = v_scale.contiguous()
+        ks, vs = k_scale.data_ptr(), v_scale.data_ptr()
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
+                          device=dev)
+    if fallback_flags is None:
+        fallback_flags = torch.empty((B, Hq), dtype=torch.uint8, device=dev)
+    desc = make_desc(batch=B, num_q_heads=Hq, num_kv_heads=num_kv_heads, max_seq_len=max_seq_len,
+                     chunk_size=chunk_size, page_size=page_size, max_blocks_per_seq=max_blocks,
+                     num_pages=num_pages, scale=scale, q_dtype=qd, kv_dtype=kd,
+                     out_dtype=out_dtype, head_dim=D, k_scale_ptr=ks, v_scale_ptr=vs)
+    need = fd_attn_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    desc.workspace = workspace.data_ptr()
+    desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    ev_arr = None
+    if stage_events is not None:
+        handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in stage_events]
+        if len(handles) != 4 or not all(handles):
+            raise ValueError("stage_events: 4 created HIP events (record a torch event once "
+                             "to create it)")
+        ev_arr = (ctypes.c_void_p * 4)(*handles)
+        desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _load().fd_attn_decode(ctypes.byref(desc), q.data_ptr(), k_cache.data_ptr(),
+                                v_cache.data_ptr(), seq_lens.data_ptr(),
+                                block_table.data_ptr() if page_size else None, float(phi),
+                                float(a), float(b), out.data_ptr(), fallback_flags.data_ptr(),
+                                stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return out, fallback_flags
+
+
+def default_scale(head_dim: int = 128) -> float:
+    return 1.0 / math.sqrt(head_dim)

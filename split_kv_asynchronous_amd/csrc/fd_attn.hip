@@ -1,0 +1,225 @@
+// Host side of the C ABI declared in include/fd_attn.h: validation, workspace
+// carve-up, kernel choice and launches.  No allocation, no synchronisation.
+#include <math.h>
+#include <string.h>
+
+#include "fd_common.h"
+#include "fd_merge.h"
+#include "fd_mfma.h"
+#include "fd_valu.h"
+
+namespace {
+
+using fd::Params;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+    size_t header, o_part, l_part, m_part, cflag, total;
+};
+
+Layout layout_of(size_t rows, size_t maxch)
+{
+    Layout L;
+    L.header = 0;
+    L.o_part = kAlign;
+    L.l_part = align_up(L.o_part + rows * maxch * fd::kHeadDim * sizeof(float));
+    L.m_part = align_up(L.l_part + rows * maxch * sizeof(float));
+    L.cflag = align_up(L.m_part + rows * maxch * sizeof(float));
+    L.total = align_up(L.cflag + rows * maxch);
+    return L;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by the size query and the call.
+int check_shape(const fd_attn_desc_t *d)
+{
+    if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return FD_ERR_SHAPE;
+    if (d->batch > 65535 || d->num_q_heads > 65535) return FD_ERR_SHAPE;   // grid limits
+    if (d->num_q_heads % d->num_kv_heads) return FD_ERR_SHAPE;
+    if (d->head_dim != fd::kHeadDim) return FD_ERR_SHAPE;
+    if (d->max_seq_len < 1) return FD_ERR_SHAPE;
+    if (d->chunk_size < 32 || d->chunk_size % 32) return FD_ERR_SHAPE;
+    if (d->page_size) {
+        if (!is_pow2(d->page_size) || d->page_size < 16 || d->page_size > 256) return FD_ERR_SHAPE;
+        if (d->chunk_size % d->page_size) return FD_ERR_SHAPE;
+        if (d->num_pages < 1) return FD_ERR_SHAPE;
+        if ((int64_t)d->max_blocks_per_seq * d->page_size < d->max_seq_len) return FD_ERR_SHAPE;
+    }
+    const int64_t maxch = ((int64_t)d->max_seq_len + d->chunk_size - 1) / d->chunk_size;
+    const int64_t slots = (int64_t)d->batch * d->num_q_heads * maxch;
+    if (slots >= ((int64_t)1 << 31) || maxch >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
+    if ((int64_t)d->batch * d->num_q_heads >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
+    return FD_OK;
+}
+
+// Largest divisor of g that is <= 16: the query heads one MFMA workgroup serves.
+int heads_per_block(int g)
+{
+    for (int k = g < 16 ? g : 16; k > 1; --k)
+        if (g % k == 0) return k;
+    return 1;
+}
+
+template <int KV, int QT, bool PAGED>
+void launch_valu(const Params &p, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((fd::partial_valu_kernel<KV, QT, PAGED>), grid, dim3(256), 0, s, p);
+}
+
+template <int KV, int QT, bool PAGED>
+void launch_fallback(const Params &p, int nblk, hipStream_t s)
+{
+    hipLaunchKernelGGL((fd::fallback_kernel<KV, QT, PAGED>), dim3(nblk), dim3(1024), 0, s, p);
+}
+
+template <int KV, bool PAGED>
+void launch_mfma(const Params &p, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((fd::partial_mfma_kernel<KV, PAGED>), grid, dim3(256), 0, s, p);
+}
+
+// Dispatch on (kv dtype, q dtype, paged) for the vector path.
+template <bool FALLBACK>
+void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, int nblk, hipStream_t s)
+{
+#define FD_CASE(KV, QT, PG)                                                   \
+    if (kv == KV && qt == QT && paged == PG) {                                \
+        if (FALLBACK) launch_fallback<KV, QT, PG>(p, nblk, s);                \
+        else launch_valu<KV, QT, PG>(p, grid, s);                             \
+        return;                                                               \
+    }
+    FD_CASE(FD_F32, FD_F32, false) FD_CASE(FD_F32, FD_F32, true)
+    FD_CASE(FD_F32, FD_BF16, false) FD_CASE(FD_F32, FD_BF16, true)
+    FD_CASE(FD_BF16, FD_F32, false) FD_CASE(FD_BF16, FD_F32, true)
+    FD_CASE(FD_BF16, FD_BF16, false) FD_CASE(FD_BF16, FD_BF16, true)
+    FD_CASE(FD_FP8_E4M3FN, FD_F32, false) FD_CASE(FD_FP8_E4M3FN, FD_F32, true)
+    FD_CASE(FD_FP8_E4M3FN, FD_BF16, false) FD_CASE(FD_FP8_E4M3FN, FD_BF16, true)
+#undef FD_CASE
+}
+
+}  // namespace
+
+extern "C" size_t fd_attn_workspace_size(const fd_attn_desc_t *desc)
+{
+    if (!desc || check_shape(desc) != FD_OK) return 0;
+    const size_t maxch = ((size_t)desc->max_seq_len + desc->chunk_size - 1) / desc->chunk_size;
+    return layout_of((size_t)desc->batch * desc->num_q_heads, maxch).total;
+}
+
+extern "C" const char *fd_attn_status_string(int status)
+{
+    switch (status) {
+    case FD_OK: return "ok";
+    case FD_ERR_NULL: return "a required pointer is NULL";
+    case FD_ERR_SHAPE: return "invalid or inconsistent sizes in the descriptor";
+    case FD_ERR_DTYPE: return "unsupported storage format combination";
+    case FD_ERR_ALIGN: return "q, caches and out must be 16-byte aligned";
+    case FD_ERR_BAND: return "phi, a, b must be finite with 0 <= a, b <= 64";
+    case FD_ERR_WORKSPACE: return "workspace missing, unaligned or too small";
+    case FD_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *seq_lens,
+                              const int32_t *block_table, float phi, float a, float b, void *out,
+                              uint8_t *fallback_flags, hipStream_t stream)
+{
+    if (!d || !q || !k_cache || !v_cache || !seq_lens || !out || !fallback_flags) return FD_ERR_NULL;
+    int rc = check_shape(d);
+    if (rc != FD_OK) return rc;
+    if (d->page_size && !block_table) return FD_ERR_NULL;
+    const int qt = d->q_dtype, kv = d->kv_dtype, ot = d->out_dtype;
+    if (qt != FD_F32 && qt != FD_BF16) return FD_ERR_DTYPE;
+    if (kv != FD_F32 && kv != FD_BF16 && kv != FD_FP8_E4M3FN) return FD_ERR_DTYPE;
+    if (ot != FD_F32 && ot != FD_BF16) return FD_ERR_DTYPE;
+    if (kv == FD_FP8_E4M3FN && (!d->k_scale || !d->v_scale)) return FD_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return FD_ERR_ALIGN;
+    if (!isfinite(phi) || !isfinite(a) || !isfinite(b) || a < 0.f || b < 0.f || a > 64.f ||
+        b > 64.f)
+        return FD_ERR_BAND;
+    if (!isfinite(d->scale)) return FD_ERR_SHAPE;
+    const size_t need = fd_attn_workspace_size(d);
+    if (!d->workspace || ((uintptr_t)d->workspace & (kAlign - 1)) || d->workspace_bytes < need)
+        return FD_ERR_WORKSPACE;
+
+    const int maxch = (d->max_seq_len + d->chunk_size - 1) / d->chunk_size;
+    const size_t rows = (size_t)d->batch * d->num_q_heads;
+    const Layout L = layout_of(rows, (size_t)maxch);
+    uint8_t *ws = static_cast<uint8_t *>(d->workspace);
+
+    Params p;
+    memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.seq_lens = seq_lens;
+    p.block_table = block_table;
+    p.k_scale = kv == FD_FP8_E4M3FN ? d->k_scale : nullptr;
+    p.v_scale = kv == FD_FP8_E4M3FN ? d->v_scale : nullptr;
+    p.out = out;
+    p.flags = fallback_flags;
+    p.counter = reinterpret_cast<int32_t *>(ws + L.header);
+    p.o_part = reinterpret_cast<float *>(ws + L.o_part);
+    p.l_part = reinterpret_cast<float *>(ws + L.l_part);
+    p.m_part = reinterpret_cast<float *>(ws + L.m_part);
+    p.cflag = ws + L.cflag;
+    p.batch = d->batch;
+    p.hq = d->num_q_heads;
+    p.hkv = d->num_kv_heads;
+    p.group = d->num_q_heads / d->num_kv_heads;
+    p.max_seq_len = d->max_seq_len;
+    p.chunk = d->chunk_size;
+    p.maxch = maxch;
+    p.page_shift = 0;
+    if (d->page_size)
+        while ((1 << p.page_shift) < d->page_size) ++p.page_shift;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)fd::kHeadDim);
+    p.phi = phi;
+    p.lo = (float)((double)phi - (double)a);
+    p.hi = (float)((double)phi + (double)b);
+    p.out_bf16 = ot == FD_BF16;
+
+    const bool paged = d->page_size != 0;
+    const bool use_mfma = p.group > 1 && qt == FD_BF16 && kv != FD_F32;
+    hipEvent_t *ev = d->stage_events;
+
+    (void)hipGetLastError();   // clear a stale error so the checks below see only ours
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    if (use_mfma) {
+        p.heads_per_block = heads_per_block(p.group);
+        const dim3 grid(maxch, p.hq / p.heads_per_block, p.batch);
+        if (kv == FD_BF16) {
+            if (paged) launch_mfma<FD_BF16, true>(p, grid, stream);
+            else launch_mfma<FD_BF16, false>(p, grid, stream);
+        } else {
+            if (paged) launch_mfma<FD_FP8_E4M3FN, true>(p, grid, stream);
+            else launch_mfma<FD_FP8_E4M3FN, false>(p, grid, stream);
+        }
+    } else {
+        p.heads_per_block = 1;
+        dispatch_valu<false>(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), 0, stream);
+    }
+    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    if (ev) (void)hipEventRecord(ev[1], stream);
+
+    const int total = (int)(rows * maxch);
+    const int nfb = total < 1024 ? total : 1024;
+    dispatch_valu<true>(p, kv, qt, paged, dim3(1), nfb, stream);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    if (ev) (void)hipEventRecord(ev[2], stream);
+
+    hipLaunchKernelGGL(fd::merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    if (ev) (void)hipEventRecord(ev[3], stream);
+    return FD_OK;
+}

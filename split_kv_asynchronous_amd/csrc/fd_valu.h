@@ -1,0 +1,211 @@
+// Vector-ALU chunk reduction: one query head against one chunk of its KV head.
+//
+// Used for single-query-per-KV-head attention (MHA), for fp32 caches or
+// queries, and -- in online mode -- for the fallback recompute of chunks whose
+// scores left the safe band.
+//
+// Lane mapping: a wavefront splits into four 16-lane rows; each row owns one
+// token at a time and each of its lanes owns 8 of the 128 components, so one
+// load instruction reads 4 whole consecutive tokens (1 KiB of bf16).  The
+// 16-lane dot product is finished with four DPP adds.
+#pragma once
+
+#include "fd_common.h"
+
+namespace fd {
+
+// Reduce tokens [t_begin, t_end) of row (b, h).
+//  ONLINE == false: unified maximum -- p = exp(s - phi), no maximum search
+//                   (FlashDecoding++ theory page, section 3, second formula);
+//                   writes o, l, m = phi and the chunk's band flag.
+//  ONLINE == true : ordinary online softmax with a running maximum (same
+//                   section, first formula, used by the fallback rule);
+//                   writes o, l and the chunk maximum m.
+// NW = wavefronts in the workgroup; `red` is LDS of at least NW * 132 floats.
+template <int KV, int QT, bool PAGED, bool ONLINE, int NW>
+FD_DEV void valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_end, float *red)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = lane >> 4;     // token slot inside the wavefront
+    const int sub = lane & 15;     // owns components 8*sub .. 8*sub+7
+    const int kvh = h / p.group;
+    const size_t qrow = ((size_t)b * p.hq + h) * kHeadDim;
+
+    float q[8];
+    load8<QT>(p.q, qrow + 8 * sub, q);
+    float sc = p.scale;
+    if constexpr (KV == FD_FP8_E4M3FN) sc *= p.k_scale[kvh];
+
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = 0.f;
+    float l = 0.f;
+    float m = ONLINE ? -INFINITY : p.phi;
+    bool bad = false;
+
+    constexpr int U = 4;                       // tokens per row per step
+    constexpr int STEP = NW * 4 * U;           // tokens per workgroup step
+    for (int base = t_begin; base < t_end; base += STEP) {
+        float kx[U][8], vx[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = base + (wave * U + u) * 4 + row;
+            const int tl = t < t_end ? t : t_end - 1;    // stay inside the sequence
+            const size_t off = kv_offset<PAGED>(p, b, kvh, tl) + 8 * sub;
+            load8<KV>(p.k, off, kx[u]);
+            load8<KV>(p.v, off, vx[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = base + (wave * U + u) * 4 + row;
+            const bool valid = t < t_end;
+            float part = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part = fmaf(q[j], kx[u][j], part);
+            const float s = row16_sum(part) * sc;
+            if constexpr (!ONLINE) {
+                bad |= valid && outside_band(s, p.lo, p.hi);
+                const float w = valid ? exp2_hw((s - p.phi) * kLog2e) : 0.f;
+                l += w;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = fmaf(w, vx[u][j], o[j]);
+            } else if (valid) {
+                const float m_new = fmaxf(m, s);
+                const float r = (m == m_new) ? 1.f : exp2_hw((m - m_new) * kLog2e);
+                const float w = (s == -INFINITY) ? 0.f : exp2_hw((s - m_new) * kLog2e);
+                l = fmaf(l, r, w);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = fmaf(o[j], r, w * vx[u][j]);
+                m = m_new;
+            }
+        }
+    }
+
+    // combine the four rows of the wavefront (lanes sub, sub+16, sub+32, sub+48)
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+        const float l2 = __shfl_xor(l, x);
+        if constexpr (ONLINE) {
+            const float m2 = __shfl_xor(m, x);
+            const float mm = fmaxf(m, m2);
+            const float r1 = (m == mm) ? 1.f : exp2_hw((m - mm) * kLog2e);
+            const float r2 = (m2 == mm) ? 1.f : exp2_hw((m2 - mm) * kLog2e);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = o[j] * r1 + __shfl_xor(o[j], x) * r2;
+            l = l * r1 + l2 * r2;
+            m = mm;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] += __shfl_xor(o[j], x);
+            l += l2;
+        }
+    }
+    const bool wave_bad = __any(bad);
+
+    // combine the wavefronts through LDS: red[w][0..127] = o, [128] = l, [129] = m, [130] = bad
+    if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[wave * 132 + 8 * sub + j] = o[j];
+    }
+    if (lane == 0) {
+        red[wave * 132 + 128] = l;
+        red[wave * 132 + 129] = m;
+        red[wave * 132 + 130] = wave_bad ? 1.f : 0.f;
+    }
+    __syncthreads();
+    const size_t slot = ((size_t)b * p.hq + h) * p.maxch + c;
+    float M = p.phi;
+    if constexpr (ONLINE) {
+        M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w * 132 + 129]);
+    }
+    if (threadIdx.x < kHeadDim) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            float f = 1.f;
+            if constexpr (ONLINE) {
+                const float mw = red[w * 132 + 129];
+                f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
+            }
+            acc += red[w * 132 + threadIdx.x] * f;
+        }
+        p.o_part[slot * kHeadDim + threadIdx.x] = acc;
+    }
+    if (threadIdx.x == 0) {
+        float lsum = 0.f;
+        bool any = false;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            float f = 1.f;
+            if constexpr (ONLINE) {
+                const float mw = red[w * 132 + 129];
+                f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
+            }
+            lsum += red[w * 132 + 128] * f;
+            any |= red[w * 132 + 130] != 0.f;
+        }
+        p.l_part[slot] = lsum;
+        p.m_part[slot] = M;
+        if constexpr (!ONLINE) p.cflag[slot] = any ? 1 : 0;
+    }
+    __syncthreads();   // `red` is reused by the caller
+}
+
+// Grid (maxch, Hq, B): one workgroup per (chunk, query head, sequence).
+template <int KV, int QT, bool PAGED>
+__global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
+{
+    __shared__ float red[4 * 132];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.counter = 0;
+    const int L = seq_len_of(p, b);
+    const int t0 = c * p.chunk;
+    if (t0 >= L) return;
+    valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, min(t0 + p.chunk, L), red);
+}
+
+// Fallback: every workgroup scans a strided share of the (row, chunk) flags
+// written by the chunk kernel, lists the flagged ones in LDS and recomputes
+// each with online softmax (FlashDecoding++ theory page, section 3: a block
+// whose score passes the unified-max criterion stops its asynchronous result
+// and is recomputed safely).  Grid: any size; every workgroup exits after its
+// share, so an empty flag set costs one scan.
+template <int KV, int QT, bool PAGED>
+__global__ __launch_bounds__(1024) void fallback_kernel(Params p)
+{
+    constexpr int NW = 16;
+    __shared__ float red[NW * 132];
+    __shared__ int list[1024];
+    __shared__ int count;
+    const int total = p.batch * p.hq * p.maxch;
+    const int nblk = gridDim.x;
+    int done = 0;
+    for (int base = 0; base + (int)blockIdx.x < total; base += 1024 * nblk) {
+        if (threadIdx.x == 0) count = 0;
+        __syncthreads();
+        const long e = (long)base + (long)threadIdx.x * nblk + blockIdx.x;
+        if (e < total) {
+            const int row = (int)(e / p.maxch), c = (int)(e % p.maxch);
+            const int b = row / p.hq;
+            if (c * p.chunk < seq_len_of(p, b) && p.cflag[e]) list[atomicAdd(&count, 1)] = (int)e;
+        }
+        __syncthreads();
+        const int n = count;
+        for (int i = 0; i < n; ++i) {
+            const int e2 = list[i];
+            const int row = e2 / p.maxch, c = e2 % p.maxch;
+            const int b = row / p.hq, h = row % p.hq;
+            const int L = seq_len_of(p, b);
+            const int t0 = c * p.chunk;
+            valu_chunk<KV, QT, PAGED, true, NW>(p, b, h, c, t0, min(t0 + p.chunk, L), red);
+        }
+        done += n;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0 && done) atomicAdd(p.counter, done);
+}
+
+}  // namespace fd

@@ -1,0 +1,103 @@
+"""The C-ABI library: it loads, exports every function include/fd_attn.h
+declares, sizes workspaces and rejects invalid calls before touching the GPU.
+No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import split_kv_asynchronous_amd as fd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "fd_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_attn_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert names == ["fd_attn_decode", "fd_attn_status_string", "fd_attn_workspace_size"]
+    lib = ctypes.CDLL(fd.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _desc(**kw):
+    base = dict(batch=32, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, chunk_size=1024)
+    base.update(kw)
+    return fd.make_desc(**base)
+
+
+def test_workspace_size_formula():
+    d = _desc()
+    rows, maxch = 32 * 64, 32
+    slots = rows * maxch
+    n = fd.fd_attn_workspace_size(d)
+    assert n >= 256 + slots * (128 * 4 + 4 + 4 + 1)
+    assert n < 256 + slots * (128 * 4 + 4 + 4 + 1) + 4 * 256
+    assert n % 256 == 0
+    assert fd.fd_attn_workspace_size(_desc(head_dim=64)) == 0
+    assert fd.fd_attn_workspace_size(_desc(chunk_size=48)) == 0
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        assert fd.fd_attn_status_string(code) not in ("", "unknown status")
+    assert fd.fd_attn_status_string(5) == "unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def _call(desc, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, bt=None, phi=4.0, a=20.0, b=6.0, out=FAKE,
+          flags=FAKE):
+    lib = fd._load()
+    return lib.fd_attn_decode(ctypes.byref(desc), q, k, v, lens, bt, phi, a, b, out, flags, None)
+
+
+def _valid_desc(**kw):
+    d = _desc(**kw)
+    d.workspace = 0x100000
+    d.workspace_bytes = 1 << 40
+    return d
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=63), -2), (dict(head_dim=64), -2), (dict(chunk_size=16), -2),
+    (dict(chunk_size=100), -2), (dict(max_seq_len=0), -2), (dict(batch=0), -2),
+    (dict(page_size=24, max_blocks_per_seq=2048, num_pages=10), -2),
+    (dict(page_size=16, max_blocks_per_seq=10, num_pages=10), -2),
+    (dict(page_size=64, chunk_size=32, max_blocks_per_seq=1024, num_pages=10), -2),
+])
+def test_bad_shapes(kw, code):
+    assert _call(_valid_desc(**kw)) == code
+
+
+def test_bad_pointers_dtypes_alignment_band_workspace():
+    assert _call(_valid_desc(), q=None) == -1
+    assert _call(_valid_desc(page_size=16, max_blocks_per_seq=2048, num_pages=5)) == -1
+    assert _call(_valid_desc(kv_dtype="e4m3fn")) == -1          # no scales
+    d = _valid_desc()
+    d.q_dtype = 2
+    assert _call(d) == -3
+    d = _valid_desc()
+    d.out_dtype = 7
+    assert _call(d) == -3
+    assert _call(_valid_desc(), k=FAKE + 4) == -4
+    assert _call(_valid_desc(), phi=float("nan")) == -5
+    assert _call(_valid_desc(), a=-1.0) == -5
+    assert _call(_valid_desc(), b=65.0) == -5
+    assert _call(_valid_desc(), b=float("inf")) == -5
+    d = _valid_desc()
+    d.workspace_bytes = 1000
+    assert _call(d) == -6
+    d = _valid_desc()
+    d.workspace = 0x100010
+    assert _call(d) == -6
+    d = _valid_desc()
+    d.scale = float("inf")
+    assert _call(d) == -2

@@ -1,0 +1,165 @@
+"""GPU parity: the HIP library against the float64 oracle, through the C ABI.
+
+Bar: flags bit-exact; max|gpu - oracle| <= tol * max|oracle| with tol = 2e-3
+for bf16/fp8 caches and 1e-5 for fp32 caches (float64 oracle, fp32 GPU
+accumulation).  Inputs keep every score at least 1e-3 from both band edges
+(checked by the oracle), so the flag decision does not depend on precision.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import DeviceProblem, compare
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (config, shrink) -- several chunks, ragged tails, every code path
+    (1, dict(length=1000)),
+    (2, dict(batch=2, length=3000)),
+    (3, dict(batch=3, lens=(1, 5000))),
+    (4, dict(length=9000)),
+    (5, dict(batch=5, lens=(1, 3000))),
+]
+
+
+@pytest.mark.parametrize("cfg,kw", SMALL, ids=["cfg%d" % c for c, _ in SMALL])
+def test_small_configs(cfg, kw):
+    prob = synthetic.make_config(cfg, **kw)
+    print("case cfg%d %s lens=%s" % (cfg, kw, prob.seq_lens.tolist()), flush=True)
+    dp = DeviceProblem(prob)
+    dp.run()
+    out, flags = dp.results()
+    rel, _, _ = compare(prob, out, flags)
+    print("rel err %.3e" % rel)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_configs(cfg):
+    print("case full cfg%d" % cfg, flush=True)
+    prob = synthetic.make_config(cfg)
+    dp = DeviceProblem(prob)
+    dp.run()
+    out, flags = dp.results()
+    rel, ref_out, ref_flags = compare(prob, out, flags)
+    if cfg == 4:
+        heads = sorted(set(int(h) for h in prob.perturbed[:, 0]))
+        assert np.nonzero(flags)[0].tolist() == heads
+        assert dp.recomputed() == len(prob.perturbed) == 41
+    else:
+        assert flags.sum() == 0 and dp.recomputed() == 0
+    # a second call gives the same bits
+    out1 = dp.out.clone()
+    dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, dp.out)
+    print("cfg%d rel err %.3e flagged %d" % (cfg, rel, int(flags.sum())))
+
+
+GQA_CASES = [
+    # group, kv dtype, page size, chunk, lens
+    (2, "bf16", 0, 64, [1, 31, 32, 33, 200]),
+    (4, "bf16", 16, 128, [17, 500, 1023]),
+    (6, "bf16", 0, 96, [700, 95]),
+    (8, "e4m3fn", 0, 256, [1000, 1, 257]),
+    (16, "bf16", 32, 64, [300, 129]),
+    (32, "e4m3fn", 64, 128, [640, 1]),
+    (4, "f32", 0, 64, [333, 64]),
+]
+
+
+@pytest.mark.parametrize("g,kv,page,chunk,lens", GQA_CASES)
+def test_group_sizes_layouts_dtypes(g, kv, page, chunk, lens):
+    print("case g=%d kv=%s page=%d chunk=%d lens=%s" % (g, kv, page, chunk, lens), flush=True)
+    hkv = 2
+    prob = synthetic.make_problem(batch=len(lens), num_q_heads=g * hkv, num_kv_heads=hkv,
+                                  seq_lens=lens, kv_dtype=kv, q_dtype="bf16", page_size=page,
+                                  chunk_size=chunk, seed=100 + g)
+    dp = DeviceProblem(prob)
+    dp.run()
+    compare(prob, *dp.results())
+
+
+def test_fp32_query_with_bf16_cache_and_bf16_output():
+    prob = synthetic.make_problem(batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=[900, 77],
+                                  q_dtype="f32", kv_dtype="bf16", chunk_size=128, seed=7)
+    dp = DeviceProblem(prob, out_dtype="bf16")
+    dp.run()
+    out, flags = dp.results()
+    compare(prob, out, flags, tol=6e-3)   # bf16 output adds up to 2^-9 relative rounding
+
+
+def test_zero_and_clamped_lengths():
+    prob = synthetic.make_problem(batch=4, num_q_heads=8, num_kv_heads=2, seq_lens=[0, 5, 64, 300],
+                                  chunk_size=64, max_seq_len=300, seed=8)
+    prob.seq_lens = np.array([0, 5, 64, 999], dtype=np.int32)   # 999 is clamped to 300
+    dp = DeviceProblem(prob)
+    dp.run()
+    out, flags = dp.results()
+    assert np.all(out[:8] == 0) and np.all(flags[:8] == 0)
+    compare(prob, out, flags)
+
+
+@pytest.mark.parametrize("g,kv,page", [(1, "bf16", 0), (8, "bf16", 0), (4, "e4m3fn", 16),
+                                       (1, "f32", 0), (1, "e4m3fn", 16)])
+def test_out_of_band_rows_fall_back(g, kv, page):
+    hkv = 2
+    prob = synthetic.make_problem(batch=3, num_q_heads=g * hkv, num_kv_heads=hkv,
+                                  seq_lens=[2000, 700, 1500], kv_dtype=kv, page_size=page,
+                                  chunk_size=256, seed=30 + g, phi=1.0, a=3.0, b=1.5)
+    print("case fallback g=%d kv=%s page=%d" % (g, kv, page), flush=True)
+    # narrow band [-2, 2.5]: many scores leave it, so most rows are recomputed in part
+    ref_out, ref_flags, margin = oracle.decode_exact(**prob.args())
+    assert ref_flags.sum() > 0
+    dp = DeviceProblem(prob)
+    dp.run()
+    out, flags = dp.results()
+    # a row with a score within 1e-3 of an edge may take either path; its output
+    # is the exact softmax either way, only its flag is left unchecked
+    sure = margin >= 1e-3
+    assert sure.any()
+    np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+    compare(prob, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
+    assert dp.recomputed() > 0
+
+
+def test_nan_query_row_is_flagged_and_nan():
+    prob = synthetic.make_problem(batch=2, num_q_heads=4, num_kv_heads=1, seq_lens=[300, 300],
+                                  chunk_size=64, seed=9)
+    prob.q[1, 2, 5] = 0x7FC0    # bf16 NaN
+    dp = DeviceProblem(prob)
+    dp.run()
+    out, flags = dp.results()
+    assert flags.tolist() == [0, 0, 0, 0, 0, 0, 1, 0]
+    assert np.isnan(out[6]).all() and np.isfinite(np.delete(out, 6, axis=0)).all()
+    compare(prob, out, flags)
+
+
+def test_paged_equals_contiguous_bitwise():
+    lens = [1, 16, 17, 999]
+    pg = synthetic.make_problem(batch=4, num_q_heads=16, num_kv_heads=4, seq_lens=lens,
+                                kv_dtype="bf16", page_size=16, chunk_size=64, seed=12,
+                                max_seq_len=1008)
+    ct = synthetic.make_problem(batch=4, num_q_heads=16, num_kv_heads=4, seq_lens=lens,
+                                kv_dtype="bf16", chunk_size=64, seed=12, max_seq_len=1008)
+    np.testing.assert_array_equal(ct.q, pg.q)
+    outs = []
+    for p in (pg, ct):
+        dp = DeviceProblem(p)
+        dp.run()
+        outs.append(dp.results())
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_chunk_size_and_phi_do_not_change_the_result():
+    base = synthetic.make_config(3, batch=2, lens=(3000, 9000))
+    ref_out, ref_flags, _ = oracle.decode_exact(**base.args())
+    for chunk in (32, 256, 2048):
+        for phi in (0.0, 4.0, 7.0):
+            base.chunk_size = chunk
+            dp = DeviceProblem(base)
+            dp.run(phi=phi)
+            compare(base, *dp.results(), ref=(ref_out, ref_flags))
