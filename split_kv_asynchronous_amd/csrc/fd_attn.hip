@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include "fd_chunk.h"
 #include "fd_common.h"
 #include "fd_merge.h"
 #include "fd_mfma.h"
@@ -43,7 +44,7 @@ int check_shape(const fd_attn_desc_t *d)
     if (d->batch > 65535 || d->num_q_heads > 65535) return FD_ERR_SHAPE;   // grid limits
     if (d->num_q_heads % d->num_kv_heads) return FD_ERR_SHAPE;
     if (d->head_dim != fd::kHeadDim) return FD_ERR_SHAPE;
-    if (d->max_seq_len < 1) return FD_ERR_SHAPE;
+    if (d->max_seq_len < 1 || d->max_seq_len > (1 << 24)) return FD_ERR_SHAPE;
     if (d->chunk_size < 32 || d->chunk_size % 32) return FD_ERR_SHAPE;
     if (d->page_size) {
         if (!is_pow2(d->page_size) || d->page_size < 16 || d->page_size > 256) return FD_ERR_SHAPE;
@@ -199,8 +200,10 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
         p.heads_per_block = heads_per_block(p.group);
         const dim3 grid(maxch, p.hq / p.heads_per_block, p.batch);
         if (kv == FD_BF16) {
-            if (paged) launch_mfma<FD_BF16, true>(p, grid, stream);
-            else launch_mfma<FD_BF16, false>(p, grid, stream);
+            // one workgroup per unit; workgroups past the real units exit at once
+            const dim3 flat((unsigned)((size_t)maxch * (p.hq / p.heads_per_block) * p.batch));
+            if (paged) hipLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<true>, flat, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<false>, flat, dim3(256), 0, stream, p);
         } else {
             if (paged) launch_mfma<FD_FP8_E4M3FN, true>(p, grid, stream);
             else launch_mfma<FD_FP8_E4M3FN, false>(p, grid, stream);

@@ -42,9 +42,17 @@ struct Params {
     int out_bf16;
 };
 
+// Read-only tables (lengths, block table, scales) are read through the
+// constant address space: a wave-uniform index then becomes a scalar load.
+template <typename T>
+FD_DEV const __attribute__((address_space(4))) T *as_const(const T *ptr)
+{
+    return (const __attribute__((address_space(4))) T *)(ptr);
+}
+
 FD_DEV int seq_len_of(const Params &p, int b)
 {
-    int L = p.seq_lens[b];
+    int L = as_const(p.seq_lens)[b];
     return L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
 }
 

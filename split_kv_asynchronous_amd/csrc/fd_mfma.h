@@ -48,15 +48,25 @@ FD_DEV u32x4 fp8x8_to_bf16x8(u32x2 w)
     return r;
 }
 
-// Eight consecutive cache elements as 8 packed bf16.
+// Raw storage of 8 consecutive cache elements (converted to bf16 only when used,
+// so a prefetched block stays in flight until its compute step).
+template <int KV> struct Raw8 { typedef u32x4 type; };
+template <> struct Raw8<FD_FP8_E4M3FN> { typedef u32x2 type; };
+
 template <int KV>
-FD_DEV u32x4 load8_bf16(const void *base, size_t off)
+FD_DEV typename Raw8<KV>::type load_raw8(const void *base, size_t off)
 {
-    if constexpr (KV == FD_BF16) {
+    if constexpr (KV == FD_BF16)
         return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + off);
-    } else {
-        return fp8x8_to_bf16x8(*reinterpret_cast<const u32x2 *>(static_cast<const uint8_t *>(base) + off));
-    }
+    else
+        return *reinterpret_cast<const u32x2 *>(static_cast<const uint8_t *>(base) + off);
+}
+
+template <int KV>
+FD_DEV u32x4 as_bf16x8(typename Raw8<KV>::type r)
+{
+    if constexpr (KV == FD_BF16) return r;
+    else return fp8x8_to_bf16x8(r);
 }
 
 // Two floats -> packed bf16 pair, truncated (high) and the rounded remainder (low).
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void partial_mfma_kernel(Params p)
     const int t_end = min(t_begin + p.chunk, L);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int n = lane & 15;        // head column (B/C operands), token row (A operand)
     const int g4 = lane >> 4;       // lane group: k-slice 8*g4 .. 8*g4+7
     const int GB = p.heads_per_block;
@@ -106,45 +116,103 @@ __global__ __launch_bounds__(256, 2) void partial_mfma_kernel(Params p)
                                                       8 * g4 + 32 * kk);
     }
     float sc = p.scale;
-    if constexpr (KV == FD_FP8_E4M3FN) sc *= p.k_scale[kvh];
+    if constexpr (KV == FD_FP8_E4M3FN) sc *= as_const(p.k_scale)[kvh];
     const float nphi = -p.phi * kLog2e;
 
     f32x4 o[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
-    bool bad = false;
+    int bad = 0;
 
     uint8_t *vbuf = lds + wave * kVBufBytes;
     const int nblk = (t_end - t_begin + 31) >> 5;
-    for (int j = wave; j < nblk; j += kMfmaWaves) {
+
+    // Addressing.  A cache row (one token of one KV head) is ROW bytes; every
+    // load below is a wave-uniform base plus a per-lane 32-bit offset that is
+    // the same for every block.
+    constexpr int ELT = Elem<KV>::bytes;
+    constexpr int ROW = kHeadDim * ELT;
+    const uint32_t koff = n * ROW + 8 * g4 * ELT;      // K: token row n, k-slice g4
+    const uint32_t voff = g4 * ROW + 8 * n * ELT;      // V: token g4 of 4, components 8n..
+    // contiguous: raw buffer resources over this (b, kvh) stream, L rows long,
+    // so rows past the sequence read as zero and nothing is clamped
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    const uint8_t *kpool = static_cast<const uint8_t *>(p.k);
+    const uint8_t *vpool = static_cast<const uint8_t *>(p.v);
+    const __attribute__((address_space(4))) int32_t *btab = as_const(p.block_table);
+    if constexpr (!PAGED) {
+        const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * ROW;
+        krs = __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + slice), (short)0, (int)((uint32_t)L * ROW), 0x00020000);
+        vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + slice), (short)0, (int)((uint32_t)L * ROW), 0x00020000);
+    } else {
+        btab += (size_t)b * p.max_blocks;
+    }
+    const int last_page = (L - 1) >> p.page_shift;
+    const int pmask = (1 << p.page_shift) - 1;
+    // byte offset of (page holding token t, slot of t) in the paged pool; the
+    // page index is clamped to the last valid page, whose every slot is mapped
+    auto page_row = [&](int t) -> size_t {
+        int idx = t >> p.page_shift;
+        idx = idx < last_page ? idx : last_page;
+        const size_t page = (size_t)btab[idx];
+        return ((page * p.hkv + kvh) * (size_t)(pmask + 1) + (t & pmask)) * ROW;
+    };
+
+    // One 32-token block of K (A-operand layout) and V (natural rows).
+    struct Block {
+        typename Raw8<KV>::type k[2][4];
+        typename Raw8<KV>::type v[8];
+    };
+    auto load_block = [&](Block &blk, int j) {
         const int t0 = t_begin + 32 * j;
-        // K fragments: tile tau, k-step kk; token t0 + 16*tau + n
-        u32x4 kf[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            int t = t0 + 16 * tau + n;
-            t = t < t_end ? t : t_end - 1;
-            const size_t off = kv_offset<PAGED>(p, b, kvh, t) + 8 * g4;
+            const int tb = t0 + 16 * tau;
+            if constexpr (PAGED) {
+                const uint8_t *base = kpool + page_row(tb);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kf[tau][kk] = load8_bf16<KV>(p.k, off + 32 * kk);
+                for (int kk = 0; kk < 4; ++kk)
+                    blk.k[tau][kk] = *reinterpret_cast<const typename Raw8<KV>::type *>(
+                        base + koff + 32 * kk * ELT);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    if constexpr (KV == FD_BF16)
+                        blk.k[tau][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                            krs, koff + 32 * kk * ELT, (int)((uint32_t)tb * ROW), 0));
+                    else
+                        blk.k[tau][kk] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                            krs, koff + 32 * kk * ELT, (int)((uint32_t)tb * ROW), 0));
+                }
+            }
         }
-        // V rows: instruction i covers tokens t0 + 4i .. t0 + 4i + 3; lane (n, g4)
-        // takes token t0 + 4i + g4, components 8n .. 8n+7
-        u32x4 vr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            int t = t0 + 4 * i + g4;
-            t = t < t_end ? t : t_end - 1;
-            vr[i] = load8_bf16<KV>(p.v, kv_offset<PAGED>(p, b, kvh, t) + 8 * n);
+            const int tb = t0 + 4 * i;
+            if constexpr (PAGED) {
+                blk.v[i] = *reinterpret_cast<const typename Raw8<KV>::type *>(
+                    vpool + page_row(tb) + voff);
+            } else {
+                if constexpr (KV == FD_BF16)
+                    blk.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        vrs, voff, (int)((uint32_t)tb * ROW), 0));
+                else
+                    blk.v[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                        vrs, voff, (int)((uint32_t)tb * ROW), 0));
+            }
         }
+    };
+    auto compute_block = [&](const Block &blk, int j) {
+        const int t0 = t_begin + 32 * j;
         // S^T tiles: lane (n, g4) gets tokens 16*tau + 4*g4 + r, head n
         f32x4 s[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             s[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) s[tau] = mfma_bf16(kf[tau][kk], qf[kk], s[tau]);
+            for (int kk = 0; kk < 4; ++kk)
+                s[tau] = mfma_bf16(as_bf16x8<KV>(blk.k[tau][kk]), qf[kk], s[tau]);
         }
         // band test and unified-max weights
         float w[2][4];
@@ -155,10 +223,10 @@ __global__ __launch_bounds__(256, 2) void partial_mfma_kernel(Params p)
                 const int t = t0 + 16 * tau + 4 * g4 + r;
                 const bool valid = t < t_end;
                 const float sv = s[tau][r] * sc;
-                bad |= valid && head_ok && outside_band(sv, p.lo, p.hi);
-                const float e = valid ? exp2_hw(fmaf(sv, kLog2e, nphi)) : 0.f;
-                w[tau][r] = e;
-                lsum += e;
+                bad |= (int)valid & (int)outside_band(sv, p.lo, p.hi);
+                const float e = exp2_hw(fmaf(sv, kLog2e, nphi));
+                w[tau][r] = valid ? e : 0.f;
+                lsum += w[tau][r];
             }
         }
         uint32_t h0w, h1w, h2w, h3w, l0w, l1w, l2w, l3w;
@@ -172,7 +240,8 @@ __global__ __launch_bounds__(256, 2) void partial_mfma_kernel(Params p)
         // stage V in natural layout: token t at (t/4)*kVGroupBytes + (t%4)*256
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<u32x4 *>(vbuf + i * kVGroupBytes + g4 * 256 + 16 * n) = vr[i];
+            *reinterpret_cast<u32x4 *>(vbuf + i * kVGroupBytes + g4 * 256 + 16 * n) =
+                as_bf16x8<KV>(blk.v[i]);
         __builtin_amdgcn_wave_barrier();
         // V^T fragments: lane (n, g4), dim 16*dt + n, tokens 4*g4 + r (r<4) and 16 + 4*g4 + r
         const uint16_t *vb16 = reinterpret_cast<const uint16_t *>(vbuf);
@@ -190,12 +259,29 @@ __global__ __launch_bounds__(256, 2) void partial_mfma_kernel(Params p)
             o[dt] = mfma_bf16(va, pl, o[dt]);
         }
         __builtin_amdgcn_wave_barrier();
+    };
+
+    // Software pipeline, two register buffers: the next block's loads are in
+    // flight while the current block is computed.  Past the last block the
+    // prefetch re-reads the current block (a cache hit) so that every
+    // iteration issues the same loads and the wait counts stay static.
+    Block A, B;
+    int j = wave;
+    if (j < nblk) load_block(A, j);
+    while (j < nblk) {
+        load_block(B, j + kMfmaWaves < nblk ? j + kMfmaWaves : j);
+        compute_block(A, j);
+        j += kMfmaWaves;
+        if (j >= nblk) break;
+        load_block(A, j + kMfmaWaves < nblk ? j + kMfmaWaves : j);
+        compute_block(B, j);
+        j += kMfmaWaves;
     }
 
     // per-head weight sums and band flags: reduce over the 4 lane groups
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    int badi = bad ? 1 : 0;
+    int badi = head_ok ? bad : 0;
     badi |= __shfl_xor(badi, 16);
     badi |= __shfl_xor(badi, 32);
 
