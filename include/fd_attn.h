@@ -98,9 +98,9 @@ typedef struct {
     const float *v_scale;       /* [num_kv_heads] device fp32, required iff kv_dtype is fp8 */
     void *workspace;            /* device, 256-byte aligned, >= fd_attn_workspace_size() bytes */
     size_t workspace_bytes;
-    /* Optional instrumentation: NULL, or 4 events the call records on `stream`
-     * before the chunk kernel, after it, after the fallback kernel and after
-     * the merge kernel, so a caller can time each stage. */
+    /* Optional instrumentation: NULL, or 4 caller-created events: start and
+     * stop of the chunk kernel, start and stop of the merge kernel, stamped
+     * by the kernels' own dispatches on `stream` (no extra stream work). */
     hipEvent_t *stage_events;
 } fd_attn_desc_t;
 

@@ -159,8 +159,8 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
     if stage_events is not None:
         handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in stage_events]
         if len(handles) != 4 or not all(handles):
-            raise ValueError("stage_events: 4 created HIP events (record a torch event once "
-                             "to create it)")
+            raise ValueError("stage_events: 4 created HIP events -- chunk start/stop, merge "
+                             "start/stop (record a torch event once to create it)")
         ev_arr = (ctypes.c_void_p * 4)(*handles)
         desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
     if stream is None:

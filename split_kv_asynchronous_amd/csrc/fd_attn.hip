@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/fd_attn.h: validation, workspace
 // carve-up, kernel choice and launches.  No allocation, no synchronisation.
+#include <hip/hip_ext.h>
 #include <math.h>
 #include <string.h>
 
@@ -68,9 +69,9 @@ int heads_per_block(int g)
 }
 
 template <int KV, int QT, bool PAGED>
-void launch_valu(const Params &p, dim3 grid, hipStream_t s)
+void launch_valu(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    hipLaunchKernelGGL((fd::partial_valu_kernel<KV, QT, PAGED>), grid, dim3(256), 0, s, p);
+    hipExtLaunchKernelGGL((fd::partial_valu_kernel<KV, QT, PAGED>), grid, dim3(256), 0, s, e0, e1, 0, p);
 }
 
 template <int KV, int QT, bool PAGED>
@@ -79,20 +80,15 @@ void launch_fallback(const Params &p, int nblk, hipStream_t s)
     hipLaunchKernelGGL((fd::fallback_kernel<KV, QT, PAGED>), dim3(nblk), dim3(1024), 0, s, p);
 }
 
-template <int KV, bool PAGED>
-void launch_mfma(const Params &p, dim3 grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((fd::partial_mfma_kernel<KV, PAGED>), grid, dim3(256), 0, s, p);
-}
-
 // Dispatch on (kv dtype, q dtype, paged) for the vector path.
 template <bool FALLBACK>
-void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, int nblk, hipStream_t s)
+void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, int nblk, hipStream_t s,
+                   hipEvent_t e0, hipEvent_t e1)
 {
 #define FD_CASE(KV, QT, PG)                                                   \
     if (kv == KV && qt == QT && paged == PG) {                                \
         if (FALLBACK) launch_fallback<KV, QT, PG>(p, nblk, s);                \
-        else launch_valu<KV, QT, PG>(p, grid, s);                             \
+        else launch_valu<KV, QT, PG>(p, grid, s, e0, e1);                     \
         return;                                                               \
     }
     FD_CASE(FD_F32, FD_F32, false) FD_CASE(FD_F32, FD_F32, true)
@@ -192,37 +188,62 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
 
     const bool paged = d->page_size != 0;
     const bool use_mfma = p.group > 1 && qt == FD_BF16 && kv != FD_F32;
+    // Optional stage timing: the chunk and merge kernels are launched with
+    // start/stop events stamped by their own dispatch packets, so timing adds
+    // no marker packets between the kernels.
     hipEvent_t *ev = d->stage_events;
+    hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;
+    hipEvent_t ev2 = ev ? ev[2] : nullptr, ev3 = ev ? ev[3] : nullptr;
 
     (void)hipGetLastError();   // clear a stale error so the checks below see only ours
-    if (ev) (void)hipEventRecord(ev[0], stream);
     if (use_mfma) {
         p.heads_per_block = heads_per_block(p.group);
         const dim3 grid(maxch, p.hq / p.heads_per_block, p.batch);
         if (kv == FD_BF16) {
             // one workgroup per unit; workgroups past the real units exit at once
             const dim3 flat((unsigned)((size_t)maxch * (p.hq / p.heads_per_block) * p.batch));
-            if (paged) hipLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<true>, flat, dim3(256), 0, stream, p);
-            else hipLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<false>, flat, dim3(256), 0, stream, p);
+            using Sh = fd::chunk::DefaultShape;
+            const dim3 blk(Sh::waves * 64);
+            if (paged)
+                hipExtLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<true, Sh>, flat, blk, 0, stream,
+                                      ev0, ev1, 0, p);
+            else
+                hipExtLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<false, Sh>, flat, blk, 0, stream,
+                                      ev0, ev1, 0, p);
         } else {
-            if (paged) launch_mfma<FD_FP8_E4M3FN, true>(p, grid, stream);
-            else launch_mfma<FD_FP8_E4M3FN, false>(p, grid, stream);
+            if (paged)
+                hipExtLaunchKernelGGL(fd::partial_mfma_kernel<FD_FP8_E4M3FN, true>, grid, dim3(256), 0,
+                                      stream, ev0, ev1, 0, p);
+            else
+                hipExtLaunchKernelGGL(fd::partial_mfma_kernel<FD_FP8_E4M3FN, false>, grid, dim3(256),
+                                      0, stream, ev0, ev1, 0, p);
         }
     } else {
         p.heads_per_block = 1;
-        dispatch_valu<false>(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), 0, stream);
+        dispatch_valu<false>(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), 0, stream, ev0, ev1);
     }
     if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    if (ev) (void)hipEventRecord(ev[1], stream);
 
-    const int total = (int)(rows * maxch);
-    const int nfb = total < 1024 ? total : 1024;
-    dispatch_valu<true>(p, kv, qt, paged, dim3(1), nfb, stream);
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    if (ev) (void)hipEventRecord(ev[2], stream);
+    // The bf16 grouped-query kernel and the vector kernel recompute an
+    // out-of-band chunk inside the workgroup that found it; the E4M3FN
+    // grouped-query kernel leaves it to a separate pass.
+    if (use_mfma && kv == FD_FP8_E4M3FN) {
+        const int total = (int)(rows * maxch);
+        const int nfb = total < 1024 ? total : 1024;
+        dispatch_valu<true>(p, kv, qt, paged, dim3(1), nfb, stream, nullptr, nullptr);
+        if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    }
 
-    hipLaunchKernelGGL(fd::merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+    // rows with many chunks get several wavefronts each
+    if (maxch >= 64)
+        hipExtLaunchKernelGGL(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, ev2,
+                              ev3, 0, p);
+    else if (maxch >= 16)
+        hipExtLaunchKernelGGL(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0,
+                              stream, ev2, ev3, 0, p);
+    else
+        hipExtLaunchKernelGGL(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                              stream, ev2, ev3, 0, p);
     if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    if (ev) (void)hipEventRecord(ev[3], stream);
     return FD_OK;
 }

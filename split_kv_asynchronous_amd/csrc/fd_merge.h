@@ -13,57 +13,130 @@
 
 namespace fd {
 
-// Grid ceil(B*Hq / 4), 256 threads: one wavefront per row, 2 components per lane.
+// RW wavefronts per row, 256 threads per workgroup (256 / (64 RW) rows each).
+// In a wavefront, lanes 0..31 take one chunk and lanes 32..63 the next, 4
+// components per lane, four chunk pairs in flight; the wavefronts of a row
+// split its chunks and meet in LDS.  The kernel also counts the recomputed
+// (row, chunk) pairs into the workspace counter (zeroed by this call's chunk
+// kernel).
+template <int RW>
 __global__ __launch_bounds__(256) void merge_kernel(Params p)
 {
+    constexpr int ROWS = 4 / RW;
+    __shared__ f32x4 red_o[4][32];
+    __shared__ float red_l[4];
+    __shared__ int red_n[4];
+    __shared__ float red_m[4];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= p.batch * p.hq) return;
-    const int b = row / p.hq, h = row % p.hq;
-    const int L = seq_len_of(p, b);
+    const int wave = threadIdx.x >> 6;
+    const int sub = wave % RW;                       // wavefront inside its row
+    const int row = blockIdx.x * ROWS + wave / RW;
+    const bool live = row < p.batch * p.hq;
+    const int b = live ? row / p.hq : 0, h = live ? row % p.hq : 0;
+    const int L = live ? seq_len_of(p, b) : 0;
     const int nch = (L + p.chunk - 1) / p.chunk;
     const size_t base = (size_t)row * p.maxch;
+    const int rw0 = (wave / RW) * RW;                // first wavefront of this row
 
-    int any = 0;
-    for (int c = lane; c < nch; c += 64) any |= p.cflag[base + c];
-    any = __any(any);
+    // flagged chunks of the row, and the largest chunk maximum if any
+    int nflag = 0;
+    for (int c = sub * 64 + lane; c < nch; c += 64 * RW) nflag += p.cflag[base + c];
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) nflag += __shfl_xor(nflag, x);
+    if (RW > 1) {
+        if (lane == 0) red_n[wave] = nflag;
+        __syncthreads();
+        nflag = 0;
+#pragma unroll
+        for (int w = 0; w < RW; ++w) nflag += red_n[rw0 + w];
+    }
+    const bool any = nflag != 0;
+    float M = p.phi;
+    if (any) {
+        M = -INFINITY;
+        for (int c = sub * 64 + lane; c < nch; c += 64 * RW) M = fmaxf(M, p.m_part[base + c]);
+#pragma unroll
+        for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+    }
+    if (RW > 1) {
+        if (lane == 0) red_m[wave] = M;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < RW; ++w) M = fmaxf(M, red_m[rw0 + w]);
+    }
 
-    f32x2 o = {0.f, 0.f};
-    float l = 0.f;
-    if (!any) {
-        for (int c = 0; c < nch; ++c) {
-            const f32x2 oc = *reinterpret_cast<const f32x2 *>(p.o_part + (base + c) * kHeadDim + 2 * lane);
-            o += oc;
-            l += p.l_part[base + c];
+    const int half = lane >> 5, q4 = lane & 31;
+    const float *op = p.o_part + base * kHeadDim + 4 * q4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lacc = 0.f;
+    constexpr int STEP = 2 * RW;                     // chunks per pass of all row waves
+    int c = 2 * sub + half;
+    // without a recomputed chunk every partial is against phi: plain sum;
+    // otherwise each is rescaled from its own maximum to M
+    for (; c + 3 * STEP < nch; c += 4 * STEP) {
+        f32x4 v[4];
+        float l[4], f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = *reinterpret_cast<const f32x4 *>(op + (size_t)(c + u * STEP) * kHeadDim);
+            l[u] = p.l_part[base + c + u * STEP];
+            f[u] = any ? p.m_part[base + c + u * STEP] : M;
         }
-    } else {
-        float M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmaxf(M, p.m_part[base + c]);
-        for (int c = 0; c < nch; ++c) {
-            const float mc = p.m_part[base + c];
-            const float f = (mc == M) ? 1.f : exp2_hw((mc - M) * kLog2e);
-            const f32x2 oc = *reinterpret_cast<const f32x2 *>(p.o_part + (base + c) * kHeadDim + 2 * lane);
-            o += oc * f;
-            l = fmaf(p.l_part[base + c], f, l);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float g = (f[u] == M) ? 1.f : exp2_hw((f[u] - M) * kLog2e);
+            acc += v[u] * g;
+            lacc = fmaf(l[u], g, lacc);
         }
     }
-    float vs = 1.f;
-    if (p.v_scale) vs = p.v_scale[h / p.group];
-    f32x2 r = {0.f, 0.f};
+    for (; c < nch; c += STEP) {
+        const float mc = any ? p.m_part[base + c] : M;
+        const float g = (mc == M) ? 1.f : exp2_hw((mc - M) * kLog2e);
+        acc += *reinterpret_cast<const f32x4 *>(op + (size_t)c * kHeadDim) * g;
+        lacc = fmaf(p.l_part[base + c], g, lacc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
+    lacc += __shfl_xor(lacc, 32);
+    if (RW > 1) {
+        if (half == 0) red_o[wave][q4] = acc;
+        if (lane == 0) red_l[wave] = lacc;
+        __syncthreads();
+        if (sub != 0) return;
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        lacc = 0.f;
+#pragma unroll
+        for (int w = 0; w < RW; ++w) {
+            acc += red_o[rw0 + w][q4];
+            lacc += red_l[rw0 + w];
+        }
+    }
+    if (!live) return;
+
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
     if (nch > 0) {
-        const float inv = vs / l;
-        r = o * inv;
+        float vs = 1.f;
+        if (p.v_scale) vs = p.v_scale[h / p.group];
+        r = acc * (vs / lacc);
     }
-    if (p.out_bf16) {
-        // round to nearest even
-        uint32_t a = __float_as_uint(r.x), c2 = __float_as_uint(r.y);
-        a = (r.x != r.x) ? 0x7fc0u : (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
-        c2 = (r.y != r.y) ? 0x7fc00000u : (c2 + 0x7fffu + ((c2 >> 16) & 1u)) & 0xffff0000u;
-        reinterpret_cast<uint32_t *>(p.out)[(size_t)row * (kHeadDim / 2) + lane] = a | c2;
-    } else {
-        reinterpret_cast<f32x2 *>(p.out)[(size_t)row * (kHeadDim / 2) + lane] = r;
+    if (half == 0) {
+        if (p.out_bf16) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t u = __float_as_uint(r[i]);
+                w[i] = (r[i] != r[i]) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+            }
+            reinterpret_cast<u32x2 *>(p.out)[(size_t)row * (kHeadDim / 4) + q4] =
+                u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+        } else {
+            reinterpret_cast<f32x4 *>(p.out)[(size_t)row * (kHeadDim / 4) + q4] = r;
+        }
     }
-    if (lane == 0) p.flags[row] = any ? 1 : 0;
+    if (lane == 0) {
+        p.flags[row] = any ? 1 : 0;
+        if (nflag) atomicAdd(p.counter, nflag);
+    }
 }
 
 }  // namespace fd

@@ -23,7 +23,7 @@ namespace fd {
 //                   writes o, l and the chunk maximum m.
 // NW = wavefronts in the workgroup; `red` is LDS of at least NW * 132 floats.
 template <int KV, int QT, bool PAGED, bool ONLINE, int NW>
-FD_DEV void valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_end, float *red)
+FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_end, float *red)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -151,7 +151,11 @@ FD_DEV void valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
         p.m_part[slot] = M;
         if constexpr (!ONLINE) p.cflag[slot] = any ? 1 : 0;
     }
+    bool flagged = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) flagged |= red[w * 132 + 130] != 0.f;
     __syncthreads();   // `red` is reused by the caller
+    return flagged;
 }
 
 // Grid (maxch, Hq, B): one workgroup per (chunk, query head, sequence).
@@ -164,7 +168,11 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
     const int L = seq_len_of(p, b);
     const int t0 = c * p.chunk;
     if (t0 >= L) return;
-    valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, min(t0 + p.chunk, L), red);
+    const int t1 = min(t0 + p.chunk, L);
+    // a score left the safe band: this workgroup redoes its chunk with online
+    // softmax and overwrites the partial (the chunk flag stays set)
+    if (valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, t1, red))
+        valu_chunk<KV, QT, PAGED, true, 4>(p, b, h, c, t0, t1, red);
 }
 
 // Fallback: every workgroup scans a strided share of the (row, chunk) flags
@@ -182,7 +190,6 @@ __global__ __launch_bounds__(1024) void fallback_kernel(Params p)
     __shared__ int count;
     const int total = p.batch * p.hq * p.maxch;
     const int nblk = gridDim.x;
-    int done = 0;
     for (int base = 0; base + (int)blockIdx.x < total; base += 1024 * nblk) {
         if (threadIdx.x == 0) count = 0;
         __syncthreads();
@@ -202,10 +209,8 @@ __global__ __launch_bounds__(1024) void fallback_kernel(Params p)
             const int t0 = c * p.chunk;
             valu_chunk<KV, QT, PAGED, true, NW>(p, b, h, c, t0, min(t0 + p.chunk, L), red);
         }
-        done += n;
         __syncthreads();
     }
-    if (threadIdx.x == 0 && done) atomicAdd(p.counter, done);
 }
 
 }  // namespace fd
