@@ -47,23 +47,37 @@ def partial_kernel_bytes(prob) -> int:
     return prob.kv_bytes() + qb + extra
 
 
-def cpu_baseline(prob, budget_rows=None):
-    """The oracle, untouched, on the first batch entries of the same workload."""
+def cpu_baseline(prob, min_seconds=10.0, max_passes=20):
+    """The float64 oracle, as it stands, on the host cores: whole calls of the
+    same workload repeated until about min_seconds of CPU time have passed
+    (or, for a workload too slow for one pass in that time, the first batch
+    entries only)."""
     import oracle
     B, Hq = prob.batch, prob.num_q_heads
-    nb = budget_rows or max(1, min(B, 8))
-    rows = np.arange(nb * Hq, dtype=np.int32)
+    # one batch entry first, to size the sample
     t = time.perf_counter()
-    _, _, _, threads = oracle.decode_exact(**prob.args(), rows=rows, with_threads=True)
-    dt = time.perf_counter() - t
+    oracle.decode_exact(**prob.args(), rows=np.arange(Hq, dtype=np.int32))
+    per_entry = time.perf_counter() - t
+    lens = np.clip(prob.seq_lens, 0, prob.max_seq_len).astype(np.int64)
+    est_full = per_entry * B * max(1.0, lens.mean() / max(1, lens[0]))
+    if est_full <= 2 * min_seconds:
+        nb, rows = B, None
+    else:
+        nb = max(1, min(B, int(min_seconds / max(per_entry, 1e-9))))
+        rows = np.arange(nb * Hq, dtype=np.int32)
+    passes, spent, threads = 0, 0.0, 1
+    while passes < max_passes and (passes == 0 or spent < min_seconds):
+        t = time.perf_counter()
+        _, _, _, threads = oracle.decode_exact(**prob.args(), rows=rows, with_threads=True)
+        spent += time.perf_counter() - t
+        passes += 1
     elt = {"f32": 4, "bf16": 2, "e4m3fn": 1}[prob.kv_dtype]
-    lens = np.clip(prob.seq_lens[:nb], 0, prob.max_seq_len).astype(np.int64)
-    sample_bytes = int(lens.sum()) * prob.num_kv_heads * prob.head_dim * 2 * elt
-    gbs = sample_bytes / dt / 1e9
+    sample_bytes = int(lens[:nb].sum()) * prob.num_kv_heads * prob.head_dim * 2 * elt
+    gbs = sample_bytes * passes / spent / 1e9
+    what = ("the whole call" if nb == B else "batch entries 0..%d (all %d query heads)" % (nb - 1, Hq))
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "batch entries 0..%d (all %d query heads, %d tokens), float64, %.1f s; "
-                      "calls/s equivalent %.4f" % (nb - 1, Hq, int(lens.sum()), dt,
-                                                   gbs * 1e9 / prob.kv_bytes())}
+            "sample": "%s, %d pass(es), %.1f s, float64 exact softmax + band test; "
+                      "calls/s equivalent %.4f" % (what, passes, spent, gbs * 1e9 / prob.kv_bytes())}
 
 
 def load_traffic(workload: str):
