@@ -45,7 +45,7 @@ int check_shape(const fd_attn_desc_t *d)
     if (d->batch > 65535 || d->num_q_heads > 65535) return FD_ERR_SHAPE;   // grid limits
     if (d->num_q_heads % d->num_kv_heads) return FD_ERR_SHAPE;
     if (d->head_dim != fd::kHeadDim) return FD_ERR_SHAPE;
-    if (d->max_seq_len < 1 || d->max_seq_len > (1 << 24)) return FD_ERR_SHAPE;
+    if (d->max_seq_len < 1 || d->max_seq_len > (1 << 23)) return FD_ERR_SHAPE;
     if (d->chunk_size < 32 || d->chunk_size % 32) return FD_ERR_SHAPE;
     if (d->page_size) {
         if (!is_pow2(d->page_size) || d->page_size < 16 || d->page_size > 256) return FD_ERR_SHAPE;
@@ -198,41 +198,31 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     (void)hipGetLastError();   // clear a stale error so the checks below see only ours
     if (use_mfma) {
         p.heads_per_block = heads_per_block(p.group);
-        const dim3 grid(maxch, p.hq / p.heads_per_block, p.batch);
+        // one workgroup per unit; workgroups past the real units exit at once.
+        // The unit index is blockIdx.y * gridDim.x + blockIdx.x.
+        const size_t units = (size_t)maxch * (p.hq / p.heads_per_block) * p.batch;
+        const unsigned gx = (unsigned)(units < ((size_t)1 << 20) ? units : ((size_t)1 << 20));
+        const dim3 flat(gx, (unsigned)((units + gx - 1) / gx));
+        using Sh = fd::chunk::DefaultShape;
+        const dim3 blk(Sh::waves * 64);
+#define FD_CHUNK_LAUNCH(KV, PG)                                                                  \
+        hipExtLaunchKernelGGL((fd::chunk::chunk_kernel<KV, PG, Sh>), flat, blk, 0, stream, ev0, ev1, 0, p)
         if (kv == FD_BF16) {
-            // one workgroup per unit; workgroups past the real units exit at once
-            const dim3 flat((unsigned)((size_t)maxch * (p.hq / p.heads_per_block) * p.batch));
-            using Sh = fd::chunk::DefaultShape;
-            const dim3 blk(Sh::waves * 64);
-            if (paged)
-                hipExtLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<true, Sh>, flat, blk, 0, stream,
-                                      ev0, ev1, 0, p);
-            else
-                hipExtLaunchKernelGGL(fd::chunk::chunk_bf16_kernel<false, Sh>, flat, blk, 0, stream,
-                                      ev0, ev1, 0, p);
+            if (paged) FD_CHUNK_LAUNCH(FD_BF16, true);
+            else FD_CHUNK_LAUNCH(FD_BF16, false);
         } else {
-            if (paged)
-                hipExtLaunchKernelGGL(fd::partial_mfma_kernel<FD_FP8_E4M3FN, true>, grid, dim3(256), 0,
-                                      stream, ev0, ev1, 0, p);
-            else
-                hipExtLaunchKernelGGL(fd::partial_mfma_kernel<FD_FP8_E4M3FN, false>, grid, dim3(256),
-                                      0, stream, ev0, ev1, 0, p);
+            if (paged) FD_CHUNK_LAUNCH(FD_FP8_E4M3FN, true);
+            else FD_CHUNK_LAUNCH(FD_FP8_E4M3FN, false);
         }
+#undef FD_CHUNK_LAUNCH
     } else {
         p.heads_per_block = 1;
         dispatch_valu<false>(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), 0, stream, ev0, ev1);
     }
     if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
 
-    // The bf16 grouped-query kernel and the vector kernel recompute an
-    // out-of-band chunk inside the workgroup that found it; the E4M3FN
-    // grouped-query kernel leaves it to a separate pass.
-    if (use_mfma && kv == FD_FP8_E4M3FN) {
-        const int total = (int)(rows * maxch);
-        const int nfb = total < 1024 ? total : 1024;
-        dispatch_valu<true>(p, kv, qt, paged, dim3(1), nfb, stream, nullptr, nullptr);
-        if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    }
+    // Both kernels recompute an out-of-band chunk inside the workgroup that
+    // found it: no separate fallback pass.
 
     // rows with many chunks get several wavefronts each
     if (maxch >= 64)

@@ -1,6 +1,6 @@
-// Grouped-query chunk kernel, bf16 cache: K and V stream through a per-wave
-// LDS ring filled by coalesced buffer->LDS DMA; both contractions run on the
-// matrix cores.
+// Grouped-query chunk kernel for bf16 and E4M3FN caches: K and V stream
+// through a per-wave LDS ring filled by coalesced buffer->LDS DMA; both
+// contractions run on the matrix cores.
 //
 // Work decomposition.  A unit is (sequence b, head block hb, chunk c).  The
 // grid is an upper bound on the number of units; workgroup i takes the i-th
@@ -8,19 +8,24 @@
 // workgroups past the end exit at once and no launch slot in the middle of the
 // grid is wasted on a chunk beyond its sequence.
 //
-// Shape <NW, NSUB, NST>: NW wavefronts per workgroup; a ring block holds NSUB
-// 16-token sub-tiles of K and of V; each wavefront owns an NST-stage ring.
-// The blocks of a unit are dealt round-robin to the wavefronts.  Per block:
-//   * 4*NSUB DMA instructions per tile, each moving 4 whole cache rows (1 KiB,
-//     fully coalesced) into LDS; the 16-byte pieces of a row are rotated by
-//     rot(t) so that the fragment reads below are free of bank conflicts;
-//   * the block's fragments are read out of the stage at once (4 ds_read_b128
-//     K fragments and 8 ds_read_b64_tr_b16 V^T fragments per sub-tile) and
-//     the stage is refilled before any arithmetic;
-//   * per sub-tile: S^T[16 tok x 16 heads] = K . Q^T on 4
-//     v_mfma_f32_16x16x32_bf16; band test, p = exp(s - phi) and the weight sums
-//     in registers; p split into a bf16 high part and a bf16 remainder;
-//     O^T[128 x 16 heads] += V^T . P^T on 8 x 2 v_mfma_f32_16x16x16_bf16.
+// Shape <NW, NSUB, NST>: NW wavefronts per workgroup, each owning an
+// NST-stage ring; a ring block holds NSUB compute groups of K and of V (a
+// group is 16 tokens for bf16, 32 tokens for E4M3FN: 4 KiB either way).  The
+// blocks of a unit are dealt round-robin to the wavefronts.  Per block:
+//   * 1 KiB DMA instructions, each moving whole cache rows (4 bf16 rows or 8
+//     E4M3FN rows, fully coalesced) into LDS; the 16-byte pieces of a row are
+//     rotated by rot(t) so that the fragment reads below are free of bank
+//     conflicts;
+//   * the block's fragments are read out of the stage at once -- K fragments
+//     with ds_read_b128, V^T fragments with the transposing reads
+//     ds_read_b64_tr_b16 / ds_read_b64_tr_b8 -- and the stage is refilled
+//     before any arithmetic; E4M3FN fragments are widened to bf16 in
+//     registers (exact);
+//   * S^T[16 tok x 16 heads] = K . Q^T on v_mfma_f32_16x16x32_bf16; band
+//     test, p = exp(s - phi) and the weight sums in registers; p split into a
+//     bf16 high part and a bf16 remainder; O^T[128 x 16 heads] += V^T . P^T
+//     on v_mfma_f32_16x16x16_bf16 (bf16: 16-token groups) or
+//     v_mfma_f32_16x16x32_bf16 (E4M3FN: 32-token groups).
 #pragma once
 
 #include <type_traits>
@@ -42,8 +47,7 @@ namespace fd {
 
 namespace chunk {
 
-constexpr int kRow = kHeadDim * 2;                 // bytes per bf16 cache row
-constexpr int kSubTile = 16 * kRow;                // 16 rows: 4 KiB
+constexpr int kGroupBytes = 4096;                  // one compute group of K (or V)
 constexpr int kRedStride = 16 * kHeadDim + 32;     // one wave's O^T, then l and flag-or-max per head
 
 template <int NW, int NSUB, int NST>
@@ -51,18 +55,30 @@ struct Shape {
     static constexpr int waves = NW;
     static constexpr int nsub = NSUB;
     static constexpr int nst = NST;
-    static constexpr int blk = 16 * NSUB;              // tokens per ring block
-    static constexpr int tile = NSUB * kSubTile;       // K (or V) part of a block
+    static constexpr int tile = NSUB * kGroupBytes;    // K (or V) part of a ring block
     static constexpr int stage = 2 * tile;
     static constexpr int wave_lds = NST * stage;
     static constexpr int lds = NW * wave_lds;
-    static constexpr int dma_per_block = 2 * (blk / 4);  // 1 KiB per DMA instruction
+    static constexpr int dma_per_block = 2 * tile / 1024;  // 1 KiB per DMA instruction
     static_assert(NST * dma_per_block < 64, "vmcnt cannot count that deep");
     static_assert(NW * kRedStride * 4 <= lds, "epilogue reduction must fit in the ring");
     static_assert(lds <= 160 * 1024, "LDS per workgroup");
 };
 
 using DefaultShape = Shape<FD_CHUNK_WAVES, FD_CHUNK_SUBTILES, FD_CHUNK_STAGES>;
+
+// Per storage format: row bytes, tokens per compute group, piece rotation.
+template <int KV> struct Fmt;
+template <> struct Fmt<FD_BF16> {
+    static constexpr int row = 256, group = 16, slots = 16;
+    // rotation of the 16-byte pieces of group row t (0..15)
+    static FD_DEV int rot(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
+};
+template <> struct Fmt<FD_FP8_E4M3FN> {
+    static constexpr int row = 128, group = 32, slots = 8;
+    // rotation of the 16-byte pieces of group row t (0..31)
+    static FD_DEV int rot(int t) { return (t + 4 * ((t >> 4) & 1)) & 7; }
+};
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -87,13 +103,23 @@ FD_DEV void wait_ring(int k)
     else wait_vmcnt<0>();
 }
 
-// rotation of the 16-byte pieces of row t (0..15) of a sub-tile
-FD_DEV int rot_of(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
-
 FD_DEV f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// 4 E4M3FN codes -> 4 bf16 (exact), packed as two dwords
+FD_DEV u32x2 e4m3x4_to_bf16(uint32_t w)
+{
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
+FD_DEV u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    const u32x2 a = e4m3x4_to_bf16(lo), b = e4m3x4_to_bf16(hi);
+    return u32x4{a.x, a.y, b.x, b.y};
 }
 
 // wave-wide inclusive prefix sum
@@ -155,15 +181,23 @@ FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
     return r;
 }
 
-template <bool PAGED, typename S>
-__global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
+template <int KV, bool PAGED, typename S>
+__global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
 {
+    using F = Fmt<KV>;
+    constexpr bool FP8 = KV == FD_FP8_E4M3FN;
     constexpr int NW = S::waves;
     constexpr int NSUB = S::nsub;
     constexpr int NST = S::nst;
+    constexpr int ROW = F::row;
+    constexpr int GRP = F::group;                  // tokens per compute group
+    constexpr int BLK = NSUB * GRP;                // tokens per ring block
+    constexpr int RPI = 1024 / ROW;                // rows per DMA instruction
+    constexpr int LPR = 64 / RPI;                  // lanes per row in a DMA instruction
+    constexpr int DMA_TILE = S::tile / 1024;       // DMA instructions per K (or V) tile
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
     __shared__ int flagged_heads;
-    if ((blockIdx.x | threadIdx.x) == 0) *p.counter = 0;
+    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) *p.counter = 0;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -172,7 +206,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
     const int GB = p.heads_per_block;
     const int nhb = p.hq / GB;
 
-    const Unit U = find_unit(p, blockIdx.x, nhb, lane);
+    const Unit U = find_unit(p, blockIdx.y * gridDim.x + blockIdx.x, nhb, lane);
     if (!U.ok) return;
     const int b = __builtin_amdgcn_readfirstlane(U.b);
     const int hb = __builtin_amdgcn_readfirstlane(U.hb);
@@ -184,24 +218,39 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
     const int kvh = h0 / p.group;
     const bool head_ok = n < GB;
 
-    // Q^T fragments (B operand of the S product)
+    // Q^T fragments (B operand of the S product).  The k index of MFMA step kk
+    // maps to query components 8*g4 + 32*kk + j (bf16) or 16*(g4 + 4*(kk/2)) +
+    // 8*(kk%2) + j (E4M3FN, matching 16-byte K pieces); K uses the same map.
+    // The loads are inline assembly, invisible to the compiler's wait
+    // tracking: that tracking cannot follow the data-dependent number of DMAs
+    // issued behind them and would drain the whole ring before the first
+    // block.  The ring prologue's explicit wait covers them (they are older
+    // than every DMA); heads past the block read a valid row and are zeroed.
     u32x4 qf[4];
+    {
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) +
+                               ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        qf[kk] = u32x4{0u, 0u, 0u, 0u};
-        if (head_ok)
-            qf[kk] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.q) +
-                                                      ((size_t)b * p.hq + h0 + n) * kHeadDim +
-                                                      8 * g4 + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) {
+            const int d0 = FP8 ? 16 * (g4 + 4 * (kk >> 1)) + 8 * (kk & 1) : 8 * g4 + 32 * kk;
+            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[kk]) : "v"(qrow + d0) : "memory");
+        }
     }
-    const float sc = p.scale;
+    float sc = p.scale;
+    if constexpr (FP8) sc *= as_const(p.k_scale)[kvh];
     const float nphi = -p.phi * kLog2e;
 
-    // ---- DMA addressing: instruction i of a tile moves rows 4i .. 4i+3; lane
-    // (n, g4) fetches piece (n - rot) & 15 of row 4i + g4 so that LDS slot n of
-    // that row holds it (rot depends on the row's parity within a sub-tile)
-    const uint32_t dma_voff_even = g4 * kRow + 16 * ((n - rot_of(g4)) & 15);
-    const uint32_t dma_voff_odd = g4 * kRow + 16 * ((n - rot_of(4 + g4)) & 15);
+    // ---- DMA addressing: instruction i of a tile moves rows RPI*i .. +RPI-1;
+    // lane l fetches, of row RPI*i + l/LPR, the piece that belongs in LDS slot
+    // l%LPR.  The rotation depends on i only through i%4 (period 2 for bf16,
+    // 4 for E4M3FN), so four offsets per lane cover every instruction.
+    uint32_t dma_voff[4];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        const int r = (RPI * i4 + lane / LPR) % GRP;          // group row
+        const int slot = lane % LPR;
+        dma_voff[i4] = (lane / LPR) * ROW + 16 * ((slot - F::rot(r)) & (F::slots - 1));
+    }
     uint8_t *ring = lds + wave * S::wave_lds;
 
     __amdgpu_buffer_rsrc_t krs, vrs;
@@ -209,8 +258,8 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
     const uint8_t *vpool = static_cast<const uint8_t *>(p.v);
     const __attribute__((address_space(4))) int32_t *btab = as_const(p.block_table);
     if constexpr (!PAGED) {
-        const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * kRow;
-        const int nrec = (int)((uint32_t)L * kRow);
+        const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * ROW;
+        const int nrec = (int)((uint32_t)L * ROW);
         krs = __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + slice), (short)0, nrec, 0x00020000);
         vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + slice), (short)0, nrec, 0x00020000);
     } else {
@@ -219,60 +268,95 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
     const int last_page = (L - 1) >> p.page_shift;
     const int pmask = (1 << p.page_shift) - 1;
 
-    const int nblk = (t_end - t_begin + S::blk - 1) / S::blk;
+    const int nblk = (t_end - t_begin + BLK - 1) / BLK;
 
-    auto issue = [&](int j, int stage) {
+    // Page-table entries of ring block jb, one per 16 tokens (a page holds at
+    // least 16).  Blocks past the unit read the last valid page's entry.
+    constexpr int NPG = PAGED ? BLK / 16 : 1;
+    auto load_pages = [&](int jb, int (&pg)[NPG]) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int g = 0; g < NPG; ++g) {
+                const int idx = (t_begin + BLK * jb + 16 * g) >> p.page_shift;
+                pg[g] = btab[idx < last_page ? idx : last_page];
+            }
+        } else {
+            pg[0] = 0;
+        }
+    };
+
+    auto issue = [&](int j, int stage, const int (&pg)[NPG]) {
         uint8_t *kt = ring + stage * S::stage;
         uint8_t *vt = kt + S::tile;
+        const int tb = t_begin + BLK * j;
+        size_t page_off = 0;
 #pragma unroll
-        for (int u = 0; u < NSUB; ++u) {
-            const int t0 = t_begin + S::blk * j + 16 * u;
-            size_t page_off = 0;
+        for (int i = 0; i < DMA_TILE; ++i) {
+            const int t0 = tb + RPI * i;                        // first row of this instruction
             if constexpr (PAGED) {
-                // a 16-token sub-tile never straddles a page (pages hold >= 16 tokens)
-                int idx = t0 >> p.page_shift;
-                idx = idx < last_page ? idx : last_page;
-                page_off = (((size_t)btab[idx] * p.hkv + kvh) * (size_t)(pmask + 1) + (t0 & pmask)) * kRow;
+                // the rows of one instruction never straddle a page
+                if (i * RPI % 16 == 0)
+                    page_off = (((size_t)pg[i * RPI / 16] * p.hkv + kvh) * (size_t)(pmask + 1) + (t0 & pmask)) * ROW;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t vo = (i & 1) ? dma_voff_odd : dma_voff_even;
-                lds_void *kd = (lds_void *)(kt + u * kSubTile + i * 1024);
-                lds_void *vd = (lds_void *)(vt + u * kSubTile + i * 1024);
-                if constexpr (PAGED) {
-                    __builtin_amdgcn_global_load_lds(kpool + page_off + i * 4 * kRow + vo, kd, 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(vpool + page_off + i * 4 * kRow + vo, vd, 16, 0, 0);
-                } else {
-                    const int so = (int)((uint32_t)(t0 + 4 * i) * kRow);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
-                }
+            const uint32_t vo = dma_voff[i & 3];
+            lds_void *kd = (lds_void *)(kt + i * 1024);
+            lds_void *vd = (lds_void *)(vt + i * 1024);
+            if constexpr (PAGED) {
+                const size_t off = page_off + (size_t)((i * RPI) % 16) * ROW + vo;
+                __builtin_amdgcn_global_load_lds(kpool + off, kd, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vpool + off, vd, 16, 0, 0);
+            } else {
+                const int so = (int)((uint32_t)t0 * ROW);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
             }
         }
     };
 
-    // fragment read addresses inside a sub-tile (bytes)
-    // K: lane (n, g4), k-step kk: row n, piece g4 + 4kk
+    // ---- fragment read addresses inside a compute group (bytes)
+    // K, bf16: step kk -> row n, piece g4 + 4kk.  E4M3FN: for tile tau and
+    // half m, row 16*tau + n, piece g4 + 4m (16 codes = steps 2m and 2m+1).
     uint32_t k_rd[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * kRow + 16 * ((g4 + 4 * kk + rot_of(n)) & 15);
-    // V (transposing read): lane i of group g4 addresses row 4g4 + i/4,
-    // components 16dt + 4(i%4) .. +3, i.e. half (i & 1) of piece 2dt + (i%4)/2
-    const int vt_tok = 4 * g4 + (n >> 2);
+    for (int q4 = 0; q4 < 4; ++q4) {
+        if constexpr (FP8) {
+            const int tau = q4 >> 1, m = q4 & 1, r = 16 * tau + n;
+            k_rd[q4] = r * ROW + 16 * ((g4 + 4 * m + F::rot(r)) & (F::slots - 1));
+        } else {
+            k_rd[q4] = n * ROW + 16 * ((g4 + 4 * q4 + F::rot(n)) & (F::slots - 1));
+        }
+    }
+    // V^T (transposing reads), dim tile dt.
+    // bf16: lane i of group g4 addresses row 4g4 + i/4, components
+    //   16dt + 4(i%4) .. +3 (half i&1 of piece 2dt + (i%4)/2); lane k then holds
+    //   component 16dt + k of rows 4g4 .. 4g4+3.
+    // E4M3FN: lane i of group g4 addresses row T(i/2), components 16dt +
+    //   8(i%2) .. +7 (half i&1 of piece dt), with T(j) = 4g4 + j (j < 4) or
+    //   16 + 4g4 + j - 4; lane k then holds component 16dt + k of rows T(0..7),
+    //   the token order in which the two S tiles hand over their weights.
     uint32_t v_rd[8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-        v_rd[dt] = vt_tok * kRow + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + rot_of(vt_tok)) & 15);
+    for (int dt = 0; dt < 8; ++dt) {
+        if constexpr (FP8) {
+            const int jj = n >> 1;
+            const int r = jj < 4 ? 4 * g4 + jj : 16 + 4 * g4 + jj - 4;
+            v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((dt + F::rot(r)) & (F::slots - 1));
+        } else {
+            const int r = 4 * g4 + (n >> 2);
+            v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + F::rot(r)) & (F::slots - 1));
+        }
+    }
 
     float *red = reinterpret_cast<float *>(lds);
 
     // One pass over the unit's blocks.  ONLINE == false: weights exp(s - phi)
     // against the preset constant, band test per head.  ONLINE == true: the
-    // ordinary running-maximum softmax, the maximum advanced once per
-    // sub-tile.  Leaves this wave's O^T, weight sum, and band flag (or running
+    // ordinary running-maximum softmax, the maximum advanced once per compute
+    // group.  Leaves this wave's O^T, weight sum, and band flag (or running
     // maximum) in red[wave].
     auto run = [&](auto online_tag) {
         constexpr bool ONLINE = decltype(online_tag)::value;
+        constexpr int NT = FP8 ? 2 : 1;            // S tiles per compute group
         f32x4 o[8];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -282,15 +366,28 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
 
         int j = wave;
         int issued = 0;
+        {
+            int pg[NST][NPG];
 #pragma unroll
-        for (int k = 0; k < NST; ++k)
-            if (j + k * NW < nblk) {
-                issue(j + k * NW, k);
-                ++issued;
-            }
+            for (int k = 0; k < NST; ++k) load_pages(j + k * NW, pg[k]);
+#pragma unroll
+            for (int k = 0; k < NST; ++k)
+                if (j + k * NW < nblk) {
+                    issue(j + k * NW, k, pg[k]);
+                    ++issued;
+                }
+        }
+        // page-table entries are fetched one ring refill ahead of their use
+        int pg_next[NPG];
+        load_pages(j + NST * NW, pg_next);
         // the query loads were issued before the ring prologue: once at most
         // the prologue's DMAs are outstanding, the queries have arrived
         wait_ring<S::dma_per_block, NST>(issued);
+        asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]) : : "memory");
+        if (!head_ok) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0u, 0u, 0u, 0u};
+        }
         int stage = 0;
 #pragma unroll 1
         for (; j < nblk; j += NW) {
@@ -305,19 +402,22 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
             // inline assembly: the compiler cannot tell them apart from ring
             // slots still being filled and would drain every DMA in flight
             // before them; the explicit waits here do the ordering instead.
-            u32x4 kf[NSUB][4];
-            u32x2 va[NSUB][8];
+            u32x4 kraw[NSUB][4];
+            u32x2 vraw[NSUB][8];
 #pragma unroll
             for (int u = 0; u < NSUB; ++u) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const uint32_t addr = (uint32_t)(uintptr_t)(kt + u * kSubTile + k_rd[kk]);
-                    asm volatile("ds_read_b128 %0, %1" : "=v"(kf[u][kk]) : "v"(addr) : "memory");
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint32_t addr = (uint32_t)(uintptr_t)(kt + u * kGroupBytes + k_rd[q4]);
+                    asm volatile("ds_read_b128 %0, %1" : "=v"(kraw[u][q4]) : "v"(addr) : "memory");
                 }
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
-                    const uint32_t addr = (uint32_t)(uintptr_t)(vt + u * kSubTile + v_rd[dt]);
-                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(va[u][dt]) : "v"(addr) : "memory");
+                    const uint32_t addr = (uint32_t)(uintptr_t)(vt + u * kGroupBytes + v_rd[dt]);
+                    if constexpr (FP8)
+                        asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(vraw[u][dt]) : "v"(addr) : "memory");
+                    else
+                        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vraw[u][dt]) : "v"(addr) : "memory");
                 }
             }
             // all reads of the stage have returned (the fragments are tied to
@@ -325,40 +425,58 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
 #pragma unroll
             for (int u = 0; u < NSUB; ++u)
                 asm volatile("s_waitcnt lgkmcnt(0)"
-                             : "+v"(va[u][0]), "+v"(va[u][1]), "+v"(va[u][2]), "+v"(va[u][3]),
-                               "+v"(va[u][4]), "+v"(va[u][5]), "+v"(va[u][6]), "+v"(va[u][7]),
-                               "+v"(kf[u][0]), "+v"(kf[u][1]), "+v"(kf[u][2]), "+v"(kf[u][3])
+                             : "+v"(vraw[u][0]), "+v"(vraw[u][1]), "+v"(vraw[u][2]), "+v"(vraw[u][3]),
+                               "+v"(vraw[u][4]), "+v"(vraw[u][5]), "+v"(vraw[u][6]), "+v"(vraw[u][7]),
+                               "+v"(kraw[u][0]), "+v"(kraw[u][1]), "+v"(kraw[u][2]), "+v"(kraw[u][3])
                              :
                              : "memory");
-            if (j + NST * NW < nblk) issue(j + NST * NW, stage);
+            if (j + NST * NW < nblk) issue(j + NST * NW, stage, pg_next);
+            load_pages(j + (NST + 1) * NW, pg_next);
             stage = stage + 1 == NST ? 0 : stage + 1;
 
 #pragma unroll
             for (int u = 0; u < NSUB; ++u) {
-                // S^T: rows = tokens 4*g4 + r of the sub-tile, column = head n
-                f32x4 s = {0.f, 0.f, 0.f, 0.f};
+                const int tg = t_begin + BLK * j + GRP * u;      // first token of the group
+                // S^T tiles: rows = tokens 16*tau + 4*g4 + r of the group, column = head n
+                f32x4 s[NT];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) s = mfma_bf16(kf[u][kk], qf[kk], s);
-                const int t0 = t_begin + S::blk * j + 16 * u;
-                float w[4];
+                for (int tau = 0; tau < NT; ++tau) {
+                    s[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        u32x4 kf;
+                        if constexpr (FP8) {
+                            const u32x4 r = kraw[u][2 * tau + (kk >> 1)];
+                            kf = (kk & 1) ? e4m3x8_to_bf16(r.z, r.w) : e4m3x8_to_bf16(r.x, r.y);
+                        } else {
+                            kf = kraw[u][kk];
+                        }
+                        s[tau] = mfma_bf16(kf, qf[kk], s[tau]);
+                    }
+                }
+                float w[NT][4];
                 if constexpr (!ONLINE) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool valid = t0 + 4 * g4 + r < t_end;
-                        const float sv = s[r] * sc;
-                        bad |= (int)valid & (int)outside_band(sv, p.lo, p.hi);
-                        const float e = exp2_hw(fmaf(sv, kLog2e, nphi));
-                        w[r] = valid ? e : 0.f;
-                        lsum += w[r];
-                    }
-                } else {
-                    float sv[4], mx = -INFINITY;
+                    for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool valid = t0 + 4 * g4 + r < t_end;
-                        sv[r] = valid ? s[r] * sc : -INFINITY;
-                        mx = fmaxf(mx, sv[r]);
-                    }
+                        for (int r = 0; r < 4; ++r) {
+                            const bool valid = tg + 16 * tau + 4 * g4 + r < t_end;
+                            const float sv = s[tau][r] * sc;
+                            bad |= (int)valid & (int)outside_band(sv, p.lo, p.hi);
+                            const float e = exp2_hw(fmaf(sv, kLog2e, nphi));
+                            w[tau][r] = valid ? e : 0.f;
+                            lsum += w[tau][r];
+                        }
+                } else {
+                    float sv[NT][4], mx = -INFINITY;
+#pragma unroll
+                    for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool valid = tg + 16 * tau + 4 * g4 + r < t_end;
+                            sv[tau][r] = valid ? s[tau][r] * sc : -INFINITY;
+                            mx = fmaxf(mx, sv[tau][r]);
+                        }
                     mx = fmaxf(mx, __shfl_xor(mx, 16));
                     mx = fmaxf(mx, __shfl_xor(mx, 32));
                     const float mnew = fmaxf(mrun, mx);
@@ -367,24 +485,42 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_bf16_kernel(Params p)
                     for (int dt = 0; dt < 8; ++dt) o[dt] *= f;
                     lsum *= f;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        w[r] = (sv[r] == -INFINITY) ? 0.f : exp2_hw((sv[r] - mnew) * kLog2e);
-                        lsum += w[r];
-                    }
+                    for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            w[tau][r] = (sv[tau][r] == -INFINITY) ? 0.f
+                                                                  : exp2_hw((sv[tau][r] - mnew) * kLog2e);
+                            lsum += w[tau][r];
+                        }
                     mrun = mnew;
                 }
-                uint32_t h01, h23, l01, l23;
-                split_pair(w[0], w[1], h01, l01);
-                split_pair(w[2], w[3], h23, l23);
-                const u32x2 ph = {h01, h23}, pl = {l01, l23};
+                if constexpr (FP8) {
+                    // P^T over 32 tokens: k = 8*g4 + j <-> tile j/4, row 4*g4 + j%4
+                    uint32_t h0w, h1w, h2w, h3w, l0w, l1w, l2w, l3w;
+                    split_pair(w[0][0], w[0][1], h0w, l0w);
+                    split_pair(w[0][2], w[0][3], h1w, l1w);
+                    split_pair(w[NT - 1][0], w[NT - 1][1], h2w, l2w);
+                    split_pair(w[NT - 1][2], w[NT - 1][3], h3w, l3w);
+                    const u32x4 ph = {h0w, h1w, h2w, h3w}, pl = {l0w, l1w, l2w, l3w};
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    o[dt] = mfma16(va[u][dt], ph, o[dt]);
-                    o[dt] = mfma16(va[u][dt], pl, o[dt]);
+                    for (int dt = 0; dt < 8; ++dt) {
+                        const u32x4 va = e4m3x8_to_bf16(vraw[u][dt].x, vraw[u][dt].y);
+                        o[dt] = mfma_bf16(va, ph, o[dt]);
+                        o[dt] = mfma_bf16(va, pl, o[dt]);
+                    }
+                } else {
+                    uint32_t h01, h23, l01, l23;
+                    split_pair(w[0][0], w[0][1], h01, l01);
+                    split_pair(w[0][2], w[0][3], h23, l23);
+                    const u32x2 ph = {h01, h23}, pl = {l01, l23};
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) {
+                        o[dt] = mfma16(vraw[u][dt], ph, o[dt]);
+                        o[dt] = mfma16(vraw[u][dt], pl, o[dt]);
+                    }
                 }
             }
         }
-
         // per-head weight sums and flags over the 4 lane groups
         lsum += __shfl_xor(lsum, 16);
         lsum += __shfl_xor(lsum, 32);

@@ -69,6 +69,7 @@ def _valid_desc(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(num_q_heads=63), -2), (dict(head_dim=64), -2), (dict(chunk_size=16), -2),
     (dict(chunk_size=100), -2), (dict(max_seq_len=0), -2), (dict(batch=0), -2),
+    (dict(max_seq_len=(1 << 23) + 1), -2),
     (dict(page_size=24, max_blocks_per_seq=2048, num_pages=10), -2),
     (dict(page_size=16, max_blocks_per_seq=10, num_pages=10), -2),
     (dict(page_size=64, chunk_size=32, max_blocks_per_seq=1024, num_pages=10), -2),
