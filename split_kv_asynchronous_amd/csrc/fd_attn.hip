@@ -6,9 +6,11 @@
 
 #include "fd_chunk.h"
 #include "fd_common.h"
+#include "fd_coop.h"
 #include "fd_merge.h"
 #include "fd_mfma.h"
 #include "fd_valu.h"
+
 
 namespace {
 
@@ -74,21 +76,13 @@ void launch_valu(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEv
     hipExtLaunchKernelGGL((fd::partial_valu_kernel<KV, QT, PAGED>), grid, dim3(256), 0, s, e0, e1, 0, p);
 }
 
-template <int KV, int QT, bool PAGED>
-void launch_fallback(const Params &p, int nblk, hipStream_t s)
-{
-    hipLaunchKernelGGL((fd::fallback_kernel<KV, QT, PAGED>), dim3(nblk), dim3(1024), 0, s, p);
-}
-
 // Dispatch on (kv dtype, q dtype, paged) for the vector path.
-template <bool FALLBACK>
-void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, int nblk, hipStream_t s,
-                   hipEvent_t e0, hipEvent_t e1)
+void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, hipStream_t s, hipEvent_t e0,
+                   hipEvent_t e1)
 {
 #define FD_CASE(KV, QT, PG)                                                   \
     if (kv == KV && qt == QT && paged == PG) {                                \
-        if (FALLBACK) launch_fallback<KV, QT, PG>(p, nblk, s);                \
-        else launch_valu<KV, QT, PG>(p, grid, s, e0, e1);                     \
+        launch_valu<KV, QT, PG>(p, grid, s, e0, e1);                          \
         return;                                                               \
     }
     FD_CASE(FD_F32, FD_F32, false) FD_CASE(FD_F32, FD_F32, true)
@@ -198,26 +192,34 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     (void)hipGetLastError();   // clear a stale error so the checks below see only ours
     if (use_mfma) {
         p.heads_per_block = heads_per_block(p.group);
-        // one workgroup per unit; workgroups past the real units exit at once.
-        // The unit index is blockIdx.y * gridDim.x + blockIdx.x.
+        // One workgroup per unit; workgroups past the real units exit at once.
+        // The unit index is blockIdx.y * gridDim.x + blockIdx.x.  bf16 caches
+        // run the per-wavefront-ring kernel, E4M3FN caches the cooperative
+        // one (each measured the faster for its format).
         const size_t units = (size_t)maxch * (p.hq / p.heads_per_block) * p.batch;
         const unsigned gx = (unsigned)(units < ((size_t)1 << 20) ? units : ((size_t)1 << 20));
         const dim3 flat(gx, (unsigned)((units + gx - 1) / gx));
-        using Sh = fd::chunk::DefaultShape;
-        const dim3 blk(Sh::waves * 64);
-#define FD_CHUNK_LAUNCH(KV, PG)                                                                  \
-        hipExtLaunchKernelGGL((fd::chunk::chunk_kernel<KV, PG, Sh>), flat, blk, 0, stream, ev0, ev1, 0, p)
+        using ChunkShape = fd::chunk::DefaultShape;
+        using CoopShape = fd::coop::DefaultShape;
+        const dim3 blk_chunk(ChunkShape::waves * 64), blk_coop(CoopShape::waves * 64);
         if (kv == FD_BF16) {
-            if (paged) FD_CHUNK_LAUNCH(FD_BF16, true);
-            else FD_CHUNK_LAUNCH(FD_BF16, false);
+            if (paged)
+                hipExtLaunchKernelGGL((fd::chunk::chunk_kernel<FD_BF16, true, ChunkShape>), flat, blk_chunk, 0,
+                                      stream, ev0, ev1, 0, p);
+            else
+                hipExtLaunchKernelGGL((fd::chunk::chunk_kernel<FD_BF16, false, ChunkShape>), flat, blk_chunk, 0,
+                                      stream, ev0, ev1, 0, p);
         } else {
-            if (paged) FD_CHUNK_LAUNCH(FD_FP8_E4M3FN, true);
-            else FD_CHUNK_LAUNCH(FD_FP8_E4M3FN, false);
+            if (paged)
+                hipExtLaunchKernelGGL((fd::coop::chunk_kernel<FD_FP8_E4M3FN, true, CoopShape>), flat, blk_coop, 0,
+                                      stream, ev0, ev1, 0, p);
+            else
+                hipExtLaunchKernelGGL((fd::coop::chunk_kernel<FD_FP8_E4M3FN, false, CoopShape>), flat, blk_coop,
+                                      0, stream, ev0, ev1, 0, p);
         }
-#undef FD_CHUNK_LAUNCH
     } else {
         p.heads_per_block = 1;
-        dispatch_valu<false>(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), 0, stream, ev0, ev1);
+        dispatch_valu(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), stream, ev0, ev1);
     }
     if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
 

@@ -30,8 +30,7 @@
 
 #include <type_traits>
 
-#include "fd_common.h"
-#include "fd_mfma.h"
+#include "fd_ring.h"
 
 #ifndef FD_CHUNK_WAVES
 #define FD_CHUNK_WAVES 4
@@ -47,7 +46,8 @@ namespace fd {
 
 namespace chunk {
 
-constexpr int kGroupBytes = 4096;                  // one compute group of K (or V)
+using namespace ring;
+
 constexpr int kRedStride = 16 * kHeadDim + 32;     // one wave's O^T, then l and flag-or-max per head
 
 template <int NW, int NSUB, int NST>
@@ -66,120 +66,6 @@ struct Shape {
 };
 
 using DefaultShape = Shape<FD_CHUNK_WAVES, FD_CHUNK_SUBTILES, FD_CHUNK_STAGES>;
-
-// Per storage format: row bytes, tokens per compute group, piece rotation.
-template <int KV> struct Fmt;
-template <> struct Fmt<FD_BF16> {
-    static constexpr int row = 256, group = 16, slots = 16;
-    // rotation of the 16-byte pieces of group row t (0..15)
-    static FD_DEV int rot(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
-};
-template <> struct Fmt<FD_FP8_E4M3FN> {
-    static constexpr int row = 128, group = 32, slots = 8;
-    // rotation of the 16-byte pieces of group row t (0..31)
-    static FD_DEV int rot(int t) { return (t + 4 * ((t >> 4) & 1)) & 7; }
-};
-
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-template <int N>
-FD_DEV void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// wait until at most k ring blocks (of D DMA instructions each) are in flight
-template <int D, int KMAX>
-FD_DEV void wait_ring(int k)
-{
-    if (KMAX > 3 && k >= 4) wait_vmcnt<(KMAX > 3 ? 4 * D : 0)>();
-    else if (KMAX > 2 && k == 3) wait_vmcnt<(KMAX > 2 ? 3 * D : 0)>();
-    else if (KMAX > 1 && k == 2) wait_vmcnt<(KMAX > 1 ? 2 * D : 0)>();
-    else if (KMAX > 0 && k == 1) wait_vmcnt<D>();
-    else wait_vmcnt<0>();
-}
-
-FD_DEV f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
-// 4 E4M3FN codes -> 4 bf16 (exact), packed as two dwords
-FD_DEV u32x2 e4m3x4_to_bf16(uint32_t w)
-{
-    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
-}
-
-FD_DEV u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi)
-{
-    const u32x2 a = e4m3x4_to_bf16(lo), b = e4m3x4_to_bf16(hi);
-    return u32x4{a.x, a.y, b.x, b.y};
-}
-
-// wave-wide inclusive prefix sum
-FD_DEV int wave_scan(int x, int lane)
-{
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    return x;
-}
-
-struct Unit {
-    int b, hb, c;
-    bool ok;
-};
-
-// The u-th unit of "full chunks of every sequence, then the partial last
-// chunks", sequence-major inside each part, head blocks outer, chunks inner.
-FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
-{
-    Unit r = {0, 0, 0, false};
-    int base = 0;
-#pragma unroll 1
-    for (int part = 0; part < 2; ++part) {
-#pragma unroll 1
-        for (int b0 = 0; b0 < p.batch; b0 += 64) {
-            const int b = b0 + lane;
-            int cnt = 0;
-            if (b < p.batch) {
-                const int L = seq_len_of(p, b);
-                cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk) ? nhb : 0);
-            }
-            const int incl = wave_scan(cnt, lane);
-            const int total = __shfl(incl, 63);
-            if (u < base + total) {
-                const uint64_t m = __ballot(base + incl > u);
-                const int hit = __builtin_ctzll(m);
-                const int before = base + __shfl(incl - cnt, hit);
-                const int bb = b0 + hit;
-                const int L = seq_len_of(p, bb);
-                const int rem = u - before;
-                r.b = bb;
-                if (part == 0) {
-                    const int F = L / p.chunk;
-                    r.hb = rem / F;
-                    r.c = rem % F;
-                } else {
-                    r.hb = rem;
-                    r.c = L / p.chunk;
-                }
-                r.ok = true;
-                return r;
-            }
-            base += total;
-        }
-    }
-    return r;
-}
 
 template <int KV, bool PAGED, typename S>
 __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
@@ -548,7 +434,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
         float acc = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) acc += red[w2 * kRedStride + d * 16 + hh];
-        const size_t slot = ((size_t)b * p.hq + h0 + hh) * p.maxch + c;
+        const size_t slot = part_slot(p, b, h0 + hh, c);
         p.o_part[slot * kHeadDim + d] = acc;
     }
     if (wave == 0) {
@@ -560,7 +446,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
                 l += red[w2 * kRedStride + 2048 + lane];
                 f |= red[w2 * kRedStride + 2064 + lane] != 0.f;
             }
-            const size_t slot = ((size_t)b * p.hq + h0 + lane) * p.maxch + c;
+            const size_t slot = part_slot(p, b, h0 + lane, c);
             p.l_part[slot] = l;
             p.m_part[slot] = p.phi;
             p.cflag[slot] = f;
@@ -590,7 +476,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
             const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
             acc += red[w2 * kRedStride + d * 16 + hh] * f;
         }
-        const size_t slot = ((size_t)b * p.hq + h0 + hh) * p.maxch + c;
+        const size_t slot = part_slot(p, b, h0 + hh, c);
         p.o_part[slot * kHeadDim + d] = acc;
     }
     if (threadIdx.x < GB && ((fmask >> threadIdx.x) & 1)) {
@@ -605,7 +491,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
             const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
             l += red[w2 * kRedStride + 2048 + hh] * f;
         }
-        const size_t slot = ((size_t)b * p.hq + h0 + hh) * p.maxch + c;
+        const size_t slot = part_slot(p, b, h0 + hh, c);
         p.l_part[slot] = l;
         p.m_part[slot] = M;
     }

@@ -50,6 +50,13 @@ FD_DEV const __attribute__((address_space(4))) T *as_const(const T *ptr)
     return (const __attribute__((address_space(4))) T *)(ptr);
 }
 
+// Workspace slot of the partial of (sequence b, query head h, chunk c): the
+// partials of one chunk of a sequence are contiguous over the heads.
+FD_DEV size_t part_slot(const Params &p, int b, int h, int c)
+{
+    return ((size_t)b * p.maxch + c) * p.hq + h;
+}
+
 FD_DEV int seq_len_of(const Params &p, int b)
 {
     int L = as_const(p.seq_lens)[b];

@@ -35,12 +35,13 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
     const int b = live ? row / p.hq : 0, h = live ? row % p.hq : 0;
     const int L = live ? seq_len_of(p, b) : 0;
     const int nch = (L + p.chunk - 1) / p.chunk;
-    const size_t base = (size_t)row * p.maxch;
+    const size_t base = part_slot(p, b, h, 0);   // chunk c at base + c * hq
+    const size_t cs = p.hq;
     const int rw0 = (wave / RW) * RW;                // first wavefront of this row
 
     // flagged chunks of the row, and the largest chunk maximum if any
     int nflag = 0;
-    for (int c = sub * 64 + lane; c < nch; c += 64 * RW) nflag += p.cflag[base + c];
+    for (int c = sub * 64 + lane; c < nch; c += 64 * RW) nflag += p.cflag[base + c * cs];
 #pragma unroll
     for (int x = 1; x < 64; x <<= 1) nflag += __shfl_xor(nflag, x);
     if (RW > 1) {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
     float M = p.phi;
     if (any) {
         M = -INFINITY;
-        for (int c = sub * 64 + lane; c < nch; c += 64 * RW) M = fmaxf(M, p.m_part[base + c]);
+        for (int c = sub * 64 + lane; c < nch; c += 64 * RW) M = fmaxf(M, p.m_part[base + c * cs]);
 #pragma unroll
         for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
     }
@@ -78,9 +79,9 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
         float l[4], f[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            v[u] = *reinterpret_cast<const f32x4 *>(op + (size_t)(c + u * STEP) * kHeadDim);
-            l[u] = p.l_part[base + c + u * STEP];
-            f[u] = any ? p.m_part[base + c + u * STEP] : M;
+            v[u] = *reinterpret_cast<const f32x4 *>(op + (size_t)(c + u * STEP) * cs * kHeadDim);
+            l[u] = p.l_part[base + (c + u * STEP) * cs];
+            f[u] = any ? p.m_part[base + (c + u * STEP) * cs] : M;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -90,10 +91,10 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
         }
     }
     for (; c < nch; c += STEP) {
-        const float mc = any ? p.m_part[base + c] : M;
+        const float mc = any ? p.m_part[base + c * cs] : M;
         const float g = (mc == M) ? 1.f : exp2_hw((mc - M) * kLog2e);
-        acc += *reinterpret_cast<const f32x4 *>(op + (size_t)c * kHeadDim) * g;
-        lacc = fmaf(p.l_part[base + c], g, lacc);
+        acc += *reinterpret_cast<const f32x4 *>(op + (size_t)c * cs * kHeadDim) * g;
+        lacc = fmaf(p.l_part[base + c * cs], g, lacc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);

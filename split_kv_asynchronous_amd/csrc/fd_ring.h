@@ -1,0 +1,134 @@
+// Pieces shared by the grouped-query chunk kernels: cache formats and their
+// LDS piece rotation, vector-memory waits for the DMA rings, matrix-core and
+// E4M3FN conversion helpers, and the unit list.
+#pragma once
+
+#include "fd_common.h"
+#include "fd_mfma.h"
+
+namespace fd {
+
+namespace ring {
+
+constexpr int kGroupBytes = 4096;   // one compute group of K (or V): 16 bf16 or 32 E4M3FN tokens
+
+// Per storage format: row bytes, tokens per compute group, piece rotation.
+// A cache row is moved into LDS as 16-byte pieces; piece j of group row t
+// lands in slot (j + rot(t)) mod slots, which keeps the K fragment reads
+// (ds_read_b128) and the transposing V reads free of bank conflicts.
+template <int KV> struct Fmt;
+template <> struct Fmt<FD_BF16> {
+    static constexpr int row = 256, group = 16, slots = 16;
+    static FD_DEV int rot(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }   // t = 0..15
+};
+template <> struct Fmt<FD_FP8_E4M3FN> {
+    static constexpr int row = 128, group = 32, slots = 8;
+    static FD_DEV int rot(int t) { return (t + 4 * ((t >> 4) & 1)) & 7; }   // t = 0..31
+};
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+FD_DEV void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most min(k, KMAX) * D vector-memory operations are in flight.
+// Loads complete in order, so with k = the ring blocks issued after block X
+// (D operations each) this waits exactly for block X and everything older.
+template <int D, int KMAX>
+FD_DEV void wait_ring(int k)
+{
+    if constexpr (KMAX <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (k >= KMAX) wait_vmcnt<KMAX * D>();
+        else wait_ring<D, KMAX - 1>(k);
+    }
+}
+
+FD_DEV f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// 4 E4M3FN codes -> 4 bf16 (exact), packed as two dwords
+FD_DEV u32x2 e4m3x4_to_bf16(uint32_t w)
+{
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
+FD_DEV u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    const u32x2 a = e4m3x4_to_bf16(lo), b = e4m3x4_to_bf16(hi);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+
+// wave-wide inclusive prefix sum
+FD_DEV int wave_scan(int x, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+struct Unit {
+    int b, hb, c;
+    bool ok;
+};
+
+// The u-th unit of "full chunks of every sequence, then the partial last
+// chunks", sequence-major inside each part, head blocks outer, chunks inner.
+FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
+{
+    Unit r = {0, 0, 0, false};
+    int base = 0;
+#pragma unroll 1
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll 1
+        for (int b0 = 0; b0 < p.batch; b0 += 64) {
+            const int b = b0 + lane;
+            int cnt = 0;
+            if (b < p.batch) {
+                const int L = seq_len_of(p, b);
+                cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk) ? nhb : 0);
+            }
+            const int incl = wave_scan(cnt, lane);
+            const int total = __builtin_amdgcn_readlane(incl, 63);
+            if (u < base + total) {
+                const uint64_t m = __ballot(base + incl > u);
+                const int hit = __builtin_ctzll(m);
+                const int before = base + __builtin_amdgcn_readlane(incl - cnt, hit);
+                const int bb = b0 + hit;
+                const int L = seq_len_of(p, bb);
+                const int rem = u - before;
+                r.b = bb;
+                if (part == 0) {
+                    const int F = L / p.chunk;
+                    r.hb = rem / F;
+                    r.c = rem % F;
+                } else {
+                    r.hb = rem;
+                    r.c = L / p.chunk;
+                }
+                r.ok = true;
+                return r;
+            }
+            base += total;
+        }
+    }
+    return r;
+}
+
+}  // namespace ring
+}  // namespace fd

@@ -114,7 +114,7 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
         red[wave * 132 + 130] = wave_bad ? 1.f : 0.f;
     }
     __syncthreads();
-    const size_t slot = ((size_t)b * p.hq + h) * p.maxch + c;
+    const size_t slot = part_slot(p, b, h, c);
     float M = p.phi;
     if constexpr (ONLINE) {
         M = -INFINITY;
