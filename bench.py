@@ -1,12 +1,15 @@
 """Benchmark: unified-max split-KV decode attention on one MI355X.
 
-A step is one fd_attn_decode call (chunk kernel + fallback pass + merge) over
-the 32K-context grouped-query workload (batch 32, 64 query / 8 KV heads,
-head_dim 128, ragged lengths U{1024..32768}, bf16 cache, chunk 1024), inputs
-resident in HBM.  Prints one JSON line: KV GB/s (valid K and V bytes / time
-per call), calls/s, the chunk kernel's roofline (algorithmic bytes / its
-average duration from HIP events recorded around it on its stream), and the
-float64 CPU oracle timed on a bounded sample as a reported baseline.
+A step is one fd_attn_decode call -- the chunk kernel (partials, in-place
+recompute of out-of-band chunks) and the merge, which for grids beyond one
+round of workgroups is a second small launch -- over the 32K-context
+grouped-query workload (batch 32, 64 query / 8 KV heads, head_dim 128, ragged
+lengths U{1024..32768}, bf16 cache, chunk 1024), inputs resident in HBM.
+Prints one JSON line: KV GB/s (valid K and V bytes / time per call),
+calls/s, the chunk kernel's roofline (algorithmic bytes / its average
+duration from start/stop events stamped by its own dispatch on its stream),
+and the float64 CPU oracle timed on a bounded sample as a reported
+baseline.
 
     python bench.py [--steps K] [--warmup W] [--config N]
 """
@@ -36,15 +39,31 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def partial_kernel_bytes(prob) -> int:
+def kernel_bytes(prob, fused) -> int:
     """Algorithmic bytes the chunk kernel must move: every valid K and V
-    element once, the queries, the lengths and the used block-table entries."""
+    element once, the queries, the lengths and the used block-table entries,
+    plus the output rows and flags when it also merges.  Chunk partials are
+    overhead, not counted."""
     qb = prob.q.nbytes
     lens = np.clip(prob.seq_lens, 0, prob.max_seq_len).astype(np.int64)
     extra = prob.seq_lens.nbytes
     if prob.page_size:
         extra += int((-(-lens // prob.page_size)).sum()) * 4
+    if fused:
+        rows = prob.batch * prob.num_q_heads
+        extra += rows * prob.head_dim * 4 + rows
     return prob.kv_bytes() + qb + extra
+
+
+def merges_in_chunk_kernel(prob) -> bool:
+    """Whether the library merges inside the chunk kernel for this problem
+    (grids of at most 512 units; the rule lives in fd_attn.hip)."""
+    g = prob.num_q_heads // prob.num_kv_heads
+    heads = max(k for k in range(1, min(g, 16) + 1) if g % k == 0) if g > 1 else 1
+    mfma = g > 1 and prob.q_dtype == "bf16" and prob.kv_dtype != "f32"
+    blocks = prob.num_q_heads // heads if mfma else prob.num_q_heads
+    maxch = -(-prob.max_seq_len // prob.chunk_size)
+    return maxch * blocks * prob.batch <= 512
 
 
 def cpu_baseline(prob, min_seconds=10.0, max_passes=20):
@@ -81,7 +100,7 @@ def cpu_baseline(prob, min_seconds=10.0, max_passes=20):
 
 
 def load_traffic(workload: str):
-    """HBM bytes per chunk-kernel launch from committed rocprofv3 counter runs,
+    """HBM bytes per kernel launch from committed rocprofv3 counter runs,
     if they were taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -127,9 +146,9 @@ def main():
         dp.run()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back calls; the chunk and merge kernels of every
-    # call stamp their start/stop into that call's events
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # timed region: K back-to-back calls; the chunk kernel of every call stamps
+    # its start/stop into that call's events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for row in evs:            # create the HIP events before the timed region
         for e in row:
             e.record(stream)
@@ -140,16 +159,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     per_call = elapsed / K
-    # events 0/1 and 2/3 are stamped by the chunk and merge kernels' dispatches
-    chunk_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
-    between_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
-    merge_ms = [evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]
-    call_ms = [evs[i][0].elapsed_time(evs[i][3]) for i in range(K)]
+    # events 0/1 are stamped by the chunk kernel's dispatch
+    kernel_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
 
     kv = prob.kv_bytes()
     value = kv / per_call / 1e9
-    chunk_s = float(np.mean(chunk_ms)) / 1e3
-    achieved = partial_kernel_bytes(prob) / chunk_s / 1e9
+    kernel_s = float(np.mean(kernel_ms)) / 1e3
+    fused = merges_in_chunk_kernel(prob)
+    nbytes = kernel_bytes(prob, fused)
+    achieved = nbytes / kernel_s / 1e9
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -179,15 +197,12 @@ def main():
                    "phi": prob.phi, "band": [prob.phi - prob.a, prob.phi + prob.b]},
         "calls_per_s": round(1.0 / per_call, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "stage_ms": {"chunk": round(float(np.mean(chunk_ms)), 5),
-                     "between": round(float(np.mean(between_ms)), 5),
-                     "merge": round(float(np.mean(merge_ms)), 5),
-                     "call_events": round(float(np.mean(call_ms)), 5)},
+        "kernel_ms": round(float(np.mean(kernel_ms)), 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(prob.workload),
-                     "kernel": "partial (chunk) kernel",
-                     "bytes_per_launch": partial_kernel_bytes(prob)},
+                     "kernel": "chunk kernel" + (" (with the merge)" if fused else ""),
+                     "bytes_per_launch": nbytes},
         "source_hash": source_hash(),
     }
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(prob)

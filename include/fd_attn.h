@@ -23,11 +23,14 @@
  * up to fp32 rounding.
  *
  * Ownership and threading: every pointer is device memory owned by the
- * caller.  The library never allocates, frees or synchronises and keeps no
- * global state; a call only enqueues kernels on `stream` and returns.  out,
- * fallback_flags and the workspace are valid once the stream has completed
- * the call.  Calls may run concurrently on different streams as long as each
- * has its own workspace and outputs.
+ * caller.  The library never allocates, frees or synchronises; its only
+ * global state is a call counter that gives every call a fresh epoch.  A call
+ * enqueues its kernels on `stream` and returns (one kernel for small grids,
+ * where the merge runs inside it; a chunk kernel and a merge kernel
+ * otherwise).  out, fallback_flags and the
+ * workspace are valid once the stream has completed the call.  Calls may run
+ * concurrently on different streams as long as each has its own workspace
+ * and outputs; calls that share a workspace must be ordered (one stream).
  *
  * Errors: a call returns FD_OK (0) or a negative FD_ERR_* code.  On any
  * host-detected error nothing is enqueued.  Device-resident data cannot be
@@ -98,16 +101,20 @@ typedef struct {
     const float *v_scale;       /* [num_kv_heads] device fp32, required iff kv_dtype is fp8 */
     void *workspace;            /* device, 256-byte aligned, >= fd_attn_workspace_size() bytes */
     size_t workspace_bytes;
-    /* Optional instrumentation: NULL, or 4 caller-created events: start and
-     * stop of the chunk kernel, start and stop of the merge kernel, stamped
-     * by the kernels' own dispatches on `stream` (no extra stream work). */
+    /* Optional instrumentation: NULL, or 2 caller-created events: start and
+     * stop of the call's chunk kernel (which includes the merge when that runs
+     * in the same launch), stamped by its own dispatch on `stream` (no extra
+     * stream work). */
     hipEvent_t *stage_events;
 } fd_attn_desc_t;
 
 /* Bytes of workspace a call with this descriptor needs (0 if desc is NULL or
- * its sizes are invalid).  The workspace holds per-(row, chunk) partial sums;
- * its first 4 bytes hold, after a call completes, the int32 number of
- * (row, chunk) pairs that were recomputed with online softmax. */
+ * its sizes are invalid).  The workspace holds per-(row, chunk) partial sums
+ * and per-row-group completion counters; it needs no initialisation (the
+ * counters are tagged with a per-call epoch) and its contents between calls
+ * are the library's.  After a call completes, its first 4 bytes hold the
+ * uint32 number of (row, chunk) pairs that call recomputed with online
+ * softmax, and the next 4 bytes that call's epoch. */
 size_t fd_attn_workspace_size(const fd_attn_desc_t *desc);
 
 /* One decode-attention call (see the top of this file).  phi is the preset

@@ -158,10 +158,10 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
     ev_arr = None
     if stage_events is not None:
         handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in stage_events]
-        if len(handles) != 4 or not all(handles):
-            raise ValueError("stage_events: 4 created HIP events -- chunk start/stop, merge "
-                             "start/stop (record a torch event once to create it)")
-        ev_arr = (ctypes.c_void_p * 4)(*handles)
+        if len(handles) != 2 or not all(handles):
+            raise ValueError("stage_events: 2 created HIP events -- chunk kernel start/stop "
+                             "(record a torch event once to create it)")
+        ev_arr = (ctypes.c_void_p * 2)(*handles)
         desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/fd_attn.h: validation, workspace
 // carve-up, kernel choice and launches.  No allocation, no synchronisation.
 #include <hip/hip_ext.h>
+#include <atomic>
 #include <math.h>
 #include <string.h>
 
@@ -17,11 +18,12 @@ namespace {
 using fd::Params;
 
 constexpr size_t kAlign = 256;
+constexpr size_t kFusedMaxUnits = 512;   // grids up to this many units merge in the same launch
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t header, o_part, l_part, m_part, cflag, total;
+    size_t header, o_part, l_part, m_part, cflag, rg_count, total;
 };
 
 Layout layout_of(size_t rows, size_t maxch)
@@ -32,8 +34,19 @@ Layout layout_of(size_t rows, size_t maxch)
     L.l_part = align_up(L.o_part + rows * maxch * fd::kHeadDim * sizeof(float));
     L.m_part = align_up(L.l_part + rows * maxch * sizeof(float));
     L.cflag = align_up(L.m_part + rows * maxch * sizeof(float));
-    L.total = align_up(L.cflag + rows * maxch);
+    L.rg_count = align_up(L.cflag + rows * maxch);
+    L.total = align_up(L.rg_count + rows * sizeof(unsigned long long));
     return L;
+}
+
+// A fresh nonzero epoch for every call (see fd_merge.h): the workspace's
+// counters carry the epoch of the call that last wrote them.
+uint32_t next_epoch()
+{
+    static std::atomic<uint32_t> epoch{0};
+    uint32_t e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (e == 0) e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e;
 }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -158,7 +171,9 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     p.v_scale = kv == FD_FP8_E4M3FN ? d->v_scale : nullptr;
     p.out = out;
     p.flags = fallback_flags;
-    p.counter = reinterpret_cast<int32_t *>(ws + L.header);
+    p.count_word = reinterpret_cast<unsigned long long *>(ws + L.header);
+    p.rg_count = reinterpret_cast<unsigned long long *>(ws + L.rg_count);
+    p.epoch = next_epoch();
     p.o_part = reinterpret_cast<float *>(ws + L.o_part);
     p.l_part = reinterpret_cast<float *>(ws + L.l_part);
     p.m_part = reinterpret_cast<float *>(ws + L.m_part);
@@ -182,12 +197,16 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
 
     const bool paged = d->page_size != 0;
     const bool use_mfma = p.group > 1 && qt == FD_BF16 && kv != FD_F32;
-    // Optional stage timing: the chunk and merge kernels are launched with
-    // start/stop events stamped by their own dispatch packets, so timing adds
-    // no marker packets between the kernels.
+    // Optional timing: the chunk kernel is launched with start/stop events
+    // stamped by its own dispatch packet, so timing adds no marker packets.
     hipEvent_t *ev = d->stage_events;
     hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;
-    hipEvent_t ev2 = ev ? ev[2] : nullptr, ev3 = ev ? ev[3] : nullptr;
+
+    // merge inside the chunk kernel when its grid is at most one round of
+    // workgroups (a latency-bound call, where a second launch would double the
+    // cost); larger grids merge in a separate launch
+    const size_t grid_units = (size_t)maxch * (use_mfma ? p.hq / heads_per_block(p.group) : p.hq) * p.batch;
+    p.fused = grid_units <= kFusedMaxUnits;
 
     (void)hipGetLastError();   // clear a stale error so the checks below see only ours
     if (use_mfma) {
@@ -223,19 +242,20 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     }
     if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
 
-    // Both kernels recompute an out-of-band chunk inside the workgroup that
-    // found it: no separate fallback pass.
-
-    // rows with many chunks get several wavefronts each
-    if (maxch >= 64)
-        hipExtLaunchKernelGGL(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, ev2,
-                              ev3, 0, p);
-    else if (maxch >= 16)
-        hipExtLaunchKernelGGL(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0,
-                              stream, ev2, ev3, 0, p);
-    else
-        hipExtLaunchKernelGGL(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                              stream, ev2, ev3, 0, p);
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    // Every kernel recomputes an out-of-band chunk inside the workgroup that
+    // found it.  Small grids merge inside the same launch (p.fused); larger
+    // ones in a second launch, RW wavefronts per row for rows with many chunks.
+    if (!p.fused) {
+        if (maxch >= 64)
+            hipExtLaunchKernelGGL(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, nullptr,
+                                  nullptr, 0, p);
+        else if (maxch >= 16)
+            hipExtLaunchKernelGGL(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0,
+                                  stream, nullptr, nullptr, 0, p);
+        else
+            hipExtLaunchKernelGGL(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                                  stream, nullptr, nullptr, 0, p);
+        if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    }
     return FD_OK;
 }

@@ -82,8 +82,8 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     constexpr int LPR = 64 / RPI;                  // lanes per row in a DMA instruction
     constexpr int DMA_TILE = S::tile / 1024;       // DMA instructions per K (or V) tile
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
-    __shared__ int flagged_heads;
-    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) *p.counter = 0;
+    __shared__ int flagged_heads, last_flag, merged;
+    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) epoch_add(p.count_word, p.epoch, 0);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) acc += red[w2 * kRedStride + d * 16 + hh];
         const size_t slot = part_slot(p, b, h0 + hh, c);
-        p.o_part[slot * kHeadDim + d] = acc;
+        part_store(p, p.o_part + slot * kHeadDim + d, acc);
     }
     if (wave == 0) {
         int f = 0;
@@ -447,54 +447,58 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
                 f |= red[w2 * kRedStride + 2064 + lane] != 0.f;
             }
             const size_t slot = part_slot(p, b, h0 + lane, c);
-            p.l_part[slot] = l;
-            p.m_part[slot] = p.phi;
-            p.cflag[slot] = f;
+            part_store(p, p.l_part + slot, l);
+            part_store(p, p.m_part + slot, p.phi);
+            part_store(p, p.cflag + slot, (uint8_t)f);
         }
         const uint64_t m = __ballot(f);
         if (lane == 0) flagged_heads = (int)(uint32_t)m;
     }
     __syncthreads();
     const int fmask = flagged_heads;
-    if (fmask == 0) return;
 
     // ---- a score of this chunk left the safe band (FlashDecoding++ theory
     // page, section 3): redo the chunk with online softmax and replace the
     // partials of the flagged heads
-    __syncthreads();   // everyone has read red[] before the ring is refilled
-    run(std::true_type{});
-    for (int idx = threadIdx.x; idx < GB * kHeadDim; idx += NW * 64) {
-        const int hh = idx >> 7, d = idx & 127;
-        if (!((fmask >> hh) & 1)) continue;
-        float M = -INFINITY;
+    if (fmask != 0) {
+        __syncthreads();   // everyone has read red[] before the ring is refilled
+        run(std::true_type{});
+        for (int idx = threadIdx.x; idx < GB * kHeadDim; idx += NW * 64) {
+            const int hh = idx >> 7, d = idx & 127;
+            if (!((fmask >> hh) & 1)) continue;
+            float M = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, red[w2 * kRedStride + 2064 + hh]);
-        float acc = 0.f;
+            for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, red[w2 * kRedStride + 2064 + hh]);
+            float acc = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            const float mw = red[w2 * kRedStride + 2064 + hh];
-            const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
-            acc += red[w2 * kRedStride + d * 16 + hh] * f;
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const float mw = red[w2 * kRedStride + 2064 + hh];
+                const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
+                acc += red[w2 * kRedStride + d * 16 + hh] * f;
+            }
+            const size_t slot = part_slot(p, b, h0 + hh, c);
+            part_store(p, p.o_part + slot * kHeadDim + d, acc);
         }
-        const size_t slot = part_slot(p, b, h0 + hh, c);
-        p.o_part[slot * kHeadDim + d] = acc;
-    }
-    if (threadIdx.x < GB && ((fmask >> threadIdx.x) & 1)) {
-        const int hh = threadIdx.x;
-        float M = -INFINITY;
+        if (threadIdx.x < GB && ((fmask >> threadIdx.x) & 1)) {
+            const int hh = threadIdx.x;
+            float M = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, red[w2 * kRedStride + 2064 + hh]);
-        float l = 0.f;
+            for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, red[w2 * kRedStride + 2064 + hh]);
+            float l = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            const float mw = red[w2 * kRedStride + 2064 + hh];
-            const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
-            l += red[w2 * kRedStride + 2048 + hh] * f;
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const float mw = red[w2 * kRedStride + 2064 + hh];
+                const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
+                l += red[w2 * kRedStride + 2048 + hh] * f;
+            }
+            const size_t slot = part_slot(p, b, h0 + hh, c);
+            part_store(p, p.l_part + slot, l);
+            part_store(p, p.m_part + slot, M);
         }
-        const size_t slot = part_slot(p, b, h0 + hh, c);
-        p.l_part[slot] = l;
-        p.m_part[slot] = M;
     }
+
+    // ---- publish the unit; the last unit of the row group merges it
+    if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) merge_group<NW>(p, b, h0, GB, merged);
 }
 
 }  // namespace chunk

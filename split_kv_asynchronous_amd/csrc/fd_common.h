@@ -31,7 +31,10 @@ struct Params {
     float *l_part;        // [B][Hq][maxch]
     float *m_part;        // [B][Hq][maxch]
     uint8_t *cflag;       // [B][Hq][maxch]
-    int32_t *counter;     // recomputed (row, chunk) pairs
+    unsigned long long *count_word;   // {recomputed (row, chunk) pairs, epoch} of the call
+    unsigned long long *rg_count;     // [B][Hq] epoch-tagged unit counts per row group (first head)
+    uint32_t epoch;                   // this call's epoch (never 0)
+    int fused;                        // the last workgroup of a row group merges it (else a merge launch)
     int batch, hq, hkv, group;   // group = hq / hkv
     int heads_per_block;         // query heads one chunk workgroup serves (MFMA path)
     int max_seq_len, chunk, maxch;

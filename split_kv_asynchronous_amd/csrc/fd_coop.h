@@ -93,7 +93,8 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     constexpr int DT = 8 / S::waves;               // 16-component tiles of O per wavefront
     constexpr int NT = FP8 ? 2 : 1;                // 16-token score tiles per group
     __shared__ __attribute__((aligned(1024))) uint8_t ring[S::lds];
-    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) *p.counter = 0;
+    __shared__ int last_flag, merged;
+    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) epoch_add(p.count_word, p.epoch, 0);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -437,29 +438,33 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     run(std::false_type{});
     if (head_ok) {
 #pragma unroll
-        for (int dl = 0; dl < DT; ++dl) *reinterpret_cast<f32x4 *>(orow + 16 * dl) = o[dl];
+        for (int dl = 0; dl < DT; ++dl) part_store4(p, orow + 16 * dl, o[dl]);
         if (wave == 0 && g4 == 0) {
-            p.l_part[slot] = lsum;
-            p.m_part[slot] = p.phi;
-            p.cflag[slot] = (uint8_t)(bad != 0);
+            part_store(p, p.l_part + slot, lsum);
+            part_store(p, p.m_part + slot, p.phi);
+            part_store(p, p.cflag + slot, (uint8_t)(bad != 0));
         }
     }
     const uint64_t fmask = __ballot(g4 == 0 && bad != 0);   // the same in every wavefront
-    if (fmask == 0) return;
 
     // ---- a score of this chunk left the safe band (FlashDecoding++ theory
     // page, section 3): redo the chunk with online softmax and replace the
     // partials of the flagged heads
-    __builtin_amdgcn_s_barrier();   // everyone is done with the ring
-    run(std::true_type{});
-    if (head_ok && ((fmask >> n) & 1)) {
+    if (fmask != 0) {
+        __builtin_amdgcn_s_barrier();   // everyone is done with the ring
+        run(std::true_type{});
+        if (head_ok && ((fmask >> n) & 1)) {
 #pragma unroll
-        for (int dl = 0; dl < DT; ++dl) *reinterpret_cast<f32x4 *>(orow + 16 * dl) = o[dl];
-        if (wave == 0 && g4 == 0) {
-            p.l_part[slot] = lsum;
-            p.m_part[slot] = mrun;
+            for (int dl = 0; dl < DT; ++dl) part_store4(p, orow + 16 * dl, o[dl]);
+            if (wave == 0 && g4 == 0) {
+                part_store(p, p.l_part + slot, lsum);
+                part_store(p, p.m_part + slot, mrun);
+            }
         }
     }
+
+    // ---- publish the unit; the last unit of the row group merges it
+    if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) merge_group<S::waves>(p, b, h0, GB, merged);
 }
 
 }  // namespace coop

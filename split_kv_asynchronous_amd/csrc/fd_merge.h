@@ -7,18 +7,225 @@
 // partials against different maxima (phi, or the chunk's own maximum) and is
 // merged with the ordinary max rescale of split-KV softmax (the split-KV
 // figure of section 1).
+//
+// Two placements.  A grid of at most one round of workgroups (a latency-bound
+// call) merges inside the chunk kernel: the last workgroup to finish a row
+// group merges it, and the call is one launch.  Larger grids merge in a
+// separate launch: there, the per-unit publication below (store completion
+// plus a device-scope atomic, under a saturated read stream) costs more than
+// the second launch (measured 1-33% slower on the large workloads).
+//
+// "Last" is decided by a counter per row group in the workspace.  Counters
+// are 64-bit words: the high half holds the epoch of the call that wrote it,
+// the low half a count.  Every call brings a new epoch, so a word left by an
+// earlier call (or never written) is re-based to this call's epoch by the
+// first workgroup that touches it -- the workspace needs no initialisation
+// -- and the last workgroup resets its row group's count to zero, so a
+// launch replayed with the same epoch also starts from zero.
+//
+// Visibility across the chip's L2 caches: partials are written and read with
+// device-coherent (agent-scope) accesses, which bypass the non-coherent cache
+// levels, and a workgroup waits for its partial stores to complete before it
+// bumps the counter.  The ordinary acquire/release fences would instead write
+// back and invalidate a whole L2 at every unit -- measured at 4-5x the time of
+// the call.
 #pragma once
 
 #include "fd_common.h"
 
 namespace fd {
 
-// RW wavefronts per row, 256 threads per workgroup (256 / (64 RW) rows each).
-// In a wavefront, lanes 0..31 take one chunk and lanes 32..63 the next, 4
-// components per lane, four chunk pairs in flight; the wavefronts of a row
-// split its chunks and meet in LDS.  The kernel also counts the recomputed
-// (row, chunk) pairs into the workspace counter (zeroed by this call's chunk
-// kernel).
+// Adds `add` to an epoch-tagged counter and returns the count after the add.
+// Once the word carries this call's epoch (it never loses it again within the
+// call) the add is one fetch-and-add; only the re-basing of a word left by an
+// earlier call takes a compare-and-swap, and a racing re-base makes the loser
+// retry through the fetch-and-add path.  (A compare-and-swap loop for every
+// add serialises the many units of a row group that finish together.)
+FD_DEV uint32_t epoch_add(unsigned long long *w, uint32_t epoch, uint32_t add)
+{
+    unsigned long long v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        if ((uint32_t)(v >> 32) == epoch)
+            return (uint32_t)__hip_atomic_fetch_add(w, (unsigned long long)add, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) + add;
+        if (__hip_atomic_compare_exchange_strong(w, &v, ((unsigned long long)epoch << 32) | add,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return add;
+    }
+}
+
+// Device-coherent stores and loads of partials.
+template <typename T>
+FD_DEV void put(T *ptr, T v)
+{
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+FD_DEV void put4(float *ptr, f32x4 v)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) put(ptr + i, v[i]);
+}
+
+template <typename T>
+FD_DEV T get(const T *ptr)
+{
+    return __hip_atomic_load(const_cast<T *>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+FD_DEV f32x4 get4(const float *ptr)
+{
+    return f32x4{get(ptr), get(ptr + 1), get(ptr + 2), get(ptr + 3)};
+}
+
+// Partial stores: device-coherent when the chunk kernel merges (another
+// workgroup reads them during the launch), plain otherwise (the merge launch
+// reads them after this one).
+template <typename T>
+FD_DEV void part_store(const Params &p, T *ptr, T v)
+{
+    if (p.fused) put(ptr, v);
+    else *ptr = v;
+}
+
+FD_DEV void part_store4(const Params &p, float *ptr, f32x4 v)
+{
+    if (p.fused) put4(ptr, v);
+    else *reinterpret_cast<f32x4 *>(ptr) = v;
+}
+
+// Chunks a row group's sequence is cut into; an empty sequence still has one
+// (empty) unit, so its rows get written.
+FD_DEV int units_of(const Params &p, int L)
+{
+    return L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
+}
+
+// The calling workgroup has stored its partials of one unit of row group
+// `rg` (whose sequence is cut into `nunits` units).  Publishes them and
+// returns, in every thread, whether this workgroup was the last of its row
+// group.  `flag` is a workgroup-shared int.  Contains barriers: every thread
+// of the workgroup must call it, after storing its partials with part_store().
+// Without a fused merge it returns false at once.
+FD_DEV bool publish_unit(const Params &p, int rg, int nunits, int &flag)
+{
+    if (!p.fused) return false;
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's partial stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t n = epoch_add(p.rg_count + rg, p.epoch, 1);
+        flag = n == (uint32_t)nunits;
+        // the row group is complete: reset its count for a replay of this launch
+        if (flag) put(p.rg_count + rg, (unsigned long long)p.epoch << 32);
+    }
+    __syncthreads();
+    return flag != 0;
+}
+
+// One wavefront merges row (b, h): writes out[b][h][:] and fallback_flags[b][h]
+// and returns the row's number of recomputed chunks (in every lane).  Lanes
+// 0..31 take the even chunks and 32..63 the odd ones, 4 components per lane,
+// four chunk pairs in flight.
+FD_DEV int merge_row(const Params &p, int b, int h, int lane)
+{
+    const int L = seq_len_of(p, b);
+    const int nch = (L + p.chunk - 1) / p.chunk;
+    const size_t base = part_slot(p, b, h, 0);   // chunk c at base + c * hq
+    const size_t cs = p.hq;
+
+    // flagged chunks of the row, and the largest chunk maximum if any
+    int nflag = 0;
+    for (int c = lane; c < nch; c += 64) nflag += get(p.cflag + base + c * cs);
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) nflag += __shfl_xor(nflag, x);
+    const bool any = nflag != 0;
+    float M = p.phi;
+    if (any) {
+        M = -INFINITY;
+        for (int c = lane; c < nch; c += 64) M = fmaxf(M, get(p.m_part + base + c * cs));
+#pragma unroll
+        for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+    }
+
+    const int half = lane >> 5, q4 = lane & 31;
+    const float *op = p.o_part + base * kHeadDim + 4 * q4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lacc = 0.f;
+    int c = half;
+    // without a recomputed chunk every partial is against phi: plain sum;
+    // otherwise each is rescaled from its own maximum to M
+    for (; c + 6 < nch; c += 8) {
+        f32x4 v[4];
+        float l[4], f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = get4(op + (size_t)(c + 2 * u) * cs * kHeadDim);
+            l[u] = get(p.l_part + base + (c + 2 * u) * cs);
+            f[u] = any ? get(p.m_part + base + (c + 2 * u) * cs) : M;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float g = (f[u] == M) ? 1.f : exp2_hw((f[u] - M) * kLog2e);
+            acc += v[u] * g;
+            lacc = fmaf(l[u], g, lacc);
+        }
+    }
+    for (; c < nch; c += 2) {
+        const float mc = any ? get(p.m_part + base + c * cs) : M;
+        const float g = (mc == M) ? 1.f : exp2_hw((mc - M) * kLog2e);
+        acc += get4(op + (size_t)c * cs * kHeadDim) * g;
+        lacc = fmaf(get(p.l_part + base + c * cs), g, lacc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
+    lacc += __shfl_xor(lacc, 32);
+
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+    if (nch > 0) {
+        float vs = 1.f;
+        if (p.v_scale) vs = p.v_scale[h / p.group];
+        r = acc * (vs / lacc);
+    }
+    const size_t row = (size_t)b * p.hq + h;
+    if (half == 0) {
+        if (p.out_bf16) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t u = __float_as_uint(r[i]);
+                w[i] = (r[i] != r[i]) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+            }
+            reinterpret_cast<u32x2 *>(p.out)[row * (kHeadDim / 4) + q4] = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+        } else {
+            reinterpret_cast<f32x4 *>(p.out)[row * (kHeadDim / 4) + q4] = r;
+        }
+    }
+    if (lane == 0) p.flags[row] = any ? 1 : 0;
+    return nflag;
+}
+
+// The last workgroup of a row group merges rows (b, h0 .. h0 + nrows - 1),
+// its NW wavefronts taking rows round-robin, and adds the row group's
+// recomputed chunks to the call's count.  `total` is a workgroup-shared int.
+template <int NW>
+FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) total = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int r = wave; r < nrows; r += NW) mine += merge_row(p, b, h0 + r, lane);
+    if (lane == 0 && mine) atomicAdd(&total, mine);
+    __syncthreads();
+    if (threadIdx.x == 0 && total) epoch_add(p.count_word, p.epoch, (uint32_t)total);
+}
+
+// Separate merge launch (large grids): RW wavefronts per row, 256 threads per
+// workgroup (256 / (64 RW) rows each).  In a wavefront, lanes 0..31 take one
+// chunk and lanes 32..63 the next, 4 components per lane, four chunk pairs in
+// flight; the wavefronts of a row split its chunks and meet in LDS.  It also
+// adds the recomputed (row, chunk) pairs to the call's count.
 template <int RW>
 __global__ __launch_bounds__(256) void merge_kernel(Params p)
 {
@@ -136,7 +343,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
     }
     if (lane == 0) {
         p.flags[row] = any ? 1 : 0;
-        if (nflag) atomicAdd(p.counter, nflag);
+        if (nflag) epoch_add(p.count_word, p.epoch, (uint32_t)nflag);
     }
 }
 

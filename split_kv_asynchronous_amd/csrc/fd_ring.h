@@ -4,6 +4,7 @@
 #pragma once
 
 #include "fd_common.h"
+#include "fd_merge.h"
 #include "fd_mfma.h"
 
 namespace fd {
@@ -89,6 +90,8 @@ struct Unit {
 
 // The u-th unit of "full chunks of every sequence, then the partial last
 // chunks", sequence-major inside each part, head blocks outer, chunks inner.
+// An empty sequence has one empty unit in the second part, so that its rows
+// still get merged (to zeros).
 FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
 {
     Unit r = {0, 0, 0, false};
@@ -101,7 +104,7 @@ FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
             int cnt = 0;
             if (b < p.batch) {
                 const int L = seq_len_of(p, b);
-                cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk) ? nhb : 0);
+                cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk || L == 0) ? nhb : 0);
             }
             const int incl = wave_scan(cnt, lane);
             const int total = __builtin_amdgcn_readlane(incl, 63);

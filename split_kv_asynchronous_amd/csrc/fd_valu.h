@@ -11,6 +11,7 @@
 #pragma once
 
 #include "fd_common.h"
+#include "fd_merge.h"
 
 namespace fd {
 
@@ -132,7 +133,7 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
             }
             acc += red[w * 132 + threadIdx.x] * f;
         }
-        p.o_part[slot * kHeadDim + threadIdx.x] = acc;
+        part_store(p, p.o_part + slot * kHeadDim + threadIdx.x, acc);
     }
     if (threadIdx.x == 0) {
         float lsum = 0.f;
@@ -147,9 +148,9 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
             lsum += red[w * 132 + 128] * f;
             any |= red[w * 132 + 130] != 0.f;
         }
-        p.l_part[slot] = lsum;
-        p.m_part[slot] = M;
-        if constexpr (!ONLINE) p.cflag[slot] = any ? 1 : 0;
+        part_store(p, p.l_part + slot, lsum);
+        part_store(p, p.m_part + slot, M);
+        if constexpr (!ONLINE) part_store(p, p.cflag + slot, (uint8_t)(any ? 1 : 0));
     }
     bool flagged = false;
 #pragma unroll
@@ -163,54 +164,19 @@ template <int KV, int QT, bool PAGED>
 __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
 {
     __shared__ float red[4 * 132];
+    __shared__ int last_flag, merged;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.counter = 0;
+    if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) epoch_add(p.count_word, p.epoch, 0);
     const int L = seq_len_of(p, b);
     const int t0 = c * p.chunk;
-    if (t0 >= L) return;
+    // chunks past the sequence have no unit; an empty sequence has one empty unit
+    if (t0 >= L && !(c == 0 && L == 0)) return;
     const int t1 = min(t0 + p.chunk, L);
     // a score left the safe band: this workgroup redoes its chunk with online
     // softmax and overwrites the partial (the chunk flag stays set)
     if (valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, t1, red))
         valu_chunk<KV, QT, PAGED, true, 4>(p, b, h, c, t0, t1, red);
-}
-
-// Fallback: every workgroup scans a strided share of the (row, chunk) flags
-// written by the chunk kernel, lists the flagged ones in LDS and recomputes
-// each with online softmax (FlashDecoding++ theory page, section 3: a block
-// whose score passes the unified-max criterion stops its asynchronous result
-// and is recomputed safely).  Grid: any size; every workgroup exits after its
-// share, so an empty flag set costs one scan.
-template <int KV, int QT, bool PAGED>
-__global__ __launch_bounds__(1024) void fallback_kernel(Params p)
-{
-    constexpr int NW = 16;
-    __shared__ float red[NW * 132];
-    __shared__ int list[1024];
-    __shared__ int count;
-    const int total = p.batch * p.hq * p.maxch;
-    const int nblk = gridDim.x;
-    for (int base = 0; base + (int)blockIdx.x < total; base += 1024 * nblk) {
-        if (threadIdx.x == 0) count = 0;
-        __syncthreads();
-        const long e = (long)base + (long)threadIdx.x * nblk + blockIdx.x;
-        if (e < total) {
-            const int row = (int)(e / p.maxch), c = (int)(e % p.maxch);
-            const int b = row / p.hq;
-            if (c * p.chunk < seq_len_of(p, b) && p.cflag[e]) list[atomicAdd(&count, 1)] = (int)e;
-        }
-        __syncthreads();
-        const int n = count;
-        for (int i = 0; i < n; ++i) {
-            const int e2 = list[i];
-            const int row = e2 / p.maxch, c = e2 % p.maxch;
-            const int b = row / p.hq, h = row % p.hq;
-            const int L = seq_len_of(p, b);
-            const int t0 = c * p.chunk;
-            valu_chunk<KV, QT, PAGED, true, NW>(p, b, h, c, t0, min(t0 + p.chunk, L), red);
-        }
-        __syncthreads();
-    }
+    if (publish_unit(p, b * p.hq + h, units_of(p, L), last_flag)) merge_group<4>(p, b, h, 1, merged);
 }
 
 }  // namespace fd

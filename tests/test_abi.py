@@ -37,8 +37,9 @@ def test_workspace_size_formula():
     rows, maxch = 32 * 64, 32
     slots = rows * maxch
     n = fd.fd_attn_workspace_size(d)
-    assert n >= 256 + slots * (128 * 4 + 4 + 4 + 1)
-    assert n < 256 + slots * (128 * 4 + 4 + 4 + 1) + 4 * 256
+    # header, per-(row, chunk) o/l/m/flag, per-row epoch-tagged counter
+    assert n >= 256 + slots * (128 * 4 + 4 + 4 + 1) + rows * 8
+    assert n < 256 + slots * (128 * 4 + 4 + 4 + 1) + rows * 8 + 5 * 256
     assert n % 256 == 0
     assert fd.fd_attn_workspace_size(_desc(head_dim=64)) == 0
     assert fd.fd_attn_workspace_size(_desc(chunk_size=48)) == 0

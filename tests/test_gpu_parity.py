@@ -102,6 +102,59 @@ def test_zero_and_clamped_lengths():
     compare(prob, out, flags)
 
 
+@pytest.mark.parametrize("g,kv,page", [(1, "bf16", 0), (4, "bf16", 0), (4, "e4m3fn", 16),
+                                       (1, "f32", 0)])
+def test_empty_sequences_in_every_kernel(g, kv, page):
+    # an empty sequence has no chunk, yet its rows must still be written (zeros)
+    prob = synthetic.make_problem(batch=4, num_q_heads=2 * g, num_kv_heads=2,
+                                  seq_lens=[0, 300, 0, 37], kv_dtype=kv, page_size=page,
+                                  chunk_size=64, max_seq_len=320, seed=9 + g)
+    print("case empty g=%d kv=%s page=%d" % (g, kv, page), flush=True)
+    dp = DeviceProblem(prob)
+    dp.out.fill_(float("nan"))
+    dp.flags.fill_(7)
+    dp.run()
+    out, flags = dp.results()
+    rows = out.reshape(prob.batch, prob.num_q_heads, -1)
+    assert np.all(rows[0] == 0) and np.all(rows[2] == 0)
+    compare(prob, out, flags)
+
+
+def test_workspace_needs_no_initialisation():
+    # The per-row-group counters carry the epoch of the call that wrote them, so
+    # any workspace contents work, a workspace can move between problems, and
+    # every call reports its own recomputed-chunk count.
+    narrow = synthetic.make_problem(batch=3, num_q_heads=8, num_kv_heads=2,
+                                    seq_lens=[2000, 700, 1500], chunk_size=256, seed=41,
+                                    phi=1.0, a=3.0, b=1.5)
+    wide = synthetic.make_problem(batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=[900, 2100],
+                                  chunk_size=128, seed=42)
+    ref_out, ref_flags, margin = oracle.decode_exact(**narrow.args())
+    sure = margin >= 1e-3     # rows whose flag cannot depend on rounding
+    dn, dw = DeviceProblem(narrow), DeviceProblem(wide)
+    ws = dn.workspace if dn.workspace.numel() >= dw.workspace.numel() else dw.workspace
+    dn.workspace = dw.workspace = ws
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    fills = [lambda: ws.fill_(0xFF), lambda: ws.fill_(0),
+             lambda: ws.copy_(torch.randint(0, 256, (ws.numel(),), generator=gen,
+                                            dtype=torch.uint8).cuda())]
+    counts = []
+    for fill in fills:
+        fill()
+        for _ in range(2):
+            dn.run()
+            out, flags = dn.results()
+            np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+            compare(narrow, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
+            counts.append(dn.recomputed())
+        dw.run()
+        out, flags = dw.results()
+        compare(wide, out, flags)
+        assert dw.recomputed() == 0
+    # the same (deterministic) count on every call, whatever the workspace held
+    assert counts[0] > 0 and len(set(counts)) == 1, counts
+
+
 @pytest.mark.parametrize("g,kv,page", [(1, "bf16", 0), (8, "bf16", 0), (4, "e4m3fn", 16),
                                        (1, "f32", 0), (1, "e4m3fn", 16)])
 def test_out_of_band_rows_fall_back(g, kv, page):
