@@ -203,3 +203,104 @@ def decode_bf16(bits) -> np.ndarray:
     lib = _load()
     c = np.asarray(bits, dtype=np.uint16).ravel()
     return np.array([lib.orc_decode_bf16(int(x)) for x in c], dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# prefill: a block of q_len queries per sequence, causal against its keys
+# ---------------------------------------------------------------------------
+
+class _PrefillProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_double)]
+
+
+class _PrefillInputs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("kv_lens", ctypes.c_void_p)]
+
+
+def _load_prefill():
+    lib = _load()
+    if not getattr(lib, "_prefill_ready", False):
+        P, I = ctypes.POINTER(_PrefillProblem), ctypes.POINTER(_PrefillInputs)
+        lib.orc_prefill_exact.argtypes = [P, I, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_prefill_exact.restype = ctypes.c_int
+        lib.orc_prefill_unified.argtypes = [P, I, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                            ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_prefill_unified.restype = ctypes.c_int
+        lib._prefill_ready = True
+    return lib
+
+
+def _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale):
+    q = np.ascontiguousarray(q, dtype=_NP_DT[q_dtype])
+    k = np.ascontiguousarray(k, dtype=_NP_DT[kv_dtype])
+    v = np.ascontiguousarray(v, dtype=_NP_DT[kv_dtype])
+    kv_lens = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    if kv_dtype == "e4m3fn" or q_dtype == "e4m3fn":
+        raise ValueError("prefill takes f32 or bf16 operands")
+    B, Hq, Lq, D = q.shape
+    if Hq % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if k.ndim != 4 or k.shape[:2] != (B, num_kv_heads) or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("k and v must be [B][Hkv][max_seq_len][D]")
+    if kv_lens.shape != (B,):
+        raise ValueError("kv_lens must have shape [batch]")
+    prob = _PrefillProblem(B, Hq, num_kv_heads, D, k.shape[2], Lq, _DT[q_dtype], _DT[kv_dtype],
+                           float(scale))
+    keep = (q, k, v, kv_lens)
+    return prob, _PrefillInputs(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens)), keep
+
+
+def _prefill_rows(rows, total):
+    if rows is None:
+        return None, total
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if rows.size and (rows.min() < 0 or rows.max() >= total):
+        raise ValueError("row id out of range")
+    return rows, rows.size
+
+
+def prefill_exact(q, k, v, kv_lens, *, num_kv_heads, q_dtype="bf16", kv_dtype="bf16", scale,
+                  phi, a, b, rows=None, with_threads=False):
+    """Exact causal softmax attention of a query block + band flags, float64.
+
+    q [B][Hq][Lq][D]; k, v [B][Hkv][max_seq_len][D].  Query j of sequence b sits
+    at position kv_lens[b] - Lq + j and sees keys 0..position (none if negative).
+    Rows are ids (b * Hq + h) * Lq + j (default: all, in order).  Returns
+    (out [nrows][D], flags [nrows] uint8, margin [nrows]); margin is the smallest
+    distance of a visible score to a band edge.
+    """
+    prob, ins, keep = _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale)
+    B, Hq, Lq, D = keep[0].shape
+    rows, n = _prefill_rows(rows, B * Hq * Lq)
+    out = np.zeros((n, D), dtype=np.float64)
+    flags = np.zeros(n, dtype=np.uint8)
+    margin = np.zeros(n, dtype=np.float64)
+    th = _load_prefill().orc_prefill_exact(ctypes.byref(prob), ctypes.byref(ins), phi, a, b, n,
+                                           _ptr(rows), _ptr(out), _ptr(flags), _ptr(margin))
+    return (out, flags, margin, th) if with_threads else (out, flags, margin)
+
+
+def prefill_unified(q, k, v, kv_lens, *, num_kv_heads, q_dtype="bf16", kv_dtype="bf16", scale,
+                    phi, a, b, tile, rows=None):
+    """The method's steps for a causal query block, float64: key tiles of `tile`
+    tokens reduced against phi, online-softmax redo of a tile with a visible
+    out-of-band score, merge.  Returns (out, flags, redone tiles [nrows] int32)."""
+    prob, ins, keep = _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale)
+    B, Hq, Lq, D = keep[0].shape
+    rows, n = _prefill_rows(rows, B * Hq * Lq)
+    out = np.zeros((n, D), dtype=np.float64)
+    flags = np.zeros(n, dtype=np.uint8)
+    red = np.zeros(n, dtype=np.int32)
+    rc = _load_prefill().orc_prefill_unified(ctypes.byref(prob), ctypes.byref(ins), int(tile), phi,
+                                             a, b, n, _ptr(rows), _ptr(out), _ptr(flags), _ptr(red))
+    if rc < 0:
+        raise ValueError("tile must be positive")
+    return out, flags, red

@@ -40,6 +40,9 @@
  *                page block_table[b][t / page_size] at slot t % page_size
  *   query head h reads KV head h / (Hq / Hkv)
  *
+ * The prefill form (a causal block of queries per sequence, same unified
+ * maximum and band) is defined in its own section at the end of this file.
+ *
  * Readings taken where the pages are silent: the band is closed at both ends
  * and a NaN score is outside it; tokens t >= seq_lens[b] are not attended and
  * not tested; a sequence of length <= 0 gives a zero row with flag 0.
@@ -326,6 +329,228 @@ int orc_decode_unified(const orc_problem *p, const orc_inputs *in, int chunk, do
             int row = rows ? rows[i] : i;
             unified_row(p, in, row, chunk, phi, a, b, out + (size_t)i * p->head_dim, flags + i,
                         recomputed + i);
+        }
+    }
+    return threads;
+}
+
+/* ------------------------------------------------------------------ prefill */
+/*
+ * Prefill: a block of Lq query tokens per sequence attends causally to the
+ * sequence's keys (FlashDecoding++ theory page, section 3: the same unified
+ * maximum serves the prefill phase; section 1: prefill processes all prompt
+ * tokens at once).  Layouts and reading:
+ *
+ *   q, out   [B][Hq][Lq][D]      flags [B][Hq][Lq]
+ *   K/V      [B][Hkv][max_seq_len][D], contiguous
+ *   query j of sequence b sits at position pos = kv_lens[b] - Lq + j
+ *   (kv_lens clamped to [0, max_seq_len]) and attends keys t = 0 .. pos;
+ *   a query with pos < 0 has no key: zero row, flag 0.
+ *
+ * orc_prefill_exact() is the plain definition (max-subtracted softmax over
+ * the visible keys, plus the band test over those scores).
+ * orc_prefill_unified() follows the method: key tiles of `tile` tokens, each
+ * reduced against the preset phi; a tile with a visible score outside the
+ * band is redone with online softmax; tiles merged by a plain sum (max
+ * rescale only when a tile was redone).
+ */
+typedef struct {
+    int32_t batch, num_q_heads, num_kv_heads, head_dim;
+    int32_t max_seq_len, q_len;
+    int32_t q_dtype, kv_dtype;       /* ORC_F32 or ORC_BF16 */
+    double scale;
+} orc_prefill_problem;
+
+typedef struct {
+    const void *q, *k, *v;
+    const int32_t *kv_lens;
+} orc_prefill_inputs;
+
+/* keys visible to query j of sequence b */
+static int prefill_keys(const orc_prefill_problem *p, const orc_prefill_inputs *in, int b, int j)
+{
+    int kv = in->kv_lens[b];
+    if (kv < 0) kv = 0;
+    if (kv > p->max_seq_len) kv = p->max_seq_len;
+    int pos = kv - p->q_len + j;
+    return pos < 0 ? 0 : pos + 1;
+}
+
+/* scores of query row (b, h, j) against keys 0 .. n-1 */
+static void prefill_scores(const orc_prefill_problem *p, const orc_prefill_inputs *in, int b, int h,
+                           int j, int n, double *s)
+{
+    const int D = p->head_dim;
+    const int kvh = h / (p->num_q_heads / p->num_kv_heads);
+    double *qd = malloc(sizeof(double) * D);
+    for (int d = 0; d < D; d++)
+        qd[d] = elem(in->q, (((size_t)b * p->num_q_heads + h) * p->q_len + j) * D + d, p->q_dtype);
+    for (int t = 0; t < n; t++) {
+        size_t off = (((size_t)b * p->num_kv_heads + kvh) * p->max_seq_len + t) * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; d++) acc += qd[d] * elem(in->k, off + d, p->kv_dtype);
+        s[t] = p->scale * acc;
+    }
+    free(qd);
+}
+
+static void prefill_value(const orc_prefill_problem *p, const orc_prefill_inputs *in, int b, int kvh,
+                          int t, double r, double w, double *acc)
+{
+    const size_t off = (((size_t)b * p->num_kv_heads + kvh) * p->max_seq_len + t) * p->head_dim;
+    for (int d = 0; d < p->head_dim; d++) acc[d] = acc[d] * r + w * elem(in->v, off + d, p->kv_dtype);
+}
+
+/* row = (b * Hq + h) * Lq + j */
+static void prefill_exact_row(const orc_prefill_problem *p, const orc_prefill_inputs *in, int row,
+                              double phi, double a, double b_, double *out, uint8_t *flag,
+                              double *margin)
+{
+    const int D = p->head_dim, Lq = p->q_len;
+    const int j = row % Lq, bh = row / Lq;
+    const int b = bh / p->num_q_heads, h = bh % p->num_q_heads;
+    const int kvh = h / (p->num_q_heads / p->num_kv_heads);
+    const int n = prefill_keys(p, in, b, j);
+    const double lo = phi - a, hi = phi + b_;
+
+    for (int d = 0; d < D; d++) out[d] = 0.0;
+    *flag = 0;
+    if (margin) *margin = INFINITY;
+    if (n == 0) return;
+
+    double *s = malloc(sizeof(double) * n);
+    prefill_scores(p, in, b, h, j, n, s);
+    int has_nan = 0;
+    double m = -INFINITY, mg = INFINITY;
+    for (int t = 0; t < n; t++) {
+        if (outside_band(s[t], lo, hi)) *flag = 1;
+        if (isnan(s[t])) has_nan = 1;
+        else if (s[t] > m) m = s[t];
+        double dist = fmin(fabs(s[t] - lo), fabs(s[t] - hi));
+        if (!(dist >= mg)) mg = dist;
+    }
+    if (margin) *margin = mg;
+    if (has_nan) {
+        for (int d = 0; d < D; d++) out[d] = NAN;
+        free(s);
+        return;
+    }
+    double l = 0.0;
+    for (int t = 0; t < n; t++) {
+        double w = exp(s[t] - m);
+        l += w;
+        prefill_value(p, in, b, kvh, t, 1.0, w, out);
+    }
+    for (int d = 0; d < D; d++) out[d] /= l;
+    free(s);
+}
+
+/* rows: nrows row ids ((b * Hq + h) * Lq + j), or NULL for all in order */
+int orc_prefill_exact(const orc_prefill_problem *p, const orc_prefill_inputs *in, double phi,
+                      double a, double b, int nrows, const int32_t *rows, double *out,
+                      uint8_t *flags, double *margin)
+{
+    int threads = 1;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        threads = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 4)
+        for (int i = 0; i < nrows; i++) {
+            int row = rows ? rows[i] : i;
+            prefill_exact_row(p, in, row, phi, a, b, out + (size_t)i * p->head_dim, flags + i,
+                              margin ? margin + i : NULL);
+        }
+    }
+    return threads;
+}
+
+static void prefill_unified_row(const orc_prefill_problem *p, const orc_prefill_inputs *in, int row,
+                                int tile, double phi, double a, double b_, double *out,
+                                uint8_t *flag, int32_t *redone)
+{
+    const int D = p->head_dim, Lq = p->q_len;
+    const int j = row % Lq, bh = row / Lq;
+    const int b = bh / p->num_q_heads, h = bh % p->num_q_heads;
+    const int kvh = h / (p->num_q_heads / p->num_kv_heads);
+    const int n = prefill_keys(p, in, b, j);
+    const double lo = phi - a, hi = phi + b_;
+    const int ntile = (n + tile - 1) / tile;
+
+    for (int d = 0; d < D; d++) out[d] = 0.0;
+    *flag = 0;
+    *redone = 0;
+    if (n == 0) return;
+
+    double *s = malloc(sizeof(double) * n);
+    prefill_scores(p, in, b, h, j, n, s);
+    double *m_c = malloc(sizeof(double) * ntile);
+    double *l_c = malloc(sizeof(double) * ntile);
+    double *o_c = calloc((size_t)ntile * D, sizeof(double));
+
+    for (int c = 0; c < ntile; c++) {
+        const int t0 = c * tile, t1 = (t0 + tile < n) ? t0 + tile : n;
+        double *o = o_c + (size_t)c * D;
+        int bad = 0;
+        l_c[c] = 0.0;
+        m_c[c] = phi;
+        for (int t = t0; t < t1; t++) {          /* against the preset constant */
+            if (outside_band(s[t], lo, hi)) bad = 1;
+            double w = exp(s[t] - phi);
+            l_c[c] += w;
+            prefill_value(p, in, b, kvh, t, 1.0, w, o);
+        }
+        if (!bad) continue;
+        *flag = 1;                               /* redo this tile, online softmax */
+        (*redone)++;
+        double m = -INFINITY, l = 0.0;
+        for (int d = 0; d < D; d++) o[d] = 0.0;
+        for (int t = t0; t < t1; t++) {
+            double m_new = (s[t] > m || isnan(s[t])) ? s[t] : m;
+            double r = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+            double w = (s[t] == -INFINITY) ? 0.0 : exp(s[t] - m_new);
+            l = l * r + w;
+            prefill_value(p, in, b, kvh, t, r, w, o);
+            m = m_new;
+        }
+        m_c[c] = m;
+        l_c[c] = l;
+    }
+    double M = phi;
+    if (*flag) {
+        M = -INFINITY;
+        for (int c = 0; c < ntile; c++)
+            if (isnan(m_c[c]) || m_c[c] > M) M = m_c[c];
+    }
+    double l = 0.0;
+    for (int c = 0; c < ntile; c++) {
+        double f = *flag ? exp(m_c[c] - M) : 1.0;
+        l += f * l_c[c];
+        for (int d = 0; d < D; d++) out[d] += f * o_c[(size_t)c * D + d];
+    }
+    for (int d = 0; d < D; d++) out[d] /= l;
+    free(s); free(m_c); free(l_c); free(o_c);
+}
+
+int orc_prefill_unified(const orc_prefill_problem *p, const orc_prefill_inputs *in, int tile,
+                        double phi, double a, double b, int nrows, const int32_t *rows, double *out,
+                        uint8_t *flags, int32_t *redone)
+{
+    int threads = 1;
+    if (tile <= 0) return -1;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        threads = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 4)
+        for (int i = 0; i < nrows; i++) {
+            int row = rows ? rows[i] : i;
+            prefill_unified_row(p, in, row, tile, phi, a, b, out + (size_t)i * p->head_dim,
+                                flags + i, redone + i);
         }
     }
     return threads;

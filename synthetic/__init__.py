@@ -31,7 +31,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Problem", "CONFIGS", "make_config", "make_problem", "bf16_round",
+__all__ = ["Problem", "CONFIGS", "make_config", "make_problem", "PrefillProblem",
+           "PREFILL_CONFIGS", "make_prefill", "make_prefill_config", "bf16_round",
            "bf16_to_f32", "e4m3fn_encode", "e4m3fn_values"]
 
 HEAD_DIM = 128
@@ -338,3 +339,132 @@ def make_config(cfg: int, *, batch: Optional[int] = None, length: Optional[int] 
     if cfg == 4 and perturb and batch is None and length is None:
         apply_key_scaling(prob, load_perturbation_plan(), c["perturb_factor"])
     return prob
+
+
+# ----------------------------------------------------------------------------
+# prefill: a causal block of query tokens per sequence
+# ----------------------------------------------------------------------------
+
+_S_PQ, _S_PK, _S_PV = 7, 8, 9
+
+# Prefill workloads.  "lens" as above gives kv_lens; q_len queries sit at the
+# end of each sequence (q_len == kv_len: a whole prompt; q_len < kv_len: a new
+# block appended to a cached prefix).
+PREFILL_CONFIGS = {
+    1: dict(workload="prefill-gqa2x4/1-Lq300-kv300..517-bf16", batch=2, num_q_heads=4,
+            num_kv_heads=1, q_len=300, lens=("uniform", 300, 517), max_seq_len=517,
+            phi=4.0, a=20.0, b=6.0),
+    2: dict(workload="prefill-gqa2x32/8-L8192-causal-bf16", batch=2, num_q_heads=32,
+            num_kv_heads=8, q_len=8192, lens=("fixed", 8192), max_seq_len=8192,
+            phi=4.0, a=20.0, b=6.0),
+}
+
+
+@dataclasses.dataclass
+class PrefillProblem:
+    """One prefill call's inputs (bf16 bit patterns or float32, host arrays)."""
+    q: np.ndarray                 # [B][Hq][Lq][D]
+    k: np.ndarray                 # [B][Hkv][max_seq_len][D]
+    v: np.ndarray
+    kv_lens: np.ndarray           # int32 [B]
+    num_kv_heads: int
+    dtype: str                    # "bf16" | "f32" (queries and keys/values alike)
+    scale: float
+    phi: float
+    a: float
+    b: float
+    workload: str = "custom"
+
+    @property
+    def batch(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def q_len(self) -> int:
+        return self.q.shape[2]
+
+    @property
+    def head_dim(self) -> int:
+        return self.q.shape[3]
+
+    @property
+    def max_seq_len(self) -> int:
+        return self.k.shape[2]
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs that are attended, summed over heads."""
+        kv = np.clip(self.kv_lens.astype(np.int64), 0, self.max_seq_len)
+        pos = kv[:, None] - self.q_len + np.arange(self.q_len)[None, :]
+        return int(np.clip(pos + 1, 0, None).sum()) * self.num_q_heads
+
+    def args(self) -> dict:
+        """Keyword arguments shared by the oracle and the library binding."""
+        return dict(q=self.q, k=self.k, v=self.v, kv_lens=self.kv_lens,
+                    num_kv_heads=self.num_kv_heads, q_dtype=self.dtype, kv_dtype=self.dtype,
+                    scale=self.scale, phi=self.phi, a=self.a, b=self.b)
+
+
+def make_prefill(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int, kv_lens,
+                 dtype: str = "bf16", phi: float = 4.0, a: float = 20.0, b: float = 6.0,
+                 max_seq_len: Optional[int] = None, scale: Optional[float] = None,
+                 head_dim: int = HEAD_DIM, seed: int = SEED_BASE + 100,
+                 workload: str = "custom", value_sigma: float = 1.0) -> PrefillProblem:
+    """Draw one prefill problem: N(0, value_sigma^2) queries, keys and values;
+    keys/values drawn for the first kv_lens[b] positions, zero beyond."""
+    if np.isscalar(kv_lens):
+        kv_lens = np.full(batch, int(kv_lens), dtype=np.int32)
+    kv_lens = np.asarray(kv_lens, dtype=np.int32)
+    assert kv_lens.shape == (batch,)
+    assert num_q_heads % num_kv_heads == 0
+    if max_seq_len is None:
+        max_seq_len = max(1, int(kv_lens.max(initial=0)))
+    D = head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lens = np.clip(kv_lens, 0, max_seq_len)
+    sdt = np.float32 if dtype == "f32" else np.uint16
+
+    def conv(x):
+        return x if dtype == "f32" else bf16_round(x)
+
+    q = np.zeros((batch, num_q_heads, q_len, D), dtype=sdt)
+    k = np.zeros((batch, num_kv_heads, max_seq_len, D), dtype=sdt)
+    v = np.zeros_like(k)
+    sig = np.float32(value_sigma)
+
+    def fill_q(job):
+        b_, h = job
+        q[b_, h] = conv(_rng(seed, _S_PQ, b_, h).standard_normal((q_len, D), dtype=np.float32) * sig)
+
+    def fill_kv(job):
+        b_, h = job
+        n = int(lens[b_])
+        k[b_, h, :n] = conv(_draw_kv_rows(seed, _S_PK, b_, h, n, D) * sig)
+        v[b_, h, :n] = conv(_draw_kv_rows(seed, _S_PV, b_, h, n, D) * sig)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill_q, [(b_, h) for b_ in range(batch) for h in range(num_q_heads)]))
+        list(ex.map(fill_kv, [(b_, h) for b_ in range(batch) for h in range(num_kv_heads)]))
+    return PrefillProblem(q=q, k=k, v=v, kv_lens=kv_lens, num_kv_heads=num_kv_heads, dtype=dtype,
+                          scale=float(scale), phi=float(phi), a=float(a), b=float(b),
+                          workload=workload)
+
+
+def make_prefill_config(cfg: int, *, batch: Optional[int] = None, q_len: Optional[int] = None,
+                        seed: Optional[int] = None) -> PrefillProblem:
+    """The numbered prefill workload, optionally shrunk (batch, query block length)."""
+    c = dict(PREFILL_CONFIGS[cfg])
+    seed = SEED_BASE + 100 + cfg if seed is None else seed
+    B = batch or c["batch"]
+    Lq = q_len or c["q_len"]
+    kv = _draw_lens(c["lens"], B, seed)
+    if q_len is not None:
+        kv = np.maximum(kv - c["q_len"] + Lq, 0).astype(np.int32)
+    return make_prefill(batch=B, num_q_heads=c["num_q_heads"], num_kv_heads=c["num_kv_heads"],
+                        q_len=Lq, kv_lens=kv, phi=c["phi"], a=c["a"], b=c["b"],
+                        max_seq_len=max(int(kv.max(initial=1)), 1), seed=seed,
+                        workload=c["workload"])
