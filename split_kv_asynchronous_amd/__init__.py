@@ -13,8 +13,9 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["fd_attn_decode", "fd_attn_workspace_size", "fd_attn_status_string", "FdAttnError",
-           "make_desc", "library_path", "FD_F32", "FD_BF16", "FD_FP8_E4M3FN"]
+__all__ = ["fd_attn_decode", "fd_attn_prefill", "fd_attn_workspace_size",
+           "fd_attn_status_string", "FdAttnError", "make_desc", "make_prefill_desc",
+           "library_path", "FD_F32", "FD_BF16", "FD_FP8_E4M3FN"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfd_attn.so")
@@ -44,6 +45,15 @@ class FdAttnDesc(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("stage_events", ctypes.c_void_p)]
 
 
+class FdPrefillDesc(ctypes.Structure):
+    """Mirror of fd_prefill_desc_t."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("stage_events", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -66,6 +76,11 @@ def _load():
                                        ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
         lib.fd_attn_decode.restype = ctypes.c_int
+        lib.fd_attn_prefill.argtypes = [ctypes.POINTER(FdPrefillDesc), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.fd_attn_prefill.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -170,6 +185,71 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
                                 block_table.data_ptr() if page_size else None, float(phi),
                                 float(a), float(b), out.data_ptr(), fallback_flags.data_ptr(),
                                 stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return out, fallback_flags
+
+
+def make_prefill_desc(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int,
+                      max_seq_len: int, scale: Optional[float] = None, dtype: str = "bf16",
+                      out_dtype: str = "f32", head_dim: int = 128,
+                      stage_events_ptr: int = 0) -> FdPrefillDesc:
+    return FdPrefillDesc(batch, num_q_heads, num_kv_heads, head_dim, q_len, max_seq_len,
+                         -1.0 if scale is None else float(scale), _DTYPE_CODE[dtype],
+                         _DTYPE_CODE[out_dtype], stage_events_ptr or None)
+
+
+def _event_array(stage_events):
+    handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in stage_events]
+    if len(handles) != 2 or not all(handles):
+        raise ValueError("stage_events: 2 created HIP events -- kernel start/stop "
+                         "(record a torch event once to create it)")
+    return (ctypes.c_void_p * 2)(*handles)
+
+
+def fd_attn_prefill(q, k, v, kv_lens, phi: float, a: float, b: float, out=None,
+                    fallback_flags=None, *, num_kv_heads: Optional[int] = None,
+                    scale: Optional[float] = None, out_dtype: str = "f32", stream=None,
+                    stage_events: Optional[Sequence] = None):
+    """Causal prefill attention of a query block per sequence; returns (out, fallback_flags).
+
+    Layouts as in include/fd_prefill.h: q [B][Hq][q_len][128] bf16; k, v
+    [B][Hkv][max_seq_len][128] bf16; kv_lens int32 [B] (keys per sequence, the
+    query block included: query j sits at position kv_lens[b] - q_len + j).
+    bf16 data may be torch.bfloat16 or 16-bit integer bit patterns.
+    """
+    import torch
+    dev = q.device
+    B, Hq, Lq, D = q.shape
+    for t in (q, k, v, kv_lens):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on the same device")
+    for t in (q, k, v):
+        if _torch_code(t) != "bf16":
+            raise ValueError("q, k and v must be bf16")
+    if kv_lens.dtype != torch.int32:
+        raise ValueError("kv_lens must be int32")
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k and v must be [B][Hkv][max_seq_len][128]")
+    if num_kv_heads is None:
+        num_kv_heads = k.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D),
+                          dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=dev)
+    if fallback_flags is None:
+        fallback_flags = torch.empty((B, Hq, Lq), dtype=torch.uint8, device=dev)
+    desc = make_prefill_desc(batch=B, num_q_heads=Hq, num_kv_heads=num_kv_heads, q_len=Lq,
+                             max_seq_len=k.shape[2], scale=scale, out_dtype=out_dtype,
+                             head_dim=D)
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = _event_array(stage_events)
+        desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _load().fd_attn_prefill(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 kv_lens.data_ptr(), float(phi), float(a), float(b),
+                                 out.data_ptr(), fallback_flags.data_ptr(), stream)
     if rc != 0:
         raise FdAttnError(rc, fd_attn_status_string(rc))
     return out, fallback_flags

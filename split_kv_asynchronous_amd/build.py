@@ -1,11 +1,11 @@
-"""Compiles the HIP sources under csrc/ into libfd_attn.so (gfx950 only)."""
+"""Compiles the HIP sources under csrc/ (decode and prefill) into libfd_attn.so (gfx950 only)."""
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fd_attn.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("fd_attn.hip", "fd_prefill.hip")]
 LIB = os.path.join(HERE, "libfd_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -18,7 +18,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp, SRC]
+    cmd = [HIPCC] + FLAGS + ["-o", tmp] + SRCS
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -118,22 +118,12 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     // Q^T fragments (B operand of the score product).  The k index of MFMA
     // step kk maps to query components 8*g4 + 32*kk + j (bf16) or
     // 16*(g4 + 4*(kk/2)) + 8*(kk%2) + j (E4M3FN, matching 16-byte K pieces);
-    // K uses the same map.  The loads are inline assembly, invisible to the
-    // compiler's wait tracking: that tracking cannot follow the data-dependent
-    // number of DMAs issued behind them and would drain the whole ring before
-    // the first block.  The ring prologue's explicit wait covers them (they are
-    // older than every DMA); heads past the block read a valid row and are
+    // K uses the same map.  They are loaded after the ring prologue has been
+    // issued (see run below); heads past the block read a valid row and are
     // zeroed.
     u32x4 qf[4];
-    {
-        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) +
-                               ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int d0 = FP8 ? 16 * (g4 + 4 * (kk >> 1)) + 8 * (kk & 1) : 8 * g4 + 32 * kk;
-            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[kk]) : "v"(qrow + d0) : "memory");
-        }
-    }
+    const uint16_t *qlane = static_cast<const uint16_t *>(p.q) +
+                            ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim + (FP8 ? 16 : 8) * g4;
     float sc = p.scale;
     if constexpr (FP8) sc *= as_const(p.k_scale)[kvh];
     const float nphi = -p.phi * kLog2e;
@@ -275,13 +265,33 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
         // page-table entries are fetched one ring refill ahead of their use
         int pg_next[NPG];
         load_pages(NST - 1, pg_next);
-        // the query loads were issued before the ring prologue: once at most
-        // the prologue's DMAs are outstanding, the queries have arrived
-        wait_ring<DPW, NST - 1>(issued);
-        asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]) : : "memory");
-        if (!head_ok) {
+        // The query loads and their wait sit in one assembly statement
+        // (early-clobber outputs), so the compiler never holds a register that
+        // a load still in flight will write; issued after the prologue, they
+        // overlap its DMAs, which the same wait also covers.
+        if constexpr (!ONLINE) {
+            if constexpr (FP8)
+                asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                             "global_load_dwordx4 %1, %4, off offset:16\n\t"
+                             "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                             "global_load_dwordx4 %3, %4, off offset:144\n\t"
+                             "s_waitcnt vmcnt(0)"
+                             : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
+                             : "v"(qlane)
+                             : "memory");
+            else
+                asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                             "global_load_dwordx4 %1, %4, off offset:64\n\t"
+                             "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                             "global_load_dwordx4 %3, %4, off offset:192\n\t"
+                             "s_waitcnt vmcnt(0)"
+                             : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
+                             : "v"(qlane)
+                             : "memory");
+            if (!head_ok) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0u, 0u, 0u, 0u};
+                for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
 
         int stage = 0;

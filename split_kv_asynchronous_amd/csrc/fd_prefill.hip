@@ -1,0 +1,73 @@
+// Host side of fd_attn_prefill (include/fd_prefill.h): validation and the
+// launch of the causal prefill kernel.  No allocation, no synchronisation.
+#include <hip/hip_ext.h>
+#include <math.h>
+#include <string.h>
+
+#include "fd_prefill.h"
+#include "fd_prefill_kernel.h"
+
+namespace {
+
+using PrefillShape = fd::prefill::Shape<4, 2, 3>;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int fd_attn_prefill(const fd_prefill_desc_t *d, const void *q, const void *k,
+                               const void *v, const int32_t *kv_lens, float phi, float a,
+                               float b, void *out, uint8_t *fallback_flags, hipStream_t stream)
+{
+    if (!d || !q || !k || !v || !kv_lens || !out || !fallback_flags) return FD_ERR_NULL;
+    if (d->batch < 1 || d->batch > 65535 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+        return FD_ERR_SHAPE;
+    if (d->num_q_heads % d->num_kv_heads) return FD_ERR_SHAPE;
+    if (d->head_dim != fd::kHeadDim) return FD_ERR_SHAPE;
+    if (d->q_len < 1 || d->q_len > (1 << 23)) return FD_ERR_SHAPE;
+    if (d->max_seq_len < 1 || d->max_seq_len > (1 << 23)) return FD_ERR_SHAPE;
+    if (!isfinite(d->scale)) return FD_ERR_SHAPE;
+    if (d->dtype != FD_BF16) return FD_ERR_DTYPE;
+    if (d->out_dtype != FD_F32 && d->out_dtype != FD_BF16) return FD_ERR_DTYPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FD_ERR_ALIGN;
+    if (!isfinite(phi) || !isfinite(a) || !isfinite(b) || a < 0.f || b < 0.f || a > 64.f ||
+        b > 64.f)
+        return FD_ERR_BAND;
+
+    const int64_t ntiles = ((int64_t)d->q_len + PrefillShape::rows - 1) / PrefillShape::rows;
+    const int64_t total = (int64_t)d->batch * d->num_q_heads * ntiles;
+    if (total > ((int64_t)1 << 31) - 8) return FD_ERR_SHAPE;
+
+    fd::prefill::PrefillParams p;
+    memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.kv_lens = kv_lens;
+    p.out = out;
+    p.flags = fallback_flags;
+    p.batch = d->batch;
+    p.hq = d->num_q_heads;
+    p.hkv = d->num_kv_heads;
+    p.group = d->num_q_heads / d->num_kv_heads;
+    p.q_len = d->q_len;
+    p.max_seq_len = d->max_seq_len;
+    p.ntiles = (int)ntiles;
+    p.total = (int)total;
+    p.per_xcd = (int)((total + 7) / 8);
+    p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)fd::kHeadDim);
+    p.phi = phi;
+    p.lo = (float)((double)phi - (double)a);
+    p.hi = (float)((double)phi + (double)b);
+
+    hipEvent_t *ev = d->stage_events;
+    hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;
+    const dim3 grid((unsigned)(8 * (int64_t)p.per_xcd)), block(PrefillShape::waves * 64);
+    (void)hipGetLastError();
+    if (d->out_dtype == FD_BF16)
+        hipExtLaunchKernelGGL((fd::prefill::prefill_kernel<4, 2, 3, true>), grid, block, 0, stream, ev0, ev1, 0, p);
+    else
+        hipExtLaunchKernelGGL((fd::prefill::prefill_kernel<4, 2, 3, false>), grid, block, 0, stream, ev0, ev1, 0, p);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    return FD_OK;
+}

@@ -1,0 +1,392 @@
+// Causal prefill attention with the unified maximum (gfx950, bf16).
+//
+// The prefill form of the method (FlashDecoding++ theory page, section 3: the
+// preset maximum serves prefill as it serves decode): a block of q_len query
+// tokens per sequence, query j at position kv_len - q_len + j attending keys
+// 0 .. position.  Every weight is exp(s - phi) against the caller's constant,
+// so the key loop carries no running maximum and never rescales the output
+// accumulators.  A score outside [phi - a, phi + b] sets the row's flag; from
+// the first key tile in which a wavefront sees one, that wavefront continues
+// with the ordinary running-maximum online softmax, starting from its
+// unified-max sums (reference phi), so the result stays exact (the fallback
+// rule of the same section).
+//
+// Work decomposition.  A workgroup owns one (sequence b, query head h, tile of
+// M = NW * 16 * QB consecutive queries) and walks all the keys its last query
+// sees; wavefront w owns queries 16*QB*w .. 16*QB*w + 16*QB - 1 of the tile in
+// QB blocks of 16.  Work items are ordered (sequence, kv head) outer, query
+// tiles heaviest first, the heads of a KV group innermost, and dealt to the
+// eight XCDs in contiguous ranges (a launch places workgroup i on XCD i % 8),
+// so the query heads and tiles that read the same K/V share one L2.
+//
+// Ring.  NST stages of 32 keys (two 16-token groups of K and of V, 4 KiB each)
+// shared by the workgroup and filled by 1 KiB buffer->LDS DMA instructions,
+// each moving 4 whole cache rows; the 16-byte pieces of a row are rotated so
+// the fragment reads are free of bank conflicts.  One barrier per stage.
+// Per stage and wavefront:
+//   * K fragments with ds_read_b128, V^T fragments with ds_read_b64_tr_b16;
+//   * S^T[16 keys x 16 queries] = K . Q^T on v_mfma_f32_16x16x32_bf16 (Q^T
+//     fragments stay in registers), scale, causal mask, band test, weights;
+//   * weights rounded to bf16 (the weight sums add the rounded values, so the
+//     output is an exact convex combination of the values with those weights);
+//   * O^T[128 x 16 queries] += V^T . P^T on v_mfma_f32_16x16x32_bf16 over the
+//     stage's 32 keys, taken in the order the two score tiles hand them over.
+#pragma once
+
+#include "fd_ring.h"
+
+namespace fd {
+namespace prefill {
+
+using namespace ring;
+
+// Everything one prefill call's kernel needs, passed by value.
+struct PrefillParams {
+    const uint16_t *q, *k, *v;     // bf16 bit patterns
+    const int32_t *kv_lens;
+    void *out;
+    uint8_t *flags;
+    int batch, hq, hkv, group;     // group = hq / hkv
+    int q_len, max_seq_len;
+    int ntiles;                    // query tiles per (sequence, head)
+    int total;                     // work items
+    int per_xcd;                   // ceil(total / 8)
+    float scale, phi, lo, hi;
+};
+
+// Two floats -> packed bf16 pair, round to nearest even.
+FD_DEV uint32_t pack_bf16(float a, float b)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+template <int NW, int QB, int NST>
+struct Shape {
+    static constexpr int waves = NW;
+    static constexpr int qblocks = QB;                 // 16-query blocks per wavefront
+    static constexpr int nst = NST;
+    static constexpr int rows = NW * 16 * QB;          // queries per workgroup
+    static constexpr int keys = 32;                    // keys per stage
+    static constexpr int tile = 2 * kGroupBytes;       // K (or V) part of a stage
+    static constexpr int stage = 2 * tile;
+    static constexpr int lds = NST * stage;
+    static constexpr int dma_per_group = 4 / NW;       // 1 KiB DMA instructions per wave per K (or V) group
+    static constexpr int dma_per_wave = 2 * 2 * dma_per_group;
+    static_assert(NW == 2 || NW == 4, "two or four wavefronts");
+    static_assert(NST >= 2, "the ring needs two stages");
+    static_assert((NST - 1) * dma_per_wave < 64, "vmcnt cannot count that deep");
+    static_assert(lds <= 80 * 1024, "two workgroups per compute unit");
+};
+
+template <int NW, int QB, int NST, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
+{
+    using S = Shape<NW, QB, NST>;
+    using F = Fmt<FD_BF16>;
+    constexpr int ROW = F::row;                    // 256 bytes per cache row
+    constexpr int BLK = S::keys;
+    constexpr int IPG = S::dma_per_group;
+    constexpr int DPW = S::dma_per_wave;
+    constexpr int M = S::rows;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[S::lds];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int g4 = lane >> 4;
+
+    // ---- work item: contiguous ranges per XCD
+    const int wi = (int)(blockIdx.x & 7) * p.per_xcd + (int)(blockIdx.x >> 3);
+    if (wi >= p.total) return;
+    const int per_pair = p.ntiles * p.group;
+    const int pair = wi / per_pair;
+    const int rem = wi - pair * per_pair;
+    const int td = rem / p.group;
+    const int b = pair / p.hkv;
+    const int kvh = pair - b * p.hkv;
+    const int h = kvh * p.group + (rem - td * p.group);
+    const int j0 = (p.ntiles - 1 - td) * M;        // first query of the tile
+
+    int kv = as_const(p.kv_lens)[b];
+    kv = kv < 0 ? 0 : (kv > p.max_seq_len ? p.max_seq_len : kv);
+    const int off = kv - p.q_len;                  // position of query j is off + j
+    const int jw0 = j0 + wave * 16 * QB;           // this wavefront's first query
+    const int jw_end = min(jw0 + 16 * QB, p.q_len);
+    const int kend_w = jw_end > jw0 ? max(0, min(kv, off + jw_end)) : 0;   // keys the wave sees
+    const int j_end = min(j0 + M, p.q_len);
+    const int kend = max(0, min(kv, off + j_end));                        // keys the workgroup sees
+    const int nblk = (kend + BLK - 1) / BLK;
+    // every query of the wave sees keys 0 .. pos_min (stages below need no mask)
+    const int pos_min = jw0 + 16 * QB <= p.q_len ? off + jw0 : -1;
+
+    // position of query row n of block qb; -1 (no keys) past the query block
+    int pos[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int j = jw0 + 16 * qb + n;
+        pos[qb] = j < p.q_len ? off + j : -1;
+    }
+
+    const float sc = p.scale;
+    const float nphi = -p.phi * kLog2e;
+
+    // ---- DMA: wavefront w issues instructions IPG*w .. IPG*w + IPG-1 of each
+    // group of K and of V; instruction i moves group rows 4i .. 4i+3, lane l
+    // fetching, of row 4i + l/16, the piece that belongs in LDS slot l%16.
+    uint32_t dma_vo[IPG];
+#pragma unroll
+    for (int qd = 0; qd < IPG; ++qd) {
+        const int r = 4 * (IPG * wave + qd) + lane / 16;
+        dma_vo[qd] = (lane / 16) * ROW + 16 * ((lane % 16 - F::rot(r)) & (F::slots - 1));
+    }
+    const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * ROW;
+    const int nrec = (int)((uint32_t)kv * ROW);    // rows past kv read as zeros
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)((const uint8_t *)p.k + slice), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)((const uint8_t *)p.v + slice), (short)0, nrec, 0x00020000);
+
+    auto issue = [&](int jb, int stage) {
+        uint8_t *kt = ring + stage * S::stage + IPG * wave * 1024;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int qd = 0; qd < IPG; ++qd) {
+                const int t0 = BLK * jb + 16 * u + 4 * (IPG * wave + qd);
+                lds_void *kd = (lds_void *)(kt + u * kGroupBytes + qd * 1024);
+                lds_void *vd = (lds_void *)(kt + S::tile + u * kGroupBytes + qd * 1024);
+                const int so = (int)((uint32_t)t0 * ROW);
+                const uint32_t vo = dma_vo[qd];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
+            }
+        }
+    };
+
+    // ---- fragment read addresses inside a 16-token group (bytes)
+    // K, step kk: row n, piece g4 + 4kk.
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * ROW + 16 * ((g4 + 4 * kk + F::rot(n)) & (F::slots - 1));
+    // V^T, dim tile dt: lane i of group g4 addresses row 4g4 + i/4, components
+    // 16dt + 4(i%4) .. +3; lane k then holds component 16dt + k of rows
+    // 4g4 .. 4g4+3 of the group.
+    uint32_t v_rd[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const int r = 4 * g4 + (n >> 2);
+        v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + F::rot(r)) & (F::slots - 1));
+    }
+
+    f32x4 o[QB][8];
+    float lsum[QB], mrun[QB];
+    bool bad[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lsum[qb] = 0.f;
+        mrun[qb] = -INFINITY;
+        bad[qb] = false;
+    }
+    bool online = false;    // wave-uniform
+
+    // ---- ring prologue
+    int issued = 0;
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k)
+        if (k < nblk) {
+            issue(k, k);
+            ++issued;
+        }
+    // Q^T fragments (B operand of the score product): k index of MFMA step kk
+    // = component 8*g4 + 32*kk + j; the K fragments use the same map.  Rows
+    // past the block read the last row and are never stored.  The loads and
+    // their wait sit in one assembly statement (early-clobber outputs): the
+    // compiler never sees a register that a load still in flight will write.
+    // The wait also covers the prologue's DMAs, which overlap the loads.
+    u32x4 qf[QB][4];
+    {
+        const size_t head_row = ((size_t)b * p.hq + h) * p.q_len;
+        const uint16_t *qrow[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            qrow[qb] = p.q + (head_row + min(jw0 + 16 * qb + n, p.q_len - 1)) * kHeadDim + 8 * g4;
+        static_assert(QB == 2, "the query load statement is written for two blocks");
+        asm volatile("global_load_dwordx4 %0, %8, off\n\t"
+                     "global_load_dwordx4 %1, %8, off offset:64\n\t"
+                     "global_load_dwordx4 %2, %8, off offset:128\n\t"
+                     "global_load_dwordx4 %3, %8, off offset:192\n\t"
+                     "global_load_dwordx4 %4, %9, off\n\t"
+                     "global_load_dwordx4 %5, %9, off offset:64\n\t"
+                     "global_load_dwordx4 %6, %9, off offset:128\n\t"
+                     "global_load_dwordx4 %7, %9, off offset:192\n\t"
+                     "s_waitcnt vmcnt(0)"
+                     : "=&v"(qf[0][0]), "=&v"(qf[0][1]), "=&v"(qf[0][2]), "=&v"(qf[0][3]),
+                       "=&v"(qf[1][0]), "=&v"(qf[1][1]), "=&v"(qf[1][2]), "=&v"(qf[1][3])
+                     : "v"(qrow[0]), "v"(qrow[1])
+                     : "memory");
+    }
+
+    // One stage of 32 keys, one 16-query block at a time.  Key 16u + 4*g4 + r
+    // of the stage is visible to row n of block qb iff 16u + r <= pos[qb] -
+    // t0 - 4*g4; `below` says every key of the stage is visible to every row.
+    auto stage_compute = [&](int t0, bool below, const u32x4 (&kraw)[2][4], const u32x2 (&vraw)[2][8]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int dpos = below ? (1 << 30) : pos[qb] - t0 - 4 * g4;
+            float sv[2][4];
+            bool tile_bad = false;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) sacc = mfma_bf16(kraw[u][kk], qf[qb][kk], sacc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = sacc[r] * sc;
+                    const bool valid = 16 * u + r <= dpos;
+                    const bool out_of_band = valid && outside_band(x, p.lo, p.hi);
+                    bad[qb] |= out_of_band;
+                    tile_bad |= out_of_band;
+                    sv[u][r] = valid ? x : -INFINITY;
+                }
+            }
+            if (!online && __builtin_amdgcn_ballot_w64(tile_bad) != 0) {
+                // switch to online softmax.  Every sum so far is relative to
+                // phi and built from in-band scores only, so a row that saw a
+                // key continues from reference phi; a row that saw none starts
+                // from -inf.
+                online = true;
+#pragma unroll
+                for (int q2 = 0; q2 < QB; ++q2) {
+                    float l = lsum[q2];
+                    l += __shfl_xor(l, 16);
+                    l += __shfl_xor(l, 32);
+                    mrun[q2] = l > 0.f ? p.phi : -INFINITY;
+                }
+            }
+            float w[2][4];
+            if (!online) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)   // a masked key: exp2(-inf) = 0
+                        w[u][r] = exp2_hw(fmaf(sv[u][r], kLog2e, nphi));
+            } else {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[u][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = fmaxf(mrun[qb], mx);
+                const float f = (mrun[qb] == mnew) ? 1.f : exp2_hw((mrun[qb] - mnew) * kLog2e);
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= f;
+                lsum[qb] *= f;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        w[u][r] = sv[u][r] == -INFINITY ? 0.f : exp2_hw((sv[u][r] - mnew) * kLog2e);
+                mrun[qb] = mnew;
+            }
+            // P^T over the stage's 32 keys: k = 8*g4 + j <-> group j/4, row 4*g4 + j%4
+            const u32x4 pw = {pack_bf16(w[0][0], w[0][1]), pack_bf16(w[0][2], w[0][3]),
+                              pack_bf16(w[1][0], w[1][1]), pack_bf16(w[1][2], w[1][3])};
+            float ls = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ls += bf16_lo(pw[e]) + bf16_hi(pw[e]);
+            lsum[qb] += ls;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
+                o[qb][dt] = mfma_bf16(va, pw, o[qb][dt]);
+            }
+        }
+    };
+
+    int stage = 0;
+#pragma unroll 1
+    for (int s = 0; s < nblk; ++s) {
+        // this wavefront's DMAs of stage s are done (later ones may still be
+        // in flight) ...
+        wait_ring<DPW, NST - 2>(issued - s - 1);
+        // ... and so are everyone else's; everyone is done reading stage s-1
+        __builtin_amdgcn_s_barrier();
+        if (s + NST - 1 < nblk) {
+            issue(s + NST - 1, stage == 0 ? NST - 1 : stage - 1);
+            ++issued;
+        }
+        const int t0 = BLK * s;
+        const bool active = t0 < kend_w;
+        if (active) {
+            const uint32_t kt = (uint32_t)(uintptr_t)(ring + stage * S::stage);
+            u32x4 kraw[2][4];
+            u32x2 vraw[2][8];
+            // group u and the V half are immediate offsets
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint32_t addr = kt + k_rd[kk];
+                asm volatile("ds_read_b128 %0, %1" : "=v"(kraw[0][kk]) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:%2"
+                             : "=v"(kraw[1][kk]) : "v"(addr), "i"(kGroupBytes) : "memory");
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint32_t addr = kt + v_rd[dt];
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(vraw[0][dt]) : "v"(addr), "i"(S::tile) : "memory");
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(vraw[1][dt]) : "v"(addr), "i"(S::tile + kGroupBytes) : "memory");
+            }
+            // the fragments are tied to this wait so that no use moves above it
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(kraw[u][0]), "+v"(kraw[u][1]), "+v"(kraw[u][2]), "+v"(kraw[u][3])
+                             :
+                             : "memory");
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+v"(vraw[u][dt]) : : "memory");
+            }
+            // one code path for masked and unmasked stages (two instances of
+            // the stage body would double the accumulators' registers at the join)
+            stage_compute(t0, t0 + BLK - 1 <= pos_min, kraw, vraw);
+        }
+        stage = stage + 1 == NST ? 0 : stage + 1;
+    }
+
+    // ---- epilogue: weight sums and flags over the 4 lane groups, normalise, store
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float l = lsum[qb];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        int f = bad[qb] ? 1 : 0;
+        f |= __shfl_xor(f, 16);
+        f |= __shfl_xor(f, 32);
+        const int j = jw0 + 16 * qb + n;
+        if (j >= p.q_len) continue;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const size_t row = ((size_t)b * p.hq + h) * p.q_len + j;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const f32x4 x = o[qb][dt] * inv;
+            const size_t e = row * kHeadDim + 16 * dt + 4 * g4;
+            if constexpr (OUT_BF16) {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.out) + e) =
+                    u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+            } else {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + e) = x;
+            }
+        }
+        if (g4 == 0) p.flags[row] = (uint8_t)f;
+    }
+}
+
+}  // namespace prefill
+}  // namespace fd

@@ -68,3 +68,32 @@ class DeviceProblem:
         return int(self.workspace[:4].cpu().view(torch.int32).item())
 
 
+
+
+class DevicePrefill:
+    """A synthetic prefill problem resident in GPU memory."""
+
+    def __init__(self, prob, out_dtype="f32"):
+        self.prob = prob
+        self.q = to_device(prob.q, "bf16")
+        self.k = to_device(prob.k, "bf16")
+        self.v = to_device(prob.v, "bf16")
+        self.kv_lens = torch.from_numpy(prob.kv_lens).cuda()
+        self.out_dtype = out_dtype
+        self.out = torch.empty(prob.q.shape, device="cuda",
+                               dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
+        self.flags = torch.empty(prob.q.shape[:3], device="cuda", dtype=torch.uint8)
+
+    def run(self, phi=None, a=None, b=None, stream=None, stage_events=None):
+        p = self.prob
+        return fd.fd_attn_prefill(self.q, self.k, self.v, self.kv_lens,
+                                  p.phi if phi is None else phi, p.a if a is None else a,
+                                  p.b if b is None else b, self.out, self.flags,
+                                  num_kv_heads=p.num_kv_heads, scale=p.scale,
+                                  out_dtype=self.out_dtype, stream=stream,
+                                  stage_events=stage_events)
+
+    def results(self):
+        torch.cuda.synchronize()
+        out = self.out.float().cpu().numpy().reshape(-1, self.prob.head_dim).astype(np.float64)
+        return out, self.flags.cpu().numpy().reshape(-1)

@@ -13,14 +13,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "fd_attn.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fd_attn_\w+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(fd_attn_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fd_attn_decode", "fd_attn_status_string", "fd_attn_workspace_size"]
+    assert names == ["fd_attn_decode", "fd_attn_prefill", "fd_attn_status_string",
+                     "fd_attn_workspace_size"]
     lib = ctypes.CDLL(fd.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -103,3 +108,47 @@ def test_bad_pointers_dtypes_alignment_band_workspace():
     d = _valid_desc()
     d.scale = float("inf")
     assert _call(d) == -2
+
+
+def _pcall(desc, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, phi=4.0, a=20.0, b=6.0, out=FAKE, flags=FAKE):
+    lib = fd._load()
+    return lib.fd_attn_prefill(ctypes.byref(desc), q, k, v, lens, phi, a, b, out, flags, None)
+
+
+def _pdesc(**kw):
+    base = dict(batch=2, num_q_heads=32, num_kv_heads=8, q_len=8192, max_seq_len=8192)
+    base.update(kw)
+    return fd.make_prefill_desc(**base)
+
+
+def test_prefill_descriptor_layout_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "fd_prefill.h")).read()
+    body = src[src.index("typedef struct {"):src.index("} fd_prefill_desc_t;")]
+    fields = re.findall(r"^\s*\w+\s+\*?\s*(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in fd.FdPrefillDesc._fields_]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=30), -2), (dict(head_dim=64), -2), (dict(q_len=0), -2),
+    (dict(q_len=(1 << 23) + 1), -2), (dict(max_seq_len=0), -2), (dict(batch=0), -2),
+    (dict(batch=65536), -2), (dict(max_seq_len=(1 << 23) + 1), -2),
+    (dict(dtype="f32"), -3), (dict(dtype="e4m3fn"), -3), (dict(out_dtype="e4m3fn"), -3),
+])
+def test_prefill_bad_shapes_and_dtypes(kw, code):
+    assert _pcall(_pdesc(**kw)) == code
+
+
+def test_prefill_bad_pointers_alignment_band():
+    assert _pcall(_pdesc(), q=None) == -1
+    assert _pcall(_pdesc(), lens=None) == -1
+    assert _pcall(_pdesc(), flags=None) == -1
+    assert _pcall(_pdesc(), v=FAKE + 2) == -4
+    assert _pcall(_pdesc(), out=FAKE + 8) == -4
+    assert _pcall(_pdesc(), phi=float("inf")) == -5
+    assert _pcall(_pdesc(), a=65.0) == -5
+    assert _pcall(_pdesc(), b=-0.5) == -5
+    d = _pdesc()
+    d.scale = float("nan")
+    assert _pcall(d) == -2
+    assert fd._load().fd_attn_prefill(None, FAKE, FAKE, FAKE, FAKE, 4.0, 20.0, 6.0, FAKE, FAKE,
+                                      None) == -1

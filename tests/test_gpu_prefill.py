@@ -1,0 +1,171 @@
+"""GPU parity of causal prefill (fd_attn_prefill) against the float64 oracle.
+
+Bar: flags bit-exact; every output element within the bound that rounding
+the attention weights to bf16 allows.  The kernel multiplies the values by
+bf16 weights (relative error <= u = 2^-9 each) and divides by the sum of the
+same rounded weights, so each output row is an exact convex combination of
+value rows with perturbed weights:
+
+    |out' - out| <= u / (1 - u) * max_t |v_t - out| <= 2^-8 * max|v|
+
+plus fp32 accumulation error (<= 1e-5 * max|out| here).  Inputs keep every
+visible score at least 1e-3 from both band edges (checked on the oracle's
+margins), so the flag decision does not depend on precision.  Cases span
+several query tiles (128 queries) and key stages (32 keys), ragged tails,
+blocks appended to a cached prefix, sequences shorter than the block (empty
+early rows), empty sequences, and both fallback directions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_device import DevicePrefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _bound(prob):
+    vmax = float(np.abs(synthetic.bf16_to_f32(prob.v)).max())
+    return 2.0 ** -8 * vmax / (1 - 2.0 ** -9)
+
+
+def _check(prob, dp, rows=None):
+    out, flags = dp.results()
+    ref, ref_flags, margin = oracle.prefill_exact(**prob.args(), rows=rows)
+    if rows is not None:
+        out, flags = out[rows], flags[rows]
+    assert margin.min() >= 1e-3, "input puts a score within 1e-3 of a band edge"
+    np.testing.assert_array_equal(flags, ref_flags)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = float(np.abs(out - ref).max())
+    bound = _bound(prob) + 1e-5 * scale
+    assert err <= bound, "max|err| %.3e > bound %.3e" % (err, bound)
+    return err / scale, ref_flags
+
+
+CASES = {
+    "whole-and-prefixed": dict(batch=2, num_q_heads=4, num_kv_heads=1, q_len=300, kv_lens=[300, 517]),
+    "one-partial-tile": dict(batch=1, num_q_heads=2, num_kv_heads=2, q_len=37, kv_lens=[37]),
+    "short-and-empty": dict(batch=3, num_q_heads=8, num_kv_heads=2, q_len=129, kv_lens=[129, 100, 0]),
+    "single-query": dict(batch=1, num_q_heads=8, num_kv_heads=1, q_len=1, kv_lens=[700]),
+    "exact-tiles-long-prefix": dict(batch=2, num_q_heads=16, num_kv_heads=2, q_len=256,
+                                    kv_lens=[1000, 256]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_small(name):
+    kw = CASES[name]
+    print("case prefill %s %s" % (name, kw), flush=True)
+    prob = synthetic.make_prefill(**kw, seed=synthetic.SEED_BASE + 300 + sorted(CASES).index(name))
+    dp = DevicePrefill(prob)
+    dp.run()
+    rel, ref_flags = _check(prob, dp)
+    assert not ref_flags.any()
+    print("rel err %.3e" % rel)
+
+
+def test_prefill_config_small():
+    prob = synthetic.make_prefill_config(1)
+    print("case prefill config1 kv=%s" % prob.kv_lens.tolist(), flush=True)
+    dp = DevicePrefill(prob)
+    dp.run()
+    rel, _ = _check(prob, dp)
+    print("rel err %.3e" % rel)
+
+
+def test_prefill_bf16_output_is_the_rounded_f32_output():
+    prob = synthetic.make_prefill(**CASES["whole-and-prefixed"], seed=77)
+    print("case prefill bf16 out", flush=True)
+    a = DevicePrefill(prob, out_dtype="f32")
+    b = DevicePrefill(prob, out_dtype="bf16")
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.to(torch.bfloat16), b.out)
+    assert torch.equal(a.flags, b.flags)
+
+
+def test_prefill_fallback_overflow_mid_row():
+    # keys at positions 200 and 333 scaled by 8 (exact in bf16): the rows that
+    # see them score far above phi + b and switch to online softmax after
+    # several in-band stages
+    prob = synthetic.make_prefill(batch=1, num_q_heads=4, num_kv_heads=1, q_len=400,
+                                  kv_lens=[400], seed=91)
+    for t in (200, 333):
+        prob.k[0, 0, t] = synthetic.bf16_round(synthetic.bf16_to_f32(prob.k[0, 0, t]) * 8)
+    print("case prefill overflow", flush=True)
+    dp = DevicePrefill(prob)
+    dp.run()
+    rel, ref_flags = _check(prob, dp)
+    flags = ref_flags.reshape(4, 400)
+    assert flags[:, :200].sum() == 0 and flags.sum() > 0
+    print("rel err %.3e, %d rows flagged" % (rel, int(ref_flags.sum())))
+
+
+def test_prefill_fallback_underflow_everywhere():
+    # band [10, 36]: every score lies below it, so exp(s - phi) alone would
+    # underflow; every row with a key is flagged and computed online from the
+    # first stage
+    prob = synthetic.make_prefill(batch=2, num_q_heads=4, num_kv_heads=2, q_len=150,
+                                  kv_lens=[150, 90], phi=30.0, a=20.0, b=6.0, seed=92)
+    print("case prefill underflow", flush=True)
+    dp = DevicePrefill(prob)
+    dp.run()
+    rel, ref_flags = _check(prob, dp)
+    pos = np.concatenate([np.tile(np.arange(150), 4), np.tile(np.arange(150) - 60, 4)])
+    np.testing.assert_array_equal(ref_flags, (pos >= 0).astype(np.uint8))
+    print("rel err %.3e" % rel)
+
+
+def test_prefill_fallback_in_one_head_only():
+    prob = synthetic.make_prefill(batch=1, num_q_heads=8, num_kv_heads=2, q_len=256,
+                                  kv_lens=[256], seed=93)
+    prob.q[0, 5] = synthetic.bf16_round(synthetic.bf16_to_f32(prob.q[0, 5]) * 4)
+    print("case prefill one head", flush=True)
+    dp = DevicePrefill(prob)
+    dp.run()
+    rel, ref_flags = _check(prob, dp)
+    flags = ref_flags.reshape(8, 256)
+    assert flags[5].any() and flags[np.arange(8) != 5].sum() == 0
+    print("rel err %.3e" % rel)
+
+
+def test_prefill_full_config():
+    prob = synthetic.make_prefill_config(2)
+    B, Hq, Lq = prob.batch, prob.num_q_heads, prob.q_len
+    print("case prefill full config2 %s" % prob.workload, flush=True)
+    dp = DevicePrefill(prob)
+    dp.run()
+    # every visible score inside the band with margin (fp32 scores, per head),
+    # so the expected flags are all zero
+    q = dp.q.float()
+    k = dp.k.float()
+    mask = torch.ones(Lq, Lq, dtype=torch.bool, device="cuda").tril()
+    lo, hi = prob.phi - prob.a, prob.phi + prob.b
+    smin, smax = float("inf"), -float("inf")
+    for b in range(B):
+        for h in range(Hq):
+            kt = k[b, h // (Hq // prob.num_kv_heads)].t().contiguous()
+            s = torch.matmul(q[b, h], kt) * prob.scale
+            vis = s[mask]
+            smin = min(smin, float(vis.min()))
+            smax = max(smax, float(vis.max()))
+    assert smin >= lo + 1e-3 and smax <= hi - 1e-3
+    torch.cuda.synchronize()
+    assert int(dp.flags.sum()) == 0
+    # sampled rows, every query tile boundary region and both ends, against the oracle
+    rng = np.random.default_rng(5)
+    js = np.unique(np.concatenate([[0, 1, 127, 128, 129, Lq // 2, Lq - 2, Lq - 1],
+                                   rng.integers(0, Lq, 40)]))
+    bh = [(0, 0), (0, 3), (0, 31), (1, 7), (1, 16)]
+    rows = np.array([(b * Hq + h) * Lq + j for b, h in bh for j in js], dtype=np.int32)
+    rel, _ = _check(prob, dp, rows=rows)
+    out1 = dp.out.clone()
+    dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, dp.out)
+    print("full config2: rel err %.3e on %d sampled rows, scores in [%.3f, %.3f]"
+          % (rel, len(rows), smin, smax))
