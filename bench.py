@@ -12,6 +12,12 @@ and the float64 CPU oracle timed on a bounded sample as a reported
 baseline.
 
     python bench.py [--steps K] [--warmup W] [--config N]
+
+With --prefill N a step is one fd_attn_prefill call on prefill workload N
+(2: batch 2, 32 query / 8 KV heads, a causal 8192-token prompt, bf16); the
+line then reports attention TFLOP/s (4 * head_dim flops per visible
+query-key pair: the score and the weighted value) against the dense bf16
+matrix-core peak.
 """
 import argparse
 import hashlib
@@ -27,7 +33,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV GB/s and % of HBM peak; calls/sec at GQA 32K ctx"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_CONFIG = 3
+PREFILL_METRIC = "prefill-attn TFLOP/s (causal, unified max) and % of bf16 matrix peak"
 
 
 def source_hash() -> str:
@@ -99,6 +107,97 @@ def cpu_baseline(prob, min_seconds=10.0, max_passes=20):
                       "calls/s equivalent %.4f" % (what, passes, spent, gbs * 1e9 / prob.kv_bytes())}
 
 
+def prefill_cpu_baseline(prob, min_seconds=10.0):
+    """The float64 prefill oracle on the host cores: query rows drawn evenly
+    over every (sequence, head, position) until about min_seconds of CPU time
+    have passed; flops counted per visible query-key pair as on the GPU."""
+    import oracle
+    B, Hq, Lq = prob.batch, prob.num_q_heads, prob.q_len
+    kv = np.clip(prob.kv_lens.astype(np.int64), 0, prob.max_seq_len)
+    n = 64
+    spent, flops, rows_done, threads = 0.0, 0, 0, 1
+    while spent < min_seconds and rows_done < B * Hq * Lq:
+        rows = np.linspace(rows_done * 7919 % (B * Hq * Lq), B * Hq * Lq - 1, n).astype(np.int32)
+        rows = np.unique(rows % (B * Hq * Lq))
+        t = time.perf_counter()
+        _, _, _, threads = oracle.prefill_exact(**prob.args(), rows=rows, with_threads=True)
+        spent += time.perf_counter() - t
+        j = rows % Lq
+        b = rows // (Hq * Lq)
+        flops += int(np.clip(kv[b] - Lq + j + 1, 0, None).sum()) * 4 * prob.head_dim
+        rows_done += len(rows)
+        n = min(4096, n * 2)
+    tf = flops / spent / 1e12
+    return {"value": round(tf, 7), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d query rows spread over all (sequence, head, position), %.1f s, "
+                      "float64 exact causal softmax + band test" % (rows_done, spent)}
+
+
+def main_prefill(args):
+    import torch
+
+    import synthetic
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_device import DevicePrefill
+
+    t_gen = time.perf_counter()
+    prob = synthetic.make_prefill_config(args.prefill)
+    print("generated %s in %.1f s" % (prob.workload, time.perf_counter() - t_gen),
+          file=sys.stderr, flush=True)
+    dp = DevicePrefill(prob)
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        dp.run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        dp.run(stage_events=evs[i])
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / K
+    kernel_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]))
+
+    pairs = prob.visible_pairs()
+    flops = pairs * 4 * prob.head_dim
+    value = flops / per_call / 1e12
+    achieved = flops / (kernel_ms / 1e3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(per_call * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": prob.workload, "batch": prob.batch,
+                   "num_q_heads": prob.num_q_heads, "num_kv_heads": prob.num_kv_heads,
+                   "head_dim": prob.head_dim, "q_len": prob.q_len,
+                   "kv_lens": prob.kv_lens.tolist(), "visible_pairs": pairs,
+                   "flops_per_call": flops, "phi": prob.phi,
+                   "band": [prob.phi - prob.a, prob.phi + prob.b]},
+        "tokens_per_s": round(prob.batch * prob.q_len / per_call, 1),
+        "kernel_ms": round(kernel_ms, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(prob.workload), "kernel": "prefill kernel",
+                     "flops_per_launch": flops},
+        "source_hash": source_hash(),
+    }
+    res["cpu_baseline"] = None if args.no_cpu_baseline else prefill_cpu_baseline(prob)
+    print(json.dumps(res), flush=True)
+
+
 def load_traffic(workload: str):
     """HBM bytes per kernel launch from committed rocprofv3 counter runs,
     if they were taken on the current kernel sources."""
@@ -118,6 +217,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="time fd_attn_prefill on this prefill workload instead of decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
@@ -126,6 +227,9 @@ def main():
         print("bench.py measures one GPU: the decode-attention path is built and timed on a "
               "single MI355X; multi-GPU runs are not part of this library", file=sys.stderr)
         sys.exit(2)
+    if args.prefill:
+        main_prefill(args)
+        return
 
     import torch
 

@@ -55,10 +55,15 @@ extern "C" int fd_attn_prefill(const fd_prefill_desc_t *d, const void *q, const 
     p.ntiles = (int)ntiles;
     p.total = (int)total;
     p.per_xcd = (int)((total + 7) / 8);
-    p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)fd::kHeadDim);
-    p.phi = phi;
-    p.lo = (float)((double)phi - (double)a);
-    p.hi = (float)((double)phi + (double)b);
+    // the kernel works on raw scores q.k: the softmax scale moves into the
+    // exponent factor and the band edges are divided by it
+    const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)fd::kHeadDim);
+    const double log2e = 1.4426950408889634;
+    p.c1 = (float)(scale * log2e);
+    p.c0 = (float)(-(double)phi * log2e);
+    p.lo_raw = (float)(((double)phi - (double)a) / scale);
+    p.hi_raw = (float)(((double)phi + (double)b) / scale);
+    p.phi_raw = (float)((double)phi / scale);
 
     hipEvent_t *ev = d->stage_events;
     hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;

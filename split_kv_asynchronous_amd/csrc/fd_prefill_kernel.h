@@ -33,6 +33,8 @@
 //     stage's 32 keys, taken in the order the two score tiles hand them over.
 #pragma once
 
+#include <type_traits>
+
 #include "fd_ring.h"
 
 namespace fd {
@@ -51,7 +53,9 @@ struct PrefillParams {
     int ntiles;                    // query tiles per (sequence, head)
     int total;                     // work items
     int per_xcd;                   // ceil(total / 8)
-    float scale, phi, lo, hi;
+    float c1;                      // scale * log2(e): raw score -> exponent units
+    float c0;                      // -phi * log2(e)
+    float lo_raw, hi_raw, phi_raw; // band edges and phi in raw score units (divided by scale)
 };
 
 // Two floats -> packed bf16 pair, round to nearest even.
@@ -128,9 +132,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
         pos[qb] = j < p.q_len ? off + j : -1;
     }
 
-    const float sc = p.scale;
-    const float nphi = -p.phi * kLog2e;
-
     // ---- DMA: wavefront w issues instructions IPG*w .. IPG*w + IPG-1 of each
     // group of K and of V; instruction i moves group rows 4i .. 4i+3, lane l
     // fetching, of row 4i + l/16, the piece that belongs in LDS slot l%16.
@@ -179,27 +180,28 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
         v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + F::rot(r)) & (F::slots - 1));
     }
 
-    f32x4 o[QB][8];
-    float lsum[QB], mrun[QB];
-    bool bad[QB];
+    f32x4 o[QB][8];      // O^T: lane (n, g4) holds components 16dt + 4g4 + i of query n
+    f32x4 lacc[QB];      // weight sums: every entry of lane (n, g4) holds query n's sum
+    float mrun[QB];      // online softmax: running maximum (raw score units)
+    bool bad[QB];        // some visible score of query n left the band
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lsum[qb] = 0.f;
+        lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         mrun[qb] = -INFINITY;
         bad[qb] = false;
     }
-    bool online = false;    // wave-uniform
+    // A operand of all ones (bf16 1.0): ones . P^T gives every query's weight
+    // sum of the stage, from the same rounded weights that multiply V
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
     // ---- ring prologue
-    int issued = 0;
 #pragma unroll
     for (int k = 0; k < NST - 1; ++k)
-        if (k < nblk) {
-            issue(k, k);
-            ++issued;
-        }
+        if (k < nblk) issue(k, k);
+    int issued = nblk < NST - 1 ? nblk : NST - 1;
+
     // Q^T fragments (B operand of the score product): k index of MFMA step kk
     // = component 8*g4 + 32*kk + j; the K fragments use the same map.  Rows
     // past the block read the last row and are never stored.  The loads and
@@ -229,148 +231,212 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
                      : "memory");
     }
 
-    // One stage of 32 keys, one 16-query block at a time.  Key 16u + 4*g4 + r
-    // of the stage is visible to row n of block qb iff 16u + r <= pos[qb] -
-    // t0 - 4*g4; `below` says every key of the stage is visible to every row.
-    auto stage_compute = [&](int t0, bool below, const u32x4 (&kraw)[2][4], const u32x2 (&vraw)[2][8]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int dpos = below ? (1 << 30) : pos[qb] - t0 - 4 * g4;
-            float sv[2][4];
-            bool tile_bad = false;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) sacc = mfma_bf16(kraw[u][kk], qf[qb][kk], sacc);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = sacc[r] * sc;
-                    const bool valid = 16 * u + r <= dpos;
-                    const bool out_of_band = valid && outside_band(x, p.lo, p.hi);
-                    bad[qb] |= out_of_band;
-                    tile_bad |= out_of_band;
-                    sv[u][r] = valid ? x : -INFINITY;
-                }
-            }
-            if (!online && __builtin_amdgcn_ballot_w64(tile_bad) != 0) {
-                // switch to online softmax.  Every sum so far is relative to
-                // phi and built from in-band scores only, so a row that saw a
-                // key continues from reference phi; a row that saw none starts
-                // from -inf.
-                online = true;
-#pragma unroll
-                for (int q2 = 0; q2 < QB; ++q2) {
-                    float l = lsum[q2];
-                    l += __shfl_xor(l, 16);
-                    l += __shfl_xor(l, 32);
-                    mrun[q2] = l > 0.f ? p.phi : -INFINITY;
-                }
-            }
-            float w[2][4];
-            if (!online) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)   // a masked key: exp2(-inf) = 0
-                        w[u][r] = exp2_hw(fmaf(sv[u][r], kLog2e, nphi));
-            } else {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[u][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mnew = fmaxf(mrun[qb], mx);
-                const float f = (mrun[qb] == mnew) ? 1.f : exp2_hw((mrun[qb] - mnew) * kLog2e);
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= f;
-                lsum[qb] *= f;
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        w[u][r] = sv[u][r] == -INFINITY ? 0.f : exp2_hw((sv[u][r] - mnew) * kLog2e);
-                mrun[qb] = mnew;
-            }
-            // P^T over the stage's 32 keys: k = 8*g4 + j <-> group j/4, row 4*g4 + j%4
-            const u32x4 pw = {pack_bf16(w[0][0], w[0][1]), pack_bf16(w[0][2], w[0][3]),
-                              pack_bf16(w[1][0], w[1][1]), pack_bf16(w[1][2], w[1][3])};
-            float ls = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ls += bf16_lo(pw[e]) + bf16_hi(pw[e]);
-            lsum[qb] += ls;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
-                o[qb][dt] = mfma_bf16(va, pw, o[qb][dt]);
-            }
+    // ---- per-stage pieces
+    // Wait for stage s (this wavefront's DMAs, then everyone's, through the
+    // barrier, after which everyone is also done reading stage s-1) and refill
+    // the stage that s-1 used.
+    auto sync_stage = [&](int s) {
+        wait_ring<DPW, NST - 2>(issued - s - 1);
+        __builtin_amdgcn_s_barrier();
+        if (s + NST - 1 < nblk) {
+            issue(s + NST - 1, (s + NST - 1) % NST);
+            ++issued;
         }
     };
 
-    int stage = 0;
-#pragma unroll 1
-    for (int s = 0; s < nblk; ++s) {
-        // this wavefront's DMAs of stage s are done (later ones may still be
-        // in flight) ...
-        wait_ring<DPW, NST - 2>(issued - s - 1);
-        // ... and so are everyone else's; everyone is done reading stage s-1
-        __builtin_amdgcn_s_barrier();
-        if (s + NST - 1 < nblk) {
-            issue(s + NST - 1, stage == 0 ? NST - 1 : stage - 1);
-            ++issued;
+    u32x4 kraw[2][4];
+    u32x2 vraw[2][8];
+    // Read stage s's fragments (group u and the V half are immediate offsets);
+    // the fragments are tied to the wait so that no use moves above it.
+    auto read_stage = [&](int s) {
+        const uint32_t kt = (uint32_t)(uintptr_t)(ring + (s % NST) * S::stage);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t addr = kt + k_rd[kk];
+            asm volatile("ds_read_b128 %0, %1" : "=v"(kraw[0][kk]) : "v"(addr) : "memory");
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=v"(kraw[1][kk]) : "v"(addr), "i"(kGroupBytes) : "memory");
         }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t addr = kt + v_rd[dt];
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                         : "=v"(vraw[0][dt]) : "v"(addr), "i"(S::tile) : "memory");
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                         : "=v"(vraw[1][dt]) : "v"(addr), "i"(S::tile + kGroupBytes) : "memory");
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(kraw[u][0]), "+v"(kraw[u][1]), "+v"(kraw[u][2]), "+v"(kraw[u][3])
+                         :
+                         : "memory");
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+v"(vraw[u][dt]) : : "memory");
+        }
+    };
+
+    // Raw scores q.k of the stage for every query block (S^T tiles: lane
+    // (n, g4) holds keys 16u + 4g4 + r for query n) and per block the lane's
+    // largest and smallest visible score.  MASK: some key of the stage is
+    // invisible to some row -- key 16u + 4g4 + r is visible to row n of block
+    // qb iff 16u + r <= pos[qb] - t0 - 4g4 -- and invisible scores become -inf.
+    f32x4 sacc[QB][2];
+    float smax[QB], smin[QB];
+    auto score_stage = [&](int s, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int t0 = BLK * s;
-        const bool active = t0 < kend_w;
-        if (active) {
-            const uint32_t kt = (uint32_t)(uintptr_t)(ring + stage * S::stage);
-            u32x4 kraw[2][4];
-            u32x2 vraw[2][8];
-            // group u and the V half are immediate offsets
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const uint32_t addr = kt + k_rd[kk];
-                asm volatile("ds_read_b128 %0, %1" : "=v"(kraw[0][kk]) : "v"(addr) : "memory");
-                asm volatile("ds_read_b128 %0, %1 offset:%2"
-                             : "=v"(kraw[1][kk]) : "v"(addr), "i"(kGroupBytes) : "memory");
-            }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const uint32_t addr = kt + v_rd[dt];
-                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                             : "=v"(vraw[0][dt]) : "v"(addr), "i"(S::tile) : "memory");
-                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                             : "=v"(vraw[1][dt]) : "v"(addr), "i"(S::tile + kGroupBytes) : "memory");
-            }
-            // the fragments are tied to this wait so that no use moves above it
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                asm volatile("s_waitcnt lgkmcnt(0)"
-                             : "+v"(kraw[u][0]), "+v"(kraw[u][1]), "+v"(kraw[u][2]), "+v"(kraw[u][3])
-                             :
-                             : "memory");
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+v"(vraw[u][dt]) : : "memory");
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kraw[u][kk], qf[qb][kk], acc);
+                sacc[qb][u] = acc;
             }
-            // one code path for masked and unmasked stages (two instances of
-            // the stage body would double the accumulators' registers at the join)
-            stage_compute(t0, t0 + BLK - 1 <= pos_min, kraw, vraw);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int dpos = pos[qb] - t0 - 4 * g4;
+            float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = sacc[qb][u][r];
+                    if constexpr (MASK) {
+                        const bool valid = 16 * u + r <= dpos;
+                        mx = fmaxf(mx, valid ? x : -INFINITY);
+                        mn = fminf(mn, valid ? x : INFINITY);
+                        sacc[qb][u][r] = valid ? x : -INFINITY;
+                    } else {
+                        mx = fmaxf(mx, x);
+                        mn = fminf(mn, x);
+                    }
+                }
+            smax[qb] = mx;
+            smin[qb] = mn;
         }
-        stage = stage + 1 == NST ? 0 : stage + 1;
+    };
+
+    // Band test of the stage (closed band, raw score units); true if any row
+    // of the wavefront saw a score outside it.
+    auto band_stage = [&]() {
+        bool any = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const bool out = smax[qb] > p.hi_raw || smin[qb] < p.lo_raw;
+            bad[qb] |= out;
+            any |= out;
+        }
+        return __builtin_amdgcn_ballot_w64(any) != 0;
+    };
+
+    // Weights of block qb -> bf16 P^T (k = 8*g4 + j <-> group j/4, key row
+    // 4*g4 + j%4), then l += ones . P^T and O^T += V^T . P^T over 32 keys.
+    // nm is the exponent offset: -phi*log2e (unified) or -m*scale*log2e.
+    auto accumulate = [&](int qb, float nm) {
+        float w[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], p.c1, nm));  // -inf -> 0
+        const u32x4 pw = {pack_bf16(w[0][0], w[0][1]), pack_bf16(w[0][2], w[0][3]),
+                          pack_bf16(w[1][0], w[1][1]), pack_bf16(w[1][2], w[1][3])};
+        lacc[qb] = mfma_bf16(ones, pw, lacc[qb]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
+            o[qb][dt] = mfma_bf16(va, pw, o[qb][dt]);
+        }
+    };
+
+    // Stages this wavefront computes: [0, nact); of those, [0, nfull) are
+    // visible to every row (no mask).  Stages [nact, nblk) are only synchronised.
+    const int nact = min(nblk, (kend_w + BLK - 1) / BLK);
+    const int nfull = max(0, min(nact, (pos_min + 1) / BLK));
+
+    // One unified-max stage: weights exp(s - phi), no maximum, no rescaling.
+    // Returns true if some row of the wavefront sees a score outside the
+    // band; such a stage adds exactly nothing here (exponent offset -inf, so
+    // every weight is 0) and the online loop redoes it.  Accumulating
+    // unconditionally keeps the loop body free of branches around the
+    // products, so the accumulators are updated in place.
+    auto unified_stage = [&](int s, auto mask_tag) {
+        sync_stage(s);
+        read_stage(s);
+        score_stage(s, mask_tag);
+        const bool leave = band_stage();
+        const float nm = leave ? -INFINITY : p.c0;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) accumulate(qb, nm);
+        return leave;
+    };
+
+    // ---- unified-max loops (each body straight-line but for the exit)
+    int s = 0;
+    bool switched = false;
+#pragma unroll 1
+    for (; s < nfull; ++s)
+        if (unified_stage(s, std::false_type{})) {
+            switched = true;
+            break;
+        }
+    if (!switched) {
+#pragma unroll 1
+        for (; s < nact; ++s)
+            if (unified_stage(s, std::true_type{})) {
+                switched = true;
+                break;
+            }
     }
 
-    // ---- epilogue: weight sums and flags over the 4 lane groups, normalise, store
+    // ---- online softmax from the stage that left the band on.  The sums so
+    // far are relative to phi and built from in-band scores only: a row that
+    // saw a key continues from reference phi, a row that saw none from -inf.
+    if (switched) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mrun[qb] = lacc[qb][0] > 0.f ? p.phi_raw : -INFINITY;
+#pragma unroll 1
+        for (bool first = true; s < nact; ++s, first = false) {
+            if (!first) {
+                sync_stage(s);
+                read_stage(s);
+                if (s < nfull)
+                    score_stage(s, std::false_type{});
+                else
+                    score_stage(s, std::true_type{});
+                band_stage();
+            }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float mx = smax[qb];
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = fmaxf(mrun[qb], mx);
+                const float f = (mrun[qb] == mnew) ? 1.f : exp2_hw((mrun[qb] - mnew) * p.c1);
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= f;
+                lacc[qb] *= f;
+                mrun[qb] = mnew;
+                accumulate(qb, mnew == -INFINITY ? 0.f : -mnew * p.c1);
+            }
+        }
+    }
+
+    // ---- stages only the other wavefronts compute
+#pragma unroll 1
+    for (; s < nblk; ++s) sync_stage(s);
+
+    // ---- epilogue: flags over the 4 lane groups, normalise, store
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        float l = lsum[qb];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
         int f = bad[qb] ? 1 : 0;
         f |= __shfl_xor(f, 16);
         f |= __shfl_xor(f, 32);
         const int j = jw0 + 16 * qb + n;
         if (j >= p.q_len) continue;
+        const float l = lacc[qb][0];
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const size_t row = ((size_t)b * p.hq + h) * p.q_len + j;
 #pragma unroll
