@@ -65,6 +65,15 @@ FD_DEV uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// LDS slot rotation of the 16-byte pieces of group row r (0..15): piece j
+// of the row lands in slot (j + piece_rot(r)) mod 16.  The LDS serves 256
+// bytes (64 banks) per cycle.  A K fragment read (ds_read_b128) takes one
+// piece from each of 16 rows at once: the rotations of rows 0..15 are all
+// distinct.  A transposing V read (ds_read_b64_tr_b16) takes, per row, two
+// adjacent slots from 8 rows at once (0..7 or 8..15): those rows start on
+// distinct even, or distinct odd, slots, so their slot pairs are disjoint.
+FD_DEV int piece_rot(int r) { return 2 * (r & 7) + (r >> 3); }
+
 template <int NW, int QB, int NST>
 struct Shape {
     static constexpr int waves = NW;
@@ -87,8 +96,7 @@ template <int NW, int QB, int NST, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
 {
     using S = Shape<NW, QB, NST>;
-    using F = Fmt<FD_BF16>;
-    constexpr int ROW = F::row;                    // 256 bytes per cache row
+    constexpr int ROW = 256;                       // bytes per cache row (16 pieces of 16 bytes)
     constexpr int BLK = S::keys;
     constexpr int IPG = S::dma_per_group;
     constexpr int DPW = S::dma_per_wave;
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
 #pragma unroll
     for (int qd = 0; qd < IPG; ++qd) {
         const int r = 4 * (IPG * wave + qd) + lane / 16;
-        dma_vo[qd] = (lane / 16) * ROW + 16 * ((lane % 16 - F::rot(r)) & (F::slots - 1));
+        dma_vo[qd] = (lane / 16) * ROW + 16 * ((lane % 16 - piece_rot(r)) & 15);
     }
     const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * ROW;
     const int nrec = (int)((uint32_t)kv * ROW);    // rows past kv read as zeros
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
     // K, step kk: row n, piece g4 + 4kk.
     uint32_t k_rd[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * ROW + 16 * ((g4 + 4 * kk + F::rot(n)) & (F::slots - 1));
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * ROW + 16 * ((g4 + 4 * kk + piece_rot(n)) & 15);
     // V^T, dim tile dt: lane i of group g4 addresses row 4g4 + i/4, components
     // 16dt + 4(i%4) .. +3; lane k then holds component 16dt + k of rows
     // 4g4 .. 4g4+3 of the group.
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
         const int r = 4 * g4 + (n >> 2);
-        v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + F::rot(r)) & (F::slots - 1));
+        v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + piece_rot(r)) & 15);
     }
 
     f32x4 o[QB][8];      // O^T: lane (n, g4) holds components 16dt + 4g4 + i of query n
@@ -343,12 +351,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
             for (int r = 0; r < 4; ++r) w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], p.c1, nm));  // -inf -> 0
         const u32x4 pw = {pack_bf16(w[0][0], w[0][1]), pack_bf16(w[0][2], w[0][3]),
                           pack_bf16(w[1][0], w[1][1]), pack_bf16(w[1][2], w[1][3])};
+        // raised issue priority while this wavefront feeds the matrix cores:
+        // the other wavefront of the SIMD fills the gaps with its vector work
+        __builtin_amdgcn_s_setprio(1);
         lacc[qb] = mfma_bf16(ones, pw, lacc[qb]);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
             o[qb][dt] = mfma_bf16(va, pw, o[qb][dt]);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Stages this wavefront computes: [0, nact); of those, [0, nfull) are

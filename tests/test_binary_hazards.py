@@ -1,16 +1,19 @@
 """Static check of the built GPU code: no register written by a vector-memory
-load is read or overwritten before a wait that covers the load.
+or LDS load is read or overwritten before a wait that covers the load.
 
 Some kernels issue loads from inline assembly, which the compiler's own wait
 tracking does not see; if register allocation then moves, spills or reuses a
 destination register while the load is in flight, the late data lands on
-whatever the register holds by then (an address, say) and the kernel faults.
-This test disassembles every gfx950 kernel of libfd_attn.so and walks its
-control-flow graph from each vector-memory load: on every path, each
-instruction that names one of the load's destination registers must come
-after an s_waitcnt whose vmcnt is at most the number of vector-memory
-instructions issued after the load on that path (gfx9 vector memory
-operations complete in issue order).  CPU only; needs the ROCm LLVM tools.
+whatever the register holds by then (an address, say) and the kernel faults
+or computes garbage.  This test disassembles every gfx950 kernel of
+libfd_attn.so and walks its control-flow graph from each load: on every
+path, each instruction that names one of the load's destination registers
+must come after a covering s_waitcnt.  Vector-memory loads complete in issue
+order, so vmcnt(N) covers a load once N vector-memory instructions were
+issued after it.  LDS loads also complete in order, but they share lgkmcnt
+with scalar memory loads, which may complete out of order: lgkmcnt(N) covers
+an LDS load once N LDS instructions were issued after it and no scalar load
+was.  CPU only; needs the ROCm LLVM tools.
 """
 import os
 import re
@@ -85,11 +88,11 @@ def _operands(ins):
     return parts[1] if len(parts) > 1 else ""
 
 
-def _vm_wait(ins):
-    """vmcnt of an s_waitcnt, or None if it does not wait on vector memory."""
+def _wait(ins, counter):
+    """The counter's value in an s_waitcnt, or None if it does not wait on it."""
     if not ins.startswith("s_waitcnt ") and ins != "s_waitcnt":
         return None
-    m = re.search(r"vmcnt\((\d+)\)", ins)
+    m = re.search(counter + r"\((\d+)\)", ins)
     return int(m.group(1)) if m else None
 
 
@@ -112,31 +115,40 @@ def _hazards(body):
     found = []
     for i, (_, ins, _) in enumerate(body):
         op = ins.split(None, 1)[0] if ins else ""
-        if not (op.startswith(VMEM) and "load" in op) or "lds" in op or ins.endswith(" lds"):
+        vmem = op.startswith(VMEM) and "load" in op and "lds" not in op and not ins.endswith(" lds")
+        lds = op.startswith("ds_read") or op.startswith("ds_load")
+        if not (vmem or lds):
             continue
         dst = _regs(_operands(ins).split(",")[0])
         if not dst:
             continue
+        counter = "vmcnt" if vmem else "lgkmcnt"
         seen = set()
-        stack = [(j, 0) for j in successors(i)]
+        # state: (instruction, same-kind ops issued since, a scalar load issued since)
+        stack = [(j, 0, False) for j in successors(i)]
         while stack:
-            j, later = stack.pop()
-            if (j, later) in seen:
+            j, later, smem = stack.pop()
+            if (j, later, smem) in seen:
                 continue
-            seen.add((j, later))
+            seen.add((j, later, smem))
             t = body[j][1]
-            w = _vm_wait(t)
-            if w is not None and w <= later:
+            w = _wait(t, counter)
+            if w is not None and (w == 0 or (w <= later and not smem)):
                 continue                      # the load is complete on this path
             ops = _operands(t)
+            top = t.split(None, 1)[0] if t else ""
             if _regs(ops) & dst:
-                top = t.split(None, 1)[0]
-                if top.startswith(VMEM) and "load" in top and not _regs(",".join(ops.split(",")[1:])) & dst:
+                same_kind = (top.startswith(VMEM) and "load" in top) if vmem else top.startswith("ds_read")
+                if same_kind and not _regs(",".join(ops.split(",")[1:])) & dst:
                     continue                  # a newer load takes the registers over (in-order completion)
                 found.append((ins, t))
                 break
-            nxt = later + (1 if t.split(None, 1)[0].startswith(VMEM) else 0)
-            stack.extend((k, min(nxt, 64)) for k in successors(j))
+            if vmem:
+                nxt, nsmem = later + (1 if top.startswith(VMEM) else 0), smem
+            else:
+                nxt = later + (1 if top.startswith("ds_") else 0)
+                nsmem = smem or top.startswith("s_load") or top.startswith("s_buffer_load")
+            stack.extend((k, min(nxt, 64), nsmem) for k in successors(j))
     return found
 
 
