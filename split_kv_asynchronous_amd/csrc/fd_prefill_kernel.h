@@ -65,14 +65,9 @@ FD_DEV uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// LDS slot rotation of the 16-byte pieces of group row r (0..15): piece j
-// of the row lands in slot (j + piece_rot(r)) mod 16.  The LDS serves 256
-// bytes (64 banks) per cycle.  A K fragment read (ds_read_b128) takes one
-// piece from each of 16 rows at once: the rotations of rows 0..15 are all
-// distinct.  A transposing V read (ds_read_b64_tr_b16) takes, per row, two
-// adjacent slots from 8 rows at once (0..7 or 8..15): those rows start on
-// distinct even, or distinct odd, slots, so their slot pairs are disjoint.
-FD_DEV int piece_rot(int r) { return 2 * (r & 7) + (r >> 3); }
+// LDS slot rotation of the 16-byte pieces of a 16-row group (the bf16 cache
+// format's, chosen for the 64-bank LDS)
+FD_DEV int piece_rot(int r) { return Fmt<FD_BF16>::rot(r); }
 
 template <int NW, int QB, int NST>
 struct Shape {

@@ -17,10 +17,15 @@ constexpr int kGroupBytes = 4096;   // one compute group of K (or V): 16 bf16 or
 // A cache row is moved into LDS as 16-byte pieces; piece j of group row t
 // lands in slot (j + rot(t)) mod slots, which keeps the K fragment reads
 // (ds_read_b128) and the transposing V reads free of bank conflicts.
+// bf16: the LDS serves 256 bytes (64 banks) per cycle.  A K fragment read
+// takes one piece from each of 16 rows at once, and the rotations of rows
+// 0..15 are all distinct; a transposing V read takes two adjacent slots
+// from each of 8 rows at once (0..7 or 8..15), which start on distinct even,
+// or distinct odd, slots, so their slot pairs are disjoint.
 template <int KV> struct Fmt;
 template <> struct Fmt<FD_BF16> {
     static constexpr int row = 256, group = 16, slots = 16;
-    static FD_DEV int rot(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }   // t = 0..15
+    static FD_DEV int rot(int t) { return 2 * (t & 7) + (t >> 3); }   // t = 0..15
 };
 template <> struct Fmt<FD_FP8_E4M3FN> {
     static constexpr int row = 128, group = 32, slots = 8;
