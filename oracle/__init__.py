@@ -304,3 +304,58 @@ def prefill_unified(q, k, v, kv_lens, *, num_kv_heads, q_dtype="bf16", kv_dtype=
     if rc < 0:
         raise ValueError("tile must be positive")
     return out, flags, red
+
+
+# ---------------------------------------------------------------------------
+# calibration: score extremes and histogram, band choice
+# ---------------------------------------------------------------------------
+
+def _load_calib():
+    lib = _load()
+    if not getattr(lib, "_calib_ready", False):
+        P, I = ctypes.POINTER(_Problem), ctypes.POINTER(_Inputs)
+        lib.orc_score_stats.argtypes = [P, I, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_score_stats.restype = ctypes.c_int
+        lib.orc_rows_in_band.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        lib.orc_rows_in_band.restype = ctypes.c_int64
+        lib.orc_min_band_width.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int64]
+        lib.orc_min_band_width.restype = ctypes.c_double
+        lib._calib_ready = True
+    return lib
+
+
+def score_stats(q, k_cache, v_cache, seq_lens, block_table=None, *, num_kv_heads, max_seq_len,
+                page_size=0, q_dtype="bf16", kv_dtype="bf16", scale, k_scale=None, v_scale=None,
+                hist_lo=-16.0, hist_hi=16.0, nbins=0, with_threads=False, **_ignored):
+    """Per-row largest and smallest valid score (float64; empty rows -inf / +inf)
+    and, if nbins > 0, the histogram counts [below, bin 0 .. nbins-1, at or above]
+    of every valid score over [hist_lo, hist_hi)."""
+    prob, ins, keep = _marshal(q, k_cache, v_cache, seq_lens, block_table, num_kv_heads,
+                               max_seq_len, page_size, q_dtype, kv_dtype, scale, k_scale, v_scale)
+    B, Hq, _ = keep[0].shape
+    mx = np.zeros(B * Hq, dtype=np.float64)
+    mn = np.zeros(B * Hq, dtype=np.float64)
+    counts = np.zeros(max(nbins, 0) + 2, dtype=np.int64)
+    th = _load_calib().orc_score_stats(ctypes.byref(prob), ctypes.byref(ins), float(hist_lo),
+                                       float(hist_hi), int(nbins), _ptr(mx), _ptr(mn), _ptr(counts))
+    res = (mx, mn, counts if nbins > 0 else None)
+    return res + (th,) if with_threads else res
+
+
+def rows_in_band(row_max, row_min, phi, a, b) -> int:
+    """Non-empty rows whose extremes lie inside [phi - a, phi + b] (float64)."""
+    mx = np.ascontiguousarray(row_max, dtype=np.float64)
+    mn = np.ascontiguousarray(row_min, dtype=np.float64)
+    return int(_load_calib().orc_rows_in_band(_ptr(mx), _ptr(mn), mx.size, float(phi), float(a),
+                                              float(b)))
+
+
+def min_band_width(row_max, row_min, allowed) -> float:
+    """Smallest band width a + b for which all but `allowed` non-empty rows fit
+    (float64, exact over the given extremes; 0 if no row needs to fit)."""
+    mx = np.ascontiguousarray(row_max, dtype=np.float64)
+    mn = np.ascontiguousarray(row_min, dtype=np.float64)
+    return float(_load_calib().orc_min_band_width(_ptr(mx), _ptr(mn), mx.size, int(allowed)))

@@ -41,7 +41,8 @@
  *   query head h reads KV head h / (Hq / Hkv)
  *
  * The prefill form (a causal block of queries per sequence, same unified
- * maximum and band) is defined in its own section at the end of this file.
+ * maximum and band) and the calibration statistics (choosing phi and the
+ * band from observed scores) have sections of their own at the end.
  *
  * Readings taken where the pages are silent: the band is closed at both ends
  * and a NaN score is outside it; tokens t >= seq_lens[b] are not attended and
@@ -554,4 +555,109 @@ int orc_prefill_unified(const orc_prefill_problem *p, const orc_prefill_inputs *
         }
     }
     return threads;
+}
+
+/* -------------------------------------------------------------- calibration */
+/*
+ * Choosing phi from observed scores (FlashDecoding++ theory page, section 3:
+ * phi is set beforehand from the observed score distribution; rows that
+ * leave the band take the fallback).
+ *
+ * orc_score_stats(): per row (b, h) the largest and smallest valid score
+ * (empty rows: -inf / +inf) and, when nbins > 0, a histogram of every valid
+ * score: counts[0] below lo, counts[1 + i] in [lo + i w, lo + (i+1) w),
+ * counts[nbins + 1] at or above hi, w = (hi - lo) / nbins, bins by
+ * floor((s - lo) / w) in float64.
+ *
+ * A row with extremes [mn, mx] stays in band [phi - a, phi + b] iff
+ * phi - a <= mn and mx <= phi + b.  A set of rows fits one band of width
+ * W = a + b (phi placed anywhere) iff max(mx) - min(mn) <= W over the set.
+ * orc_min_band_width(): the smallest W for which all but `allowed` of the
+ * non-empty rows fit, by brute force over the smallest minimum of the set.
+ * orc_rows_in_band(): how many non-empty rows a given (phi, a, b) keeps.
+ */
+int orc_score_stats(const orc_problem *p, const orc_inputs *in, double lo, double hi, int nbins,
+                    double *row_max, double *row_min, int64_t *counts)
+{
+    const int rows = p->batch * p->num_q_heads;
+    int threads = 1;
+    if (nbins > 0) memset(counts, 0, sizeof(int64_t) * (size_t)(nbins + 2));
+    const double w = nbins > 0 ? (hi - lo) / nbins : 1.0;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        threads = omp_get_num_threads();
+#endif
+        double *s = malloc(sizeof(double) * (size_t)(p->max_seq_len > 0 ? p->max_seq_len : 1));
+        int64_t *local = nbins > 0 ? calloc((size_t)(nbins + 2), sizeof(int64_t)) : NULL;
+#pragma omp for schedule(dynamic, 4)
+        for (int r = 0; r < rows; r++) {
+            const int b = r / p->num_q_heads, h = r % p->num_q_heads;
+            const int n = seq_len_of(p, in, b);
+            row_scores(p, in, b, h, n, s);
+            double mx = -INFINITY, mn = INFINITY;
+            for (int t = 0; t < n; t++) {
+                if (s[t] > mx) mx = s[t];
+                if (s[t] < mn) mn = s[t];
+                if (local) {
+                    if (s[t] < lo) local[0]++;
+                    else if (s[t] >= hi) local[nbins + 1]++;
+                    else {
+                        int i = (int)floor((s[t] - lo) / w);
+                        if (i >= nbins) i = nbins - 1;   /* rounding right below hi */
+                        local[1 + i]++;
+                    }
+                }
+            }
+            row_max[r] = mx;
+            row_min[r] = mn;
+        }
+        if (local) {
+#pragma omp critical
+            for (int i = 0; i < nbins + 2; i++) counts[i] += local[i];
+            free(local);
+        }
+        free(s);
+    }
+    return threads;
+}
+
+int64_t orc_rows_in_band(const double *row_max, const double *row_min, int64_t n, double phi,
+                         double a, double b)
+{
+    int64_t k = 0;
+    for (int64_t r = 0; r < n; r++)
+        if (row_max[r] >= row_min[r] && phi - a <= row_min[r] && row_max[r] <= phi + b) k++;
+    return k;
+}
+
+static int cmp_double(const void *x, const void *y)
+{
+    const double u = *(const double *)x, v = *(const double *)y;
+    return (u > v) - (u < v);
+}
+
+double orc_min_band_width(const double *row_max, const double *row_min, int64_t n, int64_t allowed)
+{
+    int64_t m = 0;
+    for (int64_t r = 0; r < n; r++)
+        if (row_max[r] >= row_min[r]) m++;
+    const int64_t need = m - (allowed < 0 ? 0 : allowed);
+    if (need <= 0) return 0.0;
+    double best = INFINITY;
+    double *maxes = malloc(sizeof(double) * (size_t)m);
+    for (int64_t j = 0; j < n; j++) {
+        if (!(row_max[j] >= row_min[j])) continue;
+        const double L = row_min[j];               /* the set's smallest minimum */
+        int64_t c = 0;
+        for (int64_t r = 0; r < n; r++)
+            if (row_max[r] >= row_min[r] && row_min[r] >= L) maxes[c++] = row_max[r];
+        if (c < need) continue;
+        qsort(maxes, (size_t)c, sizeof(double), cmp_double);
+        const double W = maxes[need - 1] - L;
+        if (W < best) best = W;
+    }
+    free(maxes);
+    return best;
 }
