@@ -13,6 +13,10 @@ baseline.
 
     python bench.py [--steps K] [--warmup W] [--config N]
 
+With --stats N a step is one fd_attn_score_stats call (per-row score extremes
+and a 4096-bin histogram, the calibration pass for phi) on decode workload N;
+the line reports K bytes read per second against HBM peak.
+
 With --prefill N a step is one fd_attn_prefill call on prefill workload N
 (2: batch 2, 32 query / 8 KV heads, a causal 8192-token prompt, bf16); the
 line then reports attention TFLOP/s (4 * head_dim flops per visible
@@ -212,6 +216,86 @@ def main_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def stats_cpu_baseline(prob, min_seconds=10.0):
+    """The float64 calibration oracle (extremes + histogram) on the host cores,
+    on whole batch entries until about min_seconds have passed."""
+    import oracle
+    B, Hq = prob.batch, prob.num_q_heads
+    lens = np.clip(prob.seq_lens, 0, prob.max_seq_len).astype(np.int64)
+    elt = {"f32": 4, "bf16": 2, "e4m3fn": 1}[prob.kv_dtype]
+    spent, nbytes, done, threads = 0.0, 0, 0, 1
+    while spent < min_seconds and done < B:
+        sub = dict(prob.args())
+        sl = slice(done, done + 1)
+        sub["q"] = prob.q[sl]
+        sub["seq_lens"] = prob.seq_lens[sl]
+        if prob.page_size:
+            sub["block_table"] = prob.block_table[sl]
+        else:
+            sub["k_cache"] = prob.k_cache[sl]
+            sub["v_cache"] = prob.v_cache[sl]
+        t = time.perf_counter()
+        _, _, _, threads = oracle.score_stats(**sub, hist_lo=-8.0, hist_hi=8.0, nbins=4096,
+                                              with_threads=True)
+        spent += time.perf_counter() - t
+        nbytes += int(lens[done]) * prob.num_kv_heads * prob.head_dim * elt
+        done += 1
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "sample": "batch entries 0..%d (all %d query heads), %.1f s, float64 "
+                                        "scores, extremes and 4096-bin histogram" % (done - 1, Hq, spent)}
+
+
+def main_stats(args):
+    import torch
+
+    import split_kv_asynchronous_amd as fd
+    import synthetic
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_device import DeviceProblem
+
+    prob = synthetic.make_config(args.stats)
+    print("generated %s" % prob.workload, file=sys.stderr, flush=True)
+    dp = DeviceProblem(prob)
+
+    def run():
+        return fd.fd_attn_score_stats(dp.q, dp.k, dp.seq_lens, dp.block_table,
+                                      max_seq_len=prob.max_seq_len, chunk_size=prob.chunk_size,
+                                      num_kv_heads=prob.num_kv_heads, page_size=prob.page_size,
+                                      scale=prob.scale, k_scale=dp.k_scale, hist_lo=-8.0,
+                                      hist_hi=8.0, nbins=4096, q_dtype=prob.q_dtype,
+                                      kv_dtype=prob.kv_dtype)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        run()
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / K
+    elt = {"f32": 4, "bf16": 2, "e4m3fn": 1}[prob.kv_dtype]
+    lens = np.clip(prob.seq_lens, 0, prob.max_seq_len).astype(np.int64)
+    kbytes = int(lens.sum()) * prob.num_kv_heads * prob.head_dim * elt
+    value = kbytes / per_call / 1e9
+    res = {
+        "metric": "score-statistics pass (phi calibration): K GB/s and % of HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(per_call * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "e4m3fn": "fp8e4m3"}[prob.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": prob.workload, "k_bytes_per_call": kbytes, "nbins": 4096,
+                   "hist_range": [-8.0, 8.0]},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("stats:" + prob.workload),
+                     "kernel": "score-statistics kernel (whole call: init + pass)",
+                     "bytes_per_launch": kbytes},
+        "source_hash": source_hash(),
+    }
+    res["cpu_baseline"] = None if args.no_cpu_baseline else stats_cpu_baseline(prob)
+    print(json.dumps(res), flush=True)
+
+
 def load_traffic(workload: str):
     """HBM bytes per kernel launch from committed rocprofv3 counter runs,
     if they were taken on the current kernel sources."""
@@ -231,6 +315,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
+    ap.add_argument("--stats", type=int, default=0,
+                    help="time fd_attn_score_stats (phi calibration pass) on this decode workload")
     ap.add_argument("--prefill", type=int, default=0,
                     help="time fd_attn_prefill on this prefill workload instead of decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -243,6 +329,9 @@ def main():
         sys.exit(2)
     if args.prefill:
         main_prefill(args)
+        return
+    if args.stats:
+        main_stats(args)
         return
 
     import torch

@@ -13,7 +13,8 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["fd_attn_decode", "fd_attn_prefill", "fd_attn_workspace_size",
+__all__ = ["fd_attn_decode", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
+           "fd_attn_workspace_size",
            "fd_attn_status_string", "FdAttnError", "make_desc", "make_prefill_desc",
            "library_path", "FD_F32", "FD_BF16", "FD_FP8_E4M3FN"]
 
@@ -81,6 +82,16 @@ def _load():
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.fd_attn_prefill.restype = ctypes.c_int
+        lib.fd_attn_score_stats.argtypes = [D, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        lib.fd_attn_score_stats.restype = ctypes.c_int
+        lib.fd_attn_choose_band.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        lib.fd_attn_choose_band.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -253,6 +264,81 @@ def fd_attn_prefill(q, k, v, kv_lens, phi: float, a: float, b: float, out=None,
     if rc != 0:
         raise FdAttnError(rc, fd_attn_status_string(rc))
     return out, fallback_flags
+
+
+def fd_attn_score_stats(q, k_cache, seq_lens, block_table=None, *, max_seq_len: int,
+                        chunk_size: int = 512, num_kv_heads: Optional[int] = None,
+                        page_size: int = 0, scale: Optional[float] = None, k_scale=None,
+                        hist_lo: float = -16.0, hist_hi: float = 16.0, nbins: int = 0,
+                        q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
+                        stream=None):
+    """Per-row score extremes (and optionally a histogram) of decode inputs.
+
+    Same tensors and layouts as fd_attn_decode (V is not read).  Returns
+    (row_max [B][Hq] f32, row_min [B][Hq] f32, hist uint32 [nbins + 2] as an
+    int32 tensor of the same bits, or None).
+    """
+    import torch
+    dev = q.device
+    B, Hq, D = q.shape
+    qd = q_dtype or _torch_code(q)
+    kd = kv_dtype or _torch_code(k_cache)
+    if num_kv_heads is None:
+        num_kv_heads = k_cache.shape[1]
+    for t in (q, k_cache, seq_lens):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on the same device")
+    max_blocks = num_pages = 0
+    if page_size:
+        max_blocks = block_table.shape[1]
+        num_pages = k_cache.shape[0]
+    ks = 0
+    if kd == "e4m3fn":
+        if k_scale is None:
+            raise ValueError("fp8 caches need k_scale")
+        k_scale = k_scale.contiguous()
+        ks = k_scale.data_ptr()
+    desc = make_desc(batch=B, num_q_heads=Hq, num_kv_heads=num_kv_heads, max_seq_len=max_seq_len,
+                     chunk_size=chunk_size, page_size=page_size, max_blocks_per_seq=max_blocks,
+                     num_pages=num_pages, scale=scale, q_dtype=qd, kv_dtype=kd, head_dim=D,
+                     k_scale_ptr=ks)
+    row_max = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    row_min = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    hist = torch.empty(nbins + 2, dtype=torch.int32, device=dev) if nbins > 0 else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _load().fd_attn_score_stats(ctypes.byref(desc), q.data_ptr(), k_cache.data_ptr(),
+                                     seq_lens.data_ptr(),
+                                     block_table.data_ptr() if page_size else None,
+                                     float(hist_lo), float(hist_hi), int(nbins),
+                                     row_max.data_ptr(), row_min.data_ptr(),
+                                     hist.data_ptr() if hist is not None else None, stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return row_max, row_min, hist
+
+
+def fd_attn_choose_band(row_max, row_min, max_flag_fraction: float = 0.0, a_share: float = 0.5,
+                        max_width: float = 64.0, pad: float = 1e-3):
+    """Host band choice (include/fd_calib.h) from per-row extremes (array-likes
+    or CPU/GPU tensors).  Returns (phi, a, b, flagged_rows)."""
+    import numpy as np
+    def host(x):
+        if hasattr(x, "detach"):
+            x = x.detach().float().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(x, dtype=np.float32).ravel())
+    mx, mn = host(row_max), host(row_min)
+    if mx.shape != mn.shape:
+        raise ValueError("row_max and row_min differ in size")
+    phi, a, b = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    flagged = ctypes.c_int64()
+    rc = _load().fd_attn_choose_band(mx.ctypes.data, mn.ctypes.data, mx.size,
+                                     float(max_flag_fraction), float(a_share), float(max_width),
+                                     float(pad), ctypes.byref(phi), ctypes.byref(a),
+                                     ctypes.byref(b), ctypes.byref(flagged))
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return phi.value, a.value, b.value, flagged.value
 
 
 def default_scale(head_dim: int = 128) -> float:

@@ -24,8 +24,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fd_attn_decode", "fd_attn_prefill", "fd_attn_status_string",
-                     "fd_attn_workspace_size"]
+    assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_prefill",
+                     "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size"]
     lib = ctypes.CDLL(fd.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -152,3 +152,26 @@ def test_prefill_bad_pointers_alignment_band():
     assert _pcall(d) == -2
     assert fd._load().fd_attn_prefill(None, FAKE, FAKE, FAKE, FAKE, 4.0, 20.0, 6.0, FAKE, FAKE,
                                       None) == -1
+
+
+def _scall(desc, q=FAKE, k=FAKE, lens=FAKE, bt=None, lo=-16.0, hi=16.0, nbins=64, mx=FAKE, mn=FAKE,
+           hist=FAKE):
+    return fd._load().fd_attn_score_stats(ctypes.byref(desc), q, k, lens, bt, lo, hi, nbins, mx, mn,
+                                          hist, None)
+
+
+def test_score_stats_validation():
+    d = _desc()
+    assert _scall(d, q=None) == -1
+    assert _scall(d, mx=None) == -1
+    assert _scall(_desc(page_size=16, max_blocks_per_seq=2048, num_pages=5)) == -1
+    assert _scall(_desc(kv_dtype="e4m3fn")) == -1               # no k_scale
+    assert _scall(_desc(head_dim=64)) == -2
+    assert _scall(d, nbins=8193) == -2
+    assert _scall(d, nbins=-1) == -2
+    assert _scall(d, lo=1.0, hi=1.0) == -2
+    assert _scall(d, lo=float("nan")) == -2
+    assert _scall(d, k=FAKE + 8) == -4
+    bad = _desc()
+    bad.q_dtype = 2
+    assert _scall(bad) == -3
