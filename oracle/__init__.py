@@ -5,6 +5,9 @@ this package.  The GPU library neither imports nor links it, and the two share
 no source.  The arithmetic lives in ``fd_oracle.c`` (plain C, float64, one
 OpenMP loop over rows); this module only marshals numpy arrays.
 
+The flat GEMM of the decode linear layers (``flat_gemm``) is numpy float64
+arithmetic in this module.
+
 Functions follow the FlashDecoding++ theory page: ``decode_exact`` is the plain
 max-subtracted softmax attention plus the safe-band test (section 3, first
 formula and the fallback rule); ``decode_unified`` walks the method's steps --
@@ -359,3 +362,44 @@ def min_band_width(row_max, row_min, allowed) -> float:
     mx = np.ascontiguousarray(row_max, dtype=np.float64)
     mn = np.ascontiguousarray(row_min, dtype=np.float64)
     return float(_load_calib().orc_min_band_width(_ptr(mx), _ptr(mn), mx.size, int(allowed)))
+
+
+# ---------------------------------------------------------------------------
+# flat GEMM of the decode linear layers
+# ---------------------------------------------------------------------------
+
+def flat_gemm(a, w, *, a_dtype="bf16", w_dtype="bf16"):
+    """C = A . W^T in float64 (FlashDecoding++ theory page, section 2 item 2 and
+    section 4: the linear layers of decoding multiply a flat activation matrix
+    A [M][K], M small, by the weights W [N][K]).
+
+    The operands are decoded from their storage format by the oracle's own
+    decoders (bf16: upper half of a binary32; f32 as stored); the product is
+    numpy's float64 matrix multiply.  Returns C [M][N] float64.
+    """
+    def dec(x, dt):
+        x = np.ascontiguousarray(x)
+        if dt == "f32":
+            return x.astype(np.float64)
+        if dt == "bf16":
+            return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        raise ValueError("flat GEMM operands are f32 or bf16")
+    A = dec(a, a_dtype)
+    W = dec(w, w_dtype)
+    if A.ndim != 2 or W.ndim != 2 or A.shape[1] != W.shape[1]:
+        raise ValueError("A must be [M][K] and W [N][K]")
+    return A @ W.T
+
+
+def flat_gemm_abs(a, w, *, a_dtype="bf16", w_dtype="bf16"):
+    """|A| . |W|^T in float64: the scale of the rounding error bound of an
+    fp32 accumulation of C = A . W^T."""
+    return flat_gemm(np.abs(_as_f32(a, a_dtype)), np.abs(_as_f32(w, w_dtype)), a_dtype="f32",
+                     w_dtype="f32")
+
+
+def _as_f32(x, dt):
+    x = np.ascontiguousarray(x)
+    if dt == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return x.astype(np.float32)

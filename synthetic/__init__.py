@@ -468,3 +468,32 @@ def make_prefill_config(cfg: int, *, batch: Optional[int] = None, q_len: Optiona
                         q_len=Lq, kv_lens=kv, phi=c["phi"], a=c["a"], b=c["b"],
                         max_seq_len=max(int(kv.max(initial=1)), 1), seed=seed,
                         workload=c["workload"])
+
+
+# ----------------------------------------------------------------------------
+# flat GEMM of the decode linear layers
+# ----------------------------------------------------------------------------
+
+_S_GA, _S_GW = 10, 11
+
+# Linear layers of one decoder block of a 7B-class model (hidden 4096, FFN
+# 11008; the theory page's section 4 lists them: Q/K/V generation, the O
+# projection and the two FFN layers, with K and N fixed by the weights and M
+# the tokens of the decode step).  Shapes are (N, K); W is [N][K].
+LINEAR_LAYERS_7B = [("qkv", 3 * 4096, 4096), ("o", 4096, 4096), ("gate_up", 2 * 11008, 4096),
+                    ("down", 4096, 11008)]
+
+GEMM_CONFIGS = {
+    1: dict(workload="flatgemm-small-M5-N200-K96", m=5, layers=[("w", 200, 96)]),
+    2: dict(workload="flatgemm-7b-block-M16-bf16", m=16, layers=LINEAR_LAYERS_7B),
+}
+
+
+def make_gemm(m: int, n: int, k: int, *, seed: int = SEED_BASE + 200, layer: int = 0,
+              dtype: str = "bf16"):
+    """Activations A [m][k] and weights W [n][k], N(0, 1), in storage format."""
+    a = _rng(seed, _S_GA, layer).standard_normal((m, k), dtype=np.float32)
+    w = _rng(seed, _S_GW, layer).standard_normal((n, k), dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_round(a), bf16_round(w)
+    return a, w
