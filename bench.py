@@ -22,11 +22,18 @@ With --prefill N a step is one fd_attn_prefill call on prefill workload N
 line then reports attention TFLOP/s (4 * head_dim flops per visible
 query-key pair: the score and the weighted value) against the dense bf16
 matrix-core peak.
+
+With --gemm N a step is one pass of fd_flat_gemm over the linear layers of
+GEMM workload N (2: the Q/K/V, O, gate/up and down projections of a 7B-class
+decoder block at M = 16 decode tokens, bf16 weights); the line reports weight
+GB/s (the bytes of the four weight matrices / time per step) against HBM
+peak.
 """
 import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,12 +49,30 @@ DEFAULT_CONFIG = 3
 PREFILL_METRIC = "prefill-attn TFLOP/s (causal, unified max) and % of bf16 matrix peak"
 
 
-def source_hash() -> str:
+def source_hash(entry: str = "fd_attn.hip") -> str:
+    """Hash of one entry source and every library file it includes, so a
+    counter record stays valid until the kernels it measured change."""
+    dirs = [os.path.join(ROOT, "split_kv_asynchronous_amd", "csrc"), os.path.join(ROOT, "include")]
+    seen, todo = set(), [entry]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        for d in dirs:
+            path = os.path.join(d, name)
+            if os.path.exists(path):
+                seen.add(name)
+                text = open(path).read()
+                todo += re.findall(r'#include "([^"]+)"', text)
+                break
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "split_kv_asynchronous_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    for name in sorted(seen):
+        for d in dirs:
+            path = os.path.join(d, name)
+            if os.path.exists(path):
+                with open(path, "rb") as f:
+                    h.update(name.encode() + f.read())
+                break
     return h.hexdigest()[:16]
 
 
@@ -208,9 +233,9 @@ def main_prefill(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": load_traffic(prob.workload), "kernel": "prefill kernel",
+                     "traffic": load_traffic(prob.workload, "fd_prefill.hip"), "kernel": "prefill kernel",
                      "flops_per_launch": flops},
-        "source_hash": source_hash(),
+        "source_hash": source_hash("fd_prefill.hip"),
     }
     res["cpu_baseline"] = None if args.no_cpu_baseline else prefill_cpu_baseline(prob)
     print(json.dumps(res), flush=True)
@@ -277,6 +302,8 @@ def main_stats(args):
     lens = np.clip(prob.seq_lens, 0, prob.max_seq_len).astype(np.int64)
     kbytes = int(lens.sum()) * prob.num_kv_heads * prob.head_dim * elt
     value = kbytes / per_call / 1e9
+    if args.copy_calibration:
+        copy_calibration()
     res = {
         "metric": "score-statistics pass (phi calibration): K GB/s and % of HBM peak",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -287,16 +314,144 @@ def main_stats(args):
                    "hist_range": [-8.0, 8.0]},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic("stats:" + prob.workload),
+                     "traffic": load_traffic("stats:" + prob.workload, "fd_calib.hip"),
                      "kernel": "score-statistics kernel (whole call: init + pass)",
                      "bytes_per_launch": kbytes},
-        "source_hash": source_hash(),
+        "source_hash": source_hash("fd_calib.hip"),
     }
     res["cpu_baseline"] = None if args.no_cpu_baseline else stats_cpu_baseline(prob)
     print(json.dumps(res), flush=True)
 
 
-def load_traffic(workload: str):
+def gemm_cpu_baseline(cfg, inputs, min_seconds=10.0):
+    """The float64 flat-GEMM oracle on the host cores, layer after layer until
+    about min_seconds have passed; weight bytes per second."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    spent, nbytes, done = 0.0, 0, []
+    while spent < min_seconds:
+        for (name, n, k), (a, w) in zip(cfg["layers"], inputs):
+            t = time.perf_counter()
+            oracle.flat_gemm(a, w)
+            spent += time.perf_counter() - t
+            nbytes += w.nbytes
+            done.append(name)
+            if spent >= min_seconds:
+                break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "sample": "%d layer products (%s), %.1f s, float64 matrix multiply"
+                                        % (len(done), ",".join(done[:8]), spent)}
+
+
+def main_gemm(args):
+    import torch
+
+    import split_kv_asynchronous_amd as fd
+    import synthetic
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_device import to_device
+
+    cfg = synthetic.GEMM_CONFIGS[args.gemm]
+    m = cfg["m"]
+    inputs = [synthetic.make_gemm(m, n, k, seed=synthetic.SEED_BASE + 200 + i)
+              for i, (_, n, k) in enumerate(cfg["layers"])]
+    print("generated %s" % cfg["workload"], file=sys.stderr, flush=True)
+    # consecutive steps use different copies of the weights (as consecutive
+    # decoder blocks would), so no step finds its weights in the chip's
+    # last-level cache: > 1 GB of weights in the rotation
+    wbytes = sum(w.nbytes for _, w in inputs)
+    copies = max(1, -(-(1 << 30) // wbytes))
+    dev = [[(to_device(a, "bf16"), to_device(w, "bf16")) for a, w in inputs]]
+    for _ in range(copies - 1):
+        dev.append([(a.clone(), w.clone()) for a, w in dev[0]])
+    plans = [fd.fd_flat_gemm_plan(m, n, k) for _, n, k in cfg["layers"]]
+    outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _, n, _ in cfg["layers"]]
+    wss = [torch.empty(max(fd.fd_flat_gemm_workspace_size(m, n, k), 256), dtype=torch.uint8,
+                       device="cuda") for _, n, k in cfg["layers"]]
+    stream = torch.cuda.current_stream()
+    L = len(cfg["layers"])
+
+    def step(j, evs=None):
+        for i in range(L):
+            a, w = dev[j % copies][i]
+            fd.fd_flat_gemm(a, w, outs[i], out_dtype="bf16", workspace=wss[i],
+                            stage_events=None if evs is None else evs[i])
+
+    K, W = args.steps, args.warmup
+    for j in range(W):
+        step(j)
+    torch.cuda.synchronize()
+    # one graph per weight copy: a decode step's linear layers are replayed
+    # from a captured graph, so the host's launch cost does not gate the GPU
+    cap = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(cap):
+        for j in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(j)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for j in range(copies):
+        graphs[j].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        graphs[(W + i) % copies].replay()
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t0) / K
+    # per-kernel durations: the same K steps launched directly, each
+    # partial-sum kernel stamping start/stop events from its own dispatch
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+           for _ in range(K)]
+    for row in evs:
+        for pair in row:
+            for e in pair:
+                e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(W + i, evs[i])
+    torch.cuda.synchronize()
+    value = wbytes / per_step / 1e9
+    layers = {}
+    for li, (name, n, k) in enumerate(cfg["layers"]):
+        ms = float(np.mean([evs[i][li][0].elapsed_time(evs[i][li][1]) for i in range(K)]))
+        algo = n * k * 2 + m * k * 2 + m * n * 2      # W, A and C once; split partials are overhead
+        layers[name] = {"n": n, "k": k, "kernel_ms": round(ms, 5),
+                        "kernel_GBps": round(algo / (ms / 1e3) / 1e9, 2), "plan": plans[li],
+                        "bytes_per_launch": algo}
+    # the dominant kernel: the partial-sum kernel of the largest layer
+    big = max(layers, key=lambda x: layers[x]["n"] * layers[x]["k"])
+    achieved = layers[big]["kernel_GBps"]
+    if args.copy_calibration:
+        copy_calibration()
+    res = {
+        "metric": "flat GEMM of the decode linear layers: weight GB/s and % of HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(per_step * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg["workload"], "m": m,
+                   "layers": [[name, n, k] for name, n, k in cfg["layers"]],
+                   "weight_bytes_per_step": wbytes, "out_dtype": "bf16",
+                   "weight_copies_rotated": copies, "timing": "graph replay per step"},
+        "tflops": round(2.0 * m * sum(n * k for _, n, k in cfg["layers"]) / per_step / 1e12, 3),
+        "layers": layers,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("gemm:%s:%s" % (cfg["workload"], big), "fd_gemm.hip"),
+                     "kernel": "flat GEMM partial-sum kernel (%s layer)" % big,
+                     "bytes_per_launch": layers[big]["bytes_per_launch"]},
+        "source_hash": source_hash("fd_gemm.hip"),
+    }
+    res["cpu_baseline"] = None if args.no_cpu_baseline else gemm_cpu_baseline(cfg, inputs)
+    print(json.dumps(res), flush=True)
+
+
+def load_traffic(workload: str, entry: str = "fd_attn.hip"):
     """HBM bytes per kernel launch from committed rocprofv3 counter runs,
     if they were taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -304,7 +459,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("source_hash") != source_hash():
+    if not rec or rec.get("source_hash") != source_hash(entry):
         return None
     return rec.get("bytes_per_launch")
 
@@ -319,6 +474,8 @@ def main():
                     help="time fd_attn_score_stats (phi calibration pass) on this decode workload")
     ap.add_argument("--prefill", type=int, default=0,
                     help="time fd_attn_prefill on this prefill workload instead of decode")
+    ap.add_argument("--gemm", type=int, default=0,
+                    help="time fd_flat_gemm over the linear layers of this GEMM workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
@@ -332,6 +489,9 @@ def main():
         return
     if args.stats:
         main_stats(args)
+        return
+    if args.gemm:
+        main_gemm(args)
         return
 
     import torch

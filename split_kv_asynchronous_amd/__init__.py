@@ -14,7 +14,8 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["fd_attn_decode", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
-           "fd_attn_workspace_size",
+           "fd_attn_workspace_size", "fd_flat_gemm", "fd_flat_gemm_plan",
+           "fd_flat_gemm_workspace_size", "make_gemm_desc",
            "fd_attn_status_string", "FdAttnError", "make_desc", "make_prefill_desc",
            "library_path", "FD_F32", "FD_BF16", "FD_FP8_E4M3FN"]
 
@@ -55,6 +56,15 @@ class FdPrefillDesc(ctypes.Structure):
                 ("stage_events", ctypes.c_void_p)]
 
 
+class FdGemmDesc(ctypes.Structure):
+    """Mirror of fd_gemm_desc_t."""
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("a_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("variant", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stage_events", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -92,6 +102,15 @@ def _load():
                                             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p]
         lib.fd_attn_choose_band.restype = ctypes.c_int
+        G = ctypes.POINTER(FdGemmDesc)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.fd_flat_gemm_plan.argtypes = [G, i32p, i32p, i32p, i32p]
+        lib.fd_flat_gemm_plan.restype = ctypes.c_int
+        lib.fd_flat_gemm_workspace_size.argtypes = [G]
+        lib.fd_flat_gemm_workspace_size.restype = ctypes.c_size_t
+        lib.fd_flat_gemm.argtypes = [G, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+        lib.fd_flat_gemm.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -339,6 +358,71 @@ def fd_attn_choose_band(row_max, row_min, max_flag_fraction: float = 0.0, a_shar
     if rc != 0:
         raise FdAttnError(rc, fd_attn_status_string(rc))
     return phi.value, a.value, b.value, flagged.value
+
+
+def make_gemm_desc(*, m: int, n: int, k: int, out_dtype: str = "f32", variant: int = 0,
+                   ksplit: int = 0) -> FdGemmDesc:
+    return FdGemmDesc(m, n, k, FD_BF16, FD_BF16, _DTYPE_CODE[out_dtype], variant, ksplit,
+                      None, 0, None)
+
+
+def fd_flat_gemm_plan(m: int, n: int, k: int, *, variant: int = 0, ksplit: int = 0,
+                      out_dtype: str = "f32") -> dict:
+    """The configuration fd_flat_gemm runs for this shape (include/fd_gemm.h)."""
+    desc = make_gemm_desc(m=m, n=n, k=k, out_dtype=out_dtype, variant=variant, ksplit=ksplit)
+    v, s, per, wg = (ctypes.c_int32() for _ in range(4))
+    rc = _load().fd_flat_gemm_plan(ctypes.byref(desc), ctypes.byref(v), ctypes.byref(s),
+                                   ctypes.byref(per), ctypes.byref(wg))
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return {"variant": v.value, "ksplit": s.value, "steps_per_slice": per.value,
+            "workgroups": wg.value}
+
+
+def fd_flat_gemm_workspace_size(m: int, n: int, k: int, *, variant: int = 0, ksplit: int = 0,
+                                out_dtype: str = "f32") -> int:
+    desc = make_gemm_desc(m=m, n=n, k=k, out_dtype=out_dtype, variant=variant, ksplit=ksplit)
+    return int(_load().fd_flat_gemm_workspace_size(ctypes.byref(desc)))
+
+
+def fd_flat_gemm(a, w, out=None, *, out_dtype: str = "f32", variant: int = 0, ksplit: int = 0,
+                 workspace=None, stream=None, stage_events: Optional[Sequence] = None):
+    """C = A . W^T on device tensors (include/fd_gemm.h); returns C.
+
+    a [M][K] and w [N][K] are bf16 (torch.bfloat16 or 16-bit bit patterns);
+    C is [M][N] float32 or bfloat16.  ``workspace`` is a uint8 device tensor
+    of at least fd_flat_gemm_workspace_size() bytes (allocated here if None).
+    """
+    import torch
+    dev = a.device
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError("a must be [M][K] and w [N][K]")
+    for t in (a, w):
+        if t.device != dev or not t.is_contiguous() or _torch_code(t) != "bf16":
+            raise ValueError("a and w must be contiguous bf16 tensors on the same device")
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
+                          device=dev)
+    desc = make_gemm_desc(m=M, n=N, k=K, out_dtype=out_dtype, variant=variant, ksplit=ksplit)
+    need = int(_load().fd_flat_gemm_workspace_size(ctypes.byref(desc)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = _event_array(stage_events)
+        desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _load().fd_flat_gemm(ctypes.byref(desc), a.data_ptr(), w.data_ptr(), out.data_ptr(),
+                              stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return out
 
 
 def default_scale(head_dim: int = 128) -> float:

@@ -1,11 +1,11 @@
-"""Compiles the HIP sources under csrc/ (decode, prefill, calibration) into libfd_attn.so (gfx950 only)."""
+"""Compiles the HIP sources under csrc/ (decode, prefill, calibration, flat GEMM) into libfd_attn.so (gfx950 only)."""
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("fd_attn.hip", "fd_prefill.hip", "fd_calib.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("fd_attn.hip", "fd_prefill.hip", "fd_calib.hip", "fd_gemm.hip")]
 LIB = os.path.join(HERE, "libfd_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -18,14 +18,15 @@ def _declared_functions():
         if h.endswith(".h"):
             src = open(os.path.join(ROOT, "include", h)).read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names |= set(re.findall(r"\b(fd_attn_\w+)\s*\(", src))
+            names |= set(re.findall(r"\b(fd_(?:attn|flat_gemm)\w*)\s*\(", src))
     return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_prefill",
-                     "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size"]
+                     "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size",
+                     "fd_flat_gemm", "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size"]
     lib = ctypes.CDLL(fd.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -175,3 +176,59 @@ def test_score_stats_validation():
     bad = _desc()
     bad.q_dtype = 2
     assert _scall(bad) == -3
+
+
+def _gcall(desc, a=FAKE, w=FAKE, c=FAKE):
+    return fd._load().fd_flat_gemm(ctypes.byref(desc), a, w, c, None)
+
+
+def test_flat_gemm_plan_and_workspace():
+    # every variant and split gives slices that cover K exactly, none empty
+    for m, n, k in [(1, 16, 32), (5, 200, 96), (16, 4096, 4096), (16, 22016, 4096),
+                    (64, 4096, 11008), (100, 48, 256)]:
+        for v in range(0, 13):
+            for ks in (0, 1, 3):
+                if ks > k // 32:
+                    continue
+                p = fd.fd_flat_gemm_plan(m, n, k, variant=v, ksplit=ks)
+                steps = k // 32
+                assert 1 <= p["ksplit"] <= steps
+                assert (p["ksplit"] - 1) * p["steps_per_slice"] < steps <= p["ksplit"] * p["steps_per_slice"]
+                if v:
+                    assert p["variant"] == v
+                ws = fd.fd_flat_gemm_workspace_size(m, n, k, variant=v, ksplit=ks)
+                assert ws == (p["ksplit"] * m * n * 4 if p["ksplit"] > 1 else 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=0), -2), (dict(m=4097), -2), (dict(n=0), -2), (dict(k=48), -2), (dict(k=0), -2),
+    (dict(variant=13), -2), (dict(variant=-1), -2), (dict(ksplit=5, k=128), -2),
+])
+def test_flat_gemm_shape_errors(kw, code):
+    base = dict(m=16, n=4096, k=4096)
+    base.update(kw)
+    d = fd.make_gemm_desc(**base)
+    assert _gcall(d) == code
+    assert fd._load().fd_flat_gemm_plan(ctypes.byref(d), None, None, None, None) == code
+    assert fd._load().fd_flat_gemm_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_flat_gemm_pointer_dtype_and_workspace_errors():
+    d = fd.make_gemm_desc(m=16, n=4096, k=4096)
+    assert _gcall(d, a=None) == -1
+    assert _gcall(d, c=None) == -1
+    assert fd._load().fd_flat_gemm(None, FAKE, FAKE, FAKE, None) == -1
+    assert _gcall(d, w=FAKE + 8) == -4
+    assert _gcall(d, c=FAKE + 4) == -4
+    bad = fd.make_gemm_desc(m=16, n=4096, k=4096)
+    bad.a_dtype = 0
+    assert _gcall(bad) == -3
+    bad = fd.make_gemm_desc(m=16, n=4096, k=4096, out_dtype="e4m3fn")
+    assert _gcall(bad) == -3
+    # K split over workgroups needs a workspace: missing, unaligned, too small
+    d = fd.make_gemm_desc(m=16, n=4096, k=4096, ksplit=4)
+    assert _gcall(d) == -6
+    d.workspace, d.workspace_bytes = FAKE + 16, 1 << 30
+    assert _gcall(d) == -6
+    d.workspace, d.workspace_bytes = FAKE, 4 * 16 * 4096 * 4 - 1
+    assert _gcall(d) == -6

@@ -1,0 +1,143 @@
+"""GPU parity of the flat GEMM (fd_flat_gemm, C = A . W^T of the decode linear
+layers) against the float64 oracle.
+
+Bar: every output within the rounding bound of an fp32 sum of exact bf16
+products, 2 * gamma(K) * (|A| . |W|^T) with gamma(K) = K u / (1 - K u),
+u = 2^-24 (the factor 2 leaves room for the matrix cores' internal
+accumulation order); bf16 outputs add one bf16 rounding, 2^-8 of |C|.  Small
+shapes run every kernel variant and several K splits, with ragged M and N
+(tails of the 16-row and 16-column blocks, m-groups past 64 rows); the 7B
+block layers run at full size with the library's own pick.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_kv_asynchronous_amd as fd
+import synthetic
+from gpu_device import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _bound(a, w, k, out_dtype, ref):
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    b = 2 * gamma * oracle.flat_gemm_abs(a, w)
+    if out_dtype == "bf16":
+        b = b + 2.0 ** -8 * (np.abs(ref) + b)
+    return b + 1e-30
+
+
+def _run(a, w, out_dtype="f32", **kw):
+    A, W = to_device(a, "bf16"), to_device(w, "bf16")
+    c = fd.fd_flat_gemm(A, W, out_dtype=out_dtype, **kw)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy().astype(np.float64)
+
+
+def _check(m, n, k, out_dtype="f32", seed=300, **kw):
+    a, w = synthetic.make_gemm(m, n, k, seed=seed)
+    print("case gemm m=%d n=%d k=%d %s %s" % (m, n, k, out_dtype, kw), flush=True)
+    got = _run(a, w, out_dtype, **kw)
+    ref = oracle.flat_gemm(a, w)
+    err = np.abs(got - ref)
+    bound = _bound(a, w, k, out_dtype, ref)
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst])
+    return got
+
+
+SMALL = [(1, 16, 32), (5, 200, 96), (16, 64, 256), (17, 130, 512), (33, 48, 1024),
+         (64, 272, 320), (100, 40, 256)]
+
+
+@pytest.mark.parametrize("variant", range(1, 9))
+@pytest.mark.parametrize("m,n,k", SMALL, ids=["%dx%dx%d" % s for s in SMALL])
+def test_variants_small(variant, m, n, k):
+    for ks in (1, 3, 0):
+        if ks <= k // 32:
+            _check(m, n, k, variant=variant, ksplit=ks)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_small_config_default_plan(out_dtype):
+    cfg = synthetic.GEMM_CONFIGS[1]
+    (_, n, k), = cfg["layers"]
+    _check(cfg["m"], n, k, out_dtype)
+
+
+@pytest.mark.parametrize("layer", range(4))
+def test_7b_block_layers_full(layer):
+    cfg = synthetic.GEMM_CONFIGS[2]
+    name, n, k = cfg["layers"][layer]
+    print("layer", name, fd.fd_flat_gemm_plan(cfg["m"], n, k), flush=True)
+    _check(cfg["m"], n, k, "bf16" if layer % 2 else "f32", seed=synthetic.SEED_BASE + 200 + layer)
+
+
+@pytest.mark.parametrize("m", [1, 4, 32, 64])
+def test_7b_m_range(m):
+    # the O projection over the decode batch sizes the plan table covers
+    _check(m, 4096, 4096, seed=310 + m)
+
+
+def test_repeatable_and_workspace_reuse():
+    a, w = synthetic.make_gemm(16, 1024, 2048, seed=320)
+    A, W = to_device(a, "bf16"), to_device(w, "bf16")
+    ws = torch.empty(fd.fd_flat_gemm_workspace_size(16, 1024, 2048, ksplit=8), dtype=torch.uint8,
+                     device="cuda")
+    c1 = fd.fd_flat_gemm(A, W, ksplit=8, workspace=ws).clone()
+    c2 = fd.fd_flat_gemm(A, W, ksplit=8, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+def test_zero_weights_and_one_hot_rows():
+    # exact cases: zero weights give exact zeros; a one-hot row of W copies a column of A
+    a, _ = synthetic.make_gemm(7, 16, 128, seed=330)
+    w = np.zeros((48, 128), dtype=np.uint16)
+    got = _run(a, w, ksplit=2)
+    assert np.all(got == 0.0)
+    w[5, 17] = 0x3F80          # 1.0 in bf16
+    w[40, 127] = 0xC000        # -2.0
+    got = _run(a, w, variant=6, ksplit=1)
+    A = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(got[:, 5], A[:, 17])
+    np.testing.assert_array_equal(got[:, 40], -2.0 * A[:, 127])
+
+
+def test_graph_replays_match_eager():
+    # a captured decode step (split K: partial-sum and reduce kernels) replayed
+    # several times, with eager work and synchronisations in between, gives the
+    # eager result every time
+    shapes = [(16, 1024, 2048, 4), (3, 272, 320, 1)]
+    dev = []
+    for i, (m, n, k, ks) in enumerate(shapes):
+        a, w = synthetic.make_gemm(m, n, k, seed=340 + i)
+        A, W = to_device(a, "bf16"), to_device(w, "bf16")
+        ws = torch.empty(max(fd.fd_flat_gemm_workspace_size(m, n, k, ksplit=ks), 256),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        dev.append((A, W, ws, out, ks))
+    eager = [fd.fd_flat_gemm(A, W, ksplit=ks, workspace=ws).clone() for A, W, ws, _, ks in dev]
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for A, W, ws, out, ks in dev:
+                fd.fd_flat_gemm(A, W, out, ksplit=ks, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for _, _, ws, out, _ in dev:
+            out.fill_(float("nan"))
+            ws.fill_(0x7F)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, _, _, out, _), e in zip(dev, eager):
+            assert torch.equal(out, e), rep
+        # eager work between replays
+        fd.fd_flat_gemm(dev[0][0], dev[0][1], ksplit=2)
+        torch.cuda.synchronize()
