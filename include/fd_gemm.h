@@ -80,8 +80,11 @@ typedef struct {
  *          consecutive parts of the K slice of one column block of 16 x
  *          {4, 2, 1, 1, 1, 2, 1, 1} columns; {4, 8, 8, 16, 8, 4, 4, 8}
  *          k-steps per load batch (fewer when the rows of A need the
- *          registers). */
-#define FD_GEMM_VARIANTS 12
+ *          registers);
+ *   13, 14 weights moved by DMA into per-wavefront LDS rings of {3, 2}
+ *          stages of 4 k-steps, A staged in LDS; 4 wavefronts on 4 column
+ *          blocks of 16 columns.  K must be a multiple of 128. */
+#define FD_GEMM_VARIANTS 14
 
 /* The configuration a call with this descriptor runs (the overrides applied):
  * variant, K slices, k-steps per slice and workgroups of the partial-sum

@@ -14,17 +14,20 @@ namespace {
 
 using fd::gemm::GemmParams;
 
-// lds: A staged in LDS, 4 wavefronts on different column blocks; else wk
-// wavefronts split the workgroup's K slice of one column block and load A
-// directly.
+// kind 0: A staged in LDS, weights loaded into registers by 4 wavefronts on
+// different column blocks; kind 1: wk wavefronts split the workgroup's K
+// slice of one column block and load A directly; kind 2: weights moved by
+// DMA into per-wavefront LDS rings of nst stages of kst k-steps, A staged in
+// LDS, 4 wavefronts on different column blocks.
 struct Variant {
-    int lds, wk, nb, gu;   // staging, wavefronts along K, 16-column blocks per wavefront, k-steps per batch
+    int kind, wk, nb, gu, kst, nst;
 };
 
 constexpr Variant kVariants[FD_GEMM_VARIANTS] = {
-    {1, 1, 1, 8}, {1, 1, 2, 4}, {1, 1, 1, 16}, {1, 1, 2, 8},
-    {0, 4, 4, 4}, {0, 4, 2, 8}, {0, 4, 1, 8}, {0, 4, 1, 16},
-    {0, 8, 1, 8}, {0, 8, 2, 4}, {0, 16, 1, 4}, {0, 16, 1, 8},
+    {0, 1, 1, 8, 0, 0},  {0, 1, 2, 4, 0, 0},  {0, 1, 1, 16, 0, 0}, {0, 1, 2, 8, 0, 0},
+    {1, 4, 4, 4, 0, 0},  {1, 4, 2, 8, 0, 0},  {1, 4, 1, 8, 0, 0},  {1, 4, 1, 16, 0, 0},
+    {1, 8, 1, 8, 0, 0},  {1, 8, 2, 4, 0, 0},  {1, 16, 1, 4, 0, 0}, {1, 16, 1, 8, 0, 0},
+    {2, 1, 1, 0, 4, 3},  {2, 1, 1, 0, 4, 2},
 };
 
 constexpr size_t kLdsBudget = 64 * 1024;   // dynamic LDS without an attribute change
@@ -65,7 +68,7 @@ void rule(int m, int *variant, int *target)
 }
 
 struct Plan {
-    int variant, ksplit, per, mb, tiles, mgroups;
+    int variant, ksplit, per, mb, tiles, mgroups, ring;
 };
 
 int check(const fd_gemm_desc_t *d)
@@ -103,12 +106,19 @@ int make_plan(const fd_gemm_desc_t *d, Plan *pl)
         if (variant == 0) variant = rv;
     }
     const Variant &v = kVariants[variant - 1];
-    const int cols = (v.lds ? 4 : 1) * v.nb * 16;
+    const int cols = (v.kind == 1 ? 1 : 4) * v.nb * 16;
     const int tiles = (d->n + cols - 1) / cols;
     const int mgroups = (d->m + fd::gemm::kGemmMaxRows - 1) / fd::gemm::kGemmMaxRows;
-    // the largest slice whose rows of A fit the LDS budget
-    const int max_per = v.lds ? (int)((kLdsBudget / (16 * mb) - 16) / 64) : ksteps;
-    const int min_per = v.lds ? v.gu : v.wk * v.gu;   // at least one load batch per wavefront
+    // the largest slice whose rows of A fit the LDS budget (beside the DMA
+    // rings), in whole DMA stages
+    const size_t ring = v.kind == 2 ? (size_t)4 * v.nst * 1024 * v.kst : 0;
+    int max_per = v.kind == 1 ? ksteps : (int)(((kLdsBudget - ring) / (16 * mb) - 16) / 64);
+    if (v.kind == 2) {
+        if (ksteps % v.kst) return FD_ERR_SHAPE;          // slices of whole stages
+        max_per -= max_per % v.kst;
+        if (max_per < v.kst) return FD_ERR_SHAPE;
+    }
+    const int min_per = v.kind == 0 ? v.gu : v.kind == 1 ? v.wk * v.gu : v.nst * v.kst;
     if (ksplit == 0) {
         const int64_t base = (int64_t)tiles * mgroups;
         int want = (int)std::min<int64_t>((target + base - 1) / base, ksteps);
@@ -116,10 +126,11 @@ int make_plan(const fd_gemm_desc_t *d, Plan *pl)
         ksplit = std::max(want, 1);
     }
     int per = (ksteps + ksplit - 1) / ksplit;
+    if (v.kind == 2) per = (per + v.kst - 1) / v.kst * v.kst;
     per = std::min(per, max_per);
     ksplit = (ksteps + per - 1) / per;   // no empty slice
     if ((int64_t)tiles * ksplit >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
-    *pl = Plan{variant, ksplit, per, mb, tiles, mgroups};
+    *pl = Plan{variant, ksplit, per, mb, tiles, mgroups, (int)ring};
     return FD_OK;
 }
 
@@ -140,6 +151,15 @@ void launch_direct(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent
                           s, e0, e1, 0, gp);
 }
 
+template <int MB, int KST, int NST>
+void launch_dma(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    const size_t lds = (size_t)pl.ring + fd::gemm::gemm_lds_bytes(16 * MB, pl.per);
+    hipExtLaunchKernelGGL((fd::gemm::flat_gemm_dma_kernel<MB, KST, NST>),
+                          dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(256), lds, s,
+                          e0, e1, 0, gp);
+}
+
 template <int MB>
 void dispatch_variant(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
@@ -155,7 +175,9 @@ void dispatch_variant(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEv
     case 9: launch_direct<MB, 1, 8, 8>(gp, pl, s, e0, e1); break;
     case 10: launch_direct<MB, 2, 4, 8>(gp, pl, s, e0, e1); break;
     case 11: launch_direct<MB, 1, 4, 16>(gp, pl, s, e0, e1); break;
-    default: launch_direct<MB, 1, 8, 16>(gp, pl, s, e0, e1); break;
+    case 12: launch_direct<MB, 1, 8, 16>(gp, pl, s, e0, e1); break;
+    case 13: launch_dma<MB, 4, 3>(gp, pl, s, e0, e1); break;
+    default: launch_dma<MB, 4, 2>(gp, pl, s, e0, e1); break;
     }
 }
 

@@ -18,6 +18,7 @@
 
 #include "fd_common.h"
 #include "fd_mfma.h"
+#include "fd_ring.h"
 
 namespace fd {
 namespace gemm {
@@ -324,6 +325,178 @@ __global__ __launch_bounds__(WK * 64) void flat_gemm_direct_kernel(GemmParams p)
             for (int w = 0; w < WK - 1; ++w) v += red[w][mb][nb][lane];
             store_quad(p, slice, mg0, mrows, 16 * mb + n, col0 + 16 * nb, 4 * g4, v);
         }
+}
+
+// Eight (or four) LDS fragment reads and their wait in one assembly statement
+// (early-clobber outputs): no register a read still in flight will write is
+// ever held by the compiler.
+FD_DEV void lds_read8(const uint32_t (&a)[8], u32x4 (&o)[8])
+{
+    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\t"
+                 "ds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+                 "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+                 "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+                   "=&v"(o[6]), "=&v"(o[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                 : "memory");
+}
+
+FD_DEV void lds_read4(const uint32_t (&a)[4], u32x4 (&o)[4])
+{
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                 "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                 : "memory");
+}
+
+// Variant with the weights moved by DMA into LDS.  Each weight-load
+// instruction of the register variants touches 16 rows x 64 bytes (16 cache
+// lines, half of each); here one buffer->LDS instruction moves 1 KiB of
+// 16 / KST whole rows' pieces (KST k-steps of a row are 64 * KST contiguous
+// bytes), so the vector memory path handles half as many lines per byte.
+// Each wavefront owns a ring of NST stages of 16 weight rows x KST k-steps;
+// piece j of ring row r sits in slot (j + rot(r)) mod 4KST, so the fragment
+// reads (one piece from each of 16 rows) are free of bank conflicts.  A is
+// staged in LDS as in the first variant and shared by the 4 wavefronts (4
+// column blocks of 16).  Requires K slices that are whole stages.
+template <int MB, int KST, int NST>
+__global__ __launch_bounds__(256, 2) void flat_gemm_dma_kernel(GemmParams p)
+{
+    constexpr int PPR = 4 * KST;                           // 16-byte pieces per ring row
+    constexpr int RPI = 16 / KST;                          // ring rows per 1 KiB instruction
+    constexpr int ROWB = 64 * KST;                         // bytes per ring row
+    constexpr int STAGE = 16 * ROWB;                       // bytes per stage
+    constexpr int NF = KST * (1 + MB);                     // fragments read per stage
+    static_assert(NF % 4 == 0, "fragment reads come in fours");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int g4 = lane >> 4;
+
+    const int tile = blockIdx.x / p.ksplit;
+    const int slice = blockIdx.x - tile * p.ksplit;
+    const int mg0 = blockIdx.y * kGemmMaxRows;
+    const int mrows = min(kGemmMaxRows, p.m - mg0);
+    const int s_begin = slice * p.per;
+    const int nst = min(p.per, p.ksteps - s_begin);        // a multiple of KST
+    const int nstage = nst / KST;
+    const int kbase = 32 * s_begin;
+    const int stride = 64 * nst + 16;
+
+    uint8_t *ring = lds + wave * (NST * STAGE);
+    uint8_t *alds = lds + 4 * NST * STAGE;
+    const int col0 = (tile * 4 + wave) * 16;
+    const bool live = col0 < p.n;
+
+    // buffer resource over this wavefront's 16 weight rows (rows past N read
+    // the last row); lane l of instruction i fetches, of ring row
+    // RPI * i + l / PPR, the piece that belongs in slot l % PPR
+    const size_t rowbytes = (size_t)p.k * 2;
+    const int rowc0 = min(col0, p.n - 1);
+    const int nrows = min(16, p.n - rowc0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.w + (size_t)rowc0 * p.k), (short)0, (int)(nrows * rowbytes), 0x00020000);
+    uint32_t voff[KST];
+#pragma unroll
+    for (int i = 0; i < KST; ++i) {
+        const int r = RPI * i + lane / PPR;
+        const int piece = (lane % PPR - ring::Fmt<FD_BF16>::rot(r)) & (PPR - 1);
+        voff[i] = (uint32_t)((min(col0 + r, p.n - 1) - rowc0) * rowbytes + 16 * piece);
+    }
+    auto issue = [&](int st, int slot) {
+        uint8_t *dst = ring + slot * STAGE;
+        const int so = 2 * (kbase + 32 * KST * st);
+#pragma unroll
+        for (int i = 0; i < KST; ++i) {
+            // (the LDS pointer as a named local: written inline as a cast in
+            // the call, the host compilation pass drops the kernel's stub)
+            const uint32_t vo = voff[i];
+            ring::lds_void *d = (ring::lds_void *)(dst + 1024 * i);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, vo, so, 0, 0);
+        }
+    };
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < NST; ++k)
+            if (k < nstage) issue(k, k);
+    }
+
+    // ---- A[mg0 .. mg0 + 16MB)[kbase .. kbase + 32 nst) into LDS; rows past M are zero
+    {
+        const int cpr = 4 * nst;
+        const uint16_t *abase = p.a + (size_t)mg0 * p.k + kbase;
+        for (int i = threadIdx.x; i < 16 * MB * cpr; i += 256) {
+            const int r = i / cpr, c = i - r * cpr;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (r < mrows) v = *reinterpret_cast<const u32x4 *>(abase + (size_t)r * p.k + 8 * c);
+            *reinterpret_cast<u32x4 *>(alds + r * stride + 16 * c) = v;
+        }
+    }
+    __syncthreads();
+    if (!live) return;                                     // no barrier follows
+
+    // fragment addresses: W of k-step kk = ring row n, piece 4kk + g4;
+    // A^T of block mb, k-step j = LDS row 16mb + n, bytes 64j + 16g4
+    uint32_t wrd[KST];
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+        wrd[kk] = n * ROWB + 16 * ((4 * kk + g4 + ring::Fmt<FD_BF16>::rot(n)) & (PPR - 1));
+    const uint32_t ard = (uint32_t)(uintptr_t)alds + n * stride + 16 * g4;
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int slot = 0;
+#pragma unroll 1
+    for (int st = 0; st < nstage; ++st) {
+        // this stage's DMAs done; up to NST - 1 later stages stay in flight
+        const int ahead = min(NST - 1, nstage - 1 - st);
+        ring::wait_ring<KST, NST - 1>(ahead);
+        const uint32_t sb = (uint32_t)(uintptr_t)(ring + slot * STAGE);
+        uint32_t addr[NF];
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) {
+            addr[kk] = sb + wrd[kk];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                addr[KST + kk * MB + mb] = ard + 16 * mb * stride + 64 * (KST * st + kk);
+        }
+        u32x4 f[NF];
+#pragma unroll
+        for (int c = 0; c + 8 <= NF; c += 8) {
+            uint32_t a8[8];
+            u32x4 o8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a8[u] = addr[c + u];
+            lds_read8(a8, o8);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) f[c + u] = o8[u];
+        }
+        if constexpr (NF % 8) {
+            uint32_t a4[4];
+            u32x4 o4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a4[u] = addr[NF - 4 + u];
+            lds_read4(a4, o4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f[NF - 4 + u] = o4[u];
+        }
+        // the stage is read out: hand it back to the DMA engine, then multiply
+        if (st + NST < nstage) issue(st + NST, slot);
+        slot = slot + 1 == NST ? 0 : slot + 1;
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_bf16(f[kk], f[KST + kk * MB + mb], acc[mb]);
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) store_quad(p, slice, mg0, mrows, 16 * mb + n, col0, 4 * g4, acc[mb]);
 }
 
 // C = sum over slices of the partials, in slice order: 4 outputs per thread

@@ -53,12 +53,24 @@ SMALL = [(1, 16, 32), (5, 200, 96), (16, 64, 256), (17, 130, 512), (33, 48, 1024
          (64, 272, 320), (100, 40, 256)]
 
 
-@pytest.mark.parametrize("variant", range(1, 9))
+@pytest.mark.parametrize("variant", range(1, 15))
 @pytest.mark.parametrize("m,n,k", SMALL, ids=["%dx%dx%d" % s for s in SMALL])
 def test_variants_small(variant, m, n, k):
+    if variant in (13, 14) and (k % 128 or (variant == 13 and min(m, 64) > 48)):
+        pytest.skip("DMA variants take K in whole 128-wide stages and need LDS room for A")
     for ks in (1, 3, 0):
         if ks <= k // 32:
             _check(m, n, k, variant=variant, ksplit=ks)
+
+
+@pytest.mark.parametrize("variant", [13, 14])
+@pytest.mark.parametrize("m", [1, 16, 40])
+def test_dma_variants_7b_shapes(variant, m):
+    # full-size O projection and a 2-slice down projection through the DMA rings
+    if variant == 13 and m > 48:
+        pytest.skip("no LDS room")
+    _check(m, 4096, 4096, variant=variant, seed=350 + m)
+    _check(m, 1024, 11008, variant=variant, ksplit=2, seed=360 + m)
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
