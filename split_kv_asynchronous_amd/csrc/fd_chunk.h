@@ -180,12 +180,12 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
             lds_void *vd = (lds_void *)(vt + i * 1024);
             if constexpr (PAGED) {
                 const size_t off = page_off + (size_t)((i * RPI) % 16) * ROW + vo;
-                __builtin_amdgcn_global_load_lds(kpool + off, kd, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vpool + off, vd, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(kpool + off, kd, 16, 0, kStreamPolicy);
+                __builtin_amdgcn_global_load_lds(vpool + off, vd, 16, 0, kStreamPolicy);
             } else {
                 const int so = (int)((uint32_t)t0 * ROW);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, kStreamPolicy);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, kStreamPolicy);
             }
         }
     };

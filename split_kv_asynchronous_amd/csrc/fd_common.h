@@ -94,22 +94,28 @@ FD_DEV f32x2 fp8x2_to_f32(uint32_t w, bool high)
 }
 
 // Eight consecutive elements starting at element offset `off` -> float[8].
-template <int DT>
+// STREAM marks the loads non-temporal, for data read once per call (the K/V
+// stream) by instructions that cover whole cache lines: the caches then keep
+// what is re-read instead of the stream.  (Loads whose lanes cover only half
+// of each line, the other half following in the next instruction, lose the
+// line between the two when marked so: measured slower.)
+template <int DT, bool STREAM = false>
 FD_DEV void load8(const void *base, size_t off, float (&x)[8])
 {
+    auto ld = [](const auto *p) { return STREAM ? __builtin_nontemporal_load(p) : *p; };
     if constexpr (DT == FD_F32) {
         const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + off);
-        u32x4 a = p[0], b = p[1];
+        u32x4 a = ld(p), b = ld(p + 1);
         x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
         x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
         x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
         x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
     } else if constexpr (DT == FD_BF16) {
-        u32x4 a = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + off);
+        u32x4 a = ld(reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + off));
         x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
         x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
     } else {
-        u32x2 a = *reinterpret_cast<const u32x2 *>(static_cast<const uint8_t *>(base) + off);
+        u32x2 a = ld(reinterpret_cast<const u32x2 *>(static_cast<const uint8_t *>(base) + off));
         f32x2 c0 = fp8x2_to_f32(a.x, false), c1 = fp8x2_to_f32(a.x, true);
         f32x2 c2 = fp8x2_to_f32(a.y, false), c3 = fp8x2_to_f32(a.y, true);
         x[0] = c0.x; x[1] = c0.y; x[2] = c1.x; x[3] = c1.y;

@@ -185,13 +185,13 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
                     // a wavefront's rows of a group never straddle a page (pages hold >= 16 tokens)
                     const size_t off =
                         (((size_t)pg[u] * p.hkv + kvh) * (size_t)(pmask + 1) + (t0 & pmask)) * ROW + dma_vo[q];
-                    __builtin_amdgcn_global_load_lds(kpool + off, kd, 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(vpool + off, vd, 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(kpool + off, kd, 16, 0, kStreamPolicy);
+                    __builtin_amdgcn_global_load_lds(vpool + off, vd, 16, 0, kStreamPolicy);
                 } else {
                     const int so = (int)((uint32_t)t0 * ROW);
                     const uint32_t vo = dma_vo[q];
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, kStreamPolicy);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, kStreamPolicy);
                 }
             }
         }

@@ -43,7 +43,7 @@ constexpr TableRow kTable[] = {
     {12288, 4096, 1, 6, 7, 1},   {12288, 4096, 7, 24, 3, 4},  {12288, 4096, 25, 48, 2, 8},
     {12288, 4096, 49, 64, 5, 1},
     {4096, 4096, 1, 6, 7, 1},    {4096, 4096, 7, 24, 9, 1},   {4096, 4096, 25, 64, 5, 4},
-    {22016, 4096, 1, 2, 7, 1},   {22016, 4096, 3, 6, 7, 2},   {22016, 4096, 7, 12, 6, 1},
+    {22016, 4096, 1, 2, 14, 8},  {22016, 4096, 3, 6, 7, 2},   {22016, 4096, 7, 12, 6, 1},
     {22016, 4096, 13, 24, 1, 4}, {22016, 4096, 25, 48, 1, 8}, {22016, 4096, 49, 64, 5, 2},
     {4096, 11008, 1, 12, 8, 1},  {4096, 11008, 13, 24, 6, 4}, {4096, 11008, 25, 64, 5, 4},
 };

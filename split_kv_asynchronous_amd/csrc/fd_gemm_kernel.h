@@ -417,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void flat_gemm_dma_kernel(GemmParams p)
             // the call, the host compilation pass drops the kernel's stub)
             const uint32_t vo = voff[i];
             ring::lds_void *d = (ring::lds_void *)(dst + 1024 * i);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, vo, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, vo, so, 0, ring::kStreamPolicy);
         }
     };
     if (live) {

@@ -79,19 +79,20 @@ FD_DEV f32x4 get4(const float *ptr)
 }
 
 // Partial stores: device-coherent when the chunk kernel merges (another
-// workgroup reads them during the launch), plain otherwise (the merge launch
-// reads them after this one).
+// workgroup reads them during the launch), otherwise non-temporal (the merge
+// launch reads them after this one; with the K/V stream also non-temporal
+// this measured +3% on the 32K GQA workload).
 template <typename T>
 FD_DEV void part_store(const Params &p, T *ptr, T v)
 {
     if (p.fused) put(ptr, v);
-    else *ptr = v;
+    else __builtin_nontemporal_store(v, ptr);
 }
 
 FD_DEV void part_store4(const Params &p, float *ptr, f32x4 v)
 {
     if (p.fused) put4(ptr, v);
-    else *reinterpret_cast<f32x4 *>(ptr) = v;
+    else __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ptr));
 }
 
 // Chunks a row group's sequence is cut into; an empty sequence still has one

@@ -13,6 +13,13 @@ namespace ring {
 
 constexpr int kGroupBytes = 4096;   // one compute group of K (or V): 16 bf16 or 32 E4M3FN tokens
 
+// Cache policy of the K/V stream's DMA loads: non-temporal.  The stream is
+// read once and every DMA instruction covers whole cache lines, so the caches
+// are better left to the partial sums.  Measured on the 32K GQA decode
+// workload: 5.65 -> 6.22 TB/s for the chunk kernel, together with
+// non-temporal partial stores.
+constexpr int kStreamPolicy = 2;
+
 // Per storage format: row bytes, tokens per compute group, piece rotation.
 // A cache row is moved into LDS as 16-byte pieces; piece j of group row t
 // lands in slot (j + rot(t)) mod slots, which keeps the K fragment reads

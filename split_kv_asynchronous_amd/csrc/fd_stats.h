@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kStatsWaves * 64) void score_stats_kernel(StatsPara
         for (int u = 0; u < U; ++u) {
             const int t = base + (wave * U + u) * 4 + row;
             const int tl = t < t_end ? t : t_end - 1;    // stay inside the sequence
-            load8<KV>(p.k, kv_offset<PAGED>(p, b, kvh, tl) + 8 * sub, kx[u]);
+            load8<KV, true>(p.k, kv_offset<PAGED>(p, b, kvh, tl) + 8 * sub, kx[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

@@ -54,8 +54,8 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
             const int t = base + (wave * U + u) * 4 + row;
             const int tl = t < t_end ? t : t_end - 1;    // stay inside the sequence
             const size_t off = kv_offset<PAGED>(p, b, kvh, tl) + 8 * sub;
-            load8<KV>(p.k, off, kx[u]);
-            load8<KV>(p.v, off, vx[u]);
+            load8<KV, true>(p.k, off, kx[u]);
+            load8<KV, true>(p.v, off, vx[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
