@@ -327,32 +327,6 @@ __global__ __launch_bounds__(WK * 64) void flat_gemm_direct_kernel(GemmParams p)
         }
 }
 
-// Eight (or four) LDS fragment reads and their wait in one assembly statement
-// (early-clobber outputs): no register a read still in flight will write is
-// ever held by the compiler.
-FD_DEV void lds_read8(const uint32_t (&a)[8], u32x4 (&o)[8])
-{
-    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\t"
-                 "ds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
-                 "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
-                 "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-                   "=&v"(o[6]), "=&v"(o[7])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-                 : "memory");
-}
-
-FD_DEV void lds_read4(const uint32_t (&a)[4], u32x4 (&o)[4])
-{
-    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
-                 "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                 : "memory");
-}
-
 // Variant with the weights moved by DMA into LDS.  Each weight-load
 // instruction of the register variants touches 16 rows x 64 bytes (16 cache
 // lines, half of each); here one buffer->LDS instruction moves 1 KiB of
@@ -473,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void flat_gemm_dma_kernel(GemmParams p)
             u32x4 o8[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) a8[u] = addr[c + u];
-            lds_read8(a8, o8);
+            ring::lds_read8(a8, o8);
 #pragma unroll
             for (int u = 0; u < 8; ++u) f[c + u] = o8[u];
         }
@@ -482,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void flat_gemm_dma_kernel(GemmParams p)
             u32x4 o4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) a4[u] = addr[NF - 4 + u];
-            lds_read4(a4, o4);
+            ring::lds_read4(a4, o4);
 #pragma unroll
             for (int u = 0; u < 4; ++u) f[NF - 4 + u] = o4[u];
         }

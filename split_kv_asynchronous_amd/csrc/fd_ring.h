@@ -65,6 +65,32 @@ FD_DEV void wait_ring(int k)
     }
 }
 
+// Eight (or four) LDS fragment reads and their wait in one assembly statement
+// (early-clobber outputs): no register a read still in flight will write is
+// ever held by the compiler.
+FD_DEV void lds_read8(const uint32_t (&a)[8], u32x4 (&o)[8])
+{
+    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\t"
+                 "ds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+                 "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+                 "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+                   "=&v"(o[6]), "=&v"(o[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                 : "memory");
+}
+
+FD_DEV void lds_read4(const uint32_t (&a)[4], u32x4 (&o)[4])
+{
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                 "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                 : "memory");
+}
+
 FD_DEV f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),

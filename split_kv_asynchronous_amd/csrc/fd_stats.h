@@ -327,5 +327,163 @@ __global__ __launch_bounds__(kStatsWaves * 64) void score_stats_mfma_kernel(Stat
     }
 }
 
+// Grouped bf16 queries over a bf16 cache: K moves by DMA.  The matrix-core
+// kernel above loads each K fragment straight into registers, 16 rows x 64
+// bytes per instruction, half of every cache line it touches; here each
+// wavefront streams its 16-token groups (w, w + 4, ...) through a ring of NST
+// LDS stages with non-temporal 1 KiB buffer->LDS instructions over 4 whole
+// rows each (the decode kernel's K tile: pieces rotated so the fragment reads
+// are conflict-free), and reads the fragments back with ds_read_b128.  Scores,
+// extremes, histogram and the workgroup's exit as above.
+template <bool PAGED, int NST>
+__global__ __launch_bounds__(kStatsWaves * 64, 2) void score_stats_dma_kernel(StatsParams sp)
+{
+    constexpr int ROWB = 256;                      // bytes per K row
+    constexpr int STAGE = ring::kGroupBytes;       // 16 rows
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    __shared__ float red[kStatsWaves][2][kStatsMfmaHeads];
+    const Params &p = sp.base;
+    const int unit = blockIdx.x;
+    const int c = unit % sp.nchunk;
+    const int hb = (unit / sp.nchunk) % sp.nhb;
+    const int bk = unit / (sp.nchunk * sp.nhb);
+    const int b = bk / p.hkv, kvh = bk % p.hkv;
+    const int L = seq_len_of(p, b);
+    const int t_begin = c * kStatsChunk;
+    if (t_begin >= L) return;                     // the whole workgroup leaves together
+    const int t_end = min(t_begin + kStatsChunk, L);
+    const int h0 = kvh * p.group + hb * kStatsMfmaHeads;
+    const int nh = min(kStatsMfmaHeads, p.group - hb * kStatsMfmaHeads);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int g4 = lane >> 4;
+    const bool head_ok = n < nh;
+    uint8_t *ring = dyn + wave * (NST * STAGE);
+    uint32_t *lhist = reinterpret_cast<uint32_t *>(dyn + kStatsWaves * NST * STAGE);
+
+    if (sp.hist) {
+        for (int i = threadIdx.x; i < sp.nbins + 2; i += kStatsWaves * 64) lhist[i] = 0u;
+        __syncthreads();
+    }
+
+    const int ngroups = (t_end - t_begin + 15) / 16;
+    const int nmine = ngroups > wave ? (ngroups - wave + kStatsWaves - 1) / kStatsWaves : 0;
+    const uint8_t *kpool = static_cast<const uint8_t *>(p.k);
+    // this wavefront's i-th group into ring slot `slot`: instruction q moves
+    // rows 4q .. 4q+3, lane l fetching, of row 4q + l/16, the piece that
+    // belongs in LDS slot l%16; rows past the sequence re-read its last row
+    // (their scores are never used).  A group never straddles a page.
+    auto issue = [&](int i, int slot) {
+        const int tg = t_begin + 16 * (wave + kStatsWaves * i);
+        size_t gbase;
+        if constexpr (PAGED) {
+            const int P = 1 << p.page_shift;
+            const int page = as_const(p.block_table)[(size_t)b * p.max_blocks + (tg >> p.page_shift)];
+            gbase = (((size_t)page * p.hkv + kvh) * P + (tg & (P - 1))) * ROWB;
+        } else {
+            gbase = (((size_t)b * p.hkv + kvh) * p.max_seq_len + tg) * ROWB;
+        }
+        const int last = t_end - 1 - tg;
+        uint8_t *dst = ring + slot * STAGE;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 4 * q + (lane >> 4);
+            const int rr = r < last ? r : last;
+            const uint8_t *src = kpool + gbase + (size_t)rr * ROWB + 16 * ((lane - ring::Fmt<FD_BF16>::rot(r)) & 15);
+            ring::lds_void *d = (ring::lds_void *)(dst + 1024 * q);
+            __builtin_amdgcn_global_load_lds(src, d, 16, 0, ring::kStreamPolicy);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < NST; ++k)
+        if (k < nmine) issue(k, k);
+
+    // Q^T fragments (k index of MFMA step kk = component 8*g4 + 32*kk + j),
+    // loaded after the prologue in one statement with their wait; heads past
+    // the block read a valid row and are zeroed
+    u32x4 qf[4];
+    {
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) +
+                               ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim + 8 * g4;
+        asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                     "global_load_dwordx4 %1, %4, off offset:64\n\t"
+                     "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                     "global_load_dwordx4 %3, %4, off offset:192\n\t"
+                     "s_waitcnt vmcnt(0)"
+                     : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
+                     : "v"(qrow)
+                     : "memory");
+        if (!head_ok) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    const float sc = p.scale;
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * ROWB + 16 * ((g4 + 4 * kk + ring::Fmt<FD_BF16>::rot(n)) & 15);
+
+    float mx = -INFINITY, mn = INFINITY;
+    int slot = 0;
+#pragma unroll 1
+    for (int i = 0; i < nmine; ++i) {
+        // this group's DMAs done; up to NST - 1 later groups stay in flight
+        const int ahead = min(NST - 1, nmine - 1 - i);
+        ring::wait_ring<4, NST - 1>(ahead);
+        const uint32_t sb = (uint32_t)(uintptr_t)(ring + slot * STAGE);
+        uint32_t a4[4];
+        u32x4 kf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) a4[kk] = sb + k_rd[kk];
+        ring::lds_read4(a4, kf);
+        if (i + NST < nmine) issue(i + NST, slot);
+        slot = slot + 1 == NST ? 0 : slot + 1;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) s = mfma_bf16(kf[kk], qf[kk], s);
+        // lane (n, g4) holds tokens 16g + 4g4 + r of head n
+        const int tg = t_begin + 16 * (wave + kStatsWaves * i) + 4 * g4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = s[r] * sc;
+            if (head_ok && tg + r < t_end) {
+                mx = fmaxf(mx, x);
+                mn = fminf(mn, x);
+                if (sp.hist) atomicAdd(&lhist[hist_slot(sp, x)], 1u);
+            }
+        }
+    }
+
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    if (g4 == 0) {
+        red[wave][0][n] = mx;
+        red[wave][1][n] = mn;
+    }
+    __syncthreads();
+    if (threadIdx.x < nh) {
+        const int hh = threadIdx.x;
+        float M = -INFINITY, m = INFINITY;
+#pragma unroll
+        for (int w = 0; w < kStatsWaves; ++w) {
+            M = fmaxf(M, red[w][0][hh]);
+            m = fminf(m, red[w][1][hh]);
+        }
+        const size_t r = (size_t)b * p.hq + h0 + hh;
+        atomic_max_f32(sp.row_max + r, M);
+        atomic_min_f32(sp.row_min + r, m);
+    }
+    if (sp.hist) {
+        for (int i = threadIdx.x; i < sp.nbins + 2; i += kStatsWaves * 64) {
+            const uint32_t v = lhist[i];
+            if (v) atomicAdd(sp.hist + i, v);
+        }
+    }
+}
+
 }  // namespace stats
 }  // namespace fd

@@ -92,6 +92,18 @@ def test_stats_group16_and_empty_rows():
     assert gh2 is None and np.array_equal(gmx2, gmx) and np.array_equal(gmn2, gmn)
 
 
+@pytest.mark.parametrize("page_size,nbins", [(16, 200), (64, 8000)])
+def test_stats_paged_bf16(page_size, nbins):
+    # grouped bf16 queries over a paged bf16 cache, ragged lengths across
+    # chunk and page boundaries; 8000 bins take the two-stage ring
+    prob = synthetic.make_problem(batch=3, num_q_heads=16, num_kv_heads=2,
+                                  seq_lens=[2049, 17, 4133], page_size=page_size, seed=43)
+    print("case stats paged bf16 page %d nbins %d" % (page_size, nbins), flush=True)
+    dp = DeviceProblem(prob)
+    gmx, gmn, gh = _gpu_stats(dp, -6.0, 6.0, nbins)
+    _check(prob, gmx, gmn, gh, -6.0, 6.0, nbins)
+
+
 def test_stats_full_gqa32k():
     prob = synthetic.make_config(3)
     print("case stats full cfg3", flush=True)
