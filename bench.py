@@ -368,17 +368,22 @@ def main_gemm(args):
     dev = [[(to_device(a, "bf16"), to_device(w, "bf16")) for a, w in inputs]]
     for _ in range(copies - 1):
         dev.append([(a.clone(), w.clone()) for a, w in dev[0]])
-    plans = [fd.fd_flat_gemm_plan(m, n, k) for _, n, k in cfg["layers"]]
+    # weights are packed once, as a model would at load time, into the
+    # fragment-major layout (fd_flat_gemm_pack_weights); not timed
+    dev = [[(a, fd.fd_flat_gemm_pack_weights(w)) for a, w in blk] for blk in dev]
+    torch.cuda.synchronize()
+    plans = [fd.fd_flat_gemm_plan(m, n, k, w_layout="packed") for _, n, k in cfg["layers"]]
     outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _, n, _ in cfg["layers"]]
-    wss = [torch.empty(max(fd.fd_flat_gemm_workspace_size(m, n, k), 256), dtype=torch.uint8,
-                       device="cuda") for _, n, k in cfg["layers"]]
+    wss = [torch.empty(max(fd.fd_flat_gemm_workspace_size(m, n, k, w_layout="packed"), 256),
+                       dtype=torch.uint8, device="cuda") for _, n, k in cfg["layers"]]
+    ns = [n for _, n, _ in cfg["layers"]]
     stream = torch.cuda.current_stream()
     L = len(cfg["layers"])
 
     def step(j, evs=None):
         for i in range(L):
             a, w = dev[j % copies][i]
-            fd.fd_flat_gemm(a, w, outs[i], out_dtype="bf16", workspace=wss[i],
+            fd.fd_flat_gemm(a, w, outs[i], out_dtype="bf16", workspace=wss[i], n=ns[i],
                             stage_events=None if evs is None else evs[i])
 
     K, W = args.steps, args.warmup
@@ -437,7 +442,8 @@ def main_gemm(args):
         "config": {"workload": cfg["workload"], "m": m,
                    "layers": [[name, n, k] for name, n, k in cfg["layers"]],
                    "weight_bytes_per_step": wbytes, "out_dtype": "bf16",
-                   "weight_copies_rotated": copies, "timing": "graph replay per step"},
+                   "weight_copies_rotated": copies, "weight_layout": "packed at load",
+                   "timing": "graph replay per step"},
         "tflops": round(2.0 * m * sum(n * k for _, n, k in cfg["layers"]) / per_step / 1e12, 3),
         "layers": layers,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

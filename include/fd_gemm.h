@@ -51,6 +51,7 @@ extern "C" {
  * bfloat16):
  *   a   [m][k]   a_dtype (FD_BF16)
  *   w   [n][k]   w_dtype (FD_BF16)     one output column per row of W
+ *                (or its packed copy, w_layout = FD_GEMM_W_PACKED)
  *   c   [m][n]   out_dtype (FD_F32 or FD_BF16)
  * a, w and c must be 16-byte aligned.
  */
@@ -65,6 +66,9 @@ typedef struct {
      * (see fd_flat_gemm_plan) and the number of K slices (1 .. k / 32). */
     int32_t variant;
     int32_t ksplit;
+    /* Layout of w: FD_GEMM_W_ROWS ([n][k] row-major) or FD_GEMM_W_PACKED (the
+     * output of fd_flat_gemm_pack_weights; variants 5 .. 12 only). */
+    int32_t w_layout;
     void *workspace;            /* device, 256-byte aligned, >= fd_flat_gemm_workspace_size();
                                    may be NULL when that size is 0 */
     size_t workspace_bytes;
@@ -85,6 +89,24 @@ typedef struct {
  *          stages of 4 k-steps, A staged in LDS; 4 wavefronts on 4 column
  *          blocks of 16 columns.  K must be a multiple of 128. */
 #define FD_GEMM_VARIANTS 14
+
+#define FD_GEMM_W_ROWS 0
+#define FD_GEMM_W_PACKED 1
+
+/* Bytes of the packed copy of an n x k bf16 weight matrix: ceil(n / 16) * 16
+ * * k * 2 (0 for invalid sizes). */
+size_t fd_flat_gemm_packed_bytes(int32_t n, int32_t k);
+
+/* Packs w ([n][k] row-major bf16, 16-byte aligned) into w_packed (device,
+ * 16-byte aligned, fd_flat_gemm_packed_bytes long): ceil(n/16) blocks of 16
+ * rows, each as k/32 steps of 1 KiB holding the 64 lanes' 16-byte operand
+ * fragments of the 16x16x32 matrix-core instruction in lane order -- lane l
+ * of block cb, step j gets row 16cb + l % 16, elements 32j + 8(l / 16) ..
+ * +7; rows past n are zero.  Weights are fixed per layer, so this runs once,
+ * when they are loaded; every weight-load instruction of the GEMM then reads
+ * 1 KiB of consecutive bytes.  Asynchronous on `stream`; same size limits as
+ * fd_flat_gemm.  Returns FD_OK or an FD_ERR_* code. */
+int fd_flat_gemm_pack_weights(int32_t n, int32_t k, const void *w, void *w_packed, hipStream_t stream);
 
 /* The configuration a call with this descriptor runs (the overrides applied):
  * variant, K slices, k-steps per slice and workgroups of the partial-sum

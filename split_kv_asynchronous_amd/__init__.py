@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 
 __all__ = ["fd_attn_decode", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
            "fd_attn_workspace_size", "fd_flat_gemm", "fd_flat_gemm_plan",
-           "fd_flat_gemm_workspace_size", "make_gemm_desc",
+           "fd_flat_gemm_workspace_size", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
+           "make_gemm_desc",
            "fd_attn_status_string", "FdAttnError", "make_desc", "make_prefill_desc",
            "library_path", "FD_F32", "FD_BF16", "FD_FP8_E4M3FN"]
 
@@ -61,6 +62,7 @@ class FdGemmDesc(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("a_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("variant", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("w_layout", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stage_events", ctypes.c_void_p)]
 
@@ -111,6 +113,11 @@ def _load():
         lib.fd_flat_gemm.argtypes = [G, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p]
         lib.fd_flat_gemm.restype = ctypes.c_int
+        lib.fd_flat_gemm_packed_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        lib.fd_flat_gemm_packed_bytes.restype = ctypes.c_size_t
+        lib.fd_flat_gemm_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        lib.fd_flat_gemm_pack_weights.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -360,16 +367,44 @@ def fd_attn_choose_band(row_max, row_min, max_flag_fraction: float = 0.0, a_shar
     return phi.value, a.value, b.value, flagged.value
 
 
+_W_LAYOUT = {"rows": 0, "packed": 1}
+
+
 def make_gemm_desc(*, m: int, n: int, k: int, out_dtype: str = "f32", variant: int = 0,
-                   ksplit: int = 0) -> FdGemmDesc:
+                   ksplit: int = 0, w_layout: str = "rows") -> FdGemmDesc:
     return FdGemmDesc(m, n, k, FD_BF16, FD_BF16, _DTYPE_CODE[out_dtype], variant, ksplit,
-                      None, 0, None)
+                      _W_LAYOUT[w_layout], None, 0, None)
+
+
+def fd_flat_gemm_packed_bytes(n: int, k: int) -> int:
+    return int(_load().fd_flat_gemm_packed_bytes(n, k))
+
+
+def fd_flat_gemm_pack_weights(w, out=None, stream=None):
+    """Packs w ([N][K] bf16, device) into the fragment-major layout of
+    include/fd_gemm.h; returns a flat bf16 tensor of fd_flat_gemm_packed_bytes."""
+    import torch
+    if w.dim() != 2 or not w.is_contiguous() or _torch_code(w) != "bf16":
+        raise ValueError("w must be a contiguous [N][K] bf16 tensor")
+    N, K = w.shape
+    nbytes = fd_flat_gemm_packed_bytes(N, K)
+    if nbytes == 0:
+        raise FdAttnError(-2, fd_attn_status_string(-2))
+    if out is None:
+        out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    rc = _load().fd_flat_gemm_pack_weights(N, K, w.data_ptr(), out.data_ptr(), stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return out
 
 
 def fd_flat_gemm_plan(m: int, n: int, k: int, *, variant: int = 0, ksplit: int = 0,
-                      out_dtype: str = "f32") -> dict:
+                      out_dtype: str = "f32", w_layout: str = "rows") -> dict:
     """The configuration fd_flat_gemm runs for this shape (include/fd_gemm.h)."""
-    desc = make_gemm_desc(m=m, n=n, k=k, out_dtype=out_dtype, variant=variant, ksplit=ksplit)
+    desc = make_gemm_desc(m=m, n=n, k=k, out_dtype=out_dtype, variant=variant, ksplit=ksplit,
+                          w_layout=w_layout)
     v, s, per, wg = (ctypes.c_int32() for _ in range(4))
     rc = _load().fd_flat_gemm_plan(ctypes.byref(desc), ctypes.byref(v), ctypes.byref(s),
                                    ctypes.byref(per), ctypes.byref(wg))
@@ -380,32 +415,45 @@ def fd_flat_gemm_plan(m: int, n: int, k: int, *, variant: int = 0, ksplit: int =
 
 
 def fd_flat_gemm_workspace_size(m: int, n: int, k: int, *, variant: int = 0, ksplit: int = 0,
-                                out_dtype: str = "f32") -> int:
-    desc = make_gemm_desc(m=m, n=n, k=k, out_dtype=out_dtype, variant=variant, ksplit=ksplit)
+                                out_dtype: str = "f32", w_layout: str = "rows") -> int:
+    desc = make_gemm_desc(m=m, n=n, k=k, out_dtype=out_dtype, variant=variant, ksplit=ksplit,
+                          w_layout=w_layout)
     return int(_load().fd_flat_gemm_workspace_size(ctypes.byref(desc)))
 
 
 def fd_flat_gemm(a, w, out=None, *, out_dtype: str = "f32", variant: int = 0, ksplit: int = 0,
-                 workspace=None, stream=None, stage_events: Optional[Sequence] = None):
+                 workspace=None, stream=None, stage_events: Optional[Sequence] = None,
+                 n: Optional[int] = None):
     """C = A . W^T on device tensors (include/fd_gemm.h); returns C.
 
     a [M][K] and w [N][K] are bf16 (torch.bfloat16 or 16-bit bit patterns);
-    C is [M][N] float32 or bfloat16.  ``workspace`` is a uint8 device tensor
-    of at least fd_flat_gemm_workspace_size() bytes (allocated here if None).
+    w may instead be the flat output of fd_flat_gemm_pack_weights, with the
+    row count given as ``n``.  C is [M][N] float32 or bfloat16.
+    ``workspace`` is a uint8 device tensor of at least
+    fd_flat_gemm_workspace_size() bytes (allocated here if None).
     """
     import torch
     dev = a.device
-    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
-        raise ValueError("a must be [M][K] and w [N][K]")
+    packed = n is not None
+    if a.dim() != 2:
+        raise ValueError("a must be [M][K]")
+    M, K = a.shape
+    if packed:
+        if w.dim() != 1 or w.numel() * w.element_size() < fd_flat_gemm_packed_bytes(n, K):
+            raise ValueError("packed w must be the flat output of fd_flat_gemm_pack_weights")
+        N = n
+    else:
+        if w.dim() != 2 or a.shape[1] != w.shape[1]:
+            raise ValueError("a must be [M][K] and w [N][K]")
+        N = w.shape[0]
     for t in (a, w):
         if t.device != dev or not t.is_contiguous() or _torch_code(t) != "bf16":
             raise ValueError("a and w must be contiguous bf16 tensors on the same device")
-    M, K = a.shape
-    N = w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
                           device=dev)
-    desc = make_gemm_desc(m=M, n=N, k=K, out_dtype=out_dtype, variant=variant, ksplit=ksplit)
+    desc = make_gemm_desc(m=M, n=N, k=K, out_dtype=out_dtype, variant=variant, ksplit=ksplit,
+                          w_layout="packed" if packed else "rows")
     need = int(_load().fd_flat_gemm_workspace_size(ctypes.byref(desc)))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

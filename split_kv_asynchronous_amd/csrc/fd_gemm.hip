@@ -48,6 +48,33 @@ constexpr TableRow kTable[] = {
     {4096, 11008, 1, 12, 8, 1},  {4096, 11008, 13, 24, 6, 4}, {4096, 11008, 25, 64, 5, 4},
 };
 
+// The same for packed weights (direct variants only).
+constexpr TableRow kTablePacked[] = {
+    {12288, 4096, 1, 12, 7, 1},   {12288, 4096, 13, 48, 6, 2},  {12288, 4096, 49, 64, 5, 1},
+    {4096, 4096, 1, 2, 11, 1},    {4096, 4096, 3, 12, 7, 1},    {4096, 4096, 13, 24, 9, 1},
+    {4096, 4096, 25, 48, 10, 2},  {4096, 4096, 49, 64, 5, 4},
+    {22016, 4096, 1, 2, 7, 1},    {22016, 4096, 3, 6, 7, 4},    {22016, 4096, 7, 12, 7, 1},
+    {22016, 4096, 13, 24, 6, 2},  {22016, 4096, 25, 48, 6, 1},  {22016, 4096, 49, 64, 5, 2},
+    {4096, 11008, 1, 2, 11, 1},   {4096, 11008, 3, 12, 8, 1},   {4096, 11008, 13, 24, 6, 2},
+    {4096, 11008, 25, 64, 5, 4},
+};
+
+// Packed weights, other shapes: the direct variant with 16-column blocks up
+// to 12 rows, 32-column blocks up to 48, 64-column blocks beyond.
+void rule_packed(int m, int *variant, int *target)
+{
+    if (m <= 12) {
+        *variant = 7;
+        *target = 256;
+    } else if (m <= 48) {
+        *variant = 6;
+        *target = 512;
+    } else {
+        *variant = 5;
+        *target = 256;
+    }
+}
+
 // The rule for other shapes, read off the same measurements: up to 8 rows the
 // direct variant with 16-column blocks; up to 24 rows A staged in LDS (shared
 // by 4 column blocks); beyond, the direct variant with 64-column blocks.
@@ -68,7 +95,7 @@ void rule(int m, int *variant, int *target)
 }
 
 struct Plan {
-    int variant, ksplit, per, mb, tiles, mgroups, ring;
+    int variant, ksplit, per, mb, tiles, mgroups, ring, packed;
 };
 
 int check(const fd_gemm_desc_t *d)
@@ -79,6 +106,8 @@ int check(const fd_gemm_desc_t *d)
     if (d->a_dtype != FD_BF16 || d->w_dtype != FD_BF16) return FD_ERR_DTYPE;
     if (d->out_dtype != FD_F32 && d->out_dtype != FD_BF16) return FD_ERR_DTYPE;
     if (d->variant < 0 || d->variant > FD_GEMM_VARIANTS) return FD_ERR_SHAPE;
+    if (d->w_layout != FD_GEMM_W_ROWS && d->w_layout != FD_GEMM_W_PACKED) return FD_ERR_DTYPE;
+    if (d->w_layout == FD_GEMM_W_PACKED && d->variant && (d->variant < 5 || d->variant > 12)) return FD_ERR_SHAPE;
     if (d->ksplit < 0 || d->ksplit > d->k / 32) return FD_ERR_SHAPE;
     return FD_OK;
 }
@@ -89,9 +118,13 @@ int make_plan(const fd_gemm_desc_t *d, Plan *pl)
     if (rc != FD_OK) return rc;
     const int ksteps = d->k / 32;
     const int mb = (std::min(d->m, fd::gemm::kGemmMaxRows) + 15) / 16;
+    const bool packed = d->w_layout == FD_GEMM_W_PACKED;
     int variant = d->variant, ksplit = d->ksplit;
     if (variant == 0 || ksplit == 0) {
-        for (const TableRow &r : kTable) {
+        const TableRow *tab = packed ? kTablePacked : kTable;
+        const size_t rows = packed ? sizeof(kTablePacked) / sizeof(TableRow) : sizeof(kTable) / sizeof(TableRow);
+        for (size_t i = 0; i < rows; ++i) {
+            const TableRow &r = tab[i];
             if (r.n == d->n && r.k == d->k && r.m_lo <= d->m && d->m <= r.m_hi) {
                 if (variant == 0) variant = r.variant;
                 if (ksplit == 0) ksplit = r.ksplit;
@@ -102,7 +135,8 @@ int make_plan(const fd_gemm_desc_t *d, Plan *pl)
     int target = 256;
     {
         int rv;
-        rule(d->m, &rv, &target);
+        if (packed) rule_packed(d->m, &rv, &target);
+        else rule(d->m, &rv, &target);
         if (variant == 0) variant = rv;
     }
     const Variant &v = kVariants[variant - 1];
@@ -130,7 +164,7 @@ int make_plan(const fd_gemm_desc_t *d, Plan *pl)
     per = std::min(per, max_per);
     ksplit = (ksteps + per - 1) / per;   // no empty slice
     if ((int64_t)tiles * ksplit >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
-    *pl = Plan{variant, ksplit, per, mb, tiles, mgroups, (int)ring};
+    *pl = Plan{variant, ksplit, per, mb, tiles, mgroups, (int)ring, packed ? 1 : 0};
     return FD_OK;
 }
 
@@ -143,10 +177,10 @@ void launch_main(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t
                           lds, s, e0, e1, 0, gp);
 }
 
-template <int MB, int NB, int GU, int WK>
-void launch_direct(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+template <int MB, int NB, int GU, int WK, bool WP>
+void launch_direct_wp(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    hipExtLaunchKernelGGL((fd::gemm::flat_gemm_direct_kernel<MB, NB, GU, WK>),
+    hipExtLaunchKernelGGL((fd::gemm::flat_gemm_direct_kernel<MB, NB, GU, WK, WP>),
                           dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(WK * 64), 0,
                           s, e0, e1, 0, gp);
 }
@@ -158,6 +192,13 @@ void launch_dma(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t 
     hipExtLaunchKernelGGL((fd::gemm::flat_gemm_dma_kernel<MB, KST, NST>),
                           dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(256), lds, s,
                           e0, e1, 0, gp);
+}
+
+template <int MB, int NB, int GU, int WK>
+void launch_direct(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    if (pl.packed) launch_direct_wp<MB, NB, GU, WK, true>(gp, pl, s, e0, e1);
+    else launch_direct_wp<MB, NB, GU, WK, false>(gp, pl, s, e0, e1);
 }
 
 template <int MB>
@@ -229,6 +270,7 @@ extern "C" int fd_flat_gemm(const fd_gemm_desc_t *d, const void *a, const void *
     gp.ksplit = pl.ksplit;
     gp.per = pl.per;
     gp.out_bf16 = d->out_dtype == FD_BF16;
+    gp.nblk = (d->n + 15) / 16;
 
     hipEvent_t *ev = d->stage_events;
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
@@ -247,5 +289,25 @@ extern "C" int fd_flat_gemm(const fd_gemm_desc_t *d, const void *a, const void *
         hipLaunchKernelGGL(fd::gemm::flat_gemm_reduce_kernel, dim3(grid), dim3(256), 0, stream, gp);
         if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
     }
+    return FD_OK;
+}
+
+extern "C" size_t fd_flat_gemm_packed_bytes(int32_t n, int32_t k)
+{
+    if (n < 1 || n > (1 << 20) || k < 32 || k > (1 << 20) || k % 32) return 0;
+    return (size_t)((n + 15) / 16) * 16 * k * 2;
+}
+
+extern "C" int fd_flat_gemm_pack_weights(int32_t n, int32_t k, const void *w, void *w_packed, hipStream_t stream)
+{
+    if (!w || !w_packed) return FD_ERR_NULL;
+    if (!fd_flat_gemm_packed_bytes(n, k)) return FD_ERR_SHAPE;
+    if (!fd::host::aligned16(w) || !fd::host::aligned16(w_packed)) return FD_ERR_ALIGN;
+    const size_t nfrag = fd_flat_gemm_packed_bytes(n, k) / 16;
+    const unsigned grid = (unsigned)std::min<size_t>((nfrag + 255) / 256, 8192);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fd::gemm::pack_weights_kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(w), static_cast<uint16_t *>(w_packed), (int)n, (int)k, nfrag);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
     return FD_OK;
 }

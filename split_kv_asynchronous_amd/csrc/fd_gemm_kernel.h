@@ -35,6 +35,7 @@ struct GemmParams {
     int ksplit;             // K slices
     int per;                // k-steps per slice (the last slice may be shorter)
     int out_bf16;
+    int nblk;               // 16-row blocks of a packed W (ceil(N / 16))
 };
 
 FD_DEV uint32_t gemm_pack_bf16(float a, float b)
@@ -209,7 +210,11 @@ __global__ __launch_bounds__(WAVES * 64) void flat_gemm_kernel(GemmParams p)
 // wavefront order.  With many wavefronts per workgroup a small layer has all
 // of its weights in flight at once.  Grid as above with tiles of NB * 16
 // columns.
-template <int MB, int NB, int GU0, int WK>
+//
+// WP: W in the packed (fragment-major) layout of pack_weights_kernel, so one
+// load instruction reads 1 KiB of consecutive bytes -- whole cache lines --
+// instead of 64 bytes of each of 16 rows, and is marked non-temporal.
+template <int MB, int NB, int GU0, int WK, bool WP>
 __global__ __launch_bounds__(WK * 64) void flat_gemm_direct_kernel(GemmParams p)
 {
     // load batches sized to the register file: 4 wavefronts per SIMD leave
@@ -234,10 +239,22 @@ __global__ __launch_bounds__(WK * 64) void flat_gemm_direct_kernel(GemmParams p)
     const int kbase = 32 * (s_begin + w_begin);
 
     const int col0 = tile * NB * 16;
+    // elements between a lane's weight fragments of consecutive k-steps
+    constexpr int WSTEP = WP ? 512 : 32;
     const uint16_t *wrow[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        wrow[nb] = p.w + (size_t)min(col0 + 16 * nb + n, p.n - 1) * p.k + kbase + 8 * g4;
+    for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (WP)
+            wrow[nb] = p.w + ((size_t)min(col0 / 16 + nb, p.nblk - 1) * p.ksteps + s_begin + w_begin) * 512 + 8 * lane;
+        else
+            wrow[nb] = p.w + (size_t)min(col0 + 16 * nb + n, p.n - 1) * p.k + kbase + 8 * g4;
+    }
+    auto wload = [](const uint16_t *ptr) {
+        if constexpr (WP)
+            return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr));
+        else
+            return *reinterpret_cast<const u32x4 *>(ptr);
+    };
     // rows past the m-group read its last row (their sums are not stored)
     const uint16_t *arow[MB];
 #pragma unroll
@@ -253,7 +270,7 @@ __global__ __launch_bounds__(WK * 64) void flat_gemm_direct_kernel(GemmParams p)
         for (int u = 0; u < GU; ++u) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                buf.w[u][nb] = *reinterpret_cast<const u32x4 *>(wrow[nb] + 32 * (j0 + u));
+                buf.w[u][nb] = wload(wrow[nb] + WSTEP * (j0 + u));
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 buf.a[u][mb] = *reinterpret_cast<const u32x4 *>(arow[mb] + 32 * (j0 + u));
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(WK * 64) void flat_gemm_direct_kernel(GemmParams p)
     for (int j = nbatch * GU; j < nst; ++j) {
         u32x4 wf[NB], af[MB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wf[nb] = *reinterpret_cast<const u32x4 *>(wrow[nb] + 32 * j);
+        for (int nb = 0; nb < NB; ++nb) wf[nb] = wload(wrow[nb] + WSTEP * j);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const u32x4 *>(arow[mb] + 32 * j);
         step(wf, af);
@@ -471,6 +488,27 @@ __global__ __launch_bounds__(256, 2) void flat_gemm_dma_kernel(GemmParams p)
 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) store_quad(p, slice, mg0, mrows, 16 * mb + n, col0, 4 * g4, acc[mb]);
+}
+
+// The packed (fragment-major) weight layout: W[N][K] as ceil(N/16) blocks of
+// 16 rows, each as K/32 k-steps of 1 KiB, each holding the 64 lanes'
+// 16-byte operand fragments in lane order -- lane l gets row 16cb + l % 16,
+// components 32j + 8(l / 16) .. +7, the A-operand layout of
+// v_mfma_f32_16x16x32_bf16.  Rows past N are zero.  One thread per fragment.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *w, uint16_t *wp, int n, int k,
+                                                           size_t nfrag)
+{
+    const int ksteps = k / 32;
+    for (size_t f = (size_t)blockIdx.x * 256 + threadIdx.x; f < nfrag; f += (size_t)gridDim.x * 256) {
+        const int l = (int)(f & 63);
+        const size_t rest = f >> 6;
+        const int j = (int)(rest % ksteps);
+        const size_t cb = rest / ksteps;
+        const size_t row = 16 * cb + (l & 15);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < (size_t)n) v = *reinterpret_cast<const u32x4 *>(w + row * k + 32 * j + 8 * (l >> 4));
+        *reinterpret_cast<u32x4 *>(wp + 8 * f) = v;
+    }
 }
 
 // C = sum over slices of the partials, in slice order: 4 outputs per thread

@@ -26,7 +26,8 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_prefill",
                      "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size",
-                     "fd_flat_gemm", "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size"]
+                     "fd_flat_gemm", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
+                     "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size"]
     lib = ctypes.CDLL(fd.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -238,3 +239,23 @@ def test_flat_gemm_pointer_dtype_and_workspace_errors():
     assert _gcall(d) == -6
     d.workspace, d.workspace_bytes = FAKE, 4 * 16 * 4096 * 4 - 1
     assert _gcall(d) == -6
+
+
+def test_flat_gemm_packed_weights_host_checks():
+    assert fd.fd_flat_gemm_packed_bytes(200, 96) == 208 * 96 * 2
+    assert fd.fd_flat_gemm_packed_bytes(16, 32) == 16 * 32 * 2
+    assert fd.fd_flat_gemm_packed_bytes(0, 32) == 0
+    assert fd.fd_flat_gemm_packed_bytes(16, 48) == 0
+    lib = fd._load()
+    assert lib.fd_flat_gemm_pack_weights(16, 32, None, FAKE, None) == -1
+    assert lib.fd_flat_gemm_pack_weights(16, 40, FAKE, FAKE, None) == -2
+    assert lib.fd_flat_gemm_pack_weights(16, 32, FAKE + 8, FAKE, None) == -4
+    # packed weights take the direct variants only; unknown layouts are refused
+    p = fd.fd_flat_gemm_plan(16, 12288, 4096, w_layout="packed")
+    assert 5 <= p["variant"] <= 12
+    for v in (1, 4, 13, 14):
+        d = fd.make_gemm_desc(m=16, n=4096, k=4096, variant=v, w_layout="packed")
+        assert _gcall(d) == -2
+    d = fd.make_gemm_desc(m=16, n=4096, k=4096)
+    d.w_layout = 2
+    assert _gcall(d) == -3

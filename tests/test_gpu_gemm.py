@@ -132,14 +132,23 @@ def test_graph_replays_match_eager():
                          dtype=torch.uint8, device="cuda")
         out = torch.empty((m, n), dtype=torch.float32, device="cuda")
         dev.append((A, W, ws, out, ks))
-    eager = [fd.fd_flat_gemm(A, W, ksplit=ks, workspace=ws).clone() for A, W, ws, _, ks in dev]
+    # and a packed-weight call (the decode step's layout)
+    a, w = synthetic.make_gemm(16, 4096, 1024, seed=345)
+    Wp = fd.fd_flat_gemm_pack_weights(to_device(w, "bf16"))
+    wsp = torch.empty(max(fd.fd_flat_gemm_workspace_size(16, 4096, 1024, w_layout="packed"), 256),
+                      dtype=torch.uint8, device="cuda")
+    dev.append((to_device(a, "bf16"), Wp, wsp, torch.empty((16, 4096), dtype=torch.float32,
+                                                            device="cuda"), 0))
+    kw = [{}, {}, dict(n=4096)]
+    eager = [fd.fd_flat_gemm(A, W, ksplit=ks, workspace=ws, **x).clone()
+             for (A, W, ws, _, ks), x in zip(dev, kw)]
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g, stream=cap):
-            for A, W, ws, out, ks in dev:
-                fd.fd_flat_gemm(A, W, out, ksplit=ks, workspace=ws)
+            for (A, W, ws, out, ks), x in zip(dev, kw):
+                fd.fd_flat_gemm(A, W, out, ksplit=ks, workspace=ws, **x)
     torch.cuda.synchronize()
     for rep in range(4):
         for _, _, ws, out, _ in dev:
@@ -153,3 +162,57 @@ def test_graph_replays_match_eager():
         # eager work between replays
         fd.fd_flat_gemm(dev[0][0], dev[0][1], ksplit=2)
         torch.cuda.synchronize()
+
+
+def _pack_reference(w):
+    """The packed layout of include/fd_gemm.h, restated with numpy: block cb,
+    step j, lane l holds row 16cb + l % 16, elements 32j + 8(l // 16) .. +7;
+    rows past N are zero."""
+    n, k = w.shape
+    npad = -(-n // 16) * 16
+    wp = np.zeros((npad, k), dtype=w.dtype)
+    wp[:n] = w
+    t = wp.reshape(npad // 16, 16, k // 32, 4, 8)          # [cb, r, j, g, e]
+    return t.transpose(0, 2, 3, 1, 4).reshape(-1)          # [cb, j, l = 16g + r, e]
+
+
+@pytest.mark.parametrize("n,k", [(16, 32), (200, 96), (130, 512), (4096, 256)])
+def test_pack_weights_layout(n, k):
+    _, w = synthetic.make_gemm(1, n, k, seed=370 + n)
+    W = to_device(w, "bf16")
+    got = fd.fd_flat_gemm_pack_weights(W)
+    torch.cuda.synchronize()
+    got = got.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, _pack_reference(w))
+
+
+def _check_packed(m, n, k, out_dtype="f32", seed=380, **kw):
+    a, w = synthetic.make_gemm(m, n, k, seed=seed)
+    print("case packed gemm m=%d n=%d k=%d %s %s" % (m, n, k, out_dtype, kw), flush=True)
+    A, W = to_device(a, "bf16"), to_device(w, "bf16")
+    Wp = fd.fd_flat_gemm_pack_weights(W)
+    c = fd.fd_flat_gemm(A, Wp, out_dtype=out_dtype, n=n, **kw)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy().astype(np.float64)
+    ref = oracle.flat_gemm(a, w)
+    err = np.abs(got - ref)
+    bound = _bound(a, w, k, out_dtype, ref)
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst])
+
+
+@pytest.mark.parametrize("variant", range(5, 13))
+@pytest.mark.parametrize("m,n,k", SMALL, ids=["%dx%dx%d" % s for s in SMALL])
+def test_packed_variants_small(variant, m, n, k):
+    for ks in (1, 3, 0):
+        if ks <= k // 32:
+            _check_packed(m, n, k, variant=variant, ksplit=ks, seed=390 + m)
+
+
+@pytest.mark.parametrize("layer", range(4))
+def test_packed_7b_block_layers_full(layer):
+    cfg = synthetic.GEMM_CONFIGS[2]
+    name, n, k = cfg["layers"][layer]
+    print("layer", name, fd.fd_flat_gemm_plan(cfg["m"], n, k, w_layout="packed"), flush=True)
+    _check_packed(cfg["m"], n, k, "bf16" if layer % 2 else "f32",
+                  seed=synthetic.SEED_BASE + 200 + layer)
