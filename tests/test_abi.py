@@ -259,3 +259,17 @@ def test_flat_gemm_packed_weights_host_checks():
     d = fd.make_gemm_desc(m=16, n=4096, k=4096)
     d.w_layout = 2
     assert _gcall(d) == -3
+
+
+def test_flat_gemm_table_covers_the_7b_layers():
+    # every M of the measured ranges picks a valid plan for both weight layouts,
+    # packed weights always a direct variant, and K slices that tile K
+    for n, k in [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008)]:
+        for m in range(1, 65):
+            for layout in ("rows", "packed"):
+                p = fd.fd_flat_gemm_plan(m, n, k, w_layout=layout)
+                steps = k // 32
+                assert 1 <= p["ksplit"] <= steps
+                assert (p["ksplit"] - 1) * p["steps_per_slice"] < steps <= p["ksplit"] * p["steps_per_slice"]
+                if layout == "packed":
+                    assert 5 <= p["variant"] <= 12
