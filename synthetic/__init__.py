@@ -10,7 +10,7 @@ formats (fp32, bf16 bit patterns, OCP E4M3FN codes).  It holds none of the
 attention arithmetic: no scores, exponentials, band tests or merges.  Both the
 float64 oracle and the GPU library consume what it returns.
 
-Recipe (also stated in the design doc):
+Recipe:
   * every value ~ N(0, 1), drawn as float32 from numpy's PCG64 stream keyed by
     (seed, tensor id, batch, kv head), so any subset of rows can be drawn
     alone and is identical to the same rows of a full draw;
