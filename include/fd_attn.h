@@ -89,7 +89,9 @@ typedef struct {
     int32_t num_kv_heads;       /* >= 1 */
     int32_t head_dim;           /* must be 128 */
     int32_t max_seq_len;        /* 1 .. 2^23: contiguous capacity; seq_lens are clamped to it */
-    int32_t chunk_size;         /* split size: a multiple of 32 (and of page_size), >= 32 */
+    int32_t chunk_size;         /* split size: a multiple of 32 (and of page_size), >= 32;
+                                   0 = the library's pick: 2048 for grouped bf16 queries over
+                                   a bf16 cache, 1024 otherwise (at least page_size) */
     int32_t page_size;          /* 0 = contiguous; else a power of two in [16, 256] */
     int32_t max_blocks_per_seq; /* paged: >= ceil(max_seq_len / page_size) */
     int32_t num_pages;          /* paged: number of pages in the K/V pool (>= 1) */

@@ -89,7 +89,8 @@ void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, hipSt
 extern "C" size_t fd_attn_workspace_size(const fd_attn_desc_t *desc)
 {
     if (!desc || check_shape(desc) != FD_OK) return 0;
-    const size_t maxch = ((size_t)desc->max_seq_len + desc->chunk_size - 1) / desc->chunk_size;
+    const size_t chunk = (size_t)fd::host::chunk_of(desc);
+    const size_t maxch = ((size_t)desc->max_seq_len + chunk - 1) / chunk;
     return layout_of((size_t)desc->batch * desc->num_q_heads, maxch).total;
 }
 
@@ -132,7 +133,8 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     if (!d->workspace || ((uintptr_t)d->workspace & (kAlign - 1)) || d->workspace_bytes < need)
         return FD_ERR_WORKSPACE;
 
-    const int maxch = (d->max_seq_len + d->chunk_size - 1) / d->chunk_size;
+    const int chunk = fd::host::chunk_of(d);
+    const int maxch = (d->max_seq_len + chunk - 1) / chunk;
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     const Layout L = layout_of(rows, (size_t)maxch);
     uint8_t *ws = static_cast<uint8_t *>(d->workspace);
@@ -160,7 +162,7 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     p.hkv = d->num_kv_heads;
     p.group = d->num_q_heads / d->num_kv_heads;
     p.max_seq_len = d->max_seq_len;
-    p.chunk = d->chunk_size;
+    p.chunk = chunk;
     p.maxch = maxch;
     p.page_shift = 0;
     if (d->page_size)

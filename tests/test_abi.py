@@ -273,3 +273,12 @@ def test_flat_gemm_table_covers_the_7b_layers():
                 assert (p["ksplit"] - 1) * p["steps_per_slice"] < steps <= p["ksplit"] * p["steps_per_slice"]
                 if layout == "packed":
                     assert 5 <= p["variant"] <= 12
+
+
+def test_chunk_size_zero_is_the_library_pick():
+    # grouped bf16 queries over a bf16 cache: 2048; the other kernels: 1024
+    for kw, chunk in [(dict(), 2048), (dict(kv_dtype="e4m3fn", page_size=16, max_blocks_per_seq=2048,
+                                           num_pages=5), 1024),
+                      (dict(num_kv_heads=64), 1024), (dict(q_dtype="f32"), 1024)]:
+        auto = fd.fd_attn_workspace_size(_desc(chunk_size=0, **kw))
+        assert auto > 0 and auto == fd.fd_attn_workspace_size(_desc(chunk_size=chunk, **kw)), kw

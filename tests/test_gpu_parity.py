@@ -210,9 +210,20 @@ def test_paged_equals_contiguous_bitwise():
 def test_chunk_size_and_phi_do_not_change_the_result():
     base = synthetic.make_config(3, batch=2, lens=(3000, 9000))
     ref_out, ref_flags, _ = oracle.decode_exact(**base.args())
-    for chunk in (32, 256, 2048):
+    for chunk in (32, 256, 2048, 0):          # 0: the library's pick
         for phi in (0.0, 4.0, 7.0):
             base.chunk_size = chunk
             dp = DeviceProblem(base)
             dp.run(phi=phi)
             compare(base, *dp.results(), ref=(ref_out, ref_flags))
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_library_chunk_pick(cfg):
+    # chunk_size 0 on the MHA vector kernel and the paged fp8 kernel
+    prob = synthetic.make_config(cfg, batch=3, lens=(100, 4000))
+    prob.chunk_size = 0
+    print("case chunk pick cfg%d" % cfg, flush=True)
+    dp = DeviceProblem(prob)
+    dp.run()
+    compare(prob, *dp.results())
