@@ -165,26 +165,22 @@ extern "C" int fd_attn_score_stats(const fd_attn_desc_t *d, const void *q, const
     if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
     const size_t lds = take_hist ? sizeof(uint32_t) * (size_t)(nbins + 2) : 0;
     const dim3 grid((unsigned)units), block(fd::stats::kStatsWaves * 64);
-    if (use_mfma && kv == FD_BF16) {
-        // bf16 cache: K through DMA rings, 3 stages per wavefront, or 2 when
-        // the histogram leaves too little of the 64 KiB of LDS
+    if (use_mfma) {
+        // K through DMA rings, 3 stages per wavefront, or 2 when the
+        // histogram leaves too little of the 64 KiB of LDS
         const size_t fixed = sizeof(float) * fd::stats::kStatsWaves * 2 * fd::stats::kStatsMfmaHeads;
         const bool deep = (size_t)fd::stats::kStatsWaves * 3 * fd::ring::kGroupBytes + lds + fixed <= 64 * 1024;
-        const size_t ring = (size_t)fd::stats::kStatsWaves * (deep ? 3 : 2) * fd::ring::kGroupBytes;
-        const size_t dl = ring + lds;
-        if (deep && d->page_size)
-            hipLaunchKernelGGL((fd::stats::score_stats_dma_kernel<true, 3>), grid, block, dl, stream, sp);
-        else if (deep)
-            hipLaunchKernelGGL((fd::stats::score_stats_dma_kernel<false, 3>), grid, block, dl, stream, sp);
-        else if (d->page_size)
-            hipLaunchKernelGGL((fd::stats::score_stats_dma_kernel<true, 2>), grid, block, dl, stream, sp);
-        else
-            hipLaunchKernelGGL((fd::stats::score_stats_dma_kernel<false, 2>), grid, block, dl, stream, sp);
-    } else if (use_mfma) {
-        if (d->page_size)
-            hipLaunchKernelGGL((fd::stats::score_stats_mfma_kernel<FD_FP8_E4M3FN, true>), grid, block, lds, stream, sp);
-        else
-            hipLaunchKernelGGL((fd::stats::score_stats_mfma_kernel<FD_FP8_E4M3FN, false>), grid, block, lds, stream, sp);
+        const size_t dl = (size_t)fd::stats::kStatsWaves * (deep ? 3 : 2) * fd::ring::kGroupBytes + lds;
+        const bool pg = d->page_size != 0;
+#define FD_DMA(KV, PG, NST) hipLaunchKernelGGL((fd::stats::score_stats_dma_kernel<KV, PG, NST>), grid, block, dl, stream, sp)
+        if (kv == FD_BF16) {
+            if (deep) { if (pg) FD_DMA(FD_BF16, true, 3); else FD_DMA(FD_BF16, false, 3); }
+            else { if (pg) FD_DMA(FD_BF16, true, 2); else FD_DMA(FD_BF16, false, 2); }
+        } else {
+            if (deep) { if (pg) FD_DMA(FD_FP8_E4M3FN, true, 3); else FD_DMA(FD_FP8_E4M3FN, false, 3); }
+            else { if (pg) FD_DMA(FD_FP8_E4M3FN, true, 2); else FD_DMA(FD_FP8_E4M3FN, false, 2); }
+        }
+#undef FD_DMA
     } else {
         dispatch_stats(sp, kv, qt, d->page_size != 0, (unsigned)units, lds, stream);
     }

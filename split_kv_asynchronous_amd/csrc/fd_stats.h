@@ -198,148 +198,35 @@ __global__ __launch_bounds__(kStatsWaves * 64) void score_stats_kernel(StatsPara
     }
 }
 
-// Grouped queries with bf16 queries and a bf16 or E4M3FN cache: the scores of
-// 16 tokens against up to 16 query heads come from four
-// v_mfma_f32_16x16x32_bf16 (S^T = K . Q^T, A = K rows read straight from
-// global memory, B = the heads' Q^T fragments held in registers; E4M3FN codes
-// widened to bf16 exactly), so lane (n, g4) ends up holding 4 scores of head
-// n: its extremes need no reduction across lanes of a token.  Workgroup unit
-// as above with blocks of 16 heads; wavefront w takes the 16-token groups
-// w, w + 4, ... of the chunk, GU groups per step.
+// Query heads one matrix-core workgroup serves.
 constexpr int kStatsMfmaHeads = 16;
 
-template <int KV, bool PAGED>
-__global__ __launch_bounds__(kStatsWaves * 64) void score_stats_mfma_kernel(StatsParams sp)
-{
-    constexpr bool FP8 = KV == FD_FP8_E4M3FN;
-    constexpr int GU = 4;                          // 16-token groups per wavefront per step
-    extern __shared__ uint32_t lhist[];
-    __shared__ float red[kStatsWaves][2][kStatsMfmaHeads];
-    const Params &p = sp.base;
-    const int unit = blockIdx.x;
-    const int c = unit % sp.nchunk;
-    const int hb = (unit / sp.nchunk) % sp.nhb;
-    const int bk = unit / (sp.nchunk * sp.nhb);
-    const int b = bk / p.hkv, kvh = bk % p.hkv;
-    const int L = seq_len_of(p, b);
-    const int t_begin = c * kStatsChunk;
-    if (t_begin >= L) return;                     // the whole workgroup leaves together
-    const int t_end = min(t_begin + kStatsChunk, L);
-    const int h0 = kvh * p.group + hb * kStatsMfmaHeads;
-    const int nh = min(kStatsMfmaHeads, p.group - hb * kStatsMfmaHeads);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int n = lane & 15;
-    const int g4 = lane >> 4;
-    const bool head_ok = n < nh;
-
-    if (sp.hist) {
-        for (int i = threadIdx.x; i < sp.nbins + 2; i += kStatsWaves * 64) lhist[i] = 0u;
-        __syncthreads();
-    }
-
-    // Q^T fragments: the k index of MFMA step kk is component 8*g4 + 32*kk + j;
-    // heads past the block are zero
-    u32x4 qf[4];
-    {
-        const u32x4 *qrow = reinterpret_cast<const u32x4 *>(
-            static_cast<const uint16_t *>(p.q) + ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[kk] = head_ok ? qrow[g4 + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
-    }
-    float sc = p.scale;
-    if constexpr (FP8) sc *= as_const(p.k_scale)[kvh];
-
-    float mx = -INFINITY, mn = INFINITY;
-    const int ngroups = (t_end - t_begin + 15) / 16;
-#pragma unroll 1
-    for (int g0 = wave; g0 < ngroups; g0 += kStatsWaves * GU) {
-        // K fragments of GU groups: lane (n, g4) reads row n of the group,
-        // components 8*g4 + 32*kk .. +7 (bf16: 16 bytes; E4M3FN: 8 codes)
-        u32x4 kb[GU][4];
-        u32x2 k8[GU][4];
-#pragma unroll
-        for (int u = 0; u < GU; ++u) {
-            const int g = g0 + u * kStatsWaves;
-            int t = t_begin + 16 * g + n;
-            t = t < t_end ? t : t_end - 1;             // stay inside the sequence
-            const uint8_t *row = static_cast<const uint8_t *>(p.k) + kv_offset<PAGED>(p, b, kvh, t) * (FP8 ? 1 : 2);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if constexpr (FP8)
-                    k8[u][kk] = *reinterpret_cast<const u32x2 *>(row + 8 * g4 + 32 * kk);
-                else
-                    kb[u][kk] = *reinterpret_cast<const u32x4 *>(row + 2 * (8 * g4 + 32 * kk));
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < GU; ++u) {
-            const int g = g0 + u * kStatsWaves;
-            if (g >= ngroups) break;                   // wave-uniform
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const u32x4 a = FP8 ? ring::e4m3x8_to_bf16(k8[u][kk].x, k8[u][kk].y) : kb[u][kk];
-                s = mfma_bf16(a, qf[kk], s);
-            }
-            // lane (n, g4) holds tokens 16g + 4g4 + r of head n
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t_begin + 16 * g + 4 * g4 + r;
-                const float x = s[r] * sc;
-                if (head_ok && t < t_end) {
-                    mx = fmaxf(mx, x);
-                    mn = fminf(mn, x);
-                    if (sp.hist) atomicAdd(&lhist[hist_slot(sp, x)], 1u);
-                }
-            }
-        }
-    }
-
-    // extremes of head n over the four lane groups, then over the wavefronts
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mn = fminf(mn, __shfl_xor(mn, 16));
-    mn = fminf(mn, __shfl_xor(mn, 32));
-    if (g4 == 0) {
-        red[wave][0][n] = mx;
-        red[wave][1][n] = mn;
-    }
-    __syncthreads();
-    if (threadIdx.x < nh) {
-        const int hh = threadIdx.x;
-        float M = -INFINITY, m = INFINITY;
-#pragma unroll
-        for (int w = 0; w < kStatsWaves; ++w) {
-            M = fmaxf(M, red[w][0][hh]);
-            m = fminf(m, red[w][1][hh]);
-        }
-        const size_t r = (size_t)b * p.hq + h0 + hh;
-        atomic_max_f32(sp.row_max + r, M);
-        atomic_min_f32(sp.row_min + r, m);
-    }
-    if (sp.hist) {
-        for (int i = threadIdx.x; i < sp.nbins + 2; i += kStatsWaves * 64) {
-            const uint32_t v = lhist[i];
-            if (v) atomicAdd(sp.hist + i, v);
-        }
-    }
-}
-
-// Grouped bf16 queries over a bf16 cache: K moves by DMA.  The matrix-core
-// kernel above loads each K fragment straight into registers, 16 rows x 64
-// bytes per instruction, half of every cache line it touches; here each
-// wavefront streams its 16-token groups (w, w + 4, ...) through a ring of NST
-// LDS stages with non-temporal 1 KiB buffer->LDS instructions over 4 whole
-// rows each (the decode kernel's K tile: pieces rotated so the fragment reads
-// are conflict-free), and reads the fragments back with ds_read_b128.  Scores,
-// extremes, histogram and the workgroup's exit as above.
-template <bool PAGED, int NST>
+// Grouped bf16 queries over a bf16 or E4M3FN cache: the scores of 16 tokens
+// against up to 16 query heads come from four v_mfma_f32_16x16x32_bf16
+// (S^T = K . Q^T, Q^T fragments in registers), so lane (n, g4) ends up
+// holding 4 scores of head n and its extremes need no reduction across the
+// lanes of a token.  Workgroup unit as above with blocks of 16 heads.  K
+// moves by DMA (register loads of the fragments would read 64 bytes, or 32,
+// of each of 16 rows per instruction, part of every cache line they touch;
+// measured 4.45 against 5.37 TB/s, bf16, extremes only): each wavefront
+// streams its compute groups (w, w + 4, ...: 16
+// bf16 or 32 E4M3FN tokens, 4 KiB) through a ring of NST LDS stages with
+// non-temporal 1 KiB buffer->LDS instructions over whole rows (the decode
+// kernels' K tile and piece rotation, so the fragment reads are
+// conflict-free), and reads the fragments back with ds_read_b128; E4M3FN
+// codes are widened to bf16 exactly in registers.  Scores, extremes,
+// histogram and the workgroup's exit as above.
+template <int KV, bool PAGED, int NST>
 __global__ __launch_bounds__(kStatsWaves * 64, 2) void score_stats_dma_kernel(StatsParams sp)
 {
-    constexpr int ROWB = 256;                      // bytes per K row
-    constexpr int STAGE = ring::kGroupBytes;       // 16 rows
+    using F = ring::Fmt<KV>;
+    constexpr bool FP8 = KV == FD_FP8_E4M3FN;
+    constexpr int ROWB = F::row;                   // bytes per K row
+    constexpr int GRP = F::group;                  // tokens per compute group
+    constexpr int RPI = 1024 / ROWB;               // rows per DMA instruction
+    constexpr int LPR = 64 / RPI;                  // lanes per row in a DMA instruction
+    constexpr int NT = FP8 ? 2 : 1;                // 16-token score tiles per group
+    constexpr int STAGE = ring::kGroupBytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     __shared__ float red[kStatsWaves][2][kStatsMfmaHeads];
     const Params &p = sp.base;
@@ -368,30 +255,34 @@ __global__ __launch_bounds__(kStatsWaves * 64, 2) void score_stats_dma_kernel(St
         __syncthreads();
     }
 
-    const int ngroups = (t_end - t_begin + 15) / 16;
+    const int ngroups = (t_end - t_begin + GRP - 1) / GRP;
     const int nmine = ngroups > wave ? (ngroups - wave + kStatsWaves - 1) / kStatsWaves : 0;
     const uint8_t *kpool = static_cast<const uint8_t *>(p.k);
     // this wavefront's i-th group into ring slot `slot`: instruction q moves
-    // rows 4q .. 4q+3, lane l fetching, of row 4q + l/16, the piece that
-    // belongs in LDS slot l%16; rows past the sequence re-read its last row
-    // (their scores are never used).  A group never straddles a page.
+    // rows RPI*q .. RPI*q + RPI-1, lane l fetching, of row RPI*q + l/LPR, the
+    // piece that belongs in LDS slot l%LPR; rows past the sequence re-read its
+    // last row (their scores are never used).  The rows of one instruction
+    // never straddle a page (pages hold at least 16 tokens).
     auto issue = [&](int i, int slot) {
-        const int tg = t_begin + 16 * (wave + kStatsWaves * i);
-        size_t gbase;
-        if constexpr (PAGED) {
-            const int P = 1 << p.page_shift;
-            const int page = as_const(p.block_table)[(size_t)b * p.max_blocks + (tg >> p.page_shift)];
-            gbase = (((size_t)page * p.hkv + kvh) * P + (tg & (P - 1))) * ROWB;
-        } else {
-            gbase = (((size_t)b * p.hkv + kvh) * p.max_seq_len + tg) * ROWB;
-        }
+        const int tg = t_begin + GRP * (wave + kStatsWaves * i);
         const int last = t_end - 1 - tg;
         uint8_t *dst = ring + slot * STAGE;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int r = 4 * q + (lane >> 4);
-            const int rr = r < last ? r : last;
-            const uint8_t *src = kpool + gbase + (size_t)rr * ROWB + 16 * ((lane - ring::Fmt<FD_BF16>::rot(r)) & 15);
+            const int r = RPI * q + lane / LPR;                 // group row
+            const int t = tg + (r < last ? r : last);           // its token (clamped)
+            size_t row;
+            if constexpr (PAGED) {
+                // every clamped token of the instruction lies in the page of
+                // tp: its 16-row half's first token, or the last valid token
+                const int tp = min(tg + 16 * (RPI * q / 16), t_end - 1);
+                const int P = 1 << p.page_shift;
+                const int page = as_const(p.block_table)[(size_t)b * p.max_blocks + (tp >> p.page_shift)];
+                row = ((size_t)page * p.hkv + kvh) * P + (t & (P - 1));
+            } else {
+                row = ((size_t)b * p.hkv + kvh) * p.max_seq_len + t;
+            }
+            const uint8_t *src = kpool + row * ROWB + 16 * ((lane % LPR - F::rot(r)) & (F::slots - 1));
             ring::lds_void *d = (ring::lds_void *)(dst + 1024 * q);
             __builtin_amdgcn_global_load_lds(src, d, 16, 0, ring::kStreamPolicy);
         }
@@ -400,30 +291,51 @@ __global__ __launch_bounds__(kStatsWaves * 64, 2) void score_stats_dma_kernel(St
     for (int k = 0; k < NST; ++k)
         if (k < nmine) issue(k, k);
 
-    // Q^T fragments (k index of MFMA step kk = component 8*g4 + 32*kk + j),
-    // loaded after the prologue in one statement with their wait; heads past
-    // the block read a valid row and are zeroed
+    // Q^T fragments, loaded after the prologue in one statement with their
+    // wait; heads past the block read a valid row and are zeroed.  The k
+    // index of MFMA step kk: bf16 component 8*g4 + 32*kk + j, E4M3FN
+    // 16*(g4 + 4*(kk/2)) + 8*(kk%2) + j (the K pieces' map)
     u32x4 qf[4];
     {
         const uint16_t *qrow = static_cast<const uint16_t *>(p.q) +
-                               ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim + 8 * g4;
-        asm volatile("global_load_dwordx4 %0, %4, off\n\t"
-                     "global_load_dwordx4 %1, %4, off offset:64\n\t"
-                     "global_load_dwordx4 %2, %4, off offset:128\n\t"
-                     "global_load_dwordx4 %3, %4, off offset:192\n\t"
-                     "s_waitcnt vmcnt(0)"
-                     : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
-                     : "v"(qrow)
-                     : "memory");
+                               ((size_t)b * p.hq + h0 + (head_ok ? n : 0)) * kHeadDim + (FP8 ? 16 : 8) * g4;
+        if constexpr (FP8)
+            asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                         "global_load_dwordx4 %1, %4, off offset:16\n\t"
+                         "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                         "global_load_dwordx4 %3, %4, off offset:144\n\t"
+                         "s_waitcnt vmcnt(0)"
+                         : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
+                         : "v"(qrow)
+                         : "memory");
+        else
+            asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                         "global_load_dwordx4 %1, %4, off offset:64\n\t"
+                         "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                         "global_load_dwordx4 %3, %4, off offset:192\n\t"
+                         "s_waitcnt vmcnt(0)"
+                         : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
+                         : "v"(qrow)
+                         : "memory");
         if (!head_ok) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    const float sc = p.scale;
+    float sc = p.scale;
+    if constexpr (FP8) sc *= as_const(p.k_scale)[kvh];
+    // fragment reads: bf16 step kk -> row n, piece g4 + 4kk; E4M3FN tile tau,
+    // half m -> row 16 tau + n, piece g4 + 4m (16 codes = steps 2m and 2m+1)
     uint32_t k_rd[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * ROWB + 16 * ((g4 + 4 * kk + ring::Fmt<FD_BF16>::rot(n)) & 15);
+    for (int q4 = 0; q4 < 4; ++q4) {
+        if constexpr (FP8) {
+            const int r = 16 * (q4 >> 1) + n;
+            k_rd[q4] = r * ROWB + 16 * ((g4 + 4 * (q4 & 1) + F::rot(r)) & (F::slots - 1));
+        } else {
+            k_rd[q4] = n * ROWB + 16 * ((g4 + 4 * q4 + F::rot(n)) & (F::slots - 1));
+        }
+    }
 
     float mx = -INFINITY, mn = INFINITY;
     int slot = 0;
@@ -434,24 +346,37 @@ __global__ __launch_bounds__(kStatsWaves * 64, 2) void score_stats_dma_kernel(St
         ring::wait_ring<4, NST - 1>(ahead);
         const uint32_t sb = (uint32_t)(uintptr_t)(ring + slot * STAGE);
         uint32_t a4[4];
-        u32x4 kf[4];
+        u32x4 kr[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) a4[kk] = sb + k_rd[kk];
-        ring::lds_read4(a4, kf);
+        for (int q4 = 0; q4 < 4; ++q4) a4[q4] = sb + k_rd[q4];
+        ring::lds_read4(a4, kr);
         if (i + NST < nmine) issue(i + NST, slot);
         slot = slot + 1 == NST ? 0 : slot + 1;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        const int tg = t_begin + GRP * (wave + kStatsWaves * i);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) s = mfma_bf16(kf[kk], qf[kk], s);
-        // lane (n, g4) holds tokens 16g + 4g4 + r of head n
-        const int tg = t_begin + 16 * (wave + kStatsWaves * i) + 4 * g4;
+        for (int tau = 0; tau < NT; ++tau) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float x = s[r] * sc;
-            if (head_ok && tg + r < t_end) {
-                mx = fmaxf(mx, x);
-                mn = fminf(mn, x);
-                if (sp.hist) atomicAdd(&lhist[hist_slot(sp, x)], 1u);
+            for (int kk = 0; kk < 4; ++kk) {
+                u32x4 kf;
+                if constexpr (FP8) {
+                    const u32x4 r = kr[2 * tau + (kk >> 1)];
+                    kf = (kk & 1) ? ring::e4m3x8_to_bf16(r.z, r.w) : ring::e4m3x8_to_bf16(r.x, r.y);
+                } else {
+                    kf = kr[kk];
+                }
+                s = mfma_bf16(kf, qf[kk], s);
+            }
+            // lane (n, g4) holds tokens 16 tau + 4 g4 + r of the group, head n
+            const int t0 = tg + 16 * tau + 4 * g4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = s[r] * sc;
+                if (head_ok && t0 + r < t_end) {
+                    mx = fmaxf(mx, x);
+                    mn = fminf(mn, x);
+                    if (sp.hist) atomicAdd(&lhist[hist_slot(sp, x)], 1u);
+                }
             }
         }
     }

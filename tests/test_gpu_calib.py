@@ -92,13 +92,15 @@ def test_stats_group16_and_empty_rows():
     assert gh2 is None and np.array_equal(gmx2, gmx) and np.array_equal(gmn2, gmn)
 
 
-@pytest.mark.parametrize("page_size,nbins", [(16, 200), (64, 8000)])
-def test_stats_paged_bf16(page_size, nbins):
-    # grouped bf16 queries over a paged bf16 cache, ragged lengths across
-    # chunk and page boundaries; 8000 bins take the two-stage ring
-    prob = synthetic.make_problem(batch=3, num_q_heads=16, num_kv_heads=2,
+@pytest.mark.parametrize("kv", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("page_size,nbins", [(16, 200), (64, 8000), (0, 300)])
+def test_stats_grouped_layouts(kv, page_size, nbins):
+    # grouped bf16 queries over paged and contiguous caches, ragged lengths
+    # across chunk, page and 16-token boundaries (17, 2049: a group's second
+    # half past the end); 8000 bins take the two-stage ring
+    prob = synthetic.make_problem(batch=3, num_q_heads=16, num_kv_heads=2, kv_dtype=kv,
                                   seq_lens=[2049, 17, 4133], page_size=page_size, seed=43)
-    print("case stats paged bf16 page %d nbins %d" % (page_size, nbins), flush=True)
+    print("case stats %s page %d nbins %d" % (kv, page_size, nbins), flush=True)
     dp = DeviceProblem(prob)
     gmx, gmn, gh = _gpu_stats(dp, -6.0, 6.0, nbins)
     _check(prob, gmx, gmn, gh, -6.0, 6.0, nbins)
