@@ -4,14 +4,14 @@
 #include <math.h>
 #include <string.h>
 
+#include "fd_host.h"
 #include "fd_prefill.h"
 #include "fd_prefill_kernel.h"
 
 namespace {
 
 using PrefillShape = fd::prefill::Shape<4, 2, 3>;
-
-bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+using fd::host::aligned16;
 
 }  // namespace
 
