@@ -537,6 +537,8 @@ def main():
 
     kv = prob.kv_bytes()
     value = kv / per_call / 1e9
+    rows_flagged = int(dp.results()[1].sum())
+    chunks_recomputed = dp.recomputed()
     kernel_s = float(np.mean(kernel_ms)) / 1e3
     fused = merges_in_chunk_kernel(prob)
     nbytes = kernel_bytes(prob, fused)
@@ -565,6 +567,9 @@ def main():
                    "page_size": prob.page_size, "kv_bytes_per_call": kv,
                    "phi": prob.phi, "band": [prob.phi - prob.a, prob.phi + prob.b]},
         "calls_per_s": round(1.0 / per_call, 2),
+        # fallback activity of the last call: rows flagged, (row, chunk) pairs recomputed
+        "rows_flagged": rows_flagged,
+        "chunks_recomputed": chunks_recomputed,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": round(float(np.mean(kernel_ms)), 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
