@@ -567,8 +567,8 @@ def main():
                    "page_size": prob.page_size, "kv_bytes_per_call": kv,
                    "phi": prob.phi, "band": [prob.phi - prob.a, prob.phi + prob.b]},
         "calls_per_s": round(1.0 / per_call, 2),
-        # a cache that fits the 256 MB last-level cache is re-read from it call
-        # after call: such a line is a latency figure, not an HBM one
+        # a cache under twice the 256 MB last-level cache is re-read from it, in
+        # part or whole, call after call: such a line is not an HBM figure
         "cache_resident": kv < (512 << 20),
         # fallback activity of the last call: rows flagged, (row, chunk) pairs recomputed
         "rows_flagged": rows_flagged,
