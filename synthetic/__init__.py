@@ -19,7 +19,10 @@ Recipe:
     code = nearest-even E4M3FN of x / scale (saturating at +-448);
   * ragged lengths ~ U{lo..hi} inclusive; paged caches place tokens in
     16-token pages whose physical ids are a seeded permutation of the pool,
-    assigned in (batch, token) order, unused table slots = -1.
+    assigned in (batch, token) order, unused table slots = -1;
+  * limit cases: one sequence of up to 2^23 tokens drawn in parallel blocks
+    of rows (make_long_sequence), and a large batch whose sequences share the
+    pages of a small paged problem (share_pages).
 """
 from __future__ import annotations
 
@@ -31,9 +34,9 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Problem", "CONFIGS", "make_config", "make_problem", "PrefillProblem",
-           "PREFILL_CONFIGS", "make_prefill", "make_prefill_config", "bf16_round",
-           "bf16_to_f32", "e4m3fn_encode", "e4m3fn_values"]
+__all__ = ["Problem", "CONFIGS", "make_config", "make_problem", "make_long_sequence",
+           "share_pages", "PrefillProblem", "PREFILL_CONFIGS", "make_prefill",
+           "make_prefill_config", "bf16_round", "bf16_to_f32", "e4m3fn_encode", "e4m3fn_values"]
 
 HEAD_DIM = 128
 SEED_BASE = 0x5EED0000
@@ -314,6 +317,59 @@ def apply_key_scaling(prob: Problem, plan: np.ndarray, factor: float) -> None:
         else:
             raise ValueError("key scaling is defined for f32/bf16 caches")
     prob.perturbed = np.asarray(plan, dtype=np.int32)
+
+
+_S_LONG_K, _S_LONG_V = 10, 11
+
+
+def make_long_sequence(length: int, *, num_q_heads: int, num_kv_heads: int = 1,
+                       chunk_size: int = 0, phi: float = 4.0, a: float = 20.0, b: float = 6.0,
+                       seed: int = SEED_BASE + 0x40, block: int = 1 << 20) -> Problem:
+    """One sequence of `length` tokens, contiguous bf16 cache, N(0, 1) values.
+
+    K/V rows of each KV head are drawn in blocks of `block` tokens, block i
+    from its own stream keyed by (seed, tensor id, kv head, i), so the blocks
+    are drawn (and rounded to bf16) in parallel straight into the cache."""
+    D = HEAD_DIM
+    q = bf16_round(_rng(seed, _S_Q).standard_normal((1, num_q_heads, D), dtype=np.float32))
+    k_cache = np.empty((1, num_kv_heads, length, D), dtype=np.uint16)
+    v_cache = np.empty_like(k_cache)
+    pieces = [(cache, stream, h, i) for cache, stream in ((k_cache, _S_LONG_K), (v_cache, _S_LONG_V))
+              for h in range(num_kv_heads) for i in range(-(-length // block))]
+
+    def fill(piece):
+        cache, stream, h, i = piece
+        t0, t1 = i * block, min(length, (i + 1) * block)
+        cache[0, h, t0:t1] = bf16_round(
+            _rng(seed, stream, h, i).standard_normal((t1 - t0, D), dtype=np.float32))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, pieces))
+    return Problem(q=q, k_cache=k_cache, v_cache=v_cache,
+                   seq_lens=np.array([length], dtype=np.int32), block_table=None,
+                   num_kv_heads=num_kv_heads, max_seq_len=length, page_size=0, q_dtype="bf16",
+                   kv_dtype="bf16", scale=1.0 / math.sqrt(D), phi=phi, a=a, b=b,
+                   chunk_size=chunk_size, workload="long-sequence")
+
+
+def share_pages(prob: Problem, batch: int, *, chunk_size: Optional[int] = None,
+                seed: Optional[int] = None) -> Problem:
+    """A larger batch over the page pool of a paged problem: sequence b reads
+    the pages of sequence b % prob.batch (pages shared between sequences, as a
+    common prefix is), with its own queries drawn for the new batch.  The
+    cache stays small while the batch, and with it every per-row and per-chunk
+    index of a call, grows."""
+    assert prob.page_size and prob.block_table is not None
+    seed = SEED_BASE + 0x51 if seed is None else seed
+    src = np.arange(batch) % prob.batch
+    qf = _rng(seed, _S_Q).standard_normal((batch, prob.num_q_heads, prob.head_dim),
+                                          dtype=np.float32)
+    q = qf if prob.q_dtype == "f32" else bf16_round(qf)
+    return dataclasses.replace(
+        prob, q=q, seq_lens=np.ascontiguousarray(prob.seq_lens[src]),
+        block_table=np.ascontiguousarray(prob.block_table[src]),
+        chunk_size=prob.chunk_size if chunk_size is None else chunk_size,
+        workload="shared-pages", perturbed=None)
 
 
 def make_config(cfg: int, *, batch: Optional[int] = None, length: Optional[int] = None,
