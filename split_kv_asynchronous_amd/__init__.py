@@ -13,7 +13,7 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["fd_attn_decode", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
+__all__ = ["fd_attn_decode", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
            "fd_attn_workspace_size", "fd_flat_gemm", "fd_flat_gemm_plan",
            "fd_flat_gemm_workspace_size", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
            "make_gemm_desc",
@@ -152,22 +152,49 @@ def _torch_code(t) -> str:
             torch.int16: "bf16", torch.uint16: "bf16", torch.uint8: "e4m3fn"}[t.dtype]
 
 
-def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,
+class DecodeCall:
+    """A validated fd_attn_decode call with its descriptor and pointers
+    marshalled once (prepare_decode); calling it enqueues the call again on
+    the same tensors, optionally with another band or stream.  It holds
+    references to every tensor it points at."""
+
+    def __init__(self, desc, ptrs, keep, phi, a, b, stream):
+        self.desc, self._ptrs, self._keep = desc, ptrs, keep
+        self.phi, self.a, self.b, self.stream = float(phi), float(a), float(b), stream
+        self.out, self.fallback_flags, self.workspace = keep[-3], keep[-2], keep[-1]
+        self._fn = _load().fd_attn_decode
+
+    def __call__(self, phi=None, a=None, b=None, stream=None, stage_events=None):
+        import torch
+        desc = self.desc
+        ev_arr = None
+        if stage_events is not None:
+            ev_arr = _event_array(stage_events)
+            desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+        else:
+            desc.stage_events = None
+        if stream is None:
+            stream = self.stream
+        if stream is None:
+            stream = torch.cuda.current_stream(self.out.device).cuda_stream
+        q, k, v, lens, table, out, flags = self._ptrs
+        rc = self._fn(ctypes.byref(desc), q, k, v, lens, table,
+                      self.phi if phi is None else float(phi), self.a if a is None else float(a),
+                      self.b if b is None else float(b), out, flags, stream)
+        desc.stage_events = None
+        if rc != 0:
+            raise FdAttnError(rc, fd_attn_status_string(rc))
+        return self.out, self.fallback_flags
+
+
+def prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,
                    out=None, fallback_flags=None, *, chunk_size: int, max_seq_len: int,
                    num_kv_heads: Optional[int] = None, page_size: int = 0,
                    scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
                    q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
-                   out_dtype: str = "f32", stream=None, stage_events: Optional[Sequence] = None):
-    """One decode-attention call on device tensors; returns (out, fallback_flags).
-
-    Tensors must live on the same GPU.  Layouts as in include/fd_attn.h:
-    q [B][Hq][128]; contiguous caches [B][Hkv][max_seq_len][128] or paged
-    caches [pages][Hkv][page_size][128]; seq_lens int32 [B]; block_table
-    int32 [B][max_blocks] (paged) or None.  bf16 data may be passed as
-    torch.bfloat16 or as 16-bit integer bit patterns, E4M3FN as
-    torch.float8_e4m3fn or uint8 codes.  ``workspace`` is a uint8 device
-    tensor of at least fd_attn_workspace_size() bytes (allocated here if None).
-    """
+                   out_dtype: str = "f32", stream=None) -> DecodeCall:
+    """Checks and marshals the arguments of fd_attn_decode (same meaning)
+    once; returns a DecodeCall that enqueues the call each time it is called."""
     import torch
     dev = q.device
     B, Hq, D = q.shape
@@ -207,24 +234,37 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     desc.workspace = workspace.data_ptr()
     desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    ev_arr = None
-    if stage_events is not None:
-        handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in stage_events]
-        if len(handles) != 2 or not all(handles):
-            raise ValueError("stage_events: 2 created HIP events -- chunk kernel start/stop "
-                             "(record a torch event once to create it)")
-        ev_arr = (ctypes.c_void_p * 2)(*handles)
-        desc.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = _load().fd_attn_decode(ctypes.byref(desc), q.data_ptr(), k_cache.data_ptr(),
-                                v_cache.data_ptr(), seq_lens.data_ptr(),
-                                block_table.data_ptr() if page_size else None, float(phi),
-                                float(a), float(b), out.data_ptr(), fallback_flags.data_ptr(),
-                                stream)
-    if rc != 0:
-        raise FdAttnError(rc, fd_attn_status_string(rc))
-    return out, fallback_flags
+    table = block_table if page_size else None
+    ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+            table.data_ptr() if table is not None else None, out.data_ptr(),
+            fallback_flags.data_ptr())
+    keep = (q, k_cache, v_cache, seq_lens, table, k_scale, v_scale, out, fallback_flags, workspace)
+    return DecodeCall(desc, ptrs, keep, phi, a, b, stream)
+
+
+def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,
+                   out=None, fallback_flags=None, *, chunk_size: int, max_seq_len: int,
+                   num_kv_heads: Optional[int] = None, page_size: int = 0,
+                   scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
+                   q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
+                   out_dtype: str = "f32", stream=None, stage_events: Optional[Sequence] = None):
+    """One decode-attention call on device tensors; returns (out, fallback_flags).
+
+    Tensors must live on the same GPU.  Layouts as in include/fd_attn.h:
+    q [B][Hq][128]; contiguous caches [B][Hkv][max_seq_len][128] or paged
+    caches [pages][Hkv][page_size][128]; seq_lens int32 [B]; block_table
+    int32 [B][max_blocks] (paged) or None.  bf16 data may be passed as
+    torch.bfloat16 or as 16-bit integer bit patterns, E4M3FN as
+    torch.float8_e4m3fn or uint8 codes.  ``workspace`` is a uint8 device
+    tensor of at least fd_attn_workspace_size() bytes (allocated here if None).
+    For repeated calls on the same tensors, prepare_decode marshals once.
+    """
+    call = prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi, a, b, out,
+                          fallback_flags, chunk_size=chunk_size, max_seq_len=max_seq_len,
+                          num_kv_heads=num_kv_heads, page_size=page_size, scale=scale,
+                          k_scale=k_scale, v_scale=v_scale, workspace=workspace, q_dtype=q_dtype,
+                          kv_dtype=kv_dtype, out_dtype=out_dtype, stream=stream)
+    return call(stage_events=stage_events)
 
 
 def make_prefill_desc(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int,

@@ -227,3 +227,25 @@ def test_library_chunk_pick(cfg):
     dp = DeviceProblem(prob)
     dp.run()
     compare(prob, *dp.results())
+
+
+def test_prepared_call_equals_direct_call():
+    # a DecodeCall marshalled once gives the bits of a direct call, also with
+    # the band changed per call (a band that flags every row, then the original)
+    import split_kv_asynchronous_amd as fd
+    prob = synthetic.make_config(5, batch=3, lens=(100, 4000))
+    print("case prepared call", flush=True)
+    dp = DeviceProblem(prob)
+    direct = []
+    for phi, b in ((prob.phi, prob.b), (-30.0, 0.0), (prob.phi, prob.b)):
+        o, f = fd.fd_attn_decode(dp.q, dp.k, dp.v, dp.seq_lens, dp.block_table, phi, prob.a, b,
+                                 chunk_size=prob.chunk_size, max_seq_len=prob.max_seq_len,
+                                 num_kv_heads=prob.num_kv_heads, page_size=prob.page_size,
+                                 scale=prob.scale, k_scale=dp.k_scale, v_scale=dp.v_scale)
+        direct.append((o.clone(), f.clone()))
+        dp.run(phi=phi, b=b)
+        torch.cuda.synchronize()
+        assert torch.equal(dp.out, direct[-1][0]) and torch.equal(dp.flags, direct[-1][1])
+    valid = torch.from_numpy(prob.seq_lens > 0).cuda()
+    assert torch.equal(direct[1][1].bool(), valid[:, None].expand(-1, prob.num_q_heads))
+    assert not bool(direct[0][1].any())
