@@ -127,7 +127,9 @@ struct Unit {
 };
 
 // The u-th unit of "full chunks of every sequence, then the partial last
-// chunks", sequence-major inside each part, head blocks outer, chunks inner.
+// chunks", sequence-major inside each part, chunks outer, head blocks inner:
+// consecutive workgroups write the partials of one chunk of a sequence, which
+// are contiguous over the heads.
 // An empty sequence has one empty unit in the second part, so that its rows
 // still get merged (to zeros).
 FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
@@ -155,9 +157,8 @@ FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
                 const int rem = u - before;
                 r.b = bb;
                 if (part == 0) {
-                    const int F = L / p.chunk;
-                    r.hb = rem / F;
-                    r.c = rem % F;
+                    r.hb = rem % nhb;
+                    r.c = rem / nhb;
                 } else {
                     r.hb = rem;
                     r.c = L / p.chunk;
