@@ -159,13 +159,17 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
     return flagged;
 }
 
-// Grid (maxch, Hq, B): one workgroup per (chunk, query head, sequence).
+// Grid (maxch, Hq, B): one workgroup per (chunk, query head, sequence).  The
+// (x, y) position is read in dispatch order (x fastest) as query head fastest,
+// then chunk, so consecutive workgroups write the partials of one chunk of a
+// sequence, which are contiguous over the heads.
 template <int KV, int QT, bool PAGED>
 __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
 {
     __shared__ float red[4 * 132];
     __shared__ int last_flag, merged;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const size_t xy = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int h = (int)(xy % (size_t)p.hq), c = (int)(xy / (size_t)p.hq), b = blockIdx.z;
     if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) epoch_add(p.count_word, p.epoch, 0);
     const int L = seq_len_of(p, b);
     const int t0 = c * p.chunk;
