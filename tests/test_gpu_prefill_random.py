@@ -1,0 +1,58 @@
+"""GPU parity of causal prefill on seeded random shapes, through the C ABI.
+
+Each case draws a batch, a query-head group over 1-2 KV heads, a query block
+length, per-sequence key lengths (a cached prefix before the block, a sequence
+shorter than the block, or an empty one), and either a wide band (no visible
+score leaves it) or a narrow one (rows switch to online softmax part-way).
+Bar as in the other prefill tests: every output element within the bound that
+rounding the weights to bf16 allows plus fp32 accumulation error; flags
+bit-exact on every row whose visible scores all lie at least 1e-3 from both
+band edges (a row with a score closer than that may take either path).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_device import DevicePrefill
+
+pytestmark = pytest.mark.gpu
+
+NCASES = 24
+
+
+def draw_case(i):
+    """Shape and band of case i (a pure function of i)."""
+    rng = np.random.default_rng(0x5EED4000 + i)
+    hkv = int(rng.choice([1, 2]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    batch = int(rng.integers(1, 4))
+    q_len = int(rng.integers(1, 401))
+    kv = q_len + rng.integers(-q_len // 2, 301, size=batch)
+    kv[rng.random(batch) < 0.15] = 0
+    kv = np.maximum(kv, 0).astype(np.int32)
+    if rng.random() < 0.5:
+        phi, a, b = float(rng.uniform(2.0, 5.0)), 20.0, 6.0
+    else:
+        phi, a, b = float(rng.uniform(-0.5, 1.5)), float(rng.uniform(1.5, 4.0)), float(rng.uniform(1.0, 3.0))
+    return dict(batch=batch, num_q_heads=g * hkv, num_kv_heads=hkv, q_len=q_len, kv_lens=kv,
+                phi=phi, a=a, b=b, seed=0x5EED5000 + i)
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_prefill_random_shape(i):
+    kw = draw_case(i)
+    print("case prefill %d: %s" % (i, {k: (v.tolist() if isinstance(v, np.ndarray) else v)
+                                       for k, v in kw.items()}), flush=True)
+    prob = synthetic.make_prefill(**kw)
+    ref, ref_flags, margin = oracle.prefill_exact(**prob.args())
+    dp = DevicePrefill(prob)
+    dp.run()
+    out, flags = dp.results()
+    sure = margin >= 1e-3
+    np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+    vmax = float(np.abs(synthetic.bf16_to_f32(prob.v)).max()) if prob.v.size else 0.0
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    bound = 2.0 ** -8 * vmax / (1 - 2.0 ** -9) + 1e-5 * scale
+    err = float(np.abs(out - ref).max())
+    assert err <= bound, "max|err| %.3e > bound %.3e" % (err, bound)
