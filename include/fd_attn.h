@@ -33,10 +33,16 @@
  * and outputs; calls that share a workspace must be ordered (one stream).
  *
  * Errors: a call returns FD_OK (0) or a negative FD_ERR_* code.  On any
- * host-detected error nothing is enqueued.  Device-resident data cannot be
- * checked without a synchronisation: seq_lens[b] is clamped to
- * [0, max_seq_len]; a block_table entry outside [0, num_pages) that a valid
- * token needs is undefined behaviour (it addresses memory outside the cache).
+ * host-detected error nothing is enqueued.  FD_ERR_LAUNCH comes from the
+ * status of the call's own launches; the thread's HIP last-error state is
+ * neither read nor cleared (an error the caller left there stays there).
+ * Device-resident data cannot be checked without a synchronisation:
+ * seq_lens[b] is clamped to [0, max_seq_len]; a block_table entry outside
+ * [0, num_pages) that a valid token needs is undefined behaviour (it
+ * addresses memory outside the cache).  Cache slots that no valid token uses
+ * (past seq_lens[b] in a sequence's last page or in contiguous capacity, pages
+ * no sequence uses) may hold anything, NaN included: they never reach a
+ * result.
  */
 #ifndef FD_ATTN_H
 #define FD_ATTN_H
@@ -116,7 +122,9 @@ typedef struct {
  * counters are tagged with a per-call epoch) and its contents between calls
  * are the library's.  After a call completes, its first 4 bytes hold the
  * uint32 number of (row, chunk) pairs that call recomputed with online
- * softmax, and the next 4 bytes that call's epoch. */
+ * softmax, and the next 4 bytes that call's epoch.  A call captured into a
+ * graph keeps the epoch it was captured with; every replay still counts from
+ * zero, so after each replay the first 4 bytes hold that replay's count. */
 size_t fd_attn_workspace_size(const fd_attn_desc_t *desc);
 
 /* One decode-attention call (see the top of this file).  phi is the preset

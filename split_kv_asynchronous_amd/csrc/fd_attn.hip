@@ -22,6 +22,7 @@ using fd::host::check_shape;
 
 constexpr size_t kAlign = 256;
 constexpr size_t kFusedMaxUnits = 512;   // grids up to this many units merge in the same launch
+constexpr size_t kFusedWordOffset = 64;  // header word counting a fused call's merged row groups
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -61,20 +62,17 @@ int heads_per_block(int g)
 }
 
 template <int KV, int QT, bool PAGED>
-void launch_valu(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+int launch_valu(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    hipExtLaunchKernelGGL((fd::partial_valu_kernel<KV, QT, PAGED>), grid, dim3(256), 0, s, e0, e1, 0, p);
+    return fd::host::launch(fd::partial_valu_kernel<KV, QT, PAGED>, grid, dim3(256), 0, s, e0, e1, p);
 }
 
 // Dispatch on (kv dtype, q dtype, paged) for the vector path.
-void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, hipStream_t s, hipEvent_t e0,
-                   hipEvent_t e1)
+int dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, hipStream_t s, hipEvent_t e0,
+                  hipEvent_t e1)
 {
 #define FD_CASE(KV, QT, PG)                                                   \
-    if (kv == KV && qt == QT && paged == PG) {                                \
-        launch_valu<KV, QT, PG>(p, grid, s, e0, e1);                          \
-        return;                                                               \
-    }
+    if (kv == KV && qt == QT && paged == PG) return launch_valu<KV, QT, PG>(p, grid, s, e0, e1);
     FD_CASE(FD_F32, FD_F32, false) FD_CASE(FD_F32, FD_F32, true)
     FD_CASE(FD_F32, FD_BF16, false) FD_CASE(FD_F32, FD_BF16, true)
     FD_CASE(FD_BF16, FD_F32, false) FD_CASE(FD_BF16, FD_F32, true)
@@ -82,6 +80,7 @@ void dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, hipSt
     FD_CASE(FD_FP8_E4M3FN, FD_F32, false) FD_CASE(FD_FP8_E4M3FN, FD_F32, true)
     FD_CASE(FD_FP8_E4M3FN, FD_BF16, false) FD_CASE(FD_FP8_E4M3FN, FD_BF16, true)
 #undef FD_CASE
+    return FD_ERR_DTYPE;
 }
 
 }  // namespace
@@ -151,6 +150,7 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     p.out = out;
     p.flags = fallback_flags;
     p.count_word = reinterpret_cast<unsigned long long *>(ws + L.header);
+    p.fused_word = reinterpret_cast<unsigned long long *>(ws + L.header + kFusedWordOffset);
     p.rg_count = reinterpret_cast<unsigned long long *>(ws + L.rg_count);
     p.epoch = next_epoch();
     p.o_part = reinterpret_cast<float *>(ws + L.o_part);
@@ -187,7 +187,7 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
     const size_t grid_units = (size_t)maxch * (use_mfma ? p.hq / heads_per_block(p.group) : p.hq) * p.batch;
     p.fused = grid_units <= kFusedMaxUnits;
 
-    (void)hipGetLastError();   // clear a stale error so the checks below see only ours
+    using fd::host::launch;
     if (use_mfma) {
         p.heads_per_block = heads_per_block(p.group);
         // One workgroup per unit; workgroups past the real units exit at once.
@@ -200,41 +200,36 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
         using ChunkShape = fd::chunk::DefaultShape;
         using CoopShape = fd::coop::DefaultShape;
         const dim3 blk_chunk(ChunkShape::waves * 64), blk_coop(CoopShape::waves * 64);
-        if (kv == FD_BF16) {
-            if (paged)
-                hipExtLaunchKernelGGL((fd::chunk::chunk_kernel<FD_BF16, true, ChunkShape>), flat, blk_chunk, 0,
-                                      stream, ev0, ev1, 0, p);
-            else
-                hipExtLaunchKernelGGL((fd::chunk::chunk_kernel<FD_BF16, false, ChunkShape>), flat, blk_chunk, 0,
-                                      stream, ev0, ev1, 0, p);
-        } else {
-            if (paged)
-                hipExtLaunchKernelGGL((fd::coop::chunk_kernel<FD_FP8_E4M3FN, true, CoopShape>), flat, blk_coop, 0,
-                                      stream, ev0, ev1, 0, p);
-            else
-                hipExtLaunchKernelGGL((fd::coop::chunk_kernel<FD_FP8_E4M3FN, false, CoopShape>), flat, blk_coop,
-                                      0, stream, ev0, ev1, 0, p);
-        }
+        p.ngroups = p.batch * (p.hq / p.heads_per_block);
+        if (kv == FD_BF16)
+            rc = paged ? launch(fd::chunk::chunk_kernel<FD_BF16, true, ChunkShape>, flat, blk_chunk, 0, stream,
+                                ev0, ev1, p)
+                       : launch(fd::chunk::chunk_kernel<FD_BF16, false, ChunkShape>, flat, blk_chunk, 0, stream,
+                                ev0, ev1, p);
+        else
+            rc = paged ? launch(fd::coop::chunk_kernel<FD_FP8_E4M3FN, true, CoopShape>, flat, blk_coop, 0,
+                                stream, ev0, ev1, p)
+                       : launch(fd::coop::chunk_kernel<FD_FP8_E4M3FN, false, CoopShape>, flat, blk_coop, 0,
+                                stream, ev0, ev1, p);
     } else {
         p.heads_per_block = 1;
-        dispatch_valu(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), stream, ev0, ev1);
+        p.ngroups = p.batch * p.hq;
+        rc = dispatch_valu(p, kv, qt, paged, dim3(maxch, p.hq, p.batch), stream, ev0, ev1);
     }
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    if (rc != FD_OK) return rc;
 
     // Every kernel recomputes an out-of-band chunk inside the workgroup that
     // found it.  Small grids merge inside the same launch (p.fused); larger
     // ones in a second launch, RW wavefronts per row for rows with many chunks.
     if (!p.fused) {
         if (maxch >= 64)
-            hipExtLaunchKernelGGL(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, nullptr,
-                                  nullptr, 0, p);
+            rc = launch(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, nullptr, nullptr, p);
         else if (maxch >= 16)
-            hipExtLaunchKernelGGL(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0,
-                                  stream, nullptr, nullptr, 0, p);
+            rc = launch(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, nullptr,
+                        nullptr, p);
         else
-            hipExtLaunchKernelGGL(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                                  stream, nullptr, nullptr, 0, p);
-        if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+            rc = launch(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, nullptr,
+                        nullptr, p);
     }
-    return FD_OK;
+    return rc;
 }

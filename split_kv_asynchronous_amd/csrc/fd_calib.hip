@@ -19,20 +19,17 @@ namespace {
 using fd::stats::StatsParams;
 
 template <int KV, int QT, bool PAGED>
-void launch_stats(const StatsParams &sp, unsigned grid, size_t lds, hipStream_t s)
+int launch_stats(const StatsParams &sp, unsigned grid, size_t lds, hipStream_t s)
 {
-    hipLaunchKernelGGL((fd::stats::score_stats_kernel<KV, QT, PAGED>), dim3(grid),
-                       dim3(fd::stats::kStatsWaves * 64), lds, s, sp);
+    return fd::host::launch(fd::stats::score_stats_kernel<KV, QT, PAGED>, dim3(grid),
+                            dim3(fd::stats::kStatsWaves * 64), lds, s, nullptr, nullptr, sp);
 }
 
-void dispatch_stats(const StatsParams &sp, int kv, int qt, bool paged, unsigned grid, size_t lds,
-                    hipStream_t s)
+int dispatch_stats(const StatsParams &sp, int kv, int qt, bool paged, unsigned grid, size_t lds,
+                   hipStream_t s)
 {
-#define FD_CASE(KV, QT, PG)                            \
-    if (kv == KV && qt == QT && paged == PG) {         \
-        launch_stats<KV, QT, PG>(sp, grid, lds, s);    \
-        return;                                        \
-    }
+#define FD_CASE(KV, QT, PG) \
+    if (kv == KV && qt == QT && paged == PG) return launch_stats<KV, QT, PG>(sp, grid, lds, s);
     FD_CASE(FD_F32, FD_F32, false) FD_CASE(FD_F32, FD_F32, true)
     FD_CASE(FD_F32, FD_BF16, false) FD_CASE(FD_F32, FD_BF16, true)
     FD_CASE(FD_BF16, FD_F32, false) FD_CASE(FD_BF16, FD_F32, true)
@@ -40,6 +37,7 @@ void dispatch_stats(const StatsParams &sp, int kv, int qt, bool paged, unsigned 
     FD_CASE(FD_FP8_E4M3FN, FD_F32, false) FD_CASE(FD_FP8_E4M3FN, FD_F32, true)
     FD_CASE(FD_FP8_E4M3FN, FD_BF16, false) FD_CASE(FD_FP8_E4M3FN, FD_BF16, true)
 #undef FD_CASE
+    return FD_ERR_DTYPE;
 }
 
 struct Extremes {
@@ -160,9 +158,9 @@ extern "C" int fd_attn_score_stats(const fd_attn_desc_t *d, const void *q, const
     const int64_t rows = (int64_t)d->batch * d->num_q_heads;
     const int64_t init_items = std::max<int64_t>(rows, take_hist ? nbins + 2 : 0);
     const unsigned init_grid = (unsigned)std::min<int64_t>((init_items + 255) / 256, 1024);
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(fd::stats::stats_init_kernel, dim3(init_grid), dim3(256), 0, stream, sp);
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
+    int lrc = fd::host::launch(fd::stats::stats_init_kernel, dim3(init_grid), dim3(256), 0, stream, nullptr,
+                               nullptr, sp);
+    if (lrc != FD_OK) return lrc;
     const size_t lds = take_hist ? sizeof(uint32_t) * (size_t)(nbins + 2) : 0;
     const dim3 grid((unsigned)units), block(fd::stats::kStatsWaves * 64);
     if (use_mfma) {
@@ -172,7 +170,8 @@ extern "C" int fd_attn_score_stats(const fd_attn_desc_t *d, const void *q, const
         const bool deep = (size_t)fd::stats::kStatsWaves * 3 * fd::ring::kGroupBytes + lds + fixed <= 64 * 1024;
         const size_t dl = (size_t)fd::stats::kStatsWaves * (deep ? 3 : 2) * fd::ring::kGroupBytes + lds;
         const bool pg = d->page_size != 0;
-#define FD_DMA(KV, PG, NST) hipLaunchKernelGGL((fd::stats::score_stats_dma_kernel<KV, PG, NST>), grid, block, dl, stream, sp)
+#define FD_DMA(KV, PG, NST) \
+    lrc = fd::host::launch(fd::stats::score_stats_dma_kernel<KV, PG, NST>, grid, block, dl, stream, nullptr, nullptr, sp)
         if (kv == FD_BF16) {
             if (deep) { if (pg) FD_DMA(FD_BF16, true, 3); else FD_DMA(FD_BF16, false, 3); }
             else { if (pg) FD_DMA(FD_BF16, true, 2); else FD_DMA(FD_BF16, false, 2); }
@@ -182,10 +181,9 @@ extern "C" int fd_attn_score_stats(const fd_attn_desc_t *d, const void *q, const
         }
 #undef FD_DMA
     } else {
-        dispatch_stats(sp, kv, qt, d->page_size != 0, (unsigned)units, lds, stream);
+        lrc = dispatch_stats(sp, kv, qt, d->page_size != 0, (unsigned)units, lds, stream);
     }
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    return FD_OK;
+    return lrc;
 }
 
 extern "C" int fd_attn_choose_band(const float *row_max, const float *row_min, int64_t nrows,

@@ -32,9 +32,11 @@ struct Params {
     float *m_part;        // [B][Hq][maxch]
     uint8_t *cflag;       // [B][Hq][maxch]
     unsigned long long *count_word;   // {recomputed (row, chunk) pairs, epoch} of the call
+    unsigned long long *fused_word;   // fused merge: {epoch | merged row groups << 16 | recomputed pairs}
     unsigned long long *rg_count;     // [B][Hq] epoch-tagged unit counts per row group (first head)
     uint32_t epoch;                   // this call's epoch (never 0)
     int fused;                        // the last workgroup of a row group merges it (else a merge launch)
+    int ngroups;                      // row groups of the call (sequences x head blocks)
     int batch, hq, hkv, group;   // group = hq / hkv
     int heads_per_block;         // query heads one chunk workgroup serves (MFMA path)
     int max_seq_len, chunk, maxch;

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     constexpr int NT = FP8 ? 2 : 1;                // 16-token score tiles per group
     __shared__ __attribute__((aligned(1024))) uint8_t ring[S::lds];
     __shared__ int last_flag, merged;
-    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) epoch_add(p.count_word, p.epoch, 0);
+    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) begin_call(p);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -151,7 +151,9 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     } else {
         btab += (size_t)b * p.max_blocks;
     }
-    const int last_page = (L - 1) >> p.page_shift;
+    // last page a valid token uses (0 for an empty sequence, whose table row
+    // is read but never used: the unit issues no DMA)
+    const int last_page = L > 0 ? (L - 1) >> p.page_shift : 0;
     const int pmask = (1 << p.page_shift) - 1;
 
     const int nblk = (t_end - t_begin + BLK - 1) / BLK;
@@ -348,6 +350,11 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
 #pragma unroll
             for (int u = 0; u < NSUB; ++u) {
                 const int tg = t_begin + BLK * s + GRP * u;      // first token of the group
+                if (tg + GRP > t_end) {       // the unit ends inside this group
+                    const u32x2 vm = v_tail_mask<FP8>(tg, g4, t_end);
+#pragma unroll
+                    for (int dl = 0; dl < DT; ++dl) vraw[u][dl] &= vm;
+                }
                 // S^T tiles: rows = tokens 16*tau + 4*g4 + r of the group, column = head n
                 f32x4 sacc[NT];
 #pragma unroll

@@ -169,56 +169,56 @@ int make_plan(const fd_gemm_desc_t *d, Plan *pl)
 }
 
 template <int MB, int NB, int GU, int WAVES>
-void launch_main(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+int launch_main(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     const size_t lds = fd::gemm::gemm_lds_bytes(16 * MB, pl.per);
-    hipExtLaunchKernelGGL((fd::gemm::flat_gemm_kernel<MB, NB, GU, WAVES>),
-                          dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(WAVES * 64),
-                          lds, s, e0, e1, 0, gp);
+    return fd::host::launch(fd::gemm::flat_gemm_kernel<MB, NB, GU, WAVES>,
+                            dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(WAVES * 64), lds,
+                            s, e0, e1, gp);
 }
 
 template <int MB, int NB, int GU, int WK, bool WP>
-void launch_direct_wp(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+int launch_direct_wp(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    hipExtLaunchKernelGGL((fd::gemm::flat_gemm_direct_kernel<MB, NB, GU, WK, WP>),
-                          dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(WK * 64), 0,
-                          s, e0, e1, 0, gp);
+    return fd::host::launch(fd::gemm::flat_gemm_direct_kernel<MB, NB, GU, WK, WP>,
+                            dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(WK * 64), 0, s,
+                            e0, e1, gp);
 }
 
 template <int MB, int KST, int NST>
-void launch_dma(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+int launch_dma(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     const size_t lds = (size_t)pl.ring + fd::gemm::gemm_lds_bytes(16 * MB, pl.per);
-    hipExtLaunchKernelGGL((fd::gemm::flat_gemm_dma_kernel<MB, KST, NST>),
-                          dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(256), lds, s,
-                          e0, e1, 0, gp);
+    return fd::host::launch(fd::gemm::flat_gemm_dma_kernel<MB, KST, NST>,
+                            dim3((unsigned)(pl.tiles * pl.ksplit), (unsigned)pl.mgroups), dim3(256), lds, s, e0,
+                            e1, gp);
 }
 
 template <int MB, int NB, int GU, int WK>
-void launch_direct(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+int launch_direct(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    if (pl.packed) launch_direct_wp<MB, NB, GU, WK, true>(gp, pl, s, e0, e1);
-    else launch_direct_wp<MB, NB, GU, WK, false>(gp, pl, s, e0, e1);
+    if (pl.packed) return launch_direct_wp<MB, NB, GU, WK, true>(gp, pl, s, e0, e1);
+    return launch_direct_wp<MB, NB, GU, WK, false>(gp, pl, s, e0, e1);
 }
 
 template <int MB>
-void dispatch_variant(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+int dispatch_variant(const GemmParams &gp, const Plan &pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     switch (pl.variant) {
-    case 1: launch_main<MB, 1, 8, 4>(gp, pl, s, e0, e1); break;
-    case 2: launch_main<MB, 2, 4, 4>(gp, pl, s, e0, e1); break;
-    case 3: launch_main<MB, 1, 16, 4>(gp, pl, s, e0, e1); break;
-    case 4: launch_main<MB, 2, 8, 4>(gp, pl, s, e0, e1); break;
-    case 5: launch_direct<MB, 4, 4, 4>(gp, pl, s, e0, e1); break;
-    case 6: launch_direct<MB, 2, 8, 4>(gp, pl, s, e0, e1); break;
-    case 7: launch_direct<MB, 1, 8, 4>(gp, pl, s, e0, e1); break;
-    case 8: launch_direct<MB, 1, 16, 4>(gp, pl, s, e0, e1); break;
-    case 9: launch_direct<MB, 1, 8, 8>(gp, pl, s, e0, e1); break;
-    case 10: launch_direct<MB, 2, 4, 8>(gp, pl, s, e0, e1); break;
-    case 11: launch_direct<MB, 1, 4, 16>(gp, pl, s, e0, e1); break;
-    case 12: launch_direct<MB, 1, 8, 16>(gp, pl, s, e0, e1); break;
-    case 13: launch_dma<MB, 4, 3>(gp, pl, s, e0, e1); break;
-    default: launch_dma<MB, 4, 2>(gp, pl, s, e0, e1); break;
+    case 1: return launch_main<MB, 1, 8, 4>(gp, pl, s, e0, e1);
+    case 2: return launch_main<MB, 2, 4, 4>(gp, pl, s, e0, e1);
+    case 3: return launch_main<MB, 1, 16, 4>(gp, pl, s, e0, e1);
+    case 4: return launch_main<MB, 2, 8, 4>(gp, pl, s, e0, e1);
+    case 5: return launch_direct<MB, 4, 4, 4>(gp, pl, s, e0, e1);
+    case 6: return launch_direct<MB, 2, 8, 4>(gp, pl, s, e0, e1);
+    case 7: return launch_direct<MB, 1, 8, 4>(gp, pl, s, e0, e1);
+    case 8: return launch_direct<MB, 1, 16, 4>(gp, pl, s, e0, e1);
+    case 9: return launch_direct<MB, 1, 8, 8>(gp, pl, s, e0, e1);
+    case 10: return launch_direct<MB, 2, 4, 8>(gp, pl, s, e0, e1);
+    case 11: return launch_direct<MB, 1, 4, 16>(gp, pl, s, e0, e1);
+    case 12: return launch_direct<MB, 1, 8, 16>(gp, pl, s, e0, e1);
+    case 13: return launch_dma<MB, 4, 3>(gp, pl, s, e0, e1);
+    default: return launch_dma<MB, 4, 2>(gp, pl, s, e0, e1);
     }
 }
 
@@ -274,22 +274,19 @@ extern "C" int fd_flat_gemm(const fd_gemm_desc_t *d, const void *a, const void *
 
     hipEvent_t *ev = d->stage_events;
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-    (void)hipGetLastError();
+    int lrc;
     switch (pl.mb) {
-    case 1: dispatch_variant<1>(gp, pl, stream, e0, e1); break;
-    case 2: dispatch_variant<2>(gp, pl, stream, e0, e1); break;
-    case 3: dispatch_variant<3>(gp, pl, stream, e0, e1); break;
-    default: dispatch_variant<4>(gp, pl, stream, e0, e1); break;
+    case 1: lrc = dispatch_variant<1>(gp, pl, stream, e0, e1); break;
+    case 2: lrc = dispatch_variant<2>(gp, pl, stream, e0, e1); break;
+    case 3: lrc = dispatch_variant<3>(gp, pl, stream, e0, e1); break;
+    default: lrc = dispatch_variant<4>(gp, pl, stream, e0, e1); break;
     }
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    if (pl.ksplit > 1) {
-        const size_t plane = (size_t)d->m * d->n;
-        const size_t items = plane % 4 ? plane : plane / 4;
-        const unsigned grid = (unsigned)std::min<size_t>((items + 255) / 256, 4096);
-        hipLaunchKernelGGL(fd::gemm::flat_gemm_reduce_kernel, dim3(grid), dim3(256), 0, stream, gp);
-        if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    }
-    return FD_OK;
+    if (lrc != FD_OK || pl.ksplit == 1) return lrc;
+    const size_t plane = (size_t)d->m * d->n;
+    const size_t items = plane % 4 ? plane : plane / 4;
+    const unsigned grid = (unsigned)std::min<size_t>((items + 255) / 256, 4096);
+    return fd::host::launch(fd::gemm::flat_gemm_reduce_kernel, dim3(grid), dim3(256), 0, stream, nullptr, nullptr,
+                            gp);
 }
 
 extern "C" size_t fd_flat_gemm_packed_bytes(int32_t n, int32_t k)
@@ -305,9 +302,7 @@ extern "C" int fd_flat_gemm_pack_weights(int32_t n, int32_t k, const void *w, vo
     if (!fd::host::aligned16(w) || !fd::host::aligned16(w_packed)) return FD_ERR_ALIGN;
     const size_t nfrag = fd_flat_gemm_packed_bytes(n, k) / 16;
     const unsigned grid = (unsigned)std::min<size_t>((nfrag + 255) / 256, 8192);
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(fd::gemm::pack_weights_kernel, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t *>(w), static_cast<uint16_t *>(w_packed), (int)n, (int)k, nfrag);
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    return FD_OK;
+    return fd::host::launch(fd::gemm::pack_weights_kernel, dim3(grid), dim3(256), 0, stream, nullptr, nullptr,
+                            static_cast<const uint16_t *>(w), static_cast<uint16_t *>(w_packed), (int)n, (int)k,
+                            nfrag);
 }

@@ -1,7 +1,11 @@
 // Host-side checks shared by the C-ABI entry points.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <utility>
 
 #include "fd_attn.h"
 #include "fd_common.h"
@@ -12,6 +16,25 @@ namespace host {
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Launches k(args...) on stream s (optionally stamping events e0/e1 from the
+// dispatch itself) and returns FD_OK or FD_ERR_LAUNCH from this launch's own
+// status.  The thread's last-error state is neither read nor cleared, so an
+// error that the caller's own earlier work left there stays for the caller.
+template <typename... KArgs, typename... Args>
+inline int launch(void (*k)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t e0,
+                  hipEvent_t e1, Args &&...args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> held(std::forward<Args>(args)...);
+    const hipError_t e = std::apply(
+        [&](auto &...x) {
+            void *argv[] = {static_cast<void *>(&x)...};
+            return hipExtLaunchKernel(reinterpret_cast<const void *>(k), grid, block, argv, lds, s, e0, e1, 0);
+        },
+        held);
+    return e == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
+}
 
 // The chunk size of a call: the descriptor's, or for 0 the pick measured per
 // kernel family on MI355X: 2048 tokens for grouped bf16 queries over a bf16

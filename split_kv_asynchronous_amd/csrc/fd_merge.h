@@ -95,6 +95,17 @@ FD_DEV void part_store4(const Params &p, float *ptr, f32x4 v)
     else __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ptr));
 }
 
+// First thing of a call, in one thread of the chunk launch.  With a separate
+// merge launch -- the only one that adds to the call's recomputed-pair count,
+// and it starts after this launch has ended -- the count word is reset here,
+// so a launch replayed with the same epoch (a captured graph) also counts
+// from zero.  A fused call publishes its count at its end instead
+// (merge_group).
+FD_DEV void begin_call(const Params &p)
+{
+    if (!p.fused) put(p.count_word, (unsigned long long)p.epoch << 32);
+}
+
 // Chunks a row group's sequence is cut into; an empty sequence still has one
 // (empty) unit, so its rows get written.
 FD_DEV int units_of(const Params &p, int L)
@@ -219,7 +230,18 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
     for (int r = wave; r < nrows; r += NW) mine += merge_row(p, b, h0 + r, lane);
     if (lane == 0 && mine) atomicAdd(&total, mine);
     __syncthreads();
-    if (threadIdx.x == 0 && total) epoch_add(p.count_word, p.epoch, (uint32_t)total);
+    // One add per row group into the call's fused word: merged row groups in
+    // bits 16..31, recomputed pairs in bits 0..15 (a fused grid has at most
+    // 512 units of at most 16 heads, so neither field overflows).  The last
+    // row group publishes the count and resets the word, so a replay of the
+    // launch with the same epoch starts from zero.
+    if (threadIdx.x == 0) {
+        const uint32_t v = epoch_add(p.fused_word, p.epoch, (1u << 16) | (uint32_t)total);
+        if ((int)(v >> 16) == p.ngroups) {
+            put(p.count_word, ((unsigned long long)p.epoch << 32) | (v & 0xffffu));
+            put(p.fused_word, (unsigned long long)p.epoch << 32);
+        }
+    }
 }
 
 // Separate merge launch (large grids): RW wavefronts per row, 256 threads per

@@ -68,11 +68,7 @@ extern "C" int fd_attn_prefill(const fd_prefill_desc_t *d, const void *q, const 
     hipEvent_t *ev = d->stage_events;
     hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;
     const dim3 grid((unsigned)(8 * (int64_t)p.per_xcd)), block(PrefillShape::waves * 64);
-    (void)hipGetLastError();
     if (d->out_dtype == FD_BF16)
-        hipExtLaunchKernelGGL((fd::prefill::prefill_kernel<4, 2, 3, true>), grid, block, 0, stream, ev0, ev1, 0, p);
-    else
-        hipExtLaunchKernelGGL((fd::prefill::prefill_kernel<4, 2, 3, false>), grid, block, 0, stream, ev0, ev1, 0, p);
-    if (hipGetLastError() != hipSuccess) return FD_ERR_LAUNCH;
-    return FD_OK;
+        return fd::host::launch(fd::prefill::prefill_kernel<4, 2, 3, true>, grid, block, 0, stream, ev0, ev1, p);
+    return fd::host::launch(fd::prefill::prefill_kernel<4, 2, 3, false>, grid, block, 0, stream, ev0, ev1, p);
 }

@@ -27,10 +27,12 @@
 //   * K fragments with ds_read_b128, V^T fragments with ds_read_b64_tr_b16;
 //   * S^T[16 keys x 16 queries] = K . Q^T on v_mfma_f32_16x16x32_bf16 (Q^T
 //     fragments stay in registers), scale, causal mask, band test, weights;
-//   * weights rounded to bf16 (the weight sums add the rounded values, so the
-//     output is an exact convex combination of the values with those weights);
+//   * weights split into a bf16 high part and a bf16 remainder (together a
+//     relative 2^-16; the weight sums add the same two parts, so the output
+//     is an exact convex combination of the values with those weights);
 //   * O^T[128 x 16 queries] += V^T . P^T on v_mfma_f32_16x16x32_bf16 over the
-//     stage's 32 keys, taken in the order the two score tiles hand them over.
+//     stage's 32 keys, once per part, taken in the order the two score tiles
+//     hand them over.
 #pragma once
 
 #include <type_traits>
@@ -335,25 +337,34 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
         return __builtin_amdgcn_ballot_w64(any) != 0;
     };
 
-    // Weights of block qb -> bf16 P^T (k = 8*g4 + j <-> group j/4, key row
-    // 4*g4 + j%4), then l += ones . P^T and O^T += V^T . P^T over 32 keys.
-    // nm is the exponent offset: -phi*log2e (unified) or -m*scale*log2e.
+    // Weights of block qb -> P^T as a bf16 high part and a bf16 remainder
+    // (k = 8*g4 + j <-> group j/4, key row 4*g4 + j%4), then l += ones . P^T
+    // and O^T += V^T . P^T over 32 keys, each for both parts.  The two parts
+    // carry every weight to a relative 2^-16; a single bf16 weight (2^-9)
+    // misses a 2e-3 * max|out| bar on long rows.  nm is the exponent offset:
+    // -phi*log2e (unified) or -m*scale*log2e.
     auto accumulate = [&](int qb, float nm) {
         float w[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 4; ++r) w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], p.c1, nm));  // -inf -> 0
-        const u32x4 pw = {pack_bf16(w[0][0], w[0][1]), pack_bf16(w[0][2], w[0][3]),
-                          pack_bf16(w[1][0], w[1][1]), pack_bf16(w[1][2], w[1][3])};
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_pair(w[0][0], w[0][1], h0, l0);
+        split_pair(w[0][2], w[0][3], h1, l1);
+        split_pair(w[1][0], w[1][1], h2, l2);
+        split_pair(w[1][2], w[1][3], h3, l3);
+        const u32x4 ph = {h0, h1, h2, h3}, pl = {l0, l1, l2, l3};
         // raised issue priority while this wavefront feeds the matrix cores:
         // the other wavefront of the SIMD fills the gaps with its vector work
         __builtin_amdgcn_s_setprio(1);
-        lacc[qb] = mfma_bf16(ones, pw, lacc[qb]);
+        lacc[qb] = mfma_bf16(ones, ph, lacc[qb]);
+        lacc[qb] = mfma_bf16(ones, pl, lacc[qb]);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
-            o[qb][dt] = mfma_bf16(va, pw, o[qb][dt]);
+            o[qb][dt] = mfma_bf16(va, ph, o[qb][dt]);
+            o[qb][dt] = mfma_bf16(va, pl, o[qb][dt]);
         }
         __builtin_amdgcn_s_setprio(0);
     };

@@ -110,6 +110,26 @@ FD_DEV u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi)
     return u32x4{a.x, a.y, b.x, b.y};
 }
 
+// AND-mask for the V^T fragments of the compute group that starts at token
+// tg: the entries of tokens at or past t_end become +0.  Cache slots past the
+// sequence (a page's tail, spare capacity) may hold anything, and the zero
+// weight such a token gets would still turn a NaN or an infinity there into a
+// NaN in the weight-value product.  Lane group g4 holds, per component,
+// bf16: rows 4g4 .. 4g4+3 (16-bit halves in order, two per dword);
+// E4M3FN: rows 4g4 + j (byte j of .x) and 16 + 4g4 + j (byte j of .y).
+template <bool FP8>
+FD_DEV u32x2 v_tail_mask(int tg, int g4, int t_end)
+{
+    const int n = t_end - tg - 4 * g4;     // valid rows from 4g4 on
+    if constexpr (FP8) {
+        auto bytes = [](int k) -> uint32_t { return k >= 4 ? ~0u : (k <= 0 ? 0u : (1u << (8 * k)) - 1u); };
+        return u32x2{bytes(n), bytes(n - 16)};
+    } else {
+        auto halves = [](int k) -> uint32_t { return k >= 2 ? ~0u : (k == 1 ? 0xffffu : 0u); };
+        return u32x2{halves(n), halves(n - 2)};
+    }
+}
+
 // wave-wide inclusive prefix sum
 FD_DEV int wave_scan(int x, int lane)
 {

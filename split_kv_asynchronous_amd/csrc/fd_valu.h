@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
     __shared__ int last_flag, merged;
     const size_t xy = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
     const int h = (int)(xy % (size_t)p.hq), c = (int)(xy / (size_t)p.hq), b = blockIdx.z;
-    if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) epoch_add(p.count_word, p.epoch, 0);
+    if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) begin_call(p);
     const int L = seq_len_of(p, b);
     const int t0 = c * p.chunk;
     // chunks past the sequence have no unit; an empty sequence has one empty unit
