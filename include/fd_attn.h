@@ -135,6 +135,28 @@ int fd_attn_decode(const fd_attn_desc_t *desc, const void *q, const void *k_cach
                    float phi, float a, float b, void *out, uint8_t *fallback_flags,
                    hipStream_t stream);
 
+/* The allocation-free variant of fd_attn_decode, for callers that cannot
+ * allocate device memory: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments and results as
+ * fd_attn_decode, but desc->workspace and desc->workspace_bytes are ignored:
+ * the workspace is a static device array of FD_ATTN_STATIC_WORKSPACE_BYTES
+ * inside the library, one per GPU, held from the library's load until the
+ * process ends.  A call whose fd_attn_workspace_size() exceeds that returns
+ * FD_ERR_WORKSPACE and enqueues nothing.  The first call on a device looks up
+ * that device's copy (FD_ERR_LAUNCH if the runtime cannot give its address);
+ * no call allocates or frees anything.  Every call on one GPU shares the
+ * array, which keeps the last call's partials (it needs no clearing: its
+ * counters carry a per-call epoch), so calls that overlap on one GPU -- on
+ * different streams, or from different threads -- race and give undefined
+ * results; order them on one stream.  The recomputed-pair count of the last
+ * call is in the array, not readable through this interface. */
+#define FD_ATTN_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+int fd_attn_decode_static(const fd_attn_desc_t *desc, const void *q, const void *k_cache,
+                          const void *v_cache, const int32_t *seq_lens, const int32_t *block_table,
+                          float phi, float a, float b, void *out, uint8_t *fallback_flags,
+                          hipStream_t stream);
+
 /* Static text for a status code. */
 const char *fd_attn_status_string(int status);
 

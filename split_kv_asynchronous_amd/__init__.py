@@ -13,7 +13,7 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["fd_attn_decode", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
+__all__ = ["fd_attn_decode", "fd_attn_decode_static", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
            "fd_attn_workspace_size", "fd_flat_gemm", "fd_flat_gemm_plan",
            "fd_flat_gemm_workspace_size", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
            "make_gemm_desc",
@@ -89,6 +89,8 @@ def _load():
                                        ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
         lib.fd_attn_decode.restype = ctypes.c_int
+        lib.fd_attn_decode_static.argtypes = lib.fd_attn_decode.argtypes
+        lib.fd_attn_decode_static.restype = ctypes.c_int
         lib.fd_attn_prefill.argtypes = [ctypes.POINTER(FdPrefillDesc), ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float,
@@ -187,14 +189,12 @@ class DecodeCall:
         return self.out, self.fallback_flags
 
 
-def prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,
-                   out=None, fallback_flags=None, *, chunk_size: int, max_seq_len: int,
-                   num_kv_heads: Optional[int] = None, page_size: int = 0,
-                   scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
-                   q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
-                   out_dtype: str = "f32", stream=None) -> DecodeCall:
-    """Checks and marshals the arguments of fd_attn_decode (same meaning)
-    once; returns a DecodeCall that enqueues the call each time it is called."""
+def _marshal_decode(q, k_cache, v_cache, seq_lens, block_table, out, fallback_flags, *,
+                    chunk_size, max_seq_len, num_kv_heads, page_size, scale, k_scale, v_scale,
+                    q_dtype, kv_dtype, out_dtype):
+    """Checks the tensors of a decode call; returns (descriptor without a
+    workspace, pointers, tensors to keep alive).  Allocates only a missing
+    out or fallback_flags."""
     import torch
     dev = q.device
     B, Hq, D = q.shape
@@ -217,8 +217,8 @@ def prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
     if kd == "e4m3fn":
         if k_scale is None or v_scale is None:
             raise ValueError("fp8 caches need k_scale and v_scale")
-        k_scale = k_scale.contiguous()
-        v_scale = v_scale.contiguous()
+        if not (k_scale.is_contiguous() and v_scale.is_contiguous()):
+            raise ValueError("k_scale and v_scale must be contiguous")
         ks, vs = k_scale.data_ptr(), v_scale.data_ptr()
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
@@ -229,17 +229,64 @@ def prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
                      chunk_size=chunk_size, page_size=page_size, max_blocks_per_seq=max_blocks,
                      num_pages=num_pages, scale=scale, q_dtype=qd, kv_dtype=kd,
                      out_dtype=out_dtype, head_dim=D, k_scale_ptr=ks, v_scale_ptr=vs)
-    need = fd_attn_workspace_size(desc)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    desc.workspace = workspace.data_ptr()
-    desc.workspace_bytes = workspace.numel() * workspace.element_size()
     table = block_table if page_size else None
     ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
             table.data_ptr() if table is not None else None, out.data_ptr(),
             fallback_flags.data_ptr())
-    keep = (q, k_cache, v_cache, seq_lens, table, k_scale, v_scale, out, fallback_flags, workspace)
-    return DecodeCall(desc, ptrs, keep, phi, a, b, stream)
+    keep = (q, k_cache, v_cache, seq_lens, table, k_scale, v_scale, out, fallback_flags)
+    return desc, ptrs, keep
+
+
+def prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,
+                   out=None, fallback_flags=None, *, chunk_size: int, max_seq_len: int,
+                   num_kv_heads: Optional[int] = None, page_size: int = 0,
+                   scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
+                   q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
+                   out_dtype: str = "f32", stream=None) -> DecodeCall:
+    """Checks and marshals the arguments of fd_attn_decode (same meaning)
+    once; returns a DecodeCall that enqueues the call each time it is called."""
+    import torch
+    desc, ptrs, keep = _marshal_decode(q, k_cache, v_cache, seq_lens, block_table, out, fallback_flags,
+                                       chunk_size=chunk_size, max_seq_len=max_seq_len,
+                                       num_kv_heads=num_kv_heads, page_size=page_size, scale=scale,
+                                       k_scale=k_scale, v_scale=v_scale, q_dtype=q_dtype,
+                                       kv_dtype=kv_dtype, out_dtype=out_dtype)
+    need = fd_attn_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    desc.workspace = workspace.data_ptr()
+    desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    return DecodeCall(desc, ptrs, keep + (workspace,), phi, a, b, stream)
+
+
+def fd_attn_decode_static(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float,
+                          b: float, out, fallback_flags, *, chunk_size: int, max_seq_len: int,
+                          num_kv_heads: Optional[int] = None, page_size: int = 0,
+                          scale: Optional[float] = None, k_scale=None, v_scale=None,
+                          q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
+                          out_dtype: Optional[str] = None, stream=None):
+    """fd_attn_decode_static of include/fd_attn.h: one decode call whose
+    workspace is the library's static device array, so nothing is allocated
+    here or in the library; ``out`` and ``fallback_flags`` are required.
+    Arguments otherwise as fd_attn_decode.  Returns (out, fallback_flags)."""
+    import torch
+    if out is None or fallback_flags is None:
+        raise ValueError("fd_attn_decode_static allocates nothing: pass out and fallback_flags")
+    if out_dtype is None:
+        out_dtype = "f32" if out.dtype == torch.float32 else "bf16"
+    desc, ptrs, _ = _marshal_decode(q, k_cache, v_cache, seq_lens, block_table, out, fallback_flags,
+                                    chunk_size=chunk_size, max_seq_len=max_seq_len,
+                                    num_kv_heads=num_kv_heads, page_size=page_size, scale=scale,
+                                    k_scale=k_scale, v_scale=v_scale, q_dtype=q_dtype,
+                                    kv_dtype=kv_dtype, out_dtype=out_dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    qp, kp, vp, lp, tp, op, fp = ptrs
+    rc = _load().fd_attn_decode_static(ctypes.byref(desc), qp, kp, vp, lp, tp, float(phi), float(a),
+                                       float(b), op, fp, stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return out, fallback_flags
 
 
 def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: float, b: float,

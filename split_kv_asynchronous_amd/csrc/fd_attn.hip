@@ -2,6 +2,7 @@
 // carve-up, kernel choice and launches.  No allocation, no synchronisation.
 #include <hip/hip_ext.h>
 #include <atomic>
+#include <mutex>
 #include <math.h>
 #include <string.h>
 
@@ -108,10 +109,12 @@ extern "C" const char *fd_attn_status_string(int status)
     }
 }
 
-extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void *k_cache,
-                              const void *v_cache, const int32_t *seq_lens,
-                              const int32_t *block_table, float phi, float a, float b, void *out,
-                              uint8_t *fallback_flags, hipStream_t stream)
+namespace {
+
+// Every check of a decode call but the workspace's.
+int validate(const fd_attn_desc_t *d, const void *q, const void *k_cache, const void *v_cache,
+             const int32_t *seq_lens, const int32_t *block_table, float phi, float a, float b, const void *out,
+             const uint8_t *fallback_flags)
 {
     if (!d || !q || !k_cache || !v_cache || !seq_lens || !out || !fallback_flags) return FD_ERR_NULL;
     int rc = check_shape(d);
@@ -128,15 +131,22 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
         b > 64.f)
         return FD_ERR_BAND;
     if (!isfinite(d->scale)) return FD_ERR_SHAPE;
-    const size_t need = fd_attn_workspace_size(d);
-    if (!d->workspace || ((uintptr_t)d->workspace & (kAlign - 1)) || d->workspace_bytes < need)
-        return FD_ERR_WORKSPACE;
+    return FD_OK;
+}
 
+// Enqueues a validated call with workspace `wsp` (256-byte aligned, at least
+// fd_attn_workspace_size(d) bytes).
+int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const void *v_cache,
+            const int32_t *seq_lens, const int32_t *block_table, float phi, float a, float b, void *out,
+            uint8_t *fallback_flags, void *wsp, hipStream_t stream)
+{
+    int rc = FD_OK;
+    const int qt = d->q_dtype, kv = d->kv_dtype, ot = d->out_dtype;
     const int chunk = fd::host::chunk_of(d);
     const int maxch = (d->max_seq_len + chunk - 1) / chunk;
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     const Layout L = layout_of(rows, (size_t)maxch);
-    uint8_t *ws = static_cast<uint8_t *>(d->workspace);
+    uint8_t *ws = static_cast<uint8_t *>(wsp);
 
     Params p;
     memset(&p, 0, sizeof p);
@@ -232,4 +242,64 @@ extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void
                         nullptr, p);
     }
     return rc;
+}
+
+// ---- workspace in a static device array, for callers that cannot allocate
+// (see fd_attn_decode_static).  Every GPU the library runs on holds its own
+// copy from the library's load until the process ends.  In host code the
+// array's name is only a host-side stand-in: kernels get the device address
+// that hipGetSymbolAddress gives for the device, looked up once per device
+// (with that device current) and kept.
+static __device__ __align__(256) uint8_t scratch[FD_ATTN_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+int scratch_address(hipStream_t stream, void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0, cur = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FD_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        if (hipGetDevice(&cur) != hipSuccess) return FD_ERR_LAUNCH;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return FD_ERR_LAUNCH;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p || ((uintptr_t)p & (kAlign - 1))) return FD_ERR_LAUNCH;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return FD_OK;
+}
+
+}  // namespace
+
+extern "C" int fd_attn_decode(const fd_attn_desc_t *d, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *seq_lens,
+                              const int32_t *block_table, float phi, float a, float b, void *out,
+                              uint8_t *fallback_flags, hipStream_t stream)
+{
+    const int rc = validate(d, q, k_cache, v_cache, seq_lens, block_table, phi, a, b, out, fallback_flags);
+    if (rc != FD_OK) return rc;
+    const size_t need = fd_attn_workspace_size(d);
+    if (!d->workspace || ((uintptr_t)d->workspace & (kAlign - 1)) || d->workspace_bytes < need)
+        return FD_ERR_WORKSPACE;
+    return enqueue(d, q, k_cache, v_cache, seq_lens, block_table, phi, a, b, out, fallback_flags, d->workspace,
+                   stream);
+}
+
+extern "C" int fd_attn_decode_static(const fd_attn_desc_t *d, const void *q, const void *k_cache,
+                                     const void *v_cache, const int32_t *seq_lens,
+                                     const int32_t *block_table, float phi, float a, float b, void *out,
+                                     uint8_t *fallback_flags, hipStream_t stream)
+{
+    int rc = validate(d, q, k_cache, v_cache, seq_lens, block_table, phi, a, b, out, fallback_flags);
+    if (rc != FD_OK) return rc;
+    if (fd_attn_workspace_size(d) > FD_ATTN_STATIC_WORKSPACE_BYTES) return FD_ERR_WORKSPACE;
+    void *ws = nullptr;
+    rc = scratch_address(stream, &ws);
+    if (rc != FD_OK) return rc;
+    return enqueue(d, q, k_cache, v_cache, seq_lens, block_table, phi, a, b, out, fallback_flags, ws, stream);
 }

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_prefill",
+    assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_decode_static", "fd_attn_prefill",
                      "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size",
                      "fd_flat_gemm", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
                      "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size"]
@@ -282,3 +282,22 @@ def test_chunk_size_zero_is_the_library_pick():
                       (dict(num_kv_heads=64), 1024), (dict(q_dtype="f32"), 1024)]:
         auto = fd.fd_attn_workspace_size(_desc(chunk_size=0, **kw))
         assert auto > 0 and auto == fd.fd_attn_workspace_size(_desc(chunk_size=chunk, **kw)), kw
+
+
+def test_static_workspace_variant_checks_before_the_gpu():
+    # the allocation-free entry point validates exactly as fd_attn_decode does
+    # and refuses a call whose workspace exceeds its static array
+    lib = fd._load()
+
+    def scall(d, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, table=None, phi=4.0, a=20.0, b=6.0, out=FAKE, flags=FAKE)
+        a.update(kw)
+        return lib.fd_attn_decode_static(ctypes.byref(d), a["q"], a["k"], a["v"], a["lens"], a["table"],
+                                         a["phi"], a["a"], a["b"], a["out"], a["flags"], None)
+    assert scall(_valid_desc(), q=None) == -1
+    assert scall(_valid_desc(), k=FAKE + 4) == -4
+    assert scall(_valid_desc(), b=65.0) == -5
+    assert scall(_valid_desc(head_dim=64)) == -2
+    big = _valid_desc(batch=64, num_q_heads=64, num_kv_heads=8, max_seq_len=1 << 20, chunk_size=1024)
+    assert fd.fd_attn_workspace_size(big) > (64 << 20)
+    assert scall(big) == -6
