@@ -41,3 +41,23 @@ def test_f32_operands_and_error_scale():
                                a.astype(np.float64) @ w.astype(np.float64).T, rtol=1e-14)
     ab, wb = synthetic.make_gemm(2, 6, 16, seed=3)
     assert np.all(oracle.flat_gemm_abs(ab, wb) >= np.abs(oracle.flat_gemm(ab, wb)))
+
+
+def test_error_scale_closed_forms():
+    # |A| . |W|^T pinned from both sides: equal to the product itself when no
+    # term can cancel (nonnegative operands), K for operands of +-1 whatever
+    # the signs, and a scaled column of |A| for one-hot weight rows
+    rng = np.random.default_rng(4)
+    K = 64
+    ab, wb = synthetic.make_gemm(3, 5, K, seed=4)
+    pos_a = synthetic.bf16_round(np.abs(synthetic.bf16_to_f32(ab)))
+    pos_w = synthetic.bf16_round(np.abs(synthetic.bf16_to_f32(wb)))
+    np.testing.assert_array_equal(oracle.flat_gemm_abs(ab, wb), oracle.flat_gemm(pos_a, pos_w))
+    signs_a = synthetic.bf16_round(rng.choice([-1.0, 1.0], size=(3, K)).astype(np.float32))
+    signs_w = synthetic.bf16_round(rng.choice([-1.0, 1.0], size=(5, K)).astype(np.float32))
+    np.testing.assert_array_equal(oracle.flat_gemm_abs(signs_a, signs_w), np.full((3, 5), float(K)))
+    onehot = np.zeros((3, K), dtype=np.float32)
+    onehot[0, 7], onehot[1, 0], onehot[2, K - 1] = -2.0, 0.5, -1.0
+    got = oracle.flat_gemm_abs(ab, synthetic.bf16_round(onehot))
+    A = np.abs(synthetic.bf16_to_f32(ab).astype(np.float64))
+    np.testing.assert_array_equal(got, np.stack([2.0 * A[:, 7], 0.5 * A[:, 0], A[:, K - 1]], axis=1))
