@@ -131,9 +131,39 @@ def cpu_baseline(prob, min_seconds=10.0, max_passes=20):
     sample_bytes = int(lens[:nb].sum()) * prob.num_kv_heads * prob.head_dim * 2 * elt
     gbs = sample_bytes * passes / spent / 1e9
     what = ("the whole call" if nb == B else "batch entries 0..%d (all %d query heads)" % (nb - 1, Hq))
+    # the same oracle on one core, over the first batch entry's rows (or a
+    # share of them) for about a third of the time
+    oracle.set_threads(1)
+    try:
+        n1 = max(1, min(Hq, int(Hq * (min_seconds / 3) / max(per_entry * threads, 1e-9))))
+        rows1 = np.arange(n1, dtype=np.int32)
+        t = time.perf_counter()
+        _, _, _, th1 = oracle.decode_exact(**prob.args(), rows=rows1, with_threads=True)
+        spent1 = time.perf_counter() - t
+    finally:
+        oracle.set_threads(0)
+    bytes1 = int(lens[0]) * n1 * prob.head_dim * 2 * elt   # K and V of row (0, h) each read once per row
+    one = {"value": round(bytes1 / spent1 / 1e9, 4), "unit": "GB/s", "cores": int(th1),
+           "sample": "query heads 0..%d of batch entry 0, %.1f s (K/V bytes counted once per query head)"
+                     % (n1 - 1, spent1)}
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%s, %d pass(es), %.1f s, float64 exact softmax + band test; "
-                      "calls/s equivalent %.4f" % (what, passes, spent, gbs * 1e9 / prob.kv_bytes())}
+                      "calls/s equivalent %.4f" % (what, passes, spent, gbs * 1e9 / prob.kv_bytes()),
+            "one_thread": one}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def copy_calibration():
@@ -168,7 +198,7 @@ def prefill_cpu_baseline(prob, min_seconds=10.0):
         rows_done += len(rows)
         n = min(4096, n * 2)
     tf = flops / spent / 1e12
-    return {"value": round(tf, 7), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(tf, 7), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d query rows spread over all (sequence, head, position), %.1f s, "
                       "float64 exact causal softmax + band test" % (rows_done, spent)}
 
@@ -271,7 +301,7 @@ def stats_cpu_baseline(prob, min_seconds=10.0):
         nbytes += int(lens[done]) * prob.num_kv_heads * prob.head_dim * elt
         done += 1
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "sample": "batch entries 0..%d (all %d query heads), %.1f s, float64 "
+            "kind": "oracle", "cpu_model": cpu_model(), "sample": "batch entries 0..%d (all %d query heads), %.1f s, float64 "
                                         "scores, extremes and 4096-bin histogram" % (done - 1, Hq, spent)}
 
 
@@ -348,7 +378,7 @@ def gemm_cpu_baseline(cfg, inputs, min_seconds=10.0):
             if spent >= min_seconds:
                 break
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "sample": "%d layer products (%s), %.1f s, float64 matrix multiply"
+            "kind": "oracle", "cpu_model": cpu_model(), "sample": "%d layer products (%s), %.1f s, float64 matrix multiply"
                                         % (len(done), ",".join(done[:8]), spent)}
 
 

@@ -68,6 +68,8 @@ def _load():
                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p]
         lib.orc_decode_exact.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = None
         lib.orc_decode_unified.argtypes = [P, I, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -135,6 +137,12 @@ def _rows(rows, B, Hq):
     if rows.size and (rows.min() < 0 or rows.max() >= B * Hq):
         raise ValueError("row id out of range")
     return rows, rows.size
+
+
+def set_threads(n: int) -> None:
+    """Caps the oracle's OpenMP threads at n for the calls that follow (n < 1:
+    the default, every core)."""
+    _load().orc_set_threads(int(n))
 
 
 def decode_exact(q, k_cache, v_cache, seq_lens, block_table=None, *, num_kv_heads, max_seq_len,

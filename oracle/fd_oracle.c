@@ -206,6 +206,21 @@ static void exact_row(const orc_problem *p, const orc_inputs *in, int row, doubl
 }
 
 /*
+ * Caps the OpenMP threads of the calls that follow at n (n < 1: back to the
+ * runtime's default).  Used to time the oracle on one core beside all cores.
+ */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    static int dflt = 0;
+    if (dflt == 0) dflt = omp_get_max_threads();
+    omp_set_num_threads(n > 0 ? n : dflt);
+#else
+    (void)n;
+#endif
+}
+
+/*
  * rows: nrows row ids (b * Hq + h), or NULL for all B*Hq rows in order.
  * out: [nrows][D]; flags: [nrows]; margin: [nrows] or NULL -- the smallest
  * distance from any valid score to either band edge (infinity for empty rows).
