@@ -13,19 +13,17 @@ FD_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Two floats -> packed bf16 pair, truncated (high) and the rounded remainder (low).
+// Two floats -> packed bf16 pair rounded to nearest even (high part) and the
+// packed bf16 of the remainders, also rounded to nearest even (low part):
+// high + low carries each value to a relative 2^-18.  Two hardware
+// conversions (v_cvt_pk_bf16_f32); the remainder a - high is exact in fp32.
 FD_DEV void split_pair(float a, float b, uint32_t &hi, uint32_t &lo)
 {
-    const uint32_t ua = __float_as_uint(a) & 0xffff0000u;
-    const uint32_t ub = __float_as_uint(b) & 0xffff0000u;
-    hi = (ua >> 16) | ub;
-    const float ra = a - __uint_as_float(ua);
-    const float rb = b - __uint_as_float(ub);
-    // round-to-nearest-even of the remainders to bf16
-    uint32_t xa = __float_as_uint(ra), xb = __float_as_uint(rb);
-    xa = (xa + 0x7fffu + ((xa >> 16) & 1u)) >> 16;
-    xb = (xb + 0x7fffu + ((xb >> 16) & 1u)) & 0xffff0000u;
-    lo = xa | xb;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const float ra = a - __uint_as_float(hi << 16);
+    const float rb = b - __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
 }
 
 }  // namespace fd

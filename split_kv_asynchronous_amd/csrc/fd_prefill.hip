@@ -10,7 +10,17 @@
 
 namespace {
 
-using PrefillShape = fd::prefill::Shape<4, 2, 3>;
+#ifndef FD_PREFILL_WAVES
+#define FD_PREFILL_WAVES 4
+#endif
+#ifndef FD_PREFILL_QBLOCKS
+#define FD_PREFILL_QBLOCKS 2
+#endif
+#ifndef FD_PREFILL_STAGES
+#define FD_PREFILL_STAGES 3
+#endif
+
+using PrefillShape = fd::prefill::Shape<FD_PREFILL_WAVES, FD_PREFILL_QBLOCKS, FD_PREFILL_STAGES>;
 using fd::host::aligned16;
 
 }  // namespace
@@ -69,6 +79,6 @@ extern "C" int fd_attn_prefill(const fd_prefill_desc_t *d, const void *q, const 
     hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;
     const dim3 grid((unsigned)(8 * (int64_t)p.per_xcd)), block(PrefillShape::waves * 64);
     if (d->out_dtype == FD_BF16)
-        return fd::host::launch(fd::prefill::prefill_kernel<4, 2, 3, true>, grid, block, 0, stream, ev0, ev1, p);
-    return fd::host::launch(fd::prefill::prefill_kernel<4, 2, 3, false>, grid, block, 0, stream, ev0, ev1, p);
+        return fd::host::launch(fd::prefill::prefill_kernel<FD_PREFILL_WAVES, FD_PREFILL_QBLOCKS, FD_PREFILL_STAGES, true>, grid, block, 0, stream, ev0, ev1, p);
+    return fd::host::launch(fd::prefill::prefill_kernel<FD_PREFILL_WAVES, FD_PREFILL_QBLOCKS, FD_PREFILL_STAGES, false>, grid, block, 0, stream, ev0, ev1, p);
 }

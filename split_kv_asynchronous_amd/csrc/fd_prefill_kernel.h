@@ -28,8 +28,7 @@
 //   * S^T[16 keys x 16 queries] = K . Q^T on v_mfma_f32_16x16x32_bf16 (Q^T
 //     fragments stay in registers), scale, causal mask, band test, weights;
 //   * weights split into a bf16 high part and a bf16 remainder (together a
-//     relative 2^-16; the weight sums add the same two parts, so the output
-//     is an exact convex combination of the values with those weights);
+//     relative 2^-18); the weight sums add the fp32 weights in registers;
 //   * O^T[128 x 16 queries] += V^T . P^T on v_mfma_f32_16x16x32_bf16 over the
 //     stage's 32 keys, once per part, taken in the order the two score tiles
 //     hand them over.
@@ -87,10 +86,11 @@ struct Shape {
     static_assert(NST >= 2, "the ring needs two stages");
     static_assert((NST - 1) * dma_per_wave < 64, "vmcnt cannot count that deep");
     static_assert(lds <= 80 * 1024, "two workgroups per compute unit");
+    static_assert(QB >= 1 && QB <= 4, "query blocks per wavefront");
 };
 
 template <int NW, int QB, int NST, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(PrefillParams p)
 {
     using S = Shape<NW, QB, NST>;
     constexpr int ROW = 256;                       // bytes per cache row (16 pieces of 16 bytes)
@@ -186,20 +186,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
     }
 
     f32x4 o[QB][8];      // O^T: lane (n, g4) holds components 16dt + 4g4 + i of query n
-    f32x4 lacc[QB];      // weight sums: every entry of lane (n, g4) holds query n's sum
+    float lacc[QB];      // weight sums: lane (n, g4) holds query n's sum over its keys 4g4 .. 4g4+3
     float mrun[QB];      // online softmax: running maximum (raw score units)
     bool bad[QB];        // some visible score of query n left the band
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lacc[qb] = 0.f;
         mrun[qb] = -INFINITY;
         bad[qb] = false;
     }
-    // A operand of all ones (bf16 1.0): ones . P^T gives every query's weight
-    // sum of the stage, from the same rounded weights that multiply V
-    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
     // ---- ring prologue
 #pragma unroll
@@ -216,24 +213,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
     u32x4 qf[QB][4];
     {
         const size_t head_row = ((size_t)b * p.hq + h) * p.q_len;
-        const uint16_t *qrow[QB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            qrow[qb] = p.q + (head_row + min(jw0 + 16 * qb + n, p.q_len - 1)) * kHeadDim + 8 * g4;
-        static_assert(QB == 2, "the query load statement is written for two blocks");
-        asm volatile("global_load_dwordx4 %0, %8, off\n\t"
-                     "global_load_dwordx4 %1, %8, off offset:64\n\t"
-                     "global_load_dwordx4 %2, %8, off offset:128\n\t"
-                     "global_load_dwordx4 %3, %8, off offset:192\n\t"
-                     "global_load_dwordx4 %4, %9, off\n\t"
-                     "global_load_dwordx4 %5, %9, off offset:64\n\t"
-                     "global_load_dwordx4 %6, %9, off offset:128\n\t"
-                     "global_load_dwordx4 %7, %9, off offset:192\n\t"
-                     "s_waitcnt vmcnt(0)"
-                     : "=&v"(qf[0][0]), "=&v"(qf[0][1]), "=&v"(qf[0][2]), "=&v"(qf[0][3]),
-                       "=&v"(qf[1][0]), "=&v"(qf[1][1]), "=&v"(qf[1][2]), "=&v"(qf[1][3])
-                     : "v"(qrow[0]), "v"(qrow[1])
-                     : "memory");
+        for (int qb = 0; qb < QB; ++qb) {
+            const uint16_t *qrow = p.q + (head_row + min(jw0 + 16 * qb + n, p.q_len - 1)) * kHeadDim + 8 * g4;
+            asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                         "global_load_dwordx4 %1, %4, off offset:64\n\t"
+                         "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                         "global_load_dwordx4 %3, %4, off offset:192\n\t"
+                         "s_waitcnt vmcnt(0)"
+                         : "=&v"(qf[qb][0]), "=&v"(qf[qb][1]), "=&v"(qf[qb][2]), "=&v"(qf[qb][3])
+                         : "v"(qrow)
+                         : "memory");
+        }
     }
 
     // ---- per-stage pieces
@@ -337,18 +328,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
         return __builtin_amdgcn_ballot_w64(any) != 0;
     };
 
-    // Weights of block qb -> P^T as a bf16 high part and a bf16 remainder
-    // (k = 8*g4 + j <-> group j/4, key row 4*g4 + j%4), then l += ones . P^T
-    // and O^T += V^T . P^T over 32 keys, each for both parts.  The two parts
-    // carry every weight to a relative 2^-16; a single bf16 weight (2^-9)
-    // misses a 2e-3 * max|out| bar on long rows.  nm is the exponent offset:
-    // -phi*log2e (unified) or -m*scale*log2e.
+    // Weights of block qb: the fp32 weights add into the lane's weight sum;
+    // P^T goes to the matrix cores as a bf16 high part and a bf16 remainder
+    // (k = 8*g4 + j <-> group j/4, key row 4*g4 + j%4), O^T += V^T . P^T over
+    // 32 keys for both parts.  The two parts carry every weight to a relative
+    // 2^-18; a single bf16 weight (2^-9) misses a 2e-3 * max|out| bar on long
+    // rows.  nm is the exponent offset: -phi*log2e (unified) or
+    // -m*scale*log2e.
     auto accumulate = [&](int qb, float nm) {
         float w[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], p.c1, nm));  // -inf -> 0
+            for (int r = 0; r < 4; ++r) {
+                w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], p.c1, nm));  // -inf -> 0
+                lacc[qb] += w[u][r];
+            }
         uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
         split_pair(w[0][0], w[0][1], h0, l0);
         split_pair(w[0][2], w[0][3], h1, l1);
@@ -358,8 +353,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
         // raised issue priority while this wavefront feeds the matrix cores:
         // the other wavefront of the SIMD fills the gaps with its vector work
         __builtin_amdgcn_s_setprio(1);
-        lacc[qb] = mfma_bf16(ones, ph, lacc[qb]);
-        lacc[qb] = mfma_bf16(ones, pl, lacc[qb]);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
@@ -414,7 +407,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
     // saw a key continues from reference phi, a row that saw none from -inf.
     if (switched) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mrun[qb] = lacc[qb][0] > 0.f ? p.phi_raw : -INFINITY;
+        for (int qb = 0; qb < QB; ++qb) {
+            float l = lacc[qb];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            mrun[qb] = l > 0.f ? p.phi_raw : -INFINITY;
+        }
 #pragma unroll 1
         for (bool first = true; s < nact; ++s, first = false) {
             if (!first) {
@@ -454,7 +452,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(PrefillParams p)
         f |= __shfl_xor(f, 32);
         const int j = jw0 + 16 * qb + n;
         if (j >= p.q_len) continue;
-        const float l = lacc[qb][0];
+        float l = lacc[qb];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const size_t row = ((size_t)b * p.hq + h) * p.q_len + j;
 #pragma unroll

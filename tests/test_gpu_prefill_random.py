@@ -6,7 +6,7 @@ shorter than the block, or an empty one), and either a wide band (no visible
 score leaves it) or a narrow one (rows switch to online softmax part-way).
 Bar as in the other prefill tests: max|gpu - oracle| <= 2e-3 * max|oracle|,
 and every output element within the bound the kernel's arithmetic allows
-(weights carried as a bf16 pair to a relative 2^-16, fp32 accumulation);
+(weights carried as a bf16 pair to a relative 2^-18, fp32 accumulation);
 flags bit-exact on every row whose visible scores all lie at least 1e-3 from
 both band edges (a row with a score closer than that may take either path).
 """
