@@ -92,17 +92,6 @@ def kernel_bytes(prob, fused) -> int:
     return prob.kv_bytes() + qb + extra
 
 
-def merges_in_chunk_kernel(prob) -> bool:
-    """Whether the library merges inside the chunk kernel for this problem
-    (grids of at most 512 units; the rule lives in fd_attn.hip)."""
-    g = prob.num_q_heads // prob.num_kv_heads
-    heads = max(k for k in range(1, min(g, 16) + 1) if g % k == 0) if g > 1 else 1
-    mfma = g > 1 and prob.q_dtype == "bf16" and prob.kv_dtype != "f32"
-    blocks = prob.num_q_heads // heads if mfma else prob.num_q_heads
-    maxch = -(-prob.max_seq_len // prob.chunk_size)
-    return maxch * blocks * prob.batch <= 512
-
-
 def cpu_baseline(prob, min_seconds=10.0, max_passes=20):
     """The float64 oracle, as it stands, on the host cores: whole calls of the
     same workload repeated until about min_seconds of CPU time have passed
@@ -576,12 +565,30 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
 
+    # the same call captured once into a graph and replayed K times (the
+    # per-token graph execute of a serving loop): reported beside the value
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=side):
+        dp.run()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_per_call = (time.perf_counter() - t0) / K
+    del graph
+
     kv = prob.kv_bytes()
     value = kv / per_call / 1e9
     rows_flagged = int(dp.results()[1].sum())
     chunks_recomputed = dp.recomputed()
     kernel_s = float(np.mean(kernel_ms)) / 1e3
-    fused = merges_in_chunk_kernel(prob)
+    plan = fd.fd_attn_plan(dp.desc())
+    fused = bool(plan["fused"])
     nbytes = kernel_bytes(prob, fused)
     achieved = nbytes / kernel_s / 1e9
 
@@ -608,6 +615,8 @@ def main():
                    "page_size": prob.page_size, "kv_bytes_per_call": kv,
                    "phi": prob.phi, "band": [prob.phi - prob.a, prob.phi + prob.b]},
         "calls_per_s": round(1.0 / per_call, 2),
+        "graph_ms_per_call": round(graph_per_call * 1e3, 5),
+        "plan": plan,
         # a cache under twice the 256 MB last-level cache is re-read from it, in
         # part or whole, call after call: such a line is not an HBM figure
         "cache_resident": kv < (512 << 20),

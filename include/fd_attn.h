@@ -96,8 +96,7 @@ typedef struct {
     int32_t head_dim;           /* must be 128 */
     int32_t max_seq_len;        /* 1 .. 2^23: contiguous capacity; seq_lens are clamped to it */
     int32_t chunk_size;         /* split size: a multiple of 32 (and of page_size), >= 32;
-                                   0 = the library's pick: 2048 for grouped bf16 queries over
-                                   a bf16 cache, 1024 otherwise (at least page_size) */
+                                   0 = the library's pick from its table (fd_attn_plan) */
     int32_t page_size;          /* 0 = contiguous; else a power of two in [16, 256] */
     int32_t max_blocks_per_seq; /* paged: >= ceil(max_seq_len / page_size) */
     int32_t num_pages;          /* paged: number of pages in the K/V pool (>= 1) */
@@ -114,7 +113,17 @@ typedef struct {
      * in the same launch), stamped by its own dispatch on `stream` (no extra
      * stream work). */
     hipEvent_t *stage_events;
+    /* 0: the library's plan (see fd_attn_plan).  Otherwise, for tuning and
+     * tests, FD_PLAN_SHAPE(k) forces kernel shape k of the call's family and
+     * FD_PLAN_FUSED / FD_PLAN_SPLIT force the merge into the chunk launch or
+     * into a second launch (either bit alone; the results are the same). */
+    int32_t plan;
 } fd_attn_desc_t;
+
+#define FD_PLAN_SHAPE(k) ((k) + 1)
+#define FD_PLAN_SHAPE_MASK 0x0f
+#define FD_PLAN_FUSED 0x10
+#define FD_PLAN_SPLIT 0x20
 
 /* Bytes of workspace a call with this descriptor needs (0 if desc is NULL or
  * its sizes are invalid).  The workspace holds per-(row, chunk) partial sums
@@ -156,6 +165,18 @@ int fd_attn_decode_static(const fd_attn_desc_t *desc, const void *q, const void 
                           const void *v_cache, const int32_t *seq_lens, const int32_t *block_table,
                           float phi, float a, float b, void *out, uint8_t *fallback_flags,
                           hipStream_t stream);
+
+/* The plan a call with this descriptor would run, from the library's table
+ * of measured plans (or desc->plan where it forces one): the chunk size, the
+ * kernel family (0: grouped bf16 queries over a bf16 cache; 1: grouped bf16
+ * queries over an E4M3FN cache; 2: one query per KV head, or fp32 operands),
+ * the kernel shape within the family, and whether the merge runs inside the
+ * chunk launch (1) or in a second launch (0).  The table is keyed by family,
+ * paging and max_seq_len (the offline table of shapes of the FlashDecoding++
+ * theory page, section 4).  Any output pointer may be NULL.  Returns FD_OK or
+ * FD_ERR_NULL / FD_ERR_SHAPE for an invalid descriptor. */
+int fd_attn_plan(const fd_attn_desc_t *desc, int32_t *chunk_size, int32_t *family, int32_t *shape,
+                 int32_t *fused);
 
 /* Static text for a status code. */
 const char *fd_attn_status_string(int status);

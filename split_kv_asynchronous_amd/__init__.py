@@ -13,7 +13,8 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["fd_attn_decode", "fd_attn_decode_static", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
+__all__ = ["fd_attn_decode", "fd_attn_decode_static", "fd_attn_plan", "FD_PLAN_SHAPE",
+           "FD_PLAN_FUSED", "FD_PLAN_SPLIT", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
            "fd_attn_workspace_size", "fd_flat_gemm", "fd_flat_gemm_plan",
            "fd_flat_gemm_workspace_size", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
            "make_gemm_desc",
@@ -45,7 +46,16 @@ class FdAttnDesc(ctypes.Structure):
                 ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("k_scale", ctypes.c_void_p),
                 ("v_scale", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stage_events", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stage_events", ctypes.c_void_p),
+                ("plan", ctypes.c_int32)]
+
+
+# fd_attn_desc_t.plan bits (include/fd_attn.h)
+FD_PLAN_FUSED, FD_PLAN_SPLIT = 0x10, 0x20
+
+
+def FD_PLAN_SHAPE(k: int) -> int:
+    return k + 1
 
 
 class FdPrefillDesc(ctypes.Structure):
@@ -120,6 +130,8 @@ def _load():
         lib.fd_flat_gemm_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_void_p]
         lib.fd_flat_gemm_pack_weights.restype = ctypes.c_int
+        lib.fd_attn_plan.argtypes = [D, i32p, i32p, i32p, i32p]
+        lib.fd_attn_plan.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -135,13 +147,23 @@ def make_desc(*, batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: i
               num_pages: int = 0, scale: Optional[float] = None, q_dtype: str = "bf16",
               kv_dtype: str = "bf16", out_dtype: str = "f32", head_dim: int = 128,
               k_scale_ptr: int = 0, v_scale_ptr: int = 0, workspace_ptr: int = 0,
-              workspace_bytes: int = 0, stage_events_ptr: int = 0) -> FdAttnDesc:
+              workspace_bytes: int = 0, stage_events_ptr: int = 0, plan: int = 0) -> FdAttnDesc:
     return FdAttnDesc(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, chunk_size,
                       page_size, max_blocks_per_seq, num_pages,
                       -1.0 if scale is None else float(scale), _DTYPE_CODE[q_dtype],
                       _DTYPE_CODE[kv_dtype], _DTYPE_CODE[out_dtype], k_scale_ptr or None,
                       v_scale_ptr or None, workspace_ptr or None, workspace_bytes,
-                      stage_events_ptr or None)
+                      stage_events_ptr or None, int(plan))
+
+
+def fd_attn_plan(desc: FdAttnDesc) -> dict:
+    """The plan the library runs for this descriptor (fd_attn_plan): chunk
+    size, kernel family, kernel shape, and whether the merge is fused."""
+    vals = [ctypes.c_int32() for _ in range(4)]
+    rc = _load().fd_attn_plan(ctypes.byref(desc), *[ctypes.byref(v) for v in vals])
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
+    return dict(zip(("chunk_size", "family", "shape", "fused"), (v.value for v in vals)))
 
 
 def fd_attn_workspace_size(desc: FdAttnDesc) -> int:
@@ -191,7 +213,7 @@ class DecodeCall:
 
 def _marshal_decode(q, k_cache, v_cache, seq_lens, block_table, out, fallback_flags, *,
                     chunk_size, max_seq_len, num_kv_heads, page_size, scale, k_scale, v_scale,
-                    q_dtype, kv_dtype, out_dtype):
+                    q_dtype, kv_dtype, out_dtype, plan=0):
     """Checks the tensors of a decode call; returns (descriptor without a
     workspace, pointers, tensors to keep alive).  Allocates only a missing
     out or fallback_flags."""
@@ -228,7 +250,7 @@ def _marshal_decode(q, k_cache, v_cache, seq_lens, block_table, out, fallback_fl
     desc = make_desc(batch=B, num_q_heads=Hq, num_kv_heads=num_kv_heads, max_seq_len=max_seq_len,
                      chunk_size=chunk_size, page_size=page_size, max_blocks_per_seq=max_blocks,
                      num_pages=num_pages, scale=scale, q_dtype=qd, kv_dtype=kd,
-                     out_dtype=out_dtype, head_dim=D, k_scale_ptr=ks, v_scale_ptr=vs)
+                     out_dtype=out_dtype, head_dim=D, k_scale_ptr=ks, v_scale_ptr=vs, plan=plan)
     table = block_table if page_size else None
     ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
             table.data_ptr() if table is not None else None, out.data_ptr(),
@@ -242,15 +264,16 @@ def prepare_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
                    num_kv_heads: Optional[int] = None, page_size: int = 0,
                    scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
                    q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
-                   out_dtype: str = "f32", stream=None) -> DecodeCall:
+                   out_dtype: str = "f32", stream=None, plan: int = 0) -> DecodeCall:
     """Checks and marshals the arguments of fd_attn_decode (same meaning)
-    once; returns a DecodeCall that enqueues the call each time it is called."""
+    once; returns a DecodeCall that enqueues the call each time it is called.
+    ``plan``: fd_attn_desc_t.plan (0: the library's table)."""
     import torch
     desc, ptrs, keep = _marshal_decode(q, k_cache, v_cache, seq_lens, block_table, out, fallback_flags,
                                        chunk_size=chunk_size, max_seq_len=max_seq_len,
                                        num_kv_heads=num_kv_heads, page_size=page_size, scale=scale,
                                        k_scale=k_scale, v_scale=v_scale, q_dtype=q_dtype,
-                                       kv_dtype=kv_dtype, out_dtype=out_dtype)
+                                       kv_dtype=kv_dtype, out_dtype=out_dtype, plan=plan)
     need = fd_attn_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -264,7 +287,7 @@ def fd_attn_decode_static(q, k_cache, v_cache, seq_lens, block_table, phi: float
                           num_kv_heads: Optional[int] = None, page_size: int = 0,
                           scale: Optional[float] = None, k_scale=None, v_scale=None,
                           q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
-                          out_dtype: Optional[str] = None, stream=None):
+                          out_dtype: Optional[str] = None, stream=None, plan: int = 0):
     """fd_attn_decode_static of include/fd_attn.h: one decode call whose
     workspace is the library's static device array, so nothing is allocated
     here or in the library; ``out`` and ``fallback_flags`` are required.
@@ -278,7 +301,7 @@ def fd_attn_decode_static(q, k_cache, v_cache, seq_lens, block_table, phi: float
                                     chunk_size=chunk_size, max_seq_len=max_seq_len,
                                     num_kv_heads=num_kv_heads, page_size=page_size, scale=scale,
                                     k_scale=k_scale, v_scale=v_scale, q_dtype=q_dtype,
-                                    kv_dtype=kv_dtype, out_dtype=out_dtype)
+                                    kv_dtype=kv_dtype, out_dtype=out_dtype, plan=plan)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     qp, kp, vp, lp, tp, op, fp = ptrs
@@ -294,7 +317,8 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
                    num_kv_heads: Optional[int] = None, page_size: int = 0,
                    scale: Optional[float] = None, k_scale=None, v_scale=None, workspace=None,
                    q_dtype: Optional[str] = None, kv_dtype: Optional[str] = None,
-                   out_dtype: str = "f32", stream=None, stage_events: Optional[Sequence] = None):
+                   out_dtype: str = "f32", stream=None, stage_events: Optional[Sequence] = None,
+                   plan: int = 0):
     """One decode-attention call on device tensors; returns (out, fallback_flags).
 
     Tensors must live on the same GPU.  Layouts as in include/fd_attn.h:
@@ -310,7 +334,7 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
                           fallback_flags, chunk_size=chunk_size, max_seq_len=max_seq_len,
                           num_kv_heads=num_kv_heads, page_size=page_size, scale=scale,
                           k_scale=k_scale, v_scale=v_scale, workspace=workspace, q_dtype=q_dtype,
-                          kv_dtype=kv_dtype, out_dtype=out_dtype, stream=stream)
+                          kv_dtype=kv_dtype, out_dtype=out_dtype, stream=stream, plan=plan)
     return call(stage_events=stage_events)
 
 

@@ -22,8 +22,8 @@ using fd::host::aligned16;
 using fd::host::check_shape;
 
 constexpr size_t kAlign = 256;
-constexpr size_t kFusedMaxUnits = 512;   // grids up to this many units merge in the same launch
-constexpr size_t kFusedWordOffset = 64;  // header word counting a fused call's merged row groups
+constexpr size_t kFusedWordOffset = 64;   // header word counting a fused call's merged row groups
+constexpr size_t kFusedCountOffset = 128; // header word adding up a fused call's recomputed pairs
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -54,12 +54,42 @@ uint32_t next_epoch()
     return e;
 }
 
-// Largest divisor of g that is <= 16: the query heads one MFMA workgroup serves.
-int heads_per_block(int g)
+using fd::host::heads_per_block;
+using fd::host::Plan;
+
+// Kernel shapes of the grouped families, by the plan's shape index (the
+// lists in fd_host.h).
+using ChunkShape0 = fd::chunk::Shape<4, 1, 2>;
+using ChunkShape1 = fd::chunk::Shape<4, 1, 3>;
+using ChunkShape2 = fd::chunk::Shape<2, 1, 3>;
+using CoopShape0 = fd::coop::Shape<2, 1, 3>;
+using CoopShape1 = fd::coop::Shape<4, 1, 3>;
+using CoopShape2 = fd::coop::Shape<2, 1, 4>;
+
+template <typename S, bool PAGED>
+int launch_chunk(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    for (int k = g < 16 ? g : 16; k > 1; --k)
-        if (g % k == 0) return k;
-    return 1;
+    return fd::host::launch(fd::chunk::chunk_kernel<FD_BF16, PAGED, S>, grid, dim3(S::waves * 64), 0, s, e0, e1, p);
+}
+
+template <typename S, bool PAGED>
+int launch_coop(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    return fd::host::launch(fd::coop::chunk_kernel<FD_FP8_E4M3FN, PAGED, S>, grid, dim3(S::waves * 64), 0, s, e0,
+                            e1, p);
+}
+
+template <bool PAGED>
+int dispatch_grouped(const Params &p, int family, int shape, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    if (family == fd::host::kFamGroupedBf16) {
+        if (shape == 1) return launch_chunk<ChunkShape1, PAGED>(p, grid, s, e0, e1);
+        if (shape == 2) return launch_chunk<ChunkShape2, PAGED>(p, grid, s, e0, e1);
+        return launch_chunk<ChunkShape0, PAGED>(p, grid, s, e0, e1);
+    }
+    if (shape == 1) return launch_coop<CoopShape1, PAGED>(p, grid, s, e0, e1);
+    if (shape == 2) return launch_coop<CoopShape2, PAGED>(p, grid, s, e0, e1);
+    return launch_coop<CoopShape0, PAGED>(p, grid, s, e0, e1);
 }
 
 template <int KV, int QT, bool PAGED>
@@ -92,6 +122,21 @@ extern "C" size_t fd_attn_workspace_size(const fd_attn_desc_t *desc)
     const size_t chunk = (size_t)fd::host::chunk_of(desc);
     const size_t maxch = ((size_t)desc->max_seq_len + chunk - 1) / chunk;
     return layout_of((size_t)desc->batch * desc->num_q_heads, maxch).total;
+}
+
+extern "C" int fd_attn_plan(const fd_attn_desc_t *desc, int32_t *chunk_size, int32_t *family, int32_t *shape,
+                            int32_t *fused)
+{
+    if (!desc) return FD_ERR_NULL;
+    const int rc = check_shape(desc);
+    if (rc != FD_OK) return rc;
+    Plan pl;
+    fd::host::plan_of(desc, &pl);
+    if (chunk_size) *chunk_size = pl.chunk;
+    if (family) *family = pl.family;
+    if (shape) *shape = pl.shape;
+    if (fused) *fused = pl.fused;
+    return FD_OK;
 }
 
 extern "C" const char *fd_attn_status_string(int status)
@@ -140,9 +185,11 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
             const int32_t *seq_lens, const int32_t *block_table, float phi, float a, float b, void *out,
             uint8_t *fallback_flags, void *wsp, hipStream_t stream)
 {
-    int rc = FD_OK;
     const int qt = d->q_dtype, kv = d->kv_dtype, ot = d->out_dtype;
-    const int chunk = fd::host::chunk_of(d);
+    Plan pl;
+    int rc = fd::host::plan_of(d, &pl);
+    if (rc != FD_OK) return rc;
+    const int chunk = pl.chunk;
     const int maxch = (d->max_seq_len + chunk - 1) / chunk;
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     const Layout L = layout_of(rows, (size_t)maxch);
@@ -161,6 +208,7 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     p.flags = fallback_flags;
     p.count_word = reinterpret_cast<unsigned long long *>(ws + L.header);
     p.fused_word = reinterpret_cast<unsigned long long *>(ws + L.header + kFusedWordOffset);
+    p.fused_count = reinterpret_cast<unsigned long long *>(ws + L.header + kFusedCountOffset);
     p.rg_count = reinterpret_cast<unsigned long long *>(ws + L.rg_count);
     p.epoch = next_epoch();
     p.o_part = reinterpret_cast<float *>(ws + L.o_part);
@@ -185,42 +233,26 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     p.out_bf16 = ot == FD_BF16;
 
     const bool paged = d->page_size != 0;
-    const bool use_mfma = p.group > 1 && qt == FD_BF16 && kv != FD_F32;
+    const bool use_mfma = pl.family != fd::host::kFamVector;
     // Optional timing: the chunk kernel is launched with start/stop events
     // stamped by its own dispatch packet, so timing adds no marker packets.
     hipEvent_t *ev = d->stage_events;
     hipEvent_t ev0 = ev ? ev[0] : nullptr, ev1 = ev ? ev[1] : nullptr;
 
-    // merge inside the chunk kernel when its grid is at most one round of
-    // workgroups (a latency-bound call, where a second launch would double the
-    // cost); larger grids merge in a separate launch
-    const size_t grid_units = (size_t)maxch * (use_mfma ? p.hq / heads_per_block(p.group) : p.hq) * p.batch;
-    p.fused = grid_units <= kFusedMaxUnits;
+    // the merge runs inside the chunk launch (the last workgroup of each row
+    // group merges it) or in a second launch, as the plan says
+    p.fused = pl.fused;
 
-    using fd::host::launch;
     if (use_mfma) {
         p.heads_per_block = heads_per_block(p.group);
         // One workgroup per unit; workgroups past the real units exit at once.
-        // The unit index is blockIdx.y * gridDim.x + blockIdx.x.  bf16 caches
-        // run the per-wavefront-ring kernel, E4M3FN caches the cooperative
-        // one (each measured the faster for its format).
+        // The unit index is blockIdx.y * gridDim.x + blockIdx.x.
         const size_t units = (size_t)maxch * (p.hq / p.heads_per_block) * p.batch;
         const unsigned gx = (unsigned)(units < ((size_t)1 << 20) ? units : ((size_t)1 << 20));
         const dim3 flat(gx, (unsigned)((units + gx - 1) / gx));
-        using ChunkShape = fd::chunk::DefaultShape;
-        using CoopShape = fd::coop::DefaultShape;
-        const dim3 blk_chunk(ChunkShape::waves * 64), blk_coop(CoopShape::waves * 64);
         p.ngroups = p.batch * (p.hq / p.heads_per_block);
-        if (kv == FD_BF16)
-            rc = paged ? launch(fd::chunk::chunk_kernel<FD_BF16, true, ChunkShape>, flat, blk_chunk, 0, stream,
-                                ev0, ev1, p)
-                       : launch(fd::chunk::chunk_kernel<FD_BF16, false, ChunkShape>, flat, blk_chunk, 0, stream,
-                                ev0, ev1, p);
-        else
-            rc = paged ? launch(fd::coop::chunk_kernel<FD_FP8_E4M3FN, true, CoopShape>, flat, blk_coop, 0,
-                                stream, ev0, ev1, p)
-                       : launch(fd::coop::chunk_kernel<FD_FP8_E4M3FN, false, CoopShape>, flat, blk_coop, 0,
-                                stream, ev0, ev1, p);
+        rc = paged ? dispatch_grouped<true>(p, pl.family, pl.shape, flat, stream, ev0, ev1)
+                   : dispatch_grouped<false>(p, pl.family, pl.shape, flat, stream, ev0, ev1);
     } else {
         p.heads_per_block = 1;
         p.ngroups = p.batch * p.hq;
@@ -233,12 +265,12 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     // ones in a second launch, RW wavefronts per row for rows with many chunks.
     if (!p.fused) {
         if (maxch >= 64)
-            rc = launch(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, nullptr, nullptr, p);
+            rc = fd::host::launch(fd::merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, nullptr, nullptr, p);
         else if (maxch >= 16)
-            rc = launch(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, nullptr,
+            rc = fd::host::launch(fd::merge_kernel<2>, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, nullptr,
                         nullptr, p);
         else
-            rc = launch(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, nullptr,
+            rc = fd::host::launch(fd::merge_kernel<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, nullptr,
                         nullptr, p);
     }
     return rc;

@@ -32,16 +32,6 @@
 
 #include "fd_ring.h"
 
-#ifndef FD_CHUNK_WAVES
-#define FD_CHUNK_WAVES 4
-#endif
-#ifndef FD_CHUNK_SUBTILES
-#define FD_CHUNK_SUBTILES 1
-#endif
-#ifndef FD_CHUNK_STAGES
-#define FD_CHUNK_STAGES 2
-#endif
-
 namespace fd {
 
 namespace chunk {
@@ -64,8 +54,6 @@ struct Shape {
     static_assert(NW * kRedStride * 4 <= lds, "epilogue reduction must fit in the ring");
     static_assert(lds <= 160 * 1024, "LDS per workgroup");
 };
-
-using DefaultShape = Shape<FD_CHUNK_WAVES, FD_CHUNK_SUBTILES, FD_CHUNK_STAGES>;
 
 template <int KV, bool PAGED, typename S>
 __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)

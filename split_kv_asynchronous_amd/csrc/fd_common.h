@@ -32,7 +32,8 @@ struct Params {
     float *m_part;        // [B][Hq][maxch]
     uint8_t *cflag;       // [B][Hq][maxch]
     unsigned long long *count_word;   // {recomputed (row, chunk) pairs, epoch} of the call
-    unsigned long long *fused_word;   // fused merge: {epoch | merged row groups << 16 | recomputed pairs}
+    unsigned long long *fused_word;   // fused merge: {epoch | merged row groups}
+    unsigned long long *fused_count;  // fused merge: {epoch | recomputed (row, chunk) pairs}
     unsigned long long *rg_count;     // [B][Hq] epoch-tagged unit counts per row group (first head)
     uint32_t epoch;                   // this call's epoch (never 0)
     int fused;                        // the last workgroup of a row group merges it (else a merge launch)

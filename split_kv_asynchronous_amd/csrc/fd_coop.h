@@ -42,16 +42,6 @@
 
 #include "fd_ring.h"
 
-#ifndef FD_COOP_WAVES
-#define FD_COOP_WAVES 2
-#endif
-#ifndef FD_COOP_SUBTILES
-#define FD_COOP_SUBTILES 1
-#endif
-#ifndef FD_COOP_STAGES
-#define FD_COOP_STAGES 3
-#endif
-
 namespace fd {
 
 namespace coop {
@@ -73,8 +63,6 @@ struct Shape {
     static_assert((NST - 1) * dma_per_wave < 64, "vmcnt cannot count that deep");
     static_assert(lds <= 64 * 1024, "LDS per workgroup");
 };
-
-using DefaultShape = Shape<FD_COOP_WAVES, FD_COOP_SUBTILES, FD_COOP_STAGES>;
 
 template <int KV, bool PAGED, typename S>
 __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)

@@ -36,16 +36,138 @@ inline int launch(void (*k)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStr
     return e == hipSuccess ? FD_OK : FD_ERR_LAUNCH;
 }
 
-// The chunk size of a call: the descriptor's, or for 0 the pick measured per
-// kernel family on MI355X: 2048 tokens for grouped bf16 queries over a bf16
-// cache (32K GQA workload 5.99 -> 6.26 TB/s against 1024), 1024 otherwise
-// (the paged fp8 and the vector kernels lose at 2048), at least a page.
+// ---- The plan of a decode call: kernel family, chunk size, kernel shape
+// and merge placement.  The table below was measured on MI355X (whole-call
+// time, calls replayed back to back; see kTable); a descriptor can force a
+// shape and a placement (desc->plan) for tuning and tests.
+
+enum { kFamGroupedBf16 = 0, kFamGroupedFp8 = 1, kFamVector = 2 };
+
+// Kernel family: grouped bf16 queries over a bf16 cache run the per-wavefront
+// ring kernel (fd_chunk.h), over an E4M3FN cache the cooperative kernel
+// (fd_coop.h); single queries per KV head and fp32 operands the vector kernel
+// (fd_valu.h).
+inline int family_of(const fd_attn_desc_t *d)
+{
+    const int group = d->num_q_heads / d->num_kv_heads;
+    if (group > 1 && d->q_dtype == FD_BF16 && d->kv_dtype != FD_F32)
+        return d->kv_dtype == FD_BF16 ? kFamGroupedBf16 : kFamGroupedFp8;
+    return kFamVector;
+}
+
+// Largest divisor of g that is <= 16: the query heads one MFMA workgroup serves.
+inline int heads_per_block(int g)
+{
+    for (int k = g < 16 ? g : 16; k > 1; --k)
+        if (g % k == 0) return k;
+    return 1;
+}
+
+// Kernel shapes per family (the shape index of a plan):
+//   grouped bf16: 0 = 4 wavefronts x 2 ring stages, 1 = 4 x 3, 2 = 2 x 3
+//   grouped E4M3FN: 0 = 2 wavefronts x 3 shared stages, 1 = 4 x 3, 2 = 2 x 4
+//   vector: 0 = 4 wavefronts
+constexpr int kShapes[3] = {3, 3, 1};
+
+// One row of the plan table: for calls of `family`, paged or not, whose
+// max_seq_len is at most max_len (rows in ascending max_len; the last row of
+// a family takes every longer call): the chunk size for chunk_size == 0, the
+// kernel shape at that chunk size (other chunk sizes run shape 0), and the
+// largest grid (units of sequence x head block x chunk) that merges inside
+// the chunk launch (kAllUnits: every grid).
+struct TableRow {
+    int family, paged, max_len, chunk, shape;
+    int64_t fused_units;
+};
+
+constexpr int64_t kAllUnits = (int64_t)1 << 62;
+
+// Measured on MI355X: calls replayed back to back (best of 3 x 10), every
+// chunk size 256 .. 4096 x every shape x both merge placements, on ragged
+// synthetic batches of each family, paging and length range (whole-call
+// TB/s of K/V; best against the runner-up):
+//   grouped bf16, 64/8 heads: 256 x U[256,2K] 5.66 (chunk 2048) ; 64 x
+//     U[1K,8K] 6.12 (4096, 4 waves x 3 stages; 2048: 5.94) ; 32 x U[1K,32K]
+//     6.27 (2048; merged in the launch 6.27, at 1024 6.11 both ways) ;
+//     4 x U[32K,128K] 6.11 (1024; 2048: 6.07) ; paged: 5.52, 5.98, 6.24, 5.92
+//   grouped E4M3FN, 32/8 heads: 512 x U[256,2K] 5.02 (1024) ; 64 x
+//     U[512,16K] 5.64 (1024, 2 waves x 4 stages; 3 stages 5.60; 512: 5.37) ;
+//     16 x U[16K,64K] 5.62 (2048) ; paged: 4.90, 5.48, 5.57
+//   one query per KV head, 32 heads: 64 x 2K 6.77 (2048) ; 8 x 8K 6.66
+//     (2048; 1024: 6.37) ; 1 x 128K 6.66 (4096; 1024: 6.60) ; paged: 6.49,
+//     6.35, 6.50
+// The merge inside the chunk launch lost on every large grid (by up to 40%)
+// except the grouped bf16 calls up to 32K, where it ties (within 0.1%) and
+// saves the second launch; small grids (<= 512 units, one round of
+// workgroups) merge in the launch everywhere (a 4K single-head call: 63 ->
+// 37 us).
+inline constexpr TableRow kTable[] = {
+    {kFamGroupedBf16, 0, 2048, 2048, 0, 512},
+    {kFamGroupedBf16, 0, 8192, 4096, 1, 512},
+    {kFamGroupedBf16, 0, 32768, 2048, 0, kAllUnits},
+    {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 512},
+    {kFamGroupedBf16, 1, 2048, 2048, 0, 512},
+    {kFamGroupedBf16, 1, 8192, 4096, 1, 512},
+    {kFamGroupedBf16, 1, 32768, 2048, 0, kAllUnits},
+    {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 512},
+    {kFamGroupedFp8, 0, 2048, 1024, 0, 512},
+    {kFamGroupedFp8, 0, 16384, 1024, 2, 512},
+    {kFamGroupedFp8, 0, 1 << 23, 2048, 0, 512},
+    {kFamGroupedFp8, 1, 2048, 1024, 0, 512},
+    {kFamGroupedFp8, 1, 16384, 1024, 2, 512},
+    {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 512},
+    {kFamVector, 0, 2048, 2048, 0, 512},
+    {kFamVector, 0, 8192, 2048, 0, 512},
+    {kFamVector, 0, 1 << 23, 4096, 0, 512},
+    {kFamVector, 1, 2048, 2048, 0, 512},
+    {kFamVector, 1, 8192, 2048, 0, 512},
+    {kFamVector, 1, 1 << 23, 4096, 0, 512},
+};
+
+inline const TableRow &table_row(const fd_attn_desc_t *d)
+{
+    const int fam = family_of(d), paged = d->page_size != 0;
+    const TableRow *last = nullptr;
+    for (const TableRow &r : kTable) {
+        if (r.family != fam || r.paged != paged) continue;
+        last = &r;
+        if (d->max_seq_len <= r.max_len) return r;
+    }
+    return *last;
+}
+
+// The chunk size of a call: the descriptor's, or for 0 the table's (at least
+// a page).
 inline int chunk_of(const fd_attn_desc_t *d)
 {
     if (d->chunk_size != 0) return d->chunk_size;
-    const int group = d->num_kv_heads > 0 ? d->num_q_heads / d->num_kv_heads : 1;
-    int c = (group > 1 && d->q_dtype == FD_BF16 && d->kv_dtype == FD_BF16) ? 2048 : 1024;
+    const int c = table_row(d).chunk;
     return d->page_size > c ? d->page_size : c;
+}
+
+struct Plan {
+    int family, chunk, shape, fused;
+};
+
+// The plan of a call whose shape has passed check_shape(); FD_ERR_SHAPE for
+// a forced shape or placement the family does not have.
+inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
+{
+    const TableRow &r = table_row(d);
+    pl->family = family_of(d);
+    pl->chunk = chunk_of(d);
+    const int forced_shape = (d->plan & FD_PLAN_SHAPE_MASK) - 1;
+    if (forced_shape >= kShapes[pl->family]) return FD_ERR_SHAPE;
+    pl->shape = forced_shape >= 0 ? forced_shape : (pl->chunk == r.chunk ? r.shape : 0);
+    const int place = d->plan & (FD_PLAN_FUSED | FD_PLAN_SPLIT);
+    if (place == (FD_PLAN_FUSED | FD_PLAN_SPLIT) || (d->plan & ~(FD_PLAN_SHAPE_MASK | FD_PLAN_FUSED | FD_PLAN_SPLIT)))
+        return FD_ERR_SHAPE;
+    const int64_t maxch = ((int64_t)d->max_seq_len + pl->chunk - 1) / pl->chunk;
+    const int blocks = pl->family == kFamVector ? d->num_q_heads
+                                                : d->num_q_heads / heads_per_block(d->num_q_heads / d->num_kv_heads);
+    const int64_t units = maxch * blocks * d->batch;
+    pl->fused = place == FD_PLAN_FUSED ? 1 : place == FD_PLAN_SPLIT ? 0 : units <= r.fused_units;
+    return FD_OK;
 }
 
 // Shape checks shared by the size query and the call.
@@ -68,7 +190,8 @@ inline int check_shape(const fd_attn_desc_t *d)
     const int64_t slots = (int64_t)d->batch * d->num_q_heads * maxch;
     if (slots >= ((int64_t)1 << 31) || maxch >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
     if ((int64_t)d->batch * d->num_q_heads >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
-    return FD_OK;
+    Plan pl;
+    return plan_of(d, &pl);
 }
 
 }  // namespace host

@@ -230,16 +230,20 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
     for (int r = wave; r < nrows; r += NW) mine += merge_row(p, b, h0 + r, lane);
     if (lane == 0 && mine) atomicAdd(&total, mine);
     __syncthreads();
-    // One add per row group into the call's fused word: merged row groups in
-    // bits 16..31, recomputed pairs in bits 0..15 (a fused grid has at most
-    // 512 units of at most 16 heads, so neither field overflows).  The last
-    // row group publishes the count and resets the word, so a replay of the
-    // launch with the same epoch starts from zero.
+    // The row group's recomputed pairs go into the call's fused count, then
+    // (once that add has completed) one into the count of merged row groups;
+    // the last row group publishes the call's count and resets both words, so
+    // a replay of the launch with the same epoch starts from zero.
     if (threadIdx.x == 0) {
-        const uint32_t v = epoch_add(p.fused_word, p.epoch, (1u << 16) | (uint32_t)total);
-        if ((int)(v >> 16) == p.ngroups) {
-            put(p.count_word, ((unsigned long long)p.epoch << 32) | (v & 0xffffu));
+        if (total) epoch_add(p.fused_count, p.epoch, (uint32_t)total);
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint32_t n = epoch_add(p.fused_word, p.epoch, 1);
+        if ((int)n == p.ngroups) {
+            const unsigned long long c = get(p.fused_count);
+            const uint32_t cnt = (uint32_t)(c >> 32) == p.epoch ? (uint32_t)c : 0u;
+            put(p.count_word, ((unsigned long long)p.epoch << 32) | cnt);
             put(p.fused_word, (unsigned long long)p.epoch << 32);
+            put(p.fused_count, (unsigned long long)p.epoch << 32);
         }
     }
 }

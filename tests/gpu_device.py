@@ -18,8 +18,9 @@ def to_device(arr, kind):
 class DeviceProblem:
     """A synthetic problem resident in GPU memory (inputs, workspace, outputs)."""
 
-    def __init__(self, prob, out_dtype="f32"):
+    def __init__(self, prob, out_dtype="f32", plan=0):
         self.prob = prob
+        self.plan = plan
         self.q = to_device(prob.q, prob.q_dtype)
         self.k = to_device(prob.k_cache, prob.kv_dtype)
         self.v = to_device(prob.v_cache, prob.kv_dtype)
@@ -44,7 +45,8 @@ class DeviceProblem:
                             page_size=p.page_size,
                             max_blocks_per_seq=0 if p.block_table is None else p.block_table.shape[1],
                             num_pages=p.k_cache.shape[0] if p.page_size else 0, scale=p.scale,
-                            q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, out_dtype=self.out_dtype)
+                            q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, out_dtype=self.out_dtype,
+                            plan=self.plan)
 
     def run(self, phi=None, a=None, b=None, stream=None, stage_events=None):
         # arguments are marshalled once per workspace (tests may swap it)
@@ -56,7 +58,7 @@ class DeviceProblem:
                 self.out, self.flags, chunk_size=p.chunk_size, max_seq_len=p.max_seq_len,
                 num_kv_heads=p.num_kv_heads, page_size=p.page_size, scale=p.scale,
                 k_scale=self.k_scale, v_scale=self.v_scale, workspace=self.workspace,
-                q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, out_dtype=self.out_dtype)
+                q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, out_dtype=self.out_dtype, plan=self.plan)
         return call(phi=phi, a=a, b=b, stream=stream, stage_events=stage_events)
 
     def results(self):

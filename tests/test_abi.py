@@ -24,7 +24,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_decode_static", "fd_attn_prefill",
+    assert names == ["fd_attn_choose_band", "fd_attn_decode", "fd_attn_decode_static", "fd_attn_plan",
+                     "fd_attn_prefill",
                      "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size",
                      "fd_flat_gemm", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
                      "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size"]
@@ -275,13 +276,64 @@ def test_flat_gemm_table_covers_the_7b_layers():
                     assert 5 <= p["variant"] <= 12
 
 
-def test_chunk_size_zero_is_the_library_pick():
-    # grouped bf16 queries over a bf16 cache: 2048; the other kernels: 1024
-    for kw, chunk in [(dict(), 2048), (dict(kv_dtype="e4m3fn", page_size=16, max_blocks_per_seq=2048,
-                                           num_pages=5), 1024),
-                      (dict(num_kv_heads=64), 1024), (dict(q_dtype="f32"), 1024)]:
-        auto = fd.fd_attn_workspace_size(_desc(chunk_size=0, **kw))
-        assert auto > 0 and auto == fd.fd_attn_workspace_size(_desc(chunk_size=chunk, **kw)), kw
+# The plan table (measured on MI355X; the rows of fd_host.h): per kernel
+# family, paging and max_seq_len range, the chunk size for chunk_size = 0, the
+# kernel shape at that chunk, and whether a large grid merges in the launch.
+FAMILY_KW = {0: dict(), 1: dict(kv_dtype="e4m3fn"), 2: dict(num_kv_heads=64)}
+PLAN_ROWS = [
+    # family, paged, max_seq_len probes, chunk, shape, large grid merged in the launch
+    (0, 0, (1, 2048), 2048, 0, False), (0, 0, (2049, 8192), 4096, 1, False),
+    (0, 0, (8193, 32768), 2048, 0, True), (0, 0, (32769, 1 << 20), 1024, 0, False),
+    (0, 1, (16, 2048), 2048, 0, False), (0, 1, (2064, 8192), 4096, 1, False),
+    (0, 1, (8208, 32768), 2048, 0, True), (0, 1, (32784, 1 << 20), 2048, 0, False),
+    (1, 0, (1, 2048), 1024, 0, False), (1, 0, (2049, 16384), 1024, 2, False),
+    (1, 0, (16385, 1 << 20), 2048, 0, False),
+    (1, 1, (16, 2048), 1024, 0, False), (1, 1, (2064, 16384), 1024, 2, False),
+    (1, 1, (16400, 1 << 20), 2048, 0, False),
+    (2, 0, (1, 2048), 2048, 0, False), (2, 0, (2049, 8192), 2048, 0, False),
+    (2, 0, (8193, 1 << 20), 4096, 0, False),
+    (2, 1, (16, 2048), 2048, 0, False), (2, 1, (2064, 8192), 2048, 0, False),
+    (2, 1, (8208, 1 << 20), 4096, 0, False),
+]
+
+
+@pytest.mark.parametrize("fam,paged,lens,chunk,shape,fused_big", PLAN_ROWS)
+def test_plan_table(fam, paged, lens, chunk, shape, fused_big):
+    for L in lens:
+        kw = dict(FAMILY_KW[fam], max_seq_len=L, chunk_size=0, batch=256)
+        if paged:
+            kw.update(page_size=16, max_blocks_per_seq=-(-L // 16), num_pages=5)
+        d = _desc(**kw)
+        got = fd.fd_attn_plan(d)
+        big = -(-L // chunk) * 256 * (8 if fam != 2 else 64) > 512
+        assert got == dict(chunk_size=max(chunk, 16 if paged else 0), family=fam, shape=shape,
+                           fused=int(fused_big or not big)), (kw, got)
+        # the workspace follows the plan's chunk
+        assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
+        # an explicit chunk size other than the table's runs shape 0
+        other = 512 if chunk != 512 else 256
+        assert fd.fd_attn_plan(_desc(**dict(kw, chunk_size=other)))["shape"] == 0
+
+
+def test_plan_small_grids_merge_in_the_launch_and_forced_plans():
+    small = _desc(batch=1, num_q_heads=8, num_kv_heads=1, max_seq_len=4096, chunk_size=1024)
+    assert fd.fd_attn_plan(small)["fused"] == 1
+    big = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=512)
+    assert fd.fd_attn_plan(big) == dict(chunk_size=512, family=1, shape=0, fused=0)
+    forced = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=512,
+                   plan=fd.FD_PLAN_SHAPE(2) | fd.FD_PLAN_FUSED)
+    assert fd.fd_attn_plan(forced) == dict(chunk_size=512, family=1, shape=2, fused=1)
+    split = _desc(batch=1, num_q_heads=8, num_kv_heads=1, max_seq_len=4096, chunk_size=1024,
+                  plan=fd.FD_PLAN_SPLIT)
+    assert fd.fd_attn_plan(split)["fused"] == 0
+    # a shape the family does not have, both placements, unknown bits: rejected
+    for bad in (fd.FD_PLAN_SHAPE(3), fd.FD_PLAN_FUSED | fd.FD_PLAN_SPLIT, 0x40):
+        d = _desc(plan=bad)
+        assert fd.fd_attn_workspace_size(d) == 0
+        with pytest.raises(fd.FdAttnError):
+            fd.fd_attn_plan(d)
+        assert _call(_valid_desc(plan=bad)) == -2
+    assert _call(_valid_desc(num_kv_heads=64, plan=fd.FD_PLAN_SHAPE(1))) == -2   # vector: one shape
 
 
 def test_static_workspace_variant_checks_before_the_gpu():

@@ -249,3 +249,71 @@ def test_prepared_call_equals_direct_call():
     valid = torch.from_numpy(prob.seq_lens > 0).cuda()
     assert torch.equal(direct[1][1].bool(), valid[:, None].expand(-1, prob.num_q_heads))
     assert not bool(direct[0][1].any())
+
+
+SHAPE_CASES = [
+    # group, kv dtype, page size, kernel shapes of the family
+    (8, "bf16", 0, 3),
+    (4, "bf16", 16, 3),
+    (4, "e4m3fn", 16, 3),
+    (8, "e4m3fn", 0, 3),
+    (1, "bf16", 0, 1),
+    (1, "e4m3fn", 32, 1),
+]
+
+
+@pytest.mark.parametrize("g,kv,page,nshapes", SHAPE_CASES)
+def test_every_kernel_shape_and_merge_placement(g, kv, page, nshapes):
+    # every shape of the family with the merge forced into the chunk launch
+    # and into a second launch; a narrow band sends chunks to the recompute
+    import split_kv_asynchronous_amd as fd
+    prob = synthetic.make_problem(batch=3, num_q_heads=2 * g, num_kv_heads=2, seq_lens=[1000, 37, 2200],
+                                  kv_dtype=kv, page_size=page, chunk_size=256, phi=1.0, a=3.0, b=1.5,
+                                  seed=900 + g)
+    ref_out, ref_flags, margin = oracle.decode_exact(**prob.args())
+    sure = margin >= 1e-3
+    for shape in range(nshapes):
+        for place in (fd.FD_PLAN_FUSED, fd.FD_PLAN_SPLIT):
+            plan = fd.FD_PLAN_SHAPE(shape) | place
+            print("case g=%d kv=%s page=%d shape=%d %s" % (g, kv, page, shape,
+                                                           "fused" if place == fd.FD_PLAN_FUSED else "split"),
+                  flush=True)
+            dp = DeviceProblem(prob, plan=plan)
+            got = fd.fd_attn_plan(dp.desc())
+            assert got["shape"] == shape and got["fused"] == (place == fd.FD_PLAN_FUSED)
+            dp.run()
+            out, flags = dp.results()
+            np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+            compare(prob, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
+            assert dp.recomputed() > 0
+
+
+TABLE_CASES = [
+    # one call per row of the plan table (chunk_size = 0): group, kv dtype,
+    # page size, sequence lengths, max_seq_len (selects the row)
+    (8, "bf16", 0, [2000, 1], 2048), (8, "bf16", 0, [5000, 300], 8192),
+    (8, "bf16", 0, [20000, 9000], 32768), (8, "bf16", 0, [35000, 777], 40000),
+    (4, "bf16", 16, [2048, 100], 2048), (4, "bf16", 16, [6000, 31], 8192),
+    (4, "bf16", 16, [30000, 0], 32768), (4, "bf16", 16, [34000, 2000], 36000),
+    (4, "e4m3fn", 0, [1500, 2048], 2048), (4, "e4m3fn", 0, [16000, 9], 16384),
+    (4, "e4m3fn", 0, [20000, 1], 24000),
+    (8, "e4m3fn", 16, [777, 2048], 2048), (8, "e4m3fn", 16, [12000, 4000], 16384),
+    (8, "e4m3fn", 16, [17000, 0], 20000),
+    (1, "bf16", 0, [2048, 1000], 2048), (1, "bf16", 0, [8000, 3], 8192),
+    (1, "bf16", 0, [9000, 12000], 12000),
+    (1, "bf16", 16, [1024, 2000], 2048), (1, "bf16", 16, [7000, 0], 8192),
+    (1, "f32", 16, [10000, 64], 10000),
+]
+
+
+@pytest.mark.parametrize("g,kv,page,lens,cap", TABLE_CASES)
+def test_plan_table_rows(g, kv, page, lens, cap):
+    import split_kv_asynchronous_amd as fd
+    prob = synthetic.make_problem(batch=len(lens), num_q_heads=2 * g, num_kv_heads=2, seq_lens=lens,
+                                  kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", page_size=page,
+                                  chunk_size=0, max_seq_len=cap, seed=950 + g)
+    dp = DeviceProblem(prob)
+    plan = fd.fd_attn_plan(dp.desc())
+    print("case table g=%d kv=%s page=%d cap=%d -> %s" % (g, kv, page, cap, plan), flush=True)
+    dp.run()
+    compare(prob, *dp.results())
