@@ -225,12 +225,14 @@ class _PrefillProblem(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("q_len", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("scale", ctypes.c_double)]
 
 
 class _PrefillInputs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("kv_lens", ctypes.c_void_p)]
+                ("kv_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 def _load_prefill():
@@ -249,24 +251,49 @@ def _load_prefill():
     return lib
 
 
-def _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale):
+def _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale, block_table=None,
+                     page_size=0, max_seq_len=None, k_scale=None, v_scale=None):
     q = np.ascontiguousarray(q, dtype=_NP_DT[q_dtype])
     k = np.ascontiguousarray(k, dtype=_NP_DT[kv_dtype])
     v = np.ascontiguousarray(v, dtype=_NP_DT[kv_dtype])
     kv_lens = np.ascontiguousarray(kv_lens, dtype=np.int32)
-    if kv_dtype == "e4m3fn" or q_dtype == "e4m3fn":
-        raise ValueError("prefill takes f32 or bf16 operands")
+    if q_dtype == "e4m3fn":
+        raise ValueError("prefill queries are f32 or bf16")
     B, Hq, Lq, D = q.shape
     if Hq % num_kv_heads:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
-    if k.ndim != 4 or k.shape[:2] != (B, num_kv_heads) or k.shape[3] != D or v.shape != k.shape:
-        raise ValueError("k and v must be [B][Hkv][max_seq_len][D]")
+    if k.ndim != 4 or k.shape[1] != num_kv_heads or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("k and v must be [B][Hkv][max_seq_len][D] or [pages][Hkv][page_size][D]")
     if kv_lens.shape != (B,):
         raise ValueError("kv_lens must have shape [batch]")
-    prob = _PrefillProblem(B, Hq, num_kv_heads, D, k.shape[2], Lq, _DT[q_dtype], _DT[kv_dtype],
-                           float(scale))
-    keep = (q, k, v, kv_lens)
-    return prob, _PrefillInputs(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens)), keep
+    max_blocks = 0
+    if page_size:
+        if block_table is None or k.shape[2] != page_size:
+            raise ValueError("paged K/V need a block table and [pages][Hkv][page_size][D] caches")
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        max_blocks = block_table.shape[1]
+        if max_seq_len is None or max_blocks * page_size < max_seq_len:
+            raise ValueError("paged K/V need max_seq_len <= max_blocks * page_size")
+    else:
+        if k.shape[0] != B:
+            raise ValueError("contiguous K/V are [B][Hkv][max_seq_len][D]")
+        max_seq_len = k.shape[2]
+        block_table = None
+    if kv_dtype == "e4m3fn":
+        if k_scale is None or v_scale is None:
+            raise ValueError("E4M3FN caches need k_scale and v_scale")
+        k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+        v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+    else:
+        k_scale = v_scale = None
+    prob = _PrefillProblem(B, Hq, num_kv_heads, D, int(max_seq_len), Lq, _DT[q_dtype], _DT[kv_dtype],
+                           int(page_size), int(max_blocks), float(scale))
+    keep = (q, k, v, kv_lens, block_table, k_scale, v_scale)
+    ins = _PrefillInputs(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens),
+                         None if block_table is None else _ptr(block_table),
+                         None if k_scale is None else _ptr(k_scale),
+                         None if v_scale is None else _ptr(v_scale))
+    return prob, ins, keep
 
 
 def _prefill_rows(rows, total):
@@ -279,16 +306,21 @@ def _prefill_rows(rows, total):
 
 
 def prefill_exact(q, k, v, kv_lens, *, num_kv_heads, q_dtype="bf16", kv_dtype="bf16", scale,
-                  phi, a, b, rows=None, with_threads=False):
+                  phi, a, b, rows=None, with_threads=False, block_table=None, page_size=0,
+                  max_seq_len=None, k_scale=None, v_scale=None):
     """Exact causal softmax attention of a query block + band flags, float64.
 
-    q [B][Hq][Lq][D]; k, v [B][Hkv][max_seq_len][D].  Query j of sequence b sits
-    at position kv_lens[b] - Lq + j and sees keys 0..position (none if negative).
-    Rows are ids (b * Hq + h) * Lq + j (default: all, in order).  Returns
-    (out [nrows][D], flags [nrows] uint8, margin [nrows]); margin is the smallest
-    distance of a visible score to a band edge.
+    q [B][Hq][Lq][D]; k, v contiguous [B][Hkv][max_seq_len][D] or, with
+    page_size > 0, paged [pages][Hkv][page_size][D] with block_table
+    [B][max_blocks] (max_seq_len then given); E4M3FN K/V codes are multiplied
+    by k_scale / v_scale [Hkv].  Query j of sequence b sits at position
+    kv_lens[b] - Lq + j and sees keys 0..position (none if negative).  Rows
+    are ids (b * Hq + h) * Lq + j (default: all, in order).  Returns
+    (out [nrows][D], flags [nrows] uint8, margin [nrows]); margin is the
+    smallest distance of a visible score to a band edge.
     """
-    prob, ins, keep = _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale)
+    prob, ins, keep = _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale,
+                                       block_table, page_size, max_seq_len, k_scale, v_scale)
     B, Hq, Lq, D = keep[0].shape
     rows, n = _prefill_rows(rows, B * Hq * Lq)
     out = np.zeros((n, D), dtype=np.float64)
@@ -300,11 +332,14 @@ def prefill_exact(q, k, v, kv_lens, *, num_kv_heads, q_dtype="bf16", kv_dtype="b
 
 
 def prefill_unified(q, k, v, kv_lens, *, num_kv_heads, q_dtype="bf16", kv_dtype="bf16", scale,
-                    phi, a, b, tile, rows=None):
+                    phi, a, b, tile, rows=None, block_table=None, page_size=0, max_seq_len=None,
+                    k_scale=None, v_scale=None):
     """The method's steps for a causal query block, float64: key tiles of `tile`
     tokens reduced against phi, online-softmax redo of a tile with a visible
-    out-of-band score, merge.  Returns (out, flags, redone tiles [nrows] int32)."""
-    prob, ins, keep = _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale)
+    out-of-band score, merge.  Cache layouts as prefill_exact.  Returns (out,
+    flags, redone tiles [nrows] int32)."""
+    prob, ins, keep = _marshal_prefill(q, k, v, kv_lens, num_kv_heads, q_dtype, kv_dtype, scale,
+                                       block_table, page_size, max_seq_len, k_scale, v_scale)
     B, Hq, Lq, D = keep[0].shape
     rows, n = _prefill_rows(rows, B * Hq * Lq)
     out = np.zeros((n, D), dtype=np.float64)

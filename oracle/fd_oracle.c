@@ -358,7 +358,11 @@ int orc_decode_unified(const orc_problem *p, const orc_inputs *in, int chunk, do
  * tokens at once).  Layouts and reading:
  *
  *   q, out   [B][Hq][Lq][D]      flags [B][Hq][Lq]
- *   K/V      [B][Hkv][max_seq_len][D], contiguous
+ *   K/V      contiguous [B][Hkv][max_seq_len][D], or paged
+ *            [pages][Hkv][page_size][D] with token t of sequence b in page
+ *            block_table[b][t / page_size], slot t % page_size (the decode
+ *            cache layouts); E4M3FN codes times the per-KV-head k_scale /
+ *            v_scale (the symmetric scale of the quantisation page)
  *   query j of sequence b sits at position pos = kv_lens[b] - Lq + j
  *   (kv_lens clamped to [0, max_seq_len]) and attends keys t = 0 .. pos;
  *   a query with pos < 0 has no key: zero row, flag 0.
@@ -373,14 +377,27 @@ int orc_decode_unified(const orc_problem *p, const orc_inputs *in, int chunk, do
 typedef struct {
     int32_t batch, num_q_heads, num_kv_heads, head_dim;
     int32_t max_seq_len, q_len;
-    int32_t q_dtype, kv_dtype;       /* ORC_F32 or ORC_BF16 */
+    int32_t q_dtype, kv_dtype;       /* q: ORC_F32 or ORC_BF16; K/V: also ORC_E4M3FN */
+    int32_t page_size;               /* 0 = contiguous */
+    int32_t max_blocks_per_seq;      /* row stride of block_table */
     double scale;
 } orc_prefill_problem;
 
 typedef struct {
     const void *q, *k, *v;
-    const int32_t *kv_lens;
+    const int32_t *kv_lens, *block_table;
+    const float *k_scale, *v_scale;  /* [Hkv], E4M3FN only */
 } orc_prefill_inputs;
+
+/* element offset of (sequence b, kv head kvh, key t, component 0) */
+static size_t prefill_kv_offset(const orc_prefill_problem *p, const orc_prefill_inputs *in, int b, int kvh,
+                                int t)
+{
+    if (p->page_size == 0)
+        return (((size_t)b * p->num_kv_heads + kvh) * p->max_seq_len + t) * p->head_dim;
+    int32_t page = in->block_table[(size_t)b * p->max_blocks_per_seq + t / p->page_size];
+    return (((size_t)page * p->num_kv_heads + kvh) * p->page_size + t % p->page_size) * p->head_dim;
+}
 
 /* keys visible to query j of sequence b */
 static int prefill_keys(const orc_prefill_problem *p, const orc_prefill_inputs *in, int b, int j)
@@ -398,13 +415,14 @@ static void prefill_scores(const orc_prefill_problem *p, const orc_prefill_input
 {
     const int D = p->head_dim;
     const int kvh = h / (p->num_q_heads / p->num_kv_heads);
+    const double ks = (p->kv_dtype == ORC_E4M3FN) ? (double)in->k_scale[kvh] : 1.0;
     double *qd = malloc(sizeof(double) * D);
     for (int d = 0; d < D; d++)
         qd[d] = elem(in->q, (((size_t)b * p->num_q_heads + h) * p->q_len + j) * D + d, p->q_dtype);
     for (int t = 0; t < n; t++) {
-        size_t off = (((size_t)b * p->num_kv_heads + kvh) * p->max_seq_len + t) * D;
+        size_t off = prefill_kv_offset(p, in, b, kvh, t);
         double acc = 0.0;
-        for (int d = 0; d < D; d++) acc += qd[d] * elem(in->k, off + d, p->kv_dtype);
+        for (int d = 0; d < D; d++) acc += qd[d] * (ks * elem(in->k, off + d, p->kv_dtype));
         s[t] = p->scale * acc;
     }
     free(qd);
@@ -413,8 +431,10 @@ static void prefill_scores(const orc_prefill_problem *p, const orc_prefill_input
 static void prefill_value(const orc_prefill_problem *p, const orc_prefill_inputs *in, int b, int kvh,
                           int t, double r, double w, double *acc)
 {
-    const size_t off = (((size_t)b * p->num_kv_heads + kvh) * p->max_seq_len + t) * p->head_dim;
-    for (int d = 0; d < p->head_dim; d++) acc[d] = acc[d] * r + w * elem(in->v, off + d, p->kv_dtype);
+    const size_t off = prefill_kv_offset(p, in, b, kvh, t);
+    const double vs = (p->kv_dtype == ORC_E4M3FN) ? (double)in->v_scale[kvh] : 1.0;
+    for (int d = 0; d < p->head_dim; d++)
+        acc[d] = acc[d] * r + w * (vs * elem(in->v, off + d, p->kv_dtype));
 }
 
 /* row = (b * Hq + h) * Lq + j */

@@ -418,18 +418,28 @@ PREFILL_CONFIGS = {
 
 @dataclasses.dataclass
 class PrefillProblem:
-    """One prefill call's inputs (bf16 bit patterns or float32, host arrays)."""
-    q: np.ndarray                 # [B][Hq][Lq][D]
-    k: np.ndarray                 # [B][Hkv][max_seq_len][D]
+    """One prefill call's inputs (storage formats, host arrays)."""
+    q: np.ndarray                 # [B][Hq][Lq][D]; bf16 bit patterns or float32
+    k: np.ndarray                 # contiguous [B][Hkv][max_seq_len][D] or paged [pages][Hkv][P][D]
     v: np.ndarray
     kv_lens: np.ndarray           # int32 [B]
     num_kv_heads: int
-    dtype: str                    # "bf16" | "f32" (queries and keys/values alike)
+    dtype: str                    # queries: "bf16" | "f32"
     scale: float
     phi: float
     a: float
     b: float
     workload: str = "custom"
+    kv_dtype: Optional[str] = None         # cache format ("bf16" | "f32" | "e4m3fn"); None: as dtype
+    page_size: int = 0
+    block_table: Optional[np.ndarray] = None   # int32 [B][max_blocks] (paged)
+    paged_max_seq_len: int = 0                 # max_seq_len of a paged cache
+    k_scale: Optional[np.ndarray] = None       # float32 [Hkv] (E4M3FN)
+    v_scale: Optional[np.ndarray] = None
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def batch(self) -> int:
@@ -449,7 +459,7 @@ class PrefillProblem:
 
     @property
     def max_seq_len(self) -> int:
-        return self.k.shape[2]
+        return self.paged_max_seq_len if self.page_size else self.k.shape[2]
 
     def visible_pairs(self) -> int:
         """(query, key) pairs that are attended, summed over heads."""
@@ -459,25 +469,39 @@ class PrefillProblem:
 
     def args(self) -> dict:
         """Keyword arguments shared by the oracle and the library binding."""
-        return dict(q=self.q, k=self.k, v=self.v, kv_lens=self.kv_lens,
-                    num_kv_heads=self.num_kv_heads, q_dtype=self.dtype, kv_dtype=self.dtype,
-                    scale=self.scale, phi=self.phi, a=self.a, b=self.b)
+        a = dict(q=self.q, k=self.k, v=self.v, kv_lens=self.kv_lens,
+                 num_kv_heads=self.num_kv_heads, q_dtype=self.dtype, kv_dtype=self.cache_dtype,
+                 scale=self.scale, phi=self.phi, a=self.a, b=self.b)
+        if self.page_size:
+            a.update(block_table=self.block_table, page_size=self.page_size,
+                     max_seq_len=self.max_seq_len)
+        if self.cache_dtype == "e4m3fn":
+            a.update(k_scale=self.k_scale, v_scale=self.v_scale)
+        return a
 
 
 def make_prefill(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int, kv_lens,
                  dtype: str = "bf16", phi: float = 4.0, a: float = 20.0, b: float = 6.0,
                  max_seq_len: Optional[int] = None, scale: Optional[float] = None,
                  head_dim: int = HEAD_DIM, seed: int = SEED_BASE + 100,
-                 workload: str = "custom", value_sigma: float = 1.0) -> PrefillProblem:
+                 workload: str = "custom", value_sigma: float = 1.0, kv_dtype: Optional[str] = None,
+                 page_size: int = 0, extra_pages: int = 0) -> PrefillProblem:
     """Draw one prefill problem: N(0, value_sigma^2) queries, keys and values;
-    keys/values drawn for the first kv_lens[b] positions, zero beyond."""
+    keys/values drawn for the first kv_lens[b] positions, zero beyond.  The
+    cache is stored as kv_dtype (default: dtype; E4M3FN with a per-KV-head
+    scale max|x| / 448 as in make_problem), contiguous or in pages of
+    page_size tokens with a seeded page permutation (unused slots zero).  The
+    float32 draws are the same for every format and layout."""
     if np.isscalar(kv_lens):
         kv_lens = np.full(batch, int(kv_lens), dtype=np.int32)
     kv_lens = np.asarray(kv_lens, dtype=np.int32)
     assert kv_lens.shape == (batch,)
     assert num_q_heads % num_kv_heads == 0
+    kvd = kv_dtype or dtype
     if max_seq_len is None:
         max_seq_len = max(1, int(kv_lens.max(initial=0)))
+    if page_size:
+        max_seq_len = -(-max_seq_len // page_size) * page_size
     D = head_dim
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -488,8 +512,8 @@ def make_prefill(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int,
         return x if dtype == "f32" else bf16_round(x)
 
     q = np.zeros((batch, num_q_heads, q_len, D), dtype=sdt)
-    k = np.zeros((batch, num_kv_heads, max_seq_len, D), dtype=sdt)
-    v = np.zeros_like(k)
+    kf = np.zeros((batch, num_kv_heads, max_seq_len, D), dtype=np.float32)
+    vf = np.zeros_like(kf)
     sig = np.float32(value_sigma)
 
     def fill_q(job):
@@ -499,15 +523,51 @@ def make_prefill(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int,
     def fill_kv(job):
         b_, h = job
         n = int(lens[b_])
-        k[b_, h, :n] = conv(_draw_kv_rows(seed, _S_PK, b_, h, n, D) * sig)
-        v[b_, h, :n] = conv(_draw_kv_rows(seed, _S_PV, b_, h, n, D) * sig)
+        kf[b_, h, :n] = _draw_kv_rows(seed, _S_PK, b_, h, n, D) * sig
+        vf[b_, h, :n] = _draw_kv_rows(seed, _S_PV, b_, h, n, D) * sig
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill_q, [(b_, h) for b_ in range(batch) for h in range(num_q_heads)]))
         list(ex.map(fill_kv, [(b_, h) for b_ in range(batch) for h in range(num_kv_heads)]))
+
+    k_scale = v_scale = None
+    if kvd == "e4m3fn":
+        mk = np.abs(kf).max(axis=(0, 2, 3))
+        mv = np.abs(vf).max(axis=(0, 2, 3))
+        k_scale = np.where(mk > 0, mk / 448.0, 1.0).astype(np.float32)
+        v_scale = np.where(mv > 0, mv / 448.0, 1.0).astype(np.float32)
+        k = e4m3fn_encode(kf / k_scale[None, :, None, None])
+        v = e4m3fn_encode(vf / v_scale[None, :, None, None])
+    elif kvd == "bf16":
+        k, v = bf16_round(kf), bf16_round(vf)
+    else:
+        k, v = kf, vf
+    del kf, vf
+
+    block_table = None
+    if page_size:
+        P = page_size
+        pages_per_seq = [-(-int(n) // P) for n in lens]
+        pool = int(sum(pages_per_seq)) + int(extra_pages)
+        perm = _rng(seed, _S_PERM).permutation(pool).astype(np.int32)
+        block_table = np.full((batch, max(1, max_seq_len // P)), -1, dtype=np.int32)
+        kp = np.zeros((max(1, pool), num_kv_heads, P, D), dtype=k.dtype)
+        vp = np.zeros_like(kp)
+        nxt = 0
+        for b_ in range(batch):
+            for blk in range(pages_per_seq[b_]):
+                pg = perm[nxt]
+                nxt += 1
+                block_table[b_, blk] = pg
+                t0, t1 = blk * P, min(int(lens[b_]), (blk + 1) * P)
+                kp[pg, :, :t1 - t0] = k[b_, :, t0:t1]
+                vp[pg, :, :t1 - t0] = v[b_, :, t0:t1]
+        k, v = kp, vp
     return PrefillProblem(q=q, k=k, v=v, kv_lens=kv_lens, num_kv_heads=num_kv_heads, dtype=dtype,
                           scale=float(scale), phi=float(phi), a=float(a), b=float(b),
-                          workload=workload)
+                          workload=workload, kv_dtype=kv_dtype, page_size=page_size,
+                          block_table=block_table, paged_max_seq_len=max_seq_len if page_size else 0,
+                          k_scale=k_scale, v_scale=v_scale)
 
 
 def make_prefill_config(cfg: int, *, batch: Optional[int] = None, q_len: Optional[int] = None,

@@ -183,3 +183,69 @@ def test_out_of_band_tiles_are_redone_and_still_exact():
         assert np.all(red[:48][pos >= 40] == 1) and not red[:48][pos < 40].any()
         assert np.all(fu[48:] == 1)
         np.testing.assert_array_equal(red[48:], (pos + 1 + tile - 1) // tile)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3fn"])
+def test_paged_cache_equals_contiguous_bit_for_bit(kv_dtype):
+    # the same draws stored in permuted 16-token pages (decode's paged layout)
+    kw = dict(batch=3, hq=4, hkv=2, lq=37, kv=[37, 100, 20], d=32, seed=31, dtype="bf16",
+              kv_dtype=kv_dtype)
+    flat = _small(**kw)
+    paged = _small(page_size=16, extra_pages=3, **kw)
+    assert paged.block_table is not None and paged.k.shape[2] == 16
+    a = oracle.prefill_exact(**flat.args())
+    b = oracle.prefill_exact(**paged.args())
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_e4m3fn_cache_equals_its_dequantised_values():
+    # codes times per-KV-head scales: with power-of-two scales the products are
+    # exact in float32, so an fp32 cache holding them gives the same bits
+    p = _small(batch=2, hq=4, hkv=2, lq=30, kv=[30, 45], d=16, seed=32, dtype="bf16", kv_dtype="e4m3fn")
+    p.k_scale = np.array([2.0 ** -6, 2.0 ** -5], dtype=np.float32)
+    p.v_scale = np.array([2.0 ** -7, 2.0 ** -4], dtype=np.float32)
+    dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()   # torch's decoder
+    kf = (dec(p.k) * p.k_scale[None, :, None, None]).astype(np.float32)
+    vf = (dec(p.v) * p.v_scale[None, :, None, None]).astype(np.float32)
+    args = p.args()
+    got = oracle.prefill_exact(**args)
+    args.update(k=kf, v=vf, kv_dtype="f32", k_scale=None, v_scale=None)
+    ref = oracle.prefill_exact(**args)
+    for x, y in zip(got, ref):
+        np.testing.assert_array_equal(x, y)
+    # and against torch's E4M3FN decoder with the generator's own scales
+    q = _small(batch=1, hq=2, hkv=1, lq=8, kv=8, d=16, seed=33, dtype="bf16", kv_dtype="e4m3fn")
+    kd = torch.from_numpy(q.k).view(torch.float8_e4m3fn).double().numpy() * float(q.k_scale[0])
+    vd = torch.from_numpy(q.v).view(torch.float8_e4m3fn).double().numpy() * float(q.v_scale[0])
+    out, _, _ = oracle.prefill_exact(**q.args())
+    qq = _f64(q.q, "bf16")
+    mask = np.tril(np.ones((8, 8), dtype=bool))
+    for h in range(2):
+        s = q.scale * qq[0, h] @ kd[0, 0].T
+        w = scipy.special.softmax(np.where(mask, s, -np.inf), axis=1)
+        np.testing.assert_allclose(out[h * 8:(h + 1) * 8], w @ vd[0, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_single_query_block_on_a_paged_e4m3fn_cache_is_a_decode_step():
+    p = _small(batch=3, hq=4, hkv=2, lq=1, kv=[40, 1, 97], dtype="bf16", d=32, seed=34, kv_dtype="e4m3fn",
+               page_size=16, extra_pages=2)
+    out, flags, margin = oracle.prefill_exact(**p.args())
+    ref, rflags, rmargin = oracle.decode_exact(
+        p.q[:, :, 0, :], p.k, p.v, p.kv_lens, p.block_table, num_kv_heads=2, max_seq_len=p.max_seq_len,
+        page_size=16, q_dtype="bf16", kv_dtype="e4m3fn", scale=p.scale, phi=p.phi, a=p.a, b=p.b,
+        k_scale=p.k_scale, v_scale=p.v_scale)
+    np.testing.assert_array_equal(out, ref)
+    np.testing.assert_array_equal(flags, rflags)
+    np.testing.assert_array_equal(margin, rmargin)
+
+
+def test_unified_steps_on_paged_e4m3fn_cache_equal_exact():
+    p = _small(batch=2, hq=4, hkv=2, lq=50, kv=[50, 80], d=32, seed=35, dtype="bf16", kv_dtype="e4m3fn",
+               page_size=16, phi=1.0, a=2.0, b=1.5)
+    exact, eflags, _ = oracle.prefill_exact(**p.args())
+    args = p.args()
+    uni, uflags, redone = oracle.prefill_unified(**args, tile=32)
+    assert redone.sum() > 0
+    np.testing.assert_array_equal(uflags, eflags)
+    np.testing.assert_allclose(uni, exact, rtol=1e-12, atol=1e-13)
