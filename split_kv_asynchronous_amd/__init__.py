@@ -64,7 +64,10 @@ class FdPrefillDesc(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("q_len", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("kv_dtype", ctypes.c_int),
+                ("page_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class FdGemmDesc(ctypes.Structure):
@@ -341,10 +344,14 @@ def fd_attn_decode(q, k_cache, v_cache, seq_lens, block_table, phi: float, a: fl
 def make_prefill_desc(*, batch: int, num_q_heads: int, num_kv_heads: int, q_len: int,
                       max_seq_len: int, scale: Optional[float] = None, dtype: str = "bf16",
                       out_dtype: str = "f32", head_dim: int = 128,
-                      stage_events_ptr: int = 0) -> FdPrefillDesc:
+                      stage_events_ptr: int = 0, kv_dtype: str = "bf16", page_size: int = 0,
+                      max_blocks_per_seq: int = 0, num_pages: int = 0, block_table_ptr: int = 0,
+                      k_scale_ptr: int = 0, v_scale_ptr: int = 0) -> FdPrefillDesc:
     return FdPrefillDesc(batch, num_q_heads, num_kv_heads, head_dim, q_len, max_seq_len,
                          -1.0 if scale is None else float(scale), _DTYPE_CODE[dtype],
-                         _DTYPE_CODE[out_dtype], stage_events_ptr or None)
+                         _DTYPE_CODE[out_dtype], stage_events_ptr or None, _DTYPE_CODE[kv_dtype],
+                         page_size, max_blocks_per_seq, num_pages, block_table_ptr or None,
+                         k_scale_ptr or None, v_scale_ptr or None)
 
 
 def _event_array(stage_events):
@@ -358,13 +365,18 @@ def _event_array(stage_events):
 def fd_attn_prefill(q, k, v, kv_lens, phi: float, a: float, b: float, out=None,
                     fallback_flags=None, *, num_kv_heads: Optional[int] = None,
                     scale: Optional[float] = None, out_dtype: str = "f32", stream=None,
-                    stage_events: Optional[Sequence] = None):
+                    stage_events: Optional[Sequence] = None, block_table=None, page_size: int = 0,
+                    max_seq_len: Optional[int] = None, k_scale=None, v_scale=None):
     """Causal prefill attention of a query block per sequence; returns (out, fallback_flags).
 
     Layouts as in include/fd_prefill.h: q [B][Hq][q_len][128] bf16; k, v
-    [B][Hkv][max_seq_len][128] bf16; kv_lens int32 [B] (keys per sequence, the
-    query block included: query j sits at position kv_lens[b] - q_len + j).
-    bf16 data may be torch.bfloat16 or 16-bit integer bit patterns.
+    contiguous [B][Hkv][max_seq_len][128] or, with page_size > 0, paged
+    [pages][Hkv][page_size][128] with block_table int32 [B][max_blocks] and
+    max_seq_len given; bf16 or E4M3FN (with k_scale, v_scale fp32 [Hkv]);
+    kv_lens int32 [B] (keys per sequence, the query block included: query j
+    sits at position kv_lens[b] - q_len + j).  bf16 data may be
+    torch.bfloat16 or 16-bit integer bit patterns, E4M3FN
+    torch.float8_e4m3fn or uint8 codes.
     """
     import torch
     dev = q.device
@@ -372,23 +384,42 @@ def fd_attn_prefill(q, k, v, kv_lens, phi: float, a: float, b: float, out=None,
     for t in (q, k, v, kv_lens):
         if t.device != dev or not t.is_contiguous():
             raise ValueError("all tensors must be contiguous and on the same device")
-    for t in (q, k, v):
-        if _torch_code(t) != "bf16":
-            raise ValueError("q, k and v must be bf16")
+    if _torch_code(q) != "bf16":
+        raise ValueError("q must be bf16")
+    kvd = _torch_code(k)
+    if kvd not in ("bf16", "e4m3fn") or _torch_code(v) != kvd:
+        raise ValueError("k and v must both be bf16 or both E4M3FN")
     if kv_lens.dtype != torch.int32:
         raise ValueError("kv_lens must be int32")
     if k.dim() != 4 or v.shape != k.shape:
-        raise ValueError("k and v must be [B][Hkv][max_seq_len][128]")
+        raise ValueError("k and v must be [B][Hkv][max_seq_len][128] or [pages][Hkv][page_size][128]")
     if num_kv_heads is None:
         num_kv_heads = k.shape[1]
+    max_blocks = num_pages = 0
+    table_ptr = 0
+    if page_size:
+        if block_table is None or block_table.dtype != torch.int32 or not block_table.is_contiguous():
+            raise ValueError("paged caches need a contiguous int32 block_table")
+        if max_seq_len is None:
+            raise ValueError("paged caches need max_seq_len")
+        max_blocks, num_pages, table_ptr = block_table.shape[1], k.shape[0], block_table.data_ptr()
+    else:
+        max_seq_len = k.shape[2]
+    ks = vs = 0
+    if kvd == "e4m3fn":
+        if k_scale is None or v_scale is None or not (k_scale.is_contiguous() and v_scale.is_contiguous()):
+            raise ValueError("E4M3FN caches need contiguous k_scale and v_scale")
+        ks, vs = k_scale.data_ptr(), v_scale.data_ptr()
     if out is None:
         out = torch.empty((B, Hq, Lq, D),
                           dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=dev)
     if fallback_flags is None:
         fallback_flags = torch.empty((B, Hq, Lq), dtype=torch.uint8, device=dev)
     desc = make_prefill_desc(batch=B, num_q_heads=Hq, num_kv_heads=num_kv_heads, q_len=Lq,
-                             max_seq_len=k.shape[2], scale=scale, out_dtype=out_dtype,
-                             head_dim=D)
+                             max_seq_len=max_seq_len, scale=scale, out_dtype=out_dtype,
+                             head_dim=D, kv_dtype=kvd, page_size=page_size,
+                             max_blocks_per_seq=max_blocks, num_pages=num_pages,
+                             block_table_ptr=table_ptr, k_scale_ptr=ks, v_scale_ptr=vs)
     ev_arr = None
     if stage_events is not None:
         ev_arr = _event_array(stage_events)

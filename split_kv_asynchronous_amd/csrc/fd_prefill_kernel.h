@@ -1,4 +1,5 @@
-// Causal prefill attention with the unified maximum (gfx950, bf16).
+// Causal prefill attention with the unified maximum (gfx950): bf16 queries
+// over a bf16 or E4M3FN cache, contiguous or paged.
 //
 // The prefill form of the method (FlashDecoding++ theory page, section 3: the
 // preset maximum serves prefill as it serves decode): a block of q_len query
@@ -19,12 +20,15 @@
 // eight XCDs in contiguous ranges (a launch places workgroup i on XCD i % 8),
 // so the query heads and tiles that read the same K/V share one L2.
 //
-// Ring.  NST stages of 32 keys (two 16-token groups of K and of V, 4 KiB each)
-// shared by the workgroup and filled by 1 KiB buffer->LDS DMA instructions,
-// each moving 4 whole cache rows; the 16-byte pieces of a row are rotated so
-// the fragment reads are free of bank conflicts.  One barrier per stage.
-// Per stage and wavefront:
-//   * K fragments with ds_read_b128, V^T fragments with ds_read_b64_tr_b16;
+// Ring.  NST stages of 32 keys (K and V: two 16-row groups of bf16 or one
+// 32-row group of E4M3FN, 4 KiB per group) shared by the workgroup and filled
+// by 1 KiB DMA instructions, each moving 4 (8) whole cache rows -- buffer->LDS
+// over the sequence's contiguous slice, or global->LDS per page through the
+// block table; the 16-byte pieces of a row are rotated so the fragment reads
+// are free of bank conflicts.  One barrier per stage.  Per stage and wavefront:
+//   * K fragments with ds_read_b128, V^T fragments with ds_read_b64_tr_b16
+//     (ds_read_b64_tr_b8 for E4M3FN, whose codes are widened to bf16 in
+//     registers, exactly; k_scale joins the softmax scale, v_scale the output);
 //   * S^T[16 keys x 16 queries] = K . Q^T on v_mfma_f32_16x16x32_bf16 (Q^T
 //     fragments stay in registers), scale, causal mask, band test, weights;
 //   * weights split into a bf16 high part and a bf16 remainder (together a
@@ -45,18 +49,23 @@ using namespace ring;
 
 // Everything one prefill call's kernel needs, passed by value.
 struct PrefillParams {
-    const uint16_t *q, *k, *v;     // bf16 bit patterns
+    const uint16_t *q;             // bf16 bit patterns
+    const void *k, *v;             // bf16 bit patterns or E4M3FN codes
     const int32_t *kv_lens;
+    const int32_t *block_table;    // [B][max_blocks] (paged caches)
+    const float *k_scale, *v_scale;   // [Hkv] (E4M3FN caches)
     void *out;
     uint8_t *flags;
     int batch, hq, hkv, group;     // group = hq / hkv
     int q_len, max_seq_len;
+    int page_shift, max_blocks;    // paged caches: log2(page size), row stride of block_table
     int ntiles;                    // query tiles per (sequence, head)
     int total;                     // work items
     int per_xcd;                   // ceil(total / 8)
     float c1;                      // scale * log2(e): raw score -> exponent units
     float c0;                      // -phi * log2(e)
     float lo_raw, hi_raw, phi_raw; // band edges and phi in raw score units (divided by scale)
+    float scale, lo, hi, phi;      // the same in score units (E4M3FN: divided per KV head on the GPU)
 };
 
 // Two floats -> packed bf16 pair, round to nearest even.
@@ -66,22 +75,23 @@ FD_DEV uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// LDS slot rotation of the 16-byte pieces of a 16-row group (the bf16 cache
-// format's, chosen for the 64-bank LDS)
-FD_DEV int piece_rot(int r) { return Fmt<FD_BF16>::rot(r); }
-
-template <int NW, int QB, int NST>
+// Stage geometry per cache format: a stage holds 32 keys of K and of V, as
+// two 16-row groups of 256-byte bf16 rows or one 32-row group of 128-byte
+// E4M3FN rows (4 KiB per group either way, the decode kernels' formats and
+// LDS piece rotations).
+template <int NW, int QB, int NST, int KV = FD_BF16>
 struct Shape {
     static constexpr int waves = NW;
     static constexpr int qblocks = QB;                 // 16-query blocks per wavefront
     static constexpr int nst = NST;
     static constexpr int rows = NW * 16 * QB;          // queries per workgroup
     static constexpr int keys = 32;                    // keys per stage
-    static constexpr int tile = 2 * kGroupBytes;       // K (or V) part of a stage
+    static constexpr int groups = KV == FD_FP8_E4M3FN ? 1 : 2;   // compute groups per stage
+    static constexpr int tile = groups * kGroupBytes;  // K (or V) part of a stage
     static constexpr int stage = 2 * tile;
     static constexpr int lds = NST * stage;
     static constexpr int dma_per_group = 4 / NW;       // 1 KiB DMA instructions per wave per K (or V) group
-    static constexpr int dma_per_wave = 2 * 2 * dma_per_group;
+    static constexpr int dma_per_wave = 2 * groups * dma_per_group;
     static_assert(NW == 2 || NW == 4, "two or four wavefronts");
     static_assert(NST >= 2, "the ring needs two stages");
     static_assert((NST - 1) * dma_per_wave < 64, "vmcnt cannot count that deep");
@@ -89,11 +99,17 @@ struct Shape {
     static_assert(QB >= 1 && QB <= 4, "query blocks per wavefront");
 };
 
-template <int NW, int QB, int NST, bool OUT_BF16>
+template <int NW, int QB, int NST, int KV, bool PAGED, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(PrefillParams p)
 {
-    using S = Shape<NW, QB, NST>;
-    constexpr int ROW = 256;                       // bytes per cache row (16 pieces of 16 bytes)
+    using S = Shape<NW, QB, NST, KV>;
+    using F = Fmt<KV>;
+    constexpr bool FP8 = KV == FD_FP8_E4M3FN;
+    constexpr int ROW = F::row;                    // bytes per cache row
+    constexpr int GRP = F::group;                  // rows per compute group
+    constexpr int NG = S::groups;                  // compute groups per stage
+    constexpr int RPI = 1024 / ROW;                // rows per DMA instruction
+    constexpr int LPR = 64 / RPI;                  // lanes per row in a DMA instruction
     constexpr int BLK = S::keys;
     constexpr int IPG = S::dma_per_group;
     constexpr int DPW = S::dma_per_wave;
@@ -119,6 +135,18 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
 
     int kv = as_const(p.kv_lens)[b];
     kv = kv < 0 ? 0 : (kv > p.max_seq_len ? p.max_seq_len : kv);
+
+    // raw scores are q . k with K as stored: for E4M3FN the KV head's k_scale
+    // joins the softmax scale (both positive), and v_scale the output
+    float c1 = p.c1, lo_raw = p.lo_raw, hi_raw = p.hi_raw, phi_raw = p.phi_raw, vsc = 1.f;
+    if constexpr (FP8) {
+        const float eff = p.scale * as_const(p.k_scale)[kvh];
+        c1 = eff * kLog2e;
+        lo_raw = p.lo / eff;
+        hi_raw = p.hi / eff;
+        phi_raw = p.phi / eff;
+        vsc = as_const(p.v_scale)[kvh];
+    }
     const int off = kv - p.q_len;                  // position of query j is off + j
     const int jw0 = j0 + wave * 16 * QB;           // this wavefront's first query
     const int jw_end = min(jw0 + 16 * QB, p.q_len);
@@ -138,51 +166,98 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
     }
 
     // ---- DMA: wavefront w issues instructions IPG*w .. IPG*w + IPG-1 of each
-    // group of K and of V; instruction i moves group rows 4i .. 4i+3, lane l
-    // fetching, of row 4i + l/16, the piece that belongs in LDS slot l%16.
+    // group of K and of V; instruction i moves group rows RPI*i .. RPI*i +
+    // RPI-1, lane l fetching, of row RPI*i + l/LPR, the piece that belongs in
+    // LDS slot l%LPR.
     uint32_t dma_vo[IPG];
 #pragma unroll
     for (int qd = 0; qd < IPG; ++qd) {
-        const int r = 4 * (IPG * wave + qd) + lane / 16;
-        dma_vo[qd] = (lane / 16) * ROW + 16 * ((lane % 16 - piece_rot(r)) & 15);
+        const int r = RPI * (IPG * wave + qd) + lane / LPR;
+        dma_vo[qd] = (lane / LPR) * ROW + 16 * ((lane % LPR - F::rot(r)) & (F::slots - 1));
     }
-    const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * ROW;
-    const int nrec = (int)((uint32_t)kv * ROW);    // rows past kv read as zeros
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)((const uint8_t *)p.k + slice), (short)0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)((const uint8_t *)p.v + slice), (short)0, nrec, 0x00020000);
+    const uint8_t *kpool = static_cast<const uint8_t *>(p.k);
+    const uint8_t *vpool = static_cast<const uint8_t *>(p.v);
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    const __attribute__((address_space(4))) int32_t *btab = as_const(p.block_table);
+    if constexpr (!PAGED) {
+        const size_t slice = ((size_t)b * p.hkv + kvh) * (size_t)p.max_seq_len * ROW;
+        const int nrec = (int)((uint32_t)kv * ROW);    // rows past kv read as zeros
+        krs = __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + slice), (short)0, nrec, 0x00020000);
+        vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + slice), (short)0, nrec, 0x00020000);
+    } else {
+        btab += (size_t)b * p.max_blocks;
+    }
+    // last page a key of the sequence uses; an instruction whose rows lie
+    // past kv reads through that page's table entry with an empty range
+    const int last_page = kv > 0 ? (kv - 1) >> p.page_shift : 0;
+    const int pmask = (1 << p.page_shift) - 1;
 
     auto issue = [&](int jb, int stage) {
         uint8_t *kt = ring + stage * S::stage + IPG * wave * 1024;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NG; ++u) {
 #pragma unroll
             for (int qd = 0; qd < IPG; ++qd) {
-                const int t0 = BLK * jb + 16 * u + 4 * (IPG * wave + qd);
+                const int t0 = BLK * jb + GRP * u + RPI * (IPG * wave + qd);
                 lds_void *kd = (lds_void *)(kt + u * kGroupBytes + qd * 1024);
                 lds_void *vd = (lds_void *)(kt + S::tile + u * kGroupBytes + qd * 1024);
-                const int so = (int)((uint32_t)t0 * ROW);
                 const uint32_t vo = dma_vo[qd];
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
+                if constexpr (PAGED) {
+                    // A buffer range over the page's rows of this KV head that
+                    // hold keys (rows past kv read as zeros, like the
+                    // contiguous slice past kv).  The rows of one instruction
+                    // never straddle a page (pages hold >= 16 rows).
+                    const int idx = t0 >> p.page_shift;
+                    const int page = btab[idx < last_page ? idx : last_page];
+                    const int valid = min(max(kv - (idx << p.page_shift), 0), pmask + 1);
+                    const size_t base = ((size_t)page * p.hkv + kvh) * (size_t)(pmask + 1) * ROW;
+                    const __amdgpu_buffer_rsrc_t kp = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(kpool + base), (short)0, valid * ROW, 0x00020000);
+                    const __amdgpu_buffer_rsrc_t vp = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(vpool + base), (short)0, valid * ROW, 0x00020000);
+                    const int so = (t0 & pmask) * ROW;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(kp, kd, 16, vo, so, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vp, vd, 16, vo, so, 0, 0);
+                } else {
+                    const int so = (int)((uint32_t)t0 * ROW);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, vo, so, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, so, 0, 0);
+                }
             }
         }
     };
 
-    // ---- fragment read addresses inside a 16-token group (bytes)
-    // K, step kk: row n, piece g4 + 4kk.
+    // ---- fragment read addresses inside a compute group (bytes)
+    // K, bf16: step kk -> row n, piece g4 + 4kk.  E4M3FN: for score tile tau
+    // and half m, row 16*tau + n, piece g4 + 4m (16 codes = steps 2m, 2m+1).
     uint32_t k_rd[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k_rd[kk] = n * ROW + 16 * ((g4 + 4 * kk + piece_rot(n)) & 15);
-    // V^T, dim tile dt: lane i of group g4 addresses row 4g4 + i/4, components
-    // 16dt + 4(i%4) .. +3; lane k then holds component 16dt + k of rows
-    // 4g4 .. 4g4+3 of the group.
+    for (int q4 = 0; q4 < 4; ++q4) {
+        if constexpr (FP8) {
+            const int tau = q4 >> 1, m = q4 & 1, r = 16 * tau + n;
+            k_rd[q4] = r * ROW + 16 * ((g4 + 4 * m + F::rot(r)) & (F::slots - 1));
+        } else {
+            k_rd[q4] = n * ROW + 16 * ((g4 + 4 * q4 + F::rot(n)) & (F::slots - 1));
+        }
+    }
+    // V^T, dim tile dt.  bf16: lane i of group g4 addresses row 4g4 + i/4,
+    // components 16dt + 4(i%4) .. +3; lane k then holds component 16dt + k of
+    // rows 4g4 .. 4g4+3 of the group.  E4M3FN: lane i addresses row T(i/2),
+    // components 16dt + 8(i%2) .. +7, with T(j) = 4g4 + j (j < 4) or
+    // 16 + 4g4 + j - 4; lane k then holds component 16dt + k of rows T(0..7).
+    // Either way the keys come in the order the two score tiles hand over
+    // their weights.
     uint32_t v_rd[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-        const int r = 4 * g4 + (n >> 2);
-        v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + piece_rot(r)) & 15);
+        if constexpr (FP8) {
+            const int jj = n >> 1;
+            const int r = jj < 4 ? 4 * g4 + jj : 16 + 4 * g4 + jj - 4;
+            v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((dt + F::rot(r)) & (F::slots - 1));
+        } else {
+            const int r = 4 * g4 + (n >> 2);
+            v_rd[dt] = r * ROW + 8 * (n & 1) + 16 * ((2 * dt + ((n & 3) >> 1) + F::rot(r)) & (F::slots - 1));
+        }
     }
 
     f32x4 o[QB][8];      // O^T: lane (n, g4) holds components 16dt + 4g4 + i of query n
@@ -205,7 +280,8 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
     int issued = nblk < NST - 1 ? nblk : NST - 1;
 
     // Q^T fragments (B operand of the score product): k index of MFMA step kk
-    // = component 8*g4 + 32*kk + j; the K fragments use the same map.  Rows
+    // = component 8*g4 + 32*kk + j (bf16) or 16*(g4 + 4*(kk/2)) + 8*(kk%2) + j
+    // (E4M3FN, matching its 16-byte K pieces); the K fragments use the same map.  Rows
     // past the block read the last row and are never stored.  The loads and
     // their wait sit in one assembly statement (early-clobber outputs): the
     // compiler never sees a register that a load still in flight will write.
@@ -215,15 +291,26 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
         const size_t head_row = ((size_t)b * p.hq + h) * p.q_len;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const uint16_t *qrow = p.q + (head_row + min(jw0 + 16 * qb + n, p.q_len - 1)) * kHeadDim + 8 * g4;
-            asm volatile("global_load_dwordx4 %0, %4, off\n\t"
-                         "global_load_dwordx4 %1, %4, off offset:64\n\t"
-                         "global_load_dwordx4 %2, %4, off offset:128\n\t"
-                         "global_load_dwordx4 %3, %4, off offset:192\n\t"
-                         "s_waitcnt vmcnt(0)"
-                         : "=&v"(qf[qb][0]), "=&v"(qf[qb][1]), "=&v"(qf[qb][2]), "=&v"(qf[qb][3])
-                         : "v"(qrow)
-                         : "memory");
+            const uint16_t *qrow = p.q + (head_row + min(jw0 + 16 * qb + n, p.q_len - 1)) * kHeadDim +
+                                   (FP8 ? 16 : 8) * g4;
+            if constexpr (FP8)
+                asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                             "global_load_dwordx4 %1, %4, off offset:16\n\t"
+                             "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                             "global_load_dwordx4 %3, %4, off offset:144\n\t"
+                             "s_waitcnt vmcnt(0)"
+                             : "=&v"(qf[qb][0]), "=&v"(qf[qb][1]), "=&v"(qf[qb][2]), "=&v"(qf[qb][3])
+                             : "v"(qrow)
+                             : "memory");
+            else
+                asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                             "global_load_dwordx4 %1, %4, off offset:64\n\t"
+                             "global_load_dwordx4 %2, %4, off offset:128\n\t"
+                             "global_load_dwordx4 %3, %4, off offset:192\n\t"
+                             "s_waitcnt vmcnt(0)"
+                             : "=&v"(qf[qb][0]), "=&v"(qf[qb][1]), "=&v"(qf[qb][2]), "=&v"(qf[qb][3])
+                             : "v"(qrow)
+                             : "memory");
         }
     }
 
@@ -240,35 +327,75 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
         }
     };
 
-    u32x4 kraw[2][4];
-    u32x2 vraw[2][8];
-    // Read stage s's fragments (group u and the V half are immediate offsets);
-    // the fragments are tied to the wait so that no use moves above it.
+    // The stage's operands: K fragments per score tile and MFMA step, V^T
+    // fragments per dim tile over the stage's 32 keys (bf16; E4M3FN codes are
+    // widened exactly in registers).
+    u32x4 kop[2][4];
+    u32x2 vraw[2][8];                  // bf16: the two groups' V^T fragments
+    u32x4 vop[FP8 ? 8 : 1];            // E4M3FN: the widened V^T fragments
+    auto vfrag = [&](int dt) -> u32x4 {
+        if constexpr (FP8) return vop[dt];
+        else return u32x4{vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
+    };
+    // Read stage s's fragments (group and V offsets are immediates); the
+    // fragments are tied to the wait so that no use moves above it.  Rows
+    // past kv hold zeros (buffer ranges end at kv in both layouts), so the
+    // zero weights of those masked keys never meet a NaN from an unused slot.
     auto read_stage = [&](int s) {
         const uint32_t kt = (uint32_t)(uintptr_t)(ring + (s % NST) * S::stage);
+        if constexpr (FP8) {
+            u32x4 kraw[4];
+            u32x2 v8[8];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const uint32_t addr = kt + k_rd[kk];
-            asm volatile("ds_read_b128 %0, %1" : "=v"(kraw[0][kk]) : "v"(addr) : "memory");
-            asm volatile("ds_read_b128 %0, %1 offset:%2"
-                         : "=v"(kraw[1][kk]) : "v"(addr), "i"(kGroupBytes) : "memory");
-        }
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint32_t addr = kt + k_rd[q4];
+                asm volatile("ds_read_b128 %0, %1" : "=v"(kraw[q4]) : "v"(addr) : "memory");
+            }
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const uint32_t addr = kt + v_rd[dt];
-            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                         : "=v"(vraw[0][dt]) : "v"(addr), "i"(S::tile) : "memory");
-            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                         : "=v"(vraw[1][dt]) : "v"(addr), "i"(S::tile + kGroupBytes) : "memory");
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint32_t addr = kt + v_rd[dt];
+                asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v8[dt]) : "v"(addr), "i"(S::tile) : "memory");
+            }
             asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(kraw[u][0]), "+v"(kraw[u][1]), "+v"(kraw[u][2]), "+v"(kraw[u][3])
+                         : "+v"(kraw[0]), "+v"(kraw[1]), "+v"(kraw[2]), "+v"(kraw[3])
                          :
                          : "memory");
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+v"(vraw[u][dt]) : : "memory");
+            for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+v"(v8[dt]) : : "memory");
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const u32x4 r = kraw[2 * tau + (kk >> 1)];
+                    kop[tau][kk] = (kk & 1) ? e4m3x8_to_bf16(r.z, r.w) : e4m3x8_to_bf16(r.x, r.y);
+                }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) vop[dt] = e4m3x8_to_bf16(v8[dt].x, v8[dt].y);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint32_t addr = kt + k_rd[kk];
+                asm volatile("ds_read_b128 %0, %1" : "=v"(kop[0][kk]) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:%2"
+                             : "=v"(kop[1][kk]) : "v"(addr), "i"(kGroupBytes) : "memory");
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint32_t addr = kt + v_rd[dt];
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(vraw[0][dt]) : "v"(addr), "i"(S::tile) : "memory");
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(vraw[1][dt]) : "v"(addr), "i"(S::tile + kGroupBytes) : "memory");
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(kop[u][0]), "+v"(kop[u][1]), "+v"(kop[u][2]), "+v"(kop[u][3])
+                             :
+                             : "memory");
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+v"(vraw[u][dt]) : : "memory");
+            }
         }
     };
 
@@ -288,7 +415,7 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
             for (int u = 0; u < 2; ++u) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kraw[u][kk], qf[qb][kk], acc);
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kop[u][kk], qf[qb][kk], acc);
                 sacc[qb][u] = acc;
             }
 #pragma unroll
@@ -321,7 +448,7 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
         bool any = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const bool out = smax[qb] > p.hi_raw || smin[qb] < p.lo_raw;
+            const bool out = smax[qb] > hi_raw || smin[qb] < lo_raw;
             bad[qb] |= out;
             any |= out;
         }
@@ -341,7 +468,7 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], p.c1, nm));  // -inf -> 0
+                w[u][r] = exp2_hw(fmaf(sacc[qb][u][r], c1, nm));  // -inf -> 0
                 lacc[qb] += w[u][r];
             }
         uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
@@ -355,7 +482,7 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const u32x4 va = {vraw[0][dt].x, vraw[0][dt].y, vraw[1][dt].x, vraw[1][dt].y};
+            const u32x4 va = vfrag(dt);
             o[qb][dt] = mfma_bf16(va, ph, o[qb][dt]);
             o[qb][dt] = mfma_bf16(va, pl, o[qb][dt]);
         }
@@ -411,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
             float l = lacc[qb];
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
-            mrun[qb] = l > 0.f ? p.phi_raw : -INFINITY;
+            mrun[qb] = l > 0.f ? phi_raw : -INFINITY;
         }
 #pragma unroll 1
         for (bool first = true; s < nact; ++s, first = false) {
@@ -430,12 +557,12 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 const float mnew = fmaxf(mrun[qb], mx);
-                const float f = (mrun[qb] == mnew) ? 1.f : exp2_hw((mrun[qb] - mnew) * p.c1);
+                const float f = (mrun[qb] == mnew) ? 1.f : exp2_hw((mrun[qb] - mnew) * c1);
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= f;
                 lacc[qb] *= f;
                 mrun[qb] = mnew;
-                accumulate(qb, mnew == -INFINITY ? 0.f : -mnew * p.c1);
+                accumulate(qb, mnew == -INFINITY ? 0.f : -mnew * c1);
             }
         }
     }
@@ -455,7 +582,7 @@ __global__ __launch_bounds__(NW * 64, QB > 2 ? 1 : 2) void prefill_kernel(Prefil
         float l = lacc[qb];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = l > 0.f ? vsc / l : 0.f;
         const size_t row = ((size_t)b * p.hq + h) * p.q_len + j;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {

@@ -79,9 +79,12 @@ class DevicePrefill:
     def __init__(self, prob, out_dtype="f32"):
         self.prob = prob
         self.q = to_device(prob.q, "bf16")
-        self.k = to_device(prob.k, "bf16")
-        self.v = to_device(prob.v, "bf16")
+        self.k = to_device(prob.k, prob.cache_dtype)
+        self.v = to_device(prob.v, prob.cache_dtype)
         self.kv_lens = torch.from_numpy(prob.kv_lens).cuda()
+        self.block_table = None if prob.block_table is None else torch.from_numpy(prob.block_table).cuda()
+        self.k_scale = None if prob.k_scale is None else torch.from_numpy(prob.k_scale).cuda()
+        self.v_scale = None if prob.v_scale is None else torch.from_numpy(prob.v_scale).cuda()
         self.out_dtype = out_dtype
         self.out = torch.empty(prob.q.shape, device="cuda",
                                dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
@@ -94,7 +97,10 @@ class DevicePrefill:
                                   p.b if b is None else b, self.out, self.flags,
                                   num_kv_heads=p.num_kv_heads, scale=p.scale,
                                   out_dtype=self.out_dtype, stream=stream,
-                                  stage_events=stage_events)
+                                  stage_events=stage_events, block_table=self.block_table,
+                                  page_size=p.page_size,
+                                  max_seq_len=p.max_seq_len if p.page_size else None,
+                                  k_scale=self.k_scale, v_scale=self.v_scale)
 
     def results(self):
         torch.cuda.synchronize()

@@ -127,7 +127,7 @@ def _pdesc(**kw):
 def test_prefill_descriptor_layout_matches_the_header():
     src = open(os.path.join(ROOT, "include", "fd_prefill.h")).read()
     body = src[src.index("typedef struct {"):src.index("} fd_prefill_desc_t;")]
-    fields = re.findall(r"^\s*\w+\s+\*?\s*(\w+);", body, flags=re.M)
+    fields = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+);", body, flags=re.M)
     assert fields == [f for f, _ in fd.FdPrefillDesc._fields_]
 
 
@@ -136,6 +136,13 @@ def test_prefill_descriptor_layout_matches_the_header():
     (dict(q_len=(1 << 23) + 1), -2), (dict(max_seq_len=0), -2), (dict(batch=0), -2),
     (dict(batch=65536), -2), (dict(max_seq_len=(1 << 23) + 1), -2),
     (dict(dtype="f32"), -3), (dict(dtype="e4m3fn"), -3), (dict(out_dtype="e4m3fn"), -3),
+    (dict(kv_dtype="f32"), -3),
+    (dict(page_size=12, max_blocks_per_seq=1000, num_pages=5, block_table_ptr=FAKE), -2),
+    (dict(page_size=512, max_blocks_per_seq=16, num_pages=5, block_table_ptr=FAKE), -2),
+    (dict(page_size=16, max_blocks_per_seq=511, num_pages=5, block_table_ptr=FAKE), -2),
+    (dict(page_size=16, max_blocks_per_seq=512, num_pages=0, block_table_ptr=FAKE), -2),
+    (dict(page_size=16, max_blocks_per_seq=512, num_pages=5), -1),
+    (dict(kv_dtype="e4m3fn"), -1), (dict(kv_dtype="e4m3fn", k_scale_ptr=FAKE), -1),
 ])
 def test_prefill_bad_shapes_and_dtypes(kw, code):
     assert _pcall(_pdesc(**kw)) == code

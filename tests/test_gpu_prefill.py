@@ -32,9 +32,21 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3   # max|err| relative to max|out|, bf16 operands
 
 
+def _vmax(prob):
+    """max |v| over the cache as stored (bf16 values, or E4M3FN codes times
+    v_scale), ignoring NaN in slots that no key uses."""
+    if not prob.v.size:
+        return 0.0
+    if prob.cache_dtype == "e4m3fn":
+        codes = torch.from_numpy(np.ascontiguousarray(prob.v)).view(torch.float8_e4m3fn).double().abs()
+        per_head = torch.nan_to_num(codes, nan=0.0).amax(dim=(0, 2, 3)).numpy()
+        return float((per_head * prob.v_scale.astype(np.float64)).max())
+    return float(np.nanmax(np.abs(synthetic.bf16_to_f32(prob.v))))
+
+
 def _bound(prob):
     """Elementwise error bound of the kernel's arithmetic (see the top of the file)."""
-    vmax = float(np.abs(synthetic.bf16_to_f32(prob.v)).max()) if prob.v.size else 0.0
+    vmax = _vmax(prob)
     n = max(int(np.max(prob.kv_lens, initial=0)), 1)
     gamma = n * 2.0 ** -24 / (1 - n * 2.0 ** -24)
     return (2.0 ** -17 + 2 * gamma) * vmax
@@ -191,3 +203,67 @@ def test_prefill_full_config():
     assert torch.equal(out1, dp.out)
     print("full config2: rel err %.3e on %d sampled rows, scores in [%.3f, %.3f]"
           % (rel, len(rows), smin, smax))
+
+
+FORMAT_CASES = [
+    # kv dtype, page size, case
+    ("bf16", 16, "whole-and-prefixed"), ("bf16", 32, "short-and-empty"),
+    ("e4m3fn", 0, "whole-and-prefixed"), ("e4m3fn", 0, "single-query"),
+    ("e4m3fn", 16, "exact-tiles-long-prefix"), ("e4m3fn", 64, "one-partial-tile"),
+    ("bf16", 256, "exact-tiles-long-prefix"),
+]
+
+
+@pytest.mark.parametrize("kv,page,name", FORMAT_CASES)
+def test_prefill_cache_formats(kv, page, name):
+    # E4M3FN caches (per-KV-head scales) and paged caches (permuted pages,
+    # spare pages in the pool), the decode call's formats
+    kw = CASES[name]
+    print("case prefill %s kv=%s page=%d" % (name, kv, page), flush=True)
+    prob = synthetic.make_prefill(**kw, kv_dtype=kv, page_size=page, extra_pages=2 if page else 0,
+                                  seed=synthetic.SEED_BASE + 320 + sorted(CASES).index(name))
+    dp = DevicePrefill(prob)
+    dp.run()
+    rel, ref_flags = _check(prob, dp)
+    assert not ref_flags.any()
+    print("rel err %.3e" % rel)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3fn"])
+def test_prefill_paged_equals_contiguous_bitwise(kv):
+    kw = dict(batch=3, num_q_heads=8, num_kv_heads=2, q_len=200, kv_lens=[200, 517, 64], kv_dtype=kv,
+              seed=94, phi=1.0, a=2.5, b=2.0)
+    print("case prefill paged = contiguous kv=%s" % kv, flush=True)
+    flat = DevicePrefill(synthetic.make_prefill(**kw))
+    paged = DevicePrefill(synthetic.make_prefill(**kw, page_size=16, extra_pages=5))
+    flat.run()
+    paged.run()
+    torch.cuda.synchronize()
+    assert torch.equal(flat.out, paged.out) and torch.equal(flat.flags, paged.flags)
+    assert int(flat.flags.sum()) > 0     # the narrow band sends rows to the online path
+
+
+@pytest.mark.parametrize("kv,page", [("bf16", 16), ("e4m3fn", 16), ("e4m3fn", 0), ("bf16", 0)])
+def test_prefill_unused_cache_slots_hold_nan(kv, page):
+    prob = synthetic.make_prefill(batch=3, num_q_heads=4, num_kv_heads=2, q_len=70, kv_lens=[70, 133, 20],
+                                  kv_dtype=kv, page_size=page, extra_pages=3 if page else 0,
+                                  max_seq_len=None if page else 180, seed=95)
+    nan = np.uint16(0x7FC0) if kv == "bf16" else np.uint8(0x7F)
+    lens = prob.kv_lens
+    if page:
+        used = np.zeros((prob.k.shape[0], page), dtype=bool)
+        for b, L in enumerate(lens):
+            for blk in range(-(-int(L) // page)):
+                used[prob.block_table[b, blk], :min(page, int(L) - blk * page)] = True
+        for c in (prob.k, prob.v):
+            c.transpose(0, 2, 1, 3)[~used] = nan
+    else:
+        for b, L in enumerate(lens):
+            prob.k[b, :, L:] = nan
+            prob.v[b, :, L:] = nan
+    print("case prefill nan tails kv=%s page=%d" % (kv, page), flush=True)
+    dp = DevicePrefill(prob)
+    dp.run()
+    out, _ = dp.results()
+    assert np.isfinite(out).all()
+    _check(prob, dp)

@@ -2,8 +2,9 @@
 
 Each case draws a batch, a query-head group over 1-2 KV heads, a query block
 length, per-sequence key lengths (a cached prefix before the block, a sequence
-shorter than the block, or an empty one), and either a wide band (no visible
-score leaves it) or a narrow one (rows switch to online softmax part-way).
+shorter than the block, or an empty one), either a wide band (no visible
+score leaves it) or a narrow one (rows switch to online softmax part-way), and
+a cache format (bf16 or E4M3FN) and layout (contiguous or pages of 16-128).
 Bar as in the other prefill tests: max|gpu - oracle| <= 2e-3 * max|oracle|,
 and every output element within the bound the kernel's arithmetic allows
 (weights carried as a bf16 pair to a relative 2^-18, fp32 accumulation);
@@ -37,8 +38,14 @@ def draw_case(i):
         phi, a, b = float(rng.uniform(2.0, 5.0)), 20.0, 6.0
     else:
         phi, a, b = float(rng.uniform(-0.5, 1.5)), float(rng.uniform(1.5, 4.0)), float(rng.uniform(1.0, 3.0))
+    # cache format and layout from a stream of their own (the shapes above
+    # stay what they were without them)
+    fmt = np.random.default_rng(0x5EED4100 + i)
+    kv_dtype = str(fmt.choice(["bf16", "e4m3fn"]))
+    page = int(fmt.choice([0, 0, 16, 32, 128]))
     return dict(batch=batch, num_q_heads=g * hkv, num_kv_heads=hkv, q_len=q_len, kv_lens=kv,
-                phi=phi, a=a, b=b, seed=0x5EED5000 + i)
+                phi=phi, a=a, b=b, seed=0x5EED5000 + i, kv_dtype=kv_dtype, page_size=page,
+                extra_pages=int(fmt.integers(0, 4)) if page else 0)
 
 
 @pytest.mark.parametrize("i", range(NCASES))
