@@ -85,7 +85,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     const int b = __builtin_amdgcn_readfirstlane(U.b);
     const int hb = __builtin_amdgcn_readfirstlane(U.hb);
     const int c = __builtin_amdgcn_readfirstlane(U.c);
-    const int L = seq_len_of(p, b);
+    const int L = __builtin_amdgcn_readfirstlane(U.L);
     const int t_begin = c * p.chunk;
     const int t_end = min(t_begin + p.chunk, L);
     const int h0 = hb * GB;

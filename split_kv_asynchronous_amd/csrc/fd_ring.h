@@ -142,7 +142,7 @@ FD_DEV int wave_scan(int x, int lane)
 }
 
 struct Unit {
-    int b, hb, c;
+    int b, hb, c, L;   // sequence, head block, chunk; L = the sequence's (clamped) length
     bool ok;
 };
 
@@ -152,36 +152,44 @@ struct Unit {
 // are contiguous over the heads.
 // An empty sequence has one empty unit in the second part, so that its rows
 // still get merged (to zeros).
+// The lengths are scanned 64 sequences at a time; the next block's lengths
+// are loaded (unconditionally, the index clamped into the array) while this
+// block is scanned, and the unit's own length comes from registers, so a
+// search costs one memory round trip plus one per further block reached.
 FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
 {
-    Unit r = {0, 0, 0, false};
+    Unit r = {0, 0, 0, 0, false};
+    const int last = p.batch - 1;
+    auto load = [&](int b0) {
+        const int b = b0 + lane;
+        return as_const(p.seq_lens)[b < last ? b : last];
+    };
+    int raw = load(0);
     int base = 0;
 #pragma unroll 1
     for (int part = 0; part < 2; ++part) {
 #pragma unroll 1
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
+            const int cur = raw;
+            raw = load(b0 + 64 < p.batch ? b0 + 64 : 0);     // next block; the first again for part 1
             const int b = b0 + lane;
+            const int L = b < p.batch ? min(max(cur, 0), p.max_seq_len) : -1;   // -1: no sequence
             int cnt = 0;
-            if (b < p.batch) {
-                const int L = seq_len_of(p, b);
-                cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk || L == 0) ? nhb : 0);
-            }
+            if (L >= 0) cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk || L == 0) ? nhb : 0);
             const int incl = wave_scan(cnt, lane);
             const int total = __builtin_amdgcn_readlane(incl, 63);
             if (u < base + total) {
                 const uint64_t m = __ballot(base + incl > u);
                 const int hit = __builtin_ctzll(m);
-                const int before = base + __builtin_amdgcn_readlane(incl - cnt, hit);
-                const int bb = b0 + hit;
-                const int L = seq_len_of(p, bb);
-                const int rem = u - before;
-                r.b = bb;
+                const int rem = u - base - __builtin_amdgcn_readlane(incl - cnt, hit);
+                r.b = b0 + hit;
+                r.L = __builtin_amdgcn_readlane(L, hit);
                 if (part == 0) {
                     r.hb = rem % nhb;
                     r.c = rem / nhb;
                 } else {
                     r.hb = rem;
-                    r.c = L / p.chunk;
+                    r.c = r.L / p.chunk;
                 }
                 r.ok = true;
                 return r;
