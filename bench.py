@@ -494,6 +494,59 @@ def load_traffic(workload: str, entry: str = "fd_attn.hip"):
     return rec.get("bytes_per_launch")
 
 
+# Serving-sized batches of ragged decode calls (sequences x query heads / KV
+# heads, length range, cache format, page size, chunk size): the unit search
+# of the grouped kernels at batches of hundreds to thousands of sequences.
+SERVING_CASES = [
+    ("gqa64/8-bf16-B32-1K..32K", 32, 64, 8, 1024, 32768, "bf16", 0, 1024),
+    ("gqa64/8-bf16-B512-512..4K", 512, 64, 8, 512, 4096, "bf16", 0, 1024),
+    ("gqa64/8-bf16-B2048-128..1K", 2048, 64, 8, 128, 1024, "bf16", 0, 1024),
+    ("gqa32/8-fp8-paged16-B512-512..4K", 512, 32, 8, 512, 4096, "e4m3fn", 16, 512),
+    ("gqa32/8-fp8-paged16-B2048-256..2K", 2048, 32, 8, 256, 2048, "e4m3fn", 16, 512),
+]
+
+
+def main_serving(args):
+    """One JSON line per serving-batch case: whole-call and chunk-kernel TB/s
+    of K/V over K back-to-back calls (a side measurement, not the bench line)."""
+    import torch
+
+    import split_kv_asynchronous_amd as fd
+    import synthetic
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_device import DeviceProblem
+
+    for name, B, hq, hkv, lo, hi, kv, page, chunk in SERVING_CASES:
+        lens = np.random.default_rng(3).integers(lo, hi + 1, size=B).astype(np.int32)
+        prob = synthetic.make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, seq_lens=lens, kv_dtype=kv,
+                                      page_size=page, chunk_size=chunk, seed=77, workload=name)
+        dp = DeviceProblem(prob)
+        for _ in range(args.warmup):
+            dp.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dp.run()
+        torch.cuda.synchronize()
+        per_call = (time.perf_counter() - t0) / args.steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for row in evs:
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            dp.run(stage_events=evs[i])
+        torch.cuda.synchronize()
+        kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        kvb = prob.kv_bytes()
+        print(json.dumps({"workload": name, "batch": B, "kv_bytes_per_call": kvb,
+                          "ms_per_call": round(per_call * 1e3, 5), "call_tbs": round(kvb / per_call / 1e12, 3),
+                          "kernel_ms": round(kms, 5), "kernel_tbs": round(kvb / kms / 1e9, 3),
+                          "plan": fd.fd_attn_plan(dp.desc())}), flush=True)
+        del dp
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -506,6 +559,8 @@ def main():
                     help="time fd_attn_prefill on this prefill workload instead of decode")
     ap.add_argument("--gemm", type=int, default=0,
                     help="time fd_flat_gemm over the linear layers of this GEMM workload")
+    ap.add_argument("--serving", action="store_true",
+                    help="side measurement: ragged decode at serving batch sizes, one line per case")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
@@ -514,6 +569,9 @@ def main():
         print("bench.py measures one GPU: the decode-attention path is built and timed on a "
               "single MI355X; multi-GPU runs are not part of this library", file=sys.stderr)
         sys.exit(2)
+    if args.serving:
+        main_serving(args)
+        return
     if args.prefill:
         main_prefill(args)
         return

@@ -130,14 +130,19 @@ FD_DEV u32x2 v_tail_mask(int tg, int g4, int t_end)
     }
 }
 
-// wave-wide inclusive prefix sum
-FD_DEV int wave_scan(int x, int lane)
+// Wave-wide inclusive prefix sum on DPP lane moves (no LDS round trip):
+// Hillis-Steele inside each row of 16 lanes (row_shr 1, 2, 4, 8; lanes
+// shifted in from outside the row add 0), then the total of row 0 is added to
+// row 1 and that of row 2 to row 3 (row_bcast:15 on rows 1 and 3), then the
+// total of rows 0-1 to rows 2 and 3 (row_bcast:31).  Disabled rows add 0.
+FD_DEV int wave_scan(int x)
 {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
     return x;
 }
 
@@ -146,55 +151,81 @@ struct Unit {
     bool ok;
 };
 
+// floor(L / chunk) for 0 <= L <= 2^23 through a float reciprocal, corrected
+// to the exact quotient (cheaper than an integer division per length).
+FD_DEV int div_chunk(int L, int chunk, float rcp)
+{
+    int q = (int)((float)L * rcp);
+    q -= q * chunk > L;
+    q += (q + 1) * chunk <= L;
+    return q;
+}
+
 // The u-th unit of "full chunks of every sequence, then the partial last
 // chunks", sequence-major inside each part, chunks outer, head blocks inner:
 // consecutive workgroups write the partials of one chunk of a sequence, which
 // are contiguous over the heads.
 // An empty sequence has one empty unit in the second part, so that its rows
 // still get merged (to zeros).
-// The lengths are scanned 64 sequences at a time; the next block's lengths
-// are loaded (unconditionally, the index clamped into the array) while this
-// block is scanned, and the unit's own length comes from registers, so a
-// search costs one memory round trip plus one per further block reached.
+// Every workgroup searches before it can issue a load of its own, so the
+// search is kept to one memory round trip for up to 64 * kFindBlocks
+// sequences: the lengths of that many are loaded at once (coalesced, indices
+// clamped into the array so that no load is conditional), kept in registers
+// for both parts, and scanned 64 at a time on DPP lane moves.
+constexpr int kFindBlocks = 16;
+
 FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
 {
+    constexpr int KB = kFindBlocks;
     Unit r = {0, 0, 0, 0, false};
     const int last = p.batch - 1;
-    auto load = [&](int b0) {
-        const int b = b0 + lane;
-        return as_const(p.seq_lens)[b < last ? b : last];
+    const float rcp = 1.0f / (float)p.chunk;
+    int raw[KB];
+    auto load = [&](int sb) {
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int b = sb + 64 * k + lane;
+            raw[k] = as_const(p.seq_lens)[b < last ? b : last];
+        }
     };
-    int raw = load(0);
+    const bool resident = p.batch <= 64 * KB;     // one load serves both parts
+    if (resident) load(0);
     int base = 0;
 #pragma unroll 1
     for (int part = 0; part < 2; ++part) {
 #pragma unroll 1
-        for (int b0 = 0; b0 < p.batch; b0 += 64) {
-            const int cur = raw;
-            raw = load(b0 + 64 < p.batch ? b0 + 64 : 0);     // next block; the first again for part 1
-            const int b = b0 + lane;
-            const int L = b < p.batch ? min(max(cur, 0), p.max_seq_len) : -1;   // -1: no sequence
-            int cnt = 0;
-            if (L >= 0) cnt = part == 0 ? (L / p.chunk) * nhb : ((L % p.chunk || L == 0) ? nhb : 0);
-            const int incl = wave_scan(cnt, lane);
-            const int total = __builtin_amdgcn_readlane(incl, 63);
-            if (u < base + total) {
-                const uint64_t m = __ballot(base + incl > u);
-                const int hit = __builtin_ctzll(m);
-                const int rem = u - base - __builtin_amdgcn_readlane(incl - cnt, hit);
-                r.b = b0 + hit;
-                r.L = __builtin_amdgcn_readlane(L, hit);
-                if (part == 0) {
-                    r.hb = rem % nhb;
-                    r.c = rem / nhb;
-                } else {
-                    r.hb = rem;
-                    r.c = r.L / p.chunk;
+        for (int sb = 0; sb < p.batch; sb += 64 * KB) {
+            if (!resident) load(sb);
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int b0 = sb + 64 * k;
+                if (b0 >= p.batch) break;
+                const int b = b0 + lane;
+                const int L = b < p.batch ? min(max(raw[k], 0), p.max_seq_len) : -1;   // -1: no sequence
+                const int q = div_chunk(L < 0 ? 0 : L, p.chunk, rcp);
+                const int cnt = L < 0 ? 0 : part == 0 ? q * nhb : ((L != q * p.chunk || L == 0) ? nhb : 0);
+                const int incl = wave_scan(cnt);
+                const int total = __builtin_amdgcn_readlane(incl, 63);
+                if (u < base + total) {
+                    const uint64_t m = __ballot(base + incl > u);
+                    const int hit = __builtin_ctzll(m);
+                    if (hit > 63) return r;                  // not found (never with a valid scan)
+                    const int rem = u - base - __builtin_amdgcn_readlane(incl - cnt, hit);
+                    r.b = b0 + hit;
+                    r.L = __builtin_amdgcn_readlane(L, hit);
+                    if (r.b >= p.batch || r.L < 0) return r;
+                    if (part == 0) {
+                        r.hb = rem % nhb;
+                        r.c = rem / nhb;
+                    } else {
+                        r.hb = rem;
+                        r.c = div_chunk(r.L, p.chunk, rcp);
+                    }
+                    r.ok = true;
+                    return r;
                 }
-                r.ok = true;
-                return r;
+                base += total;
             }
-            base += total;
         }
     }
     return r;
