@@ -137,19 +137,44 @@ FD_DEV bool publish_unit(const Params &p, int rg, int nunits, int &flag)
 // One wavefront merges row (b, h): writes out[b][h][:] and fallback_flags[b][h]
 // and returns the row's number of recomputed chunks (in every lane).  Lanes
 // 0..31 take the even chunks and 32..63 the odd ones, 4 components per lane,
-// four chunk pairs in flight.
+// kMergePass chunks of the row per pass with all their loads in flight; the
+// first pass is loaded together with the chunk flags (its weights wait for
+// the flags), so a row of up to kMergePass chunks costs one memory round trip
+// when no chunk was recomputed.
+constexpr int kMergePass = 16;
+
 FD_DEV int merge_row(const Params &p, int b, int h, int lane)
 {
+    constexpr int PP = kMergePass / 2;          // chunks per half-wavefront per pass
     const int L = seq_len_of(p, b);
     const int nch = (L + p.chunk - 1) / p.chunk;
     const size_t base = part_slot(p, b, h, 0);   // chunk c at base + c * hq
     const size_t cs = p.hq;
+    const int half = lane >> 5, q4 = lane & 31;
+    const float *op = p.o_part + base * kHeadDim + 4 * q4;
+
+    // one pass of partials: chunk c0 + 2u + half (clamped to the last chunk:
+    // every load stays in the row, the extra ones are not added)
+    f32x4 v[PP];
+    float l[PP], m[PP];
+    auto load_pass = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < PP; ++u) {
+            const int c = min(c0 + 2 * u + half, nch - 1);
+            v[u] = get4(op + (size_t)c * cs * kHeadDim);
+            l[u] = get(p.l_part + base + c * cs);
+            m[u] = get(p.m_part + base + c * cs);
+        }
+    };
+    if (nch > 0) load_pass(0);
 
     // flagged chunks of the row, and the largest chunk maximum if any
     int nflag = 0;
-    for (int c = lane; c < nch; c += 64) nflag += get(p.cflag + base + c * cs);
-#pragma unroll
-    for (int x = 1; x < 64; x <<= 1) nflag += __shfl_xor(nflag, x);
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        const bool fl = c < nch && get(p.cflag + base + c * cs) != 0;
+        nflag += __popcll(__ballot(fl));
+    }
     const bool any = nflag != 0;
     float M = p.phi;
     if (any) {
@@ -159,34 +184,20 @@ FD_DEV int merge_row(const Params &p, int b, int h, int lane)
         for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
     }
 
-    const int half = lane >> 5, q4 = lane & 31;
-    const float *op = p.o_part + base * kHeadDim + 4 * q4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lacc = 0.f;
-    int c = half;
     // without a recomputed chunk every partial is against phi: plain sum;
     // otherwise each is rescaled from its own maximum to M
-    for (; c + 6 < nch; c += 8) {
-        f32x4 v[4];
-        float l[4], f[4];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lacc = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 2 * PP) {
+        if (c0 > 0) load_pass(c0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v[u] = get4(op + (size_t)(c + 2 * u) * cs * kHeadDim);
-            l[u] = get(p.l_part + base + (c + 2 * u) * cs);
-            f[u] = any ? get(p.m_part + base + (c + 2 * u) * cs) : M;
+        for (int u = 0; u < PP; ++u) {
+            if (c0 + 2 * u + half < nch) {
+                const float g = (m[u] == M) ? 1.f : exp2_hw((m[u] - M) * kLog2e);
+                acc += v[u] * g;
+                lacc = fmaf(l[u], g, lacc);
+            }
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float g = (f[u] == M) ? 1.f : exp2_hw((f[u] - M) * kLog2e);
-            acc += v[u] * g;
-            lacc = fmaf(l[u], g, lacc);
-        }
-    }
-    for (; c < nch; c += 2) {
-        const float mc = any ? get(p.m_part + base + c * cs) : M;
-        const float g = (mc == M) ? 1.f : exp2_hw((mc - M) * kLog2e);
-        acc += get4(op + (size_t)c * cs * kHeadDim) * g;
-        lacc = fmaf(get(p.l_part + base + c * cs), g, lacc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
@@ -250,13 +261,18 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
 
 // Separate merge launch (large grids): RW wavefronts per row, 256 threads per
 // workgroup (256 / (64 RW) rows each).  In a wavefront, lanes 0..31 take one
-// chunk and lanes 32..63 the next, 4 components per lane, four chunk pairs in
-// flight; the wavefronts of a row split its chunks and meet in LDS.  It also
-// adds the recomputed (row, chunk) pairs to the call's count.
+// chunk and lanes 32..63 the next, 4 components per lane; the wavefronts of a
+// row split its chunks and meet in LDS.  Each wavefront loads PP chunk pairs
+// per pass with all their loads in flight, the first pass together with the
+// chunk flags.  It also adds the recomputed (row, chunk) pairs to the call's
+// count.
 template <int RW>
 __global__ __launch_bounds__(256) void merge_kernel(Params p)
 {
     constexpr int ROWS = 4 / RW;
+    // chunk pairs per wavefront per pass: rows of fewer than 16 chunks (one
+    // wavefront each) take 2, longer rows 4
+    constexpr int PP = RW == 1 ? 2 : 4;
     __shared__ f32x4 red_o[4][32];
     __shared__ float red_l[4];
     __shared__ int red_n[4];
@@ -272,12 +288,31 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
     const size_t base = part_slot(p, b, h, 0);   // chunk c at base + c * hq
     const size_t cs = p.hq;
     const int rw0 = (wave / RW) * RW;                // first wavefront of this row
+    const int half = lane >> 5, q4 = lane & 31;
+    const float *op = p.o_part + base * kHeadDim + 4 * q4;
+    constexpr int STEP = 2 * RW;                     // chunks per pass step of all row waves
+
+    // one pass: chunk c0 + 2 sub + half + STEP u (clamped to the last chunk:
+    // every load stays in the row, the extra ones are not added)
+    f32x4 v[PP];
+    float l[PP], m[PP];
+    auto load_pass = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < PP; ++u) {
+            const int c = min(c0 + 2 * sub + half + STEP * u, nch - 1);
+            v[u] = *reinterpret_cast<const f32x4 *>(op + (size_t)c * cs * kHeadDim);
+            l[u] = p.l_part[base + c * cs];
+            m[u] = p.m_part[base + c * cs];
+        }
+    };
+    if (nch > 0) load_pass(0);
 
     // flagged chunks of the row, and the largest chunk maximum if any
     int nflag = 0;
-    for (int c = sub * 64 + lane; c < nch; c += 64 * RW) nflag += p.cflag[base + c * cs];
-#pragma unroll
-    for (int x = 1; x < 64; x <<= 1) nflag += __shfl_xor(nflag, x);
+    for (int c0 = sub * 64; c0 < nch; c0 += 64 * RW) {
+        const int c = c0 + lane;
+        nflag += __popcll(__ballot(c < nch && p.cflag[base + c * cs] != 0));
+    }
     if (RW > 1) {
         if (lane == 0) red_n[wave] = nflag;
         __syncthreads();
@@ -300,35 +335,20 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
         for (int w = 0; w < RW; ++w) M = fmaxf(M, red_m[rw0 + w]);
     }
 
-    const int half = lane >> 5, q4 = lane & 31;
-    const float *op = p.o_part + base * kHeadDim + 4 * q4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lacc = 0.f;
-    constexpr int STEP = 2 * RW;                     // chunks per pass of all row waves
-    int c = 2 * sub + half;
     // without a recomputed chunk every partial is against phi: plain sum;
     // otherwise each is rescaled from its own maximum to M
-    for (; c + 3 * STEP < nch; c += 4 * STEP) {
-        f32x4 v[4];
-        float l[4], f[4];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lacc = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += STEP * PP) {
+        if (c0 > 0) load_pass(c0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v[u] = *reinterpret_cast<const f32x4 *>(op + (size_t)(c + u * STEP) * cs * kHeadDim);
-            l[u] = p.l_part[base + (c + u * STEP) * cs];
-            f[u] = any ? p.m_part[base + (c + u * STEP) * cs] : M;
+        for (int u = 0; u < PP; ++u) {
+            if (c0 + 2 * sub + half + STEP * u < nch) {
+                const float g = (m[u] == M) ? 1.f : exp2_hw((m[u] - M) * kLog2e);
+                acc += v[u] * g;
+                lacc = fmaf(l[u], g, lacc);
+            }
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float g = (f[u] == M) ? 1.f : exp2_hw((f[u] - M) * kLog2e);
-            acc += v[u] * g;
-            lacc = fmaf(l[u], g, lacc);
-        }
-    }
-    for (; c < nch; c += STEP) {
-        const float mc = any ? p.m_part[base + c * cs] : M;
-        const float g = (mc == M) ? 1.f : exp2_hw((mc - M) * kLog2e);
-        acc += *reinterpret_cast<const f32x4 *>(op + (size_t)c * cs * kHeadDim) * g;
-        lacc = fmaf(p.l_part[base + c * cs], g, lacc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
