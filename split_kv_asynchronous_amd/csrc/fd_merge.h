@@ -246,8 +246,10 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
     // the last row group publishes the call's count and resets both words, so
     // a replay of the launch with the same epoch starts from zero.
     if (threadIdx.x == 0) {
-        if (total) epoch_add(p.fused_count, p.epoch, (uint32_t)total);
-        __builtin_amdgcn_s_waitcnt(0);
+        if (total) {
+            epoch_add(p.fused_count, p.epoch, (uint32_t)total);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         const uint32_t n = epoch_add(p.fused_word, p.epoch, 1);
         if ((int)n == p.ngroups) {
             const unsigned long long c = get(p.fused_count);

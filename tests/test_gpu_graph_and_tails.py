@@ -25,25 +25,29 @@ from gpu_helpers import DeviceProblem, compare
 pytestmark = pytest.mark.gpu
 
 REPLAY_CASES = [
-    # id, group, kv dtype, page size, lens, chunk -- fused (<= 512 units) and
-    # two-launch grids, grouped and single-query kernels
-    ("fused-gqa-bf16", 4, "bf16", 0, [700, 1500], 256),
-    ("fused-gqa-e4m3fn-paged", 8, "e4m3fn", 16, [2000, 900], 128),
-    ("split-gqa-bf16", 4, "bf16", 0, [8192, 6000, 8192, 5000], 256),
-    ("split-mha-bf16", 1, "bf16", 0, [3000] * 4, 64),
-    ("split-gqa-e4m3fn-paged", 4, "e4m3fn", 16, [4096, 3000, 2500, 4000], 128),
+    # id, group, kv dtype, page size, lens, chunk, merge placement -- the merge
+    # inside the chunk launch and in a second launch, grouped and
+    # single-query kernels, small grids and grids of many rounds
+    ("fused-gqa-bf16", 4, "bf16", 0, [700, 1500], 256, "fused"),
+    ("fused-gqa-e4m3fn-paged", 8, "e4m3fn", 16, [2000, 900], 128, "fused"),
+    ("fused-large-gqa-bf16", 8, "bf16", 0, [20000, 9000, 15000, 30000], 256, "fused"),
+    ("split-gqa-bf16", 4, "bf16", 0, [8192, 6000, 8192, 5000], 256, "split"),
+    ("split-mha-bf16", 1, "bf16", 0, [3000] * 4, 64, "split"),
+    ("split-gqa-e4m3fn-paged", 4, "e4m3fn", 16, [4096, 3000, 2500, 4000], 128, "split"),
 ]
 
 
-@pytest.mark.parametrize("name,g,kv,page,lens,chunk", REPLAY_CASES, ids=[c[0] for c in REPLAY_CASES])
-def test_decode_replayed_from_a_captured_graph(name, g, kv, page, lens, chunk):
+@pytest.mark.parametrize("name,g,kv,page,lens,chunk,place", REPLAY_CASES, ids=[c[0] for c in REPLAY_CASES])
+def test_decode_replayed_from_a_captured_graph(name, g, kv, page, lens, chunk, place):
+    import split_kv_asynchronous_amd as fd
     hkv = 2 if g > 1 else 8
     # a narrow band, so that chunks leave it and are recomputed
     prob = synthetic.make_problem(batch=len(lens), num_q_heads=g * hkv, num_kv_heads=hkv, seq_lens=lens,
                                   kv_dtype=kv, page_size=page, chunk_size=chunk, phi=1.0, a=3.0, b=1.5,
                                   seed=600 + g)
     print("case replay %s" % name, flush=True)
-    dp = DeviceProblem(prob)
+    dp = DeviceProblem(prob, plan=fd.FD_PLAN_FUSED if place == "fused" else fd.FD_PLAN_SPLIT)
+    assert fd.fd_attn_plan(dp.desc())["fused"] == (place == "fused")
     dp.run()
     out0, flags0 = dp.results()
     count0 = dp.recomputed()
