@@ -36,14 +36,24 @@
 namespace fd {
 
 // Adds `add` to an epoch-tagged counter and returns the count after the add.
-// Once the word carries this call's epoch (it never loses it again within the
-// call) the add is one fetch-and-add; only the re-basing of a word left by an
-// earlier call takes a compare-and-swap, and a racing re-base makes the loser
-// retry through the fetch-and-add path.  (A compare-and-swap loop for every
-// add serialises the many units of a row group that finish together.)
+// The add is one fetch-and-add; it counts if the word it returns carries this
+// call's epoch (once a word has it, it keeps it for the rest of the call).
+// An add that returns an older epoch landed on a word left by an earlier call
+// and is void: the word is re-based to this call's epoch by a
+// compare-and-swap, whose winner's add is the first of the call, and the
+// losers add again once the word carries the epoch.  Every add made before
+// the re-base is overwritten by it, and none can follow it, so each counted
+// add is counted once.  (The earlier form read the word before every add: two
+// round trips on the unit that completes a row group, whose merge then waits
+// for them.)  A call that completes a counter leaves it at zero tagged with
+// the next epoch the host will hand out (next_tag), so that on the next call
+// on this workspace -- the usual case -- every add counts at once.
 FD_DEV uint32_t epoch_add(unsigned long long *w, uint32_t epoch, uint32_t add)
 {
-    unsigned long long v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long v = __hip_atomic_fetch_add(w, (unsigned long long)add, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(v >> 32) == epoch) return (uint32_t)v + add;
+    v += add;                                      // the word as this void add left it
     for (;;) {
         if ((uint32_t)(v >> 32) == epoch)
             return (uint32_t)__hip_atomic_fetch_add(w, (unsigned long long)add, __ATOMIC_RELAXED,
@@ -52,6 +62,14 @@ FD_DEV uint32_t epoch_add(unsigned long long *w, uint32_t epoch, uint32_t add)
                                                  __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             return add;
     }
+}
+
+// A zero count tagged with the epoch the host hands out after `epoch` (it
+// counts up and skips 0).  Any other call finds it stale and re-bases it.
+FD_DEV unsigned long long next_tag(uint32_t epoch)
+{
+    const uint32_t e = epoch + 1 == 0 ? 1u : epoch + 1;
+    return (unsigned long long)e << 32;
 }
 
 // Device-coherent stores and loads of partials.
@@ -127,8 +145,9 @@ FD_DEV bool publish_unit(const Params &p, int rg, int nunits, int &flag)
     if (threadIdx.x == 0) {
         const uint32_t n = epoch_add(p.rg_count + rg, p.epoch, 1);
         flag = n == (uint32_t)nunits;
-        // the row group is complete: reset its count for a replay of this launch
-        if (flag) put(p.rg_count + rg, (unsigned long long)p.epoch << 32);
+        // the row group is complete: zero its count for the next call (a
+        // replay of this launch with the same epoch re-bases it)
+        if (flag) put(p.rg_count + rg, next_tag(p.epoch));
     }
     __syncthreads();
     return flag != 0;
@@ -243,8 +262,8 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
     __syncthreads();
     // The row group's recomputed pairs go into the call's fused count, then
     // (once that add has completed) one into the count of merged row groups;
-    // the last row group publishes the call's count and resets both words, so
-    // a replay of the launch with the same epoch starts from zero.
+    // the last row group publishes the call's count and zeroes both words for
+    // the next call (a replay of the launch with the same epoch re-bases them).
     if (threadIdx.x == 0) {
         if (total) {
             epoch_add(p.fused_count, p.epoch, (uint32_t)total);
@@ -255,8 +274,8 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
             const unsigned long long c = get(p.fused_count);
             const uint32_t cnt = (uint32_t)(c >> 32) == p.epoch ? (uint32_t)c : 0u;
             put(p.count_word, ((unsigned long long)p.epoch << 32) | cnt);
-            put(p.fused_word, (unsigned long long)p.epoch << 32);
-            put(p.fused_count, (unsigned long long)p.epoch << 32);
+            put(p.fused_word, next_tag(p.epoch));
+            put(p.fused_count, next_tag(p.epoch));
         }
     }
 }
