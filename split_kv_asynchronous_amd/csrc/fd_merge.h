@@ -91,9 +91,12 @@ FD_DEV T get(const T *ptr)
     return __hip_atomic_load(const_cast<T *>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-FD_DEV f32x4 get4(const float *ptr)
+// Two consecutive floats in one 8-byte device-coherent load.
+FD_DEV f32x2 get2(const float *ptr)
 {
-    return f32x4{get(ptr), get(ptr + 1), get(ptr + 2), get(ptr + 3)};
+    const unsigned long long u = __hip_atomic_load(reinterpret_cast<unsigned long long *>(const_cast<float *>(ptr)),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x2{__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32))};
 }
 
 // Partial stores: device-coherent when the chunk kernel merges (another
@@ -153,103 +156,149 @@ FD_DEV bool publish_unit(const Params &p, int rg, int nunits, int &flag)
     return flag != 0;
 }
 
-// One wavefront merges row (b, h): writes out[b][h][:] and fallback_flags[b][h]
-// and returns the row's number of recomputed chunks (in every lane).  Lanes
-// 0..31 take the even chunks and 32..63 the odd ones, 4 components per lane,
-// kMergePass chunks of the row per pass with all their loads in flight; the
-// first pass is loaded together with the chunk flags (its weights wait for
-// the flags), so a row of up to kMergePass chunks costs one memory round trip
-// when no chunk was recomputed.
+// One wavefront merges up to R rows (b, h[0..nr-1]) at once: writes
+// out[b][h][:] and fallback_flags[b][h] and returns the rows' number of
+// recomputed chunks (in every lane).  Lane i holds components 2i and 2i + 1,
+// so each 8-byte device-coherent load instruction reads one chunk's whole
+// 512-byte partial (a 4-byte load per component, or 16-byte pieces split into
+// four such loads, fetch every line several times: these loads bypass the
+// L2).  kMergePass chunks of every row are in flight per pass; weight sums,
+// maxima and flags sit one chunk per lane (64 chunks at a time), are loaded
+// with the first pass, and reach the other lanes as scalars, so rows of up to
+// kMergePass chunks cost one memory round trip together when no chunk was
+// recomputed.  This runs at the end of the launch (the last unit of each row
+// group), where only such round trips are left to wait on.
 constexpr int kMergePass = 16;
 
-FD_DEV int merge_row(const Params &p, int b, int h, int lane)
+template <int R>
+FD_DEV int merge_rows(const Params &p, int b, const int (&h)[R], int nr, int lane)
 {
-    constexpr int PP = kMergePass / 2;          // chunks per half-wavefront per pass
+    constexpr int PC = kMergePass;
     const int L = seq_len_of(p, b);
     const int nch = (L + p.chunk - 1) / p.chunk;
-    const size_t base = part_slot(p, b, h, 0);   // chunk c at base + c * hq
-    const size_t cs = p.hq;
-    const int half = lane >> 5, q4 = lane & 31;
-    const float *op = p.o_part + base * kHeadDim + 4 * q4;
+    const size_t cs = p.hq;                      // chunk c of a row at its base + c * hq
+    size_t base[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) base[r] = part_slot(p, b, h[r < nr ? r : 0], 0);
 
-    // one pass of partials: chunk c0 + 2u + half (clamped to the last chunk:
-    // every load stays in the row, the extra ones are not added)
-    f32x4 v[PP];
-    float l[PP], m[PP];
+    // one pass of partials: chunks c0 .. c0 + PC - 1 (clamped to the last
+    // chunk: every load stays in the row, the extra ones are not added)
+    f32x2 v[R][PC];
     auto load_pass = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < PP; ++u) {
-            const int c = min(c0 + 2 * u + half, nch - 1);
-            v[u] = get4(op + (size_t)c * cs * kHeadDim);
-            l[u] = get(p.l_part + base + c * cs);
-            m[u] = get(p.m_part + base + c * cs);
+        for (int r = 0; r < R; ++r) {
+            if (r >= nr) break;
+            const float *op = p.o_part + base[r] * kHeadDim + 2 * lane;
+#pragma unroll
+            for (int u = 0; u < PC; ++u) v[r][u] = get2(op + (size_t)min(c0 + u, nch - 1) * cs * kHeadDim);
         }
     };
-    if (nch > 0) load_pass(0);
-
-    // flagged chunks of the row, and the largest chunk maximum if any
-    int nflag = 0;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-        const int c = c0 + lane;
-        const bool fl = c < nch && get(p.cflag + base + c * cs) != 0;
-        nflag += __popcll(__ballot(fl));
-    }
-    const bool any = nflag != 0;
-    float M = p.phi;
-    if (any) {
-        M = -INFINITY;
-        for (int c = lane; c < nch; c += 64) M = fmaxf(M, get(p.m_part + base + c * cs));
+    // chunk c64 + lane of every row: weight sum, maximum, flag
+    float lc[R], mc[R];
+    int fc[R];
+    auto load_lane = [&](int c64) {
+        const int c = min(c64 + lane, nch - 1);
 #pragma unroll
-        for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
-    }
-
-    // without a recomputed chunk every partial is against phi: plain sum;
-    // otherwise each is rescaled from its own maximum to M
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lacc = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 2 * PP) {
-        if (c0 > 0) load_pass(c0);
-#pragma unroll
-        for (int u = 0; u < PP; ++u) {
-            if (c0 + 2 * u + half < nch) {
-                const float g = (m[u] == M) ? 1.f : exp2_hw((m[u] - M) * kLog2e);
-                acc += v[u] * g;
-                lacc = fmaf(l[u], g, lacc);
-            }
+        for (int r = 0; r < R; ++r) {
+            if (r >= nr) break;
+            lc[r] = get(p.l_part + base[r] + c * cs);
+            mc[r] = get(p.m_part + base[r] + c * cs);
+            fc[r] = get(p.cflag + base[r] + c * cs);
         }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], 32);
-    lacc += __shfl_xor(lacc, 32);
-
-    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+    };
     if (nch > 0) {
-        float vs = 1.f;
-        if (p.v_scale) vs = p.v_scale[h / p.group];
-        r = acc * (vs / lacc);
+        load_pass(0);
+        load_lane(0);
     }
-    const size_t row = (size_t)b * p.hq + h;
-    if (half == 0) {
-        if (p.out_bf16) {
-            uint32_t w[4];
+
+    // flagged chunks of each row, and the largest chunk maximum if any
+    int nflag[R];
+    float M[R];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t u = __float_as_uint(r[i]);
-                w[i] = (r[i] != r[i]) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-            }
-            reinterpret_cast<u32x2 *>(p.out)[row * (kHeadDim / 4) + q4] = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+    for (int r = 0; r < R; ++r) {
+        if (r >= nr) break;
+        nflag[r] = __popcll(__ballot(lane < nch && fc[r] != 0));
+        M[r] = lane < nch ? mc[r] : -INFINITY;
+        for (int c = 64 + lane; c - lane < nch; c += 64) {     // rows of more than 64 chunks
+            const bool in = c < nch;
+            const int cc = in ? c : nch - 1;
+            nflag[r] += __popcll(__ballot(in && get(p.cflag + base[r] + cc * cs) != 0));
+            if (in) M[r] = fmaxf(M[r], get(p.m_part + base[r] + cc * cs));
+        }
+        if (nflag[r]) {
+#pragma unroll
+            for (int x = 1; x < 64; x <<= 1) M[r] = fmaxf(M[r], __shfl_xor(M[r], x));
         } else {
-            reinterpret_cast<f32x4 *>(p.out)[row * (kHeadDim / 4) + q4] = r;
+            M[r] = p.phi;
         }
     }
-    if (lane == 0) p.flags[row] = any ? 1 : 0;
-    return nflag;
+
+    // without a recomputed chunk every partial is against phi (weight 1):
+    // plain sum; otherwise each is rescaled from its own maximum to M
+    f32x2 acc[R];
+    float lsum[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc[r] = f32x2{0.f, 0.f};
+        lsum[r] = 0.f;
+    }
+    for (int c0 = 0; c0 < nch; c0 += PC) {
+        if (c0 > 0) {
+            load_pass(c0);
+            if (c0 % 64 == 0) load_lane(c0);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r >= nr) break;
+            const float gl = (mc[r] == M[r]) ? 1.f : exp2_hw((mc[r] - M[r]) * kLog2e);
+            if (c0 % 64 == 0 && c0 + lane < nch) lsum[r] = fmaf(lc[r], gl, lsum[r]);
+            const int o = c0 % 64;
+#pragma unroll
+            for (int u = 0; u < PC; ++u) {
+                if (c0 + u < nch) {
+                    const float g = nflag[r] ? __builtin_amdgcn_readlane(__float_as_int(gl), o + u) : 0;
+                    acc[r] += nflag[r] ? v[r][u] * __int_as_float(g) : v[r][u];
+                }
+            }
+        }
+    }
+
+    int total = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r >= nr) break;
+        total += nflag[r];
+        float lacc = lsum[r];
+#pragma unroll
+        for (int x = 1; x < 64; x <<= 1) lacc += __shfl_xor(lacc, x);
+        f32x2 res = {0.f, 0.f};
+        if (nch > 0) {
+            float vs = 1.f;
+            if (p.v_scale) vs = p.v_scale[h[r] / p.group];
+            res = acc[r] * (vs / lacc);
+        }
+        const size_t row = (size_t)b * p.hq + h[r];
+        if (p.out_bf16) {
+            uint32_t w[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t u = __float_as_uint(res[i]);
+                w[i] = (res[i] != res[i]) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+            }
+            reinterpret_cast<uint32_t *>(p.out)[row * (kHeadDim / 2) + lane] = w[0] | (w[1] << 16);
+        } else {
+            reinterpret_cast<f32x2 *>(p.out)[row * (kHeadDim / 2) + lane] = res;
+        }
+        if (lane == 0) p.flags[row] = nflag[r] ? 1 : 0;
+    }
+    return total;
 }
 
 // The last workgroup of a row group merges rows (b, h0 .. h0 + nrows - 1),
-// its NW wavefronts taking rows round-robin, and adds the row group's
-// recomputed chunks to the call's count.  `total` is a workgroup-shared int.
-template <int NW>
+// its NW wavefronts taking rows round-robin, R at a time, and adds the row
+// group's recomputed chunks to the call's count.  `total` is a
+// workgroup-shared int.
+template <int NW, int R = 2>
 FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
 {
     const int lane = threadIdx.x & 63;
@@ -257,7 +306,12 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
     if (threadIdx.x == 0) total = 0;
     __syncthreads();
     int mine = 0;
-    for (int r = wave; r < nrows; r += NW) mine += merge_row(p, b, h0 + r, lane);
+    for (int r = wave; r < nrows; r += R * NW) {
+        int h[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) h[k] = h0 + r + k * NW;
+        mine += merge_rows<R>(p, b, h, min(R, (nrows - 1 - r) / NW + 1), lane);
+    }
     if (lane == 0 && mine) atomicAdd(&total, mine);
     __syncthreads();
     // The row group's recomputed pairs go into the call's fused count, then

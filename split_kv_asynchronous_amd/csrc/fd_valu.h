@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
     // softmax and overwrites the partial (the chunk flag stays set)
     if (valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, t1, red))
         valu_chunk<KV, QT, PAGED, true, 4>(p, b, h, c, t0, t1, red);
-    if (publish_unit(p, b * p.hq + h, units_of(p, L), last_flag)) merge_group<4>(p, b, h, 1, merged);
+    if (publish_unit(p, b * p.hq + h, units_of(p, L), last_flag)) merge_group<4, 1>(p, b, h, 1, merged);
 }
 
 }  // namespace fd
