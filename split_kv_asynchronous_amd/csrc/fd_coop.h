@@ -438,12 +438,24 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     // lane (g4, n) holds components 16*(DT*w + dl) + 4*g4 .. +3 of head h0 + n
     const size_t slot = part_slot(p, b, h0 + (head_ok ? n : 0), c);
     float *orow = p.o_part + slot * kHeadDim + 16 * DT * wave + 4 * g4;
+    // Partials of a fused call are read by another workgroup during the
+    // launch: one 16-byte device-coherent store per piece, through a buffer
+    // range over the block's heads (the partials of one chunk of a sequence
+    // are contiguous over the heads), instead of four 4-byte coherent stores.
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        p.o_part + part_slot(p, b, h0, c) * kHeadDim, (short)0, GB * kHeadDim * 4, 0x00020000);
+    const int ooff = 4 * ((head_ok ? n : 0) * kHeadDim + 16 * DT * wave + 4 * g4);
+    auto store_o = [&](int dl) {
+        if (p.fused) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[dl]), prs, ooff + 64 * dl, 0,
+                                                            kCoherentPolicy);
+        else __builtin_nontemporal_store(o[dl], reinterpret_cast<f32x4 *>(orow + 16 * dl));
+    };
 
     // ---- unified-max pass
     run(std::false_type{});
     if (head_ok) {
 #pragma unroll
-        for (int dl = 0; dl < DT; ++dl) part_store4(p, orow + 16 * dl, o[dl]);
+        for (int dl = 0; dl < DT; ++dl) store_o(dl);
         if (wave == 0 && g4 == 0) {
             part_store(p, p.l_part + slot, lsum);
             part_store(p, p.m_part + slot, p.phi);
@@ -460,7 +472,7 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
         run(std::true_type{});
         if (head_ok && ((fmask >> n) & 1)) {
 #pragma unroll
-            for (int dl = 0; dl < DT; ++dl) part_store4(p, orow + 16 * dl, o[dl]);
+            for (int dl = 0; dl < DT; ++dl) store_o(dl);
             if (wave == 0 && g4 == 0) {
                 part_store(p, p.l_part + slot, lsum);
                 part_store(p, p.m_part + slot, mrun);
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     }
 
     // ---- publish the unit; the last unit of the row group merges it
-    if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) merge_group<S::waves>(p, b, h0, GB, merged);
+    if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) merge_group<S::waves, 1>(p, b, h0, GB, merged);
 }
 
 }  // namespace coop

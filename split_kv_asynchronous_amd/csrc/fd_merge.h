@@ -79,12 +79,6 @@ FD_DEV void put(T *ptr, T v)
     __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-FD_DEV void put4(float *ptr, f32x4 v)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) put(ptr + i, v[i]);
-}
-
 template <typename T>
 FD_DEV T get(const T *ptr)
 {
@@ -108,12 +102,6 @@ FD_DEV void part_store(const Params &p, T *ptr, T v)
 {
     if (p.fused) put(ptr, v);
     else __builtin_nontemporal_store(v, ptr);
-}
-
-FD_DEV void part_store4(const Params &p, float *ptr, f32x4 v)
-{
-    if (p.fused) put4(ptr, v);
-    else __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ptr));
 }
 
 // First thing of a call, in one thread of the chunk launch.  With a separate

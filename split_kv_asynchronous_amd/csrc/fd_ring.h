@@ -20,6 +20,10 @@ constexpr int kGroupBytes = 4096;   // one compute group of K (or V): 16 bf16 or
 // non-temporal partial stores.
 constexpr int kStreamPolicy = 2;
 
+// Cache policy of a device-coherent (agent-scope) buffer access: sc1, the
+// bit an agent-scope atomic load or store carries.
+constexpr int kCoherentPolicy = 16;
+
 // Per storage format: row bytes, tokens per compute group, piece rotation.
 // A cache row is moved into LDS as 16-byte pieces; piece j of group row t
 // lands in slot (j + rot(t)) mod slots, which keeps the K fragment reads
