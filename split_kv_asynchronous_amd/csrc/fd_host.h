@@ -73,55 +73,56 @@ constexpr int kShapes[3] = {3, 3, 1};
 // max_seq_len is at most max_len (rows in ascending max_len; the last row of
 // a family takes every longer call): the chunk size for chunk_size == 0, the
 // kernel shape at that chunk size (other chunk sizes run shape 0), and the
-// largest grid (units of sequence x head block x chunk) that merges inside
-// the chunk launch (kAllUnits: every grid).
+// largest chunk size whose calls merge inside the chunk launch (0: none).
+// Grids of at most kSmallGrid units (sequence x head block x chunk), one
+// round of workgroups, merge inside the launch whatever the row says.
 struct TableRow {
-    int family, paged, max_len, chunk, shape;
-    int64_t fused_units;
+    int family, paged, max_len, chunk, shape, fused_chunk;
 };
 
-constexpr int64_t kAllUnits = (int64_t)1 << 62;
+constexpr int64_t kSmallGrid = 512;
 
 // Measured on MI355X: calls replayed back to back (best of 3 x 10), every
 // chunk size 256 .. 4096 x every shape x both merge placements, on ragged
 // synthetic batches of each family, paging and length range (whole-call
 // TB/s of K/V; best against the runner-up):
-//   grouped bf16, 64/8 heads: 256 x U[256,2K] 5.66 (chunk 2048) ; 64 x
-//     U[1K,8K] 6.12 (4096, 4 waves x 3 stages; 2048: 5.94) ; 32 x U[1K,32K]
-//     6.27 (2048; merged in the launch 6.27, at 1024 6.11 both ways) ;
-//     4 x U[32K,128K] 6.11 (1024; 2048: 6.07) ; paged: 5.52, 5.98, 6.24, 5.92
-//   grouped E4M3FN, 32/8 heads: 512 x U[256,2K] 5.02 (1024) ; 64 x
-//     U[512,16K] 5.64 (1024, 2 waves x 4 stages; 3 stages 5.60; 512: 5.37) ;
-//     16 x U[16K,64K] 5.62 (2048) ; paged: 4.90, 5.48, 5.57
+//   grouped bf16, 64/8 heads: 256 x U[256,2K] 5.76 (chunk 2048) ; 64 x
+//     U[1K,8K] 6.12 (4096, 4 waves x 3 stages; 1024: 6.04) ; 32 x U[1K,32K]
+//     6.32 (2048; 1024: 6.17, merged in the launch 6.22) ; 4 x U[32K,128K]
+//     6.09 (1024; 2048: 5.91) ; paged: 5.56, 5.98, 6.28 (in the launch), 5.92
+//   grouped E4M3FN, 32/8 heads: 512 x U[256,2K] 5.32 (1024) ; 64 x
+//     U[512,16K] 5.75 (1024, in the launch; 512 in the launch 5.64) ;
+//     16 x U[16K,64K] 5.75 (2048) ; paged: 5.16, 5.59 (in the launch), 5.69
 //   one query per KV head, 32 heads: 64 x 2K 6.77 (2048) ; 8 x 8K 6.66
 //     (2048; 1024: 6.37) ; 1 x 128K 6.66 (4096; 1024: 6.60) ; paged: 6.49,
 //     6.35, 6.50
-// The merge inside the chunk launch lost on every large grid (by up to 40%)
-// except the grouped bf16 calls up to 32K, where it ties (within 0.1%) and
-// saves the second launch; small grids (<= 512 units, one round of
-// workgroups) merge in the launch everywhere (a 4K single-head call: 63 ->
-// 37 us).
+// Merging inside the chunk launch against a second launch, by chunk size:
+// ahead by 1-9% at chunks of 256-512 (up to 1024 for E4M3FN up to 16K and
+// bf16 up to 32K, 2048 paged), level at 2048, behind by 2-6% at 4096, on
+// the longest rows (64K-128K: more chunks per row to merge at the end of
+// the launch) and on short E4M3FN rows at chunks of 1024 and more; the
+// one-query-per-KV-head kernel was 3-60% behind at every chunk size.
 inline constexpr TableRow kTable[] = {
-    {kFamGroupedBf16, 0, 2048, 2048, 0, 512},
+    {kFamGroupedBf16, 0, 2048, 2048, 0, 0},
     {kFamGroupedBf16, 0, 8192, 4096, 1, 512},
-    {kFamGroupedBf16, 0, 32768, 2048, 0, kAllUnits},
-    {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 512},
-    {kFamGroupedBf16, 1, 2048, 2048, 0, 512},
+    {kFamGroupedBf16, 0, 32768, 2048, 0, 1024},
+    {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 0},
+    {kFamGroupedBf16, 1, 2048, 2048, 0, 0},
     {kFamGroupedBf16, 1, 8192, 4096, 1, 512},
-    {kFamGroupedBf16, 1, 32768, 2048, 0, kAllUnits},
-    {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 512},
+    {kFamGroupedBf16, 1, 32768, 2048, 0, 2048},
+    {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 0},
     {kFamGroupedFp8, 0, 2048, 1024, 0, 512},
-    {kFamGroupedFp8, 0, 16384, 1024, 2, 512},
-    {kFamGroupedFp8, 0, 1 << 23, 2048, 0, 512},
+    {kFamGroupedFp8, 0, 16384, 1024, 0, 1024},
+    {kFamGroupedFp8, 0, 1 << 23, 2048, 0, 0},
     {kFamGroupedFp8, 1, 2048, 1024, 0, 512},
-    {kFamGroupedFp8, 1, 16384, 1024, 2, 512},
-    {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 512},
-    {kFamVector, 0, 2048, 2048, 0, 512},
-    {kFamVector, 0, 8192, 2048, 0, 512},
-    {kFamVector, 0, 1 << 23, 4096, 0, 512},
-    {kFamVector, 1, 2048, 2048, 0, 512},
-    {kFamVector, 1, 8192, 2048, 0, 512},
-    {kFamVector, 1, 1 << 23, 4096, 0, 512},
+    {kFamGroupedFp8, 1, 16384, 1024, 0, 1024},
+    {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 0},
+    {kFamVector, 0, 2048, 2048, 0, 0},
+    {kFamVector, 0, 8192, 2048, 0, 0},
+    {kFamVector, 0, 1 << 23, 4096, 0, 0},
+    {kFamVector, 1, 2048, 2048, 0, 0},
+    {kFamVector, 1, 8192, 2048, 0, 0},
+    {kFamVector, 1, 1 << 23, 4096, 0, 0},
 };
 
 inline const TableRow &table_row(const fd_attn_desc_t *d)
@@ -166,7 +167,7 @@ inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
     const int blocks = pl->family == kFamVector ? d->num_q_heads
                                                 : d->num_q_heads / heads_per_block(d->num_q_heads / d->num_kv_heads);
     const int64_t units = maxch * blocks * d->batch;
-    pl->fused = place == FD_PLAN_FUSED ? 1 : place == FD_PLAN_SPLIT ? 0 : units <= r.fused_units;
+    pl->fused = place == FD_PLAN_FUSED ? 1 : place == FD_PLAN_SPLIT ? 0 : units <= kSmallGrid || pl->chunk <= r.fused_chunk;
     return FD_OK;
 }
 

@@ -285,48 +285,57 @@ def test_flat_gemm_table_covers_the_7b_layers():
 
 # The plan table (measured on MI355X; the rows of fd_host.h): per kernel
 # family, paging and max_seq_len range, the chunk size for chunk_size = 0, the
-# kernel shape at that chunk, and whether a large grid merges in the launch.
+# kernel shape at that chunk, and the largest chunk size whose calls merge in
+# the launch (0: none; grids of one round of workgroups always do).
 FAMILY_KW = {0: dict(), 1: dict(kv_dtype="e4m3fn"), 2: dict(num_kv_heads=64)}
 PLAN_ROWS = [
-    # family, paged, max_seq_len probes, chunk, shape, large grid merged in the launch
-    (0, 0, (1, 2048), 2048, 0, False), (0, 0, (2049, 8192), 4096, 1, False),
-    (0, 0, (8193, 32768), 2048, 0, True), (0, 0, (32769, 1 << 20), 1024, 0, False),
-    (0, 1, (16, 2048), 2048, 0, False), (0, 1, (2064, 8192), 4096, 1, False),
-    (0, 1, (8208, 32768), 2048, 0, True), (0, 1, (32784, 1 << 20), 2048, 0, False),
-    (1, 0, (1, 2048), 1024, 0, False), (1, 0, (2049, 16384), 1024, 2, False),
-    (1, 0, (16385, 1 << 20), 2048, 0, False),
-    (1, 1, (16, 2048), 1024, 0, False), (1, 1, (2064, 16384), 1024, 2, False),
-    (1, 1, (16400, 1 << 20), 2048, 0, False),
-    (2, 0, (1, 2048), 2048, 0, False), (2, 0, (2049, 8192), 2048, 0, False),
-    (2, 0, (8193, 1 << 20), 4096, 0, False),
-    (2, 1, (16, 2048), 2048, 0, False), (2, 1, (2064, 8192), 2048, 0, False),
-    (2, 1, (8208, 1 << 20), 4096, 0, False),
+    # family, paged, max_seq_len probes, chunk, shape, largest chunk merged in the launch
+    (0, 0, (1, 2048), 2048, 0, 0), (0, 0, (2049, 8192), 4096, 1, 512),
+    (0, 0, (8193, 32768), 2048, 0, 1024), (0, 0, (32769, 1 << 20), 1024, 0, 0),
+    (0, 1, (16, 2048), 2048, 0, 0), (0, 1, (2064, 8192), 4096, 1, 512),
+    (0, 1, (8208, 32768), 2048, 0, 2048), (0, 1, (32784, 1 << 20), 2048, 0, 0),
+    (1, 0, (1, 2048), 1024, 0, 512), (1, 0, (2049, 16384), 1024, 0, 1024),
+    (1, 0, (16385, 1 << 20), 2048, 0, 0),
+    (1, 1, (16, 2048), 1024, 0, 512), (1, 1, (2064, 16384), 1024, 0, 1024),
+    (1, 1, (16400, 1 << 20), 2048, 0, 0),
+    (2, 0, (1, 2048), 2048, 0, 0), (2, 0, (2049, 8192), 2048, 0, 0),
+    (2, 0, (8193, 1 << 20), 4096, 0, 0),
+    (2, 1, (16, 2048), 2048, 0, 0), (2, 1, (2064, 8192), 2048, 0, 0),
+    (2, 1, (8208, 1 << 20), 4096, 0, 0),
 ]
 
 
-@pytest.mark.parametrize("fam,paged,lens,chunk,shape,fused_big", PLAN_ROWS)
-def test_plan_table(fam, paged, lens, chunk, shape, fused_big):
+@pytest.mark.parametrize("fam,paged,lens,chunk,shape,fused_chunk", PLAN_ROWS)
+def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk):
     for L in lens:
         kw = dict(FAMILY_KW[fam], max_seq_len=L, chunk_size=0, batch=256)
         if paged:
             kw.update(page_size=16, max_blocks_per_seq=-(-L // 16), num_pages=5)
         d = _desc(**kw)
         got = fd.fd_attn_plan(d)
-        big = -(-L // chunk) * 256 * (8 if fam != 2 else 64) > 512
-        assert got == dict(chunk_size=max(chunk, 16 if paged else 0), family=fam, shape=shape,
-                           fused=int(fused_big or not big)), (kw, got)
+        c = max(chunk, 16 if paged else 0)
+        blocks = 8 if fam != 2 else 64
+        big = -(-L // c) * 256 * blocks > 512
+        assert got == dict(chunk_size=c, family=fam, shape=shape, fused=int(c <= fused_chunk or not big)), (kw, got)
         # the workspace follows the plan's chunk
         assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
-        # an explicit chunk size other than the table's runs shape 0
-        other = 512 if chunk != 512 else 256
-        assert fd.fd_attn_plan(_desc(**dict(kw, chunk_size=other)))["shape"] == 0
+        # an explicit chunk size other than the table's runs shape 0, and
+        # merges in the launch up to the row's largest such chunk
+        for other in (256, 512, 2048, 4096):
+            if other == chunk or other % (16 if paged else 32):
+                continue
+            p = fd.fd_attn_plan(_desc(**dict(kw, chunk_size=other)))
+            big = -(-L // other) * 256 * blocks > 512
+            assert p["shape"] == 0 and p["fused"] == int(other <= fused_chunk or not big), (kw, other, p)
 
 
 def test_plan_small_grids_merge_in_the_launch_and_forced_plans():
     small = _desc(batch=1, num_q_heads=8, num_kv_heads=1, max_seq_len=4096, chunk_size=1024)
     assert fd.fd_attn_plan(small)["fused"] == 1
     big = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=512)
-    assert fd.fd_attn_plan(big) == dict(chunk_size=512, family=1, shape=0, fused=0)
+    assert fd.fd_attn_plan(big) == dict(chunk_size=512, family=1, shape=0, fused=1)
+    big = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=2048)
+    assert fd.fd_attn_plan(big) == dict(chunk_size=2048, family=1, shape=0, fused=0)
     forced = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=512,
                    plan=fd.FD_PLAN_SHAPE(2) | fd.FD_PLAN_FUSED)
     assert fd.fd_attn_plan(forced) == dict(chunk_size=512, family=1, shape=2, fused=1)
