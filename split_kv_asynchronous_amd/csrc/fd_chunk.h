@@ -429,16 +429,16 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
         __syncthreads();
     };
 
+    // A row group whose sequence is this one chunk (or empty) needs no merge:
+    // in a fused call the unit writes its rows' outputs and flags itself, in
+    // the merge's arithmetic (the chunk's sum times v_scale over its weight
+    // sum; an empty row is zero), and stores no partial.
+    const bool direct = p.fused && L <= p.chunk;
+    const float vs = FP8 ? p.v_scale[kvh] : 1.f;
+    const size_t row0 = (size_t)b * p.hq + h0;
+
     // ---- unified-max pass: plain sums over the waves
     run(std::false_type{});
-    for (int idx = threadIdx.x; idx < GB * kHeadDim; idx += NW * 64) {
-        const int hh = idx >> 7, d = idx & 127;
-        float acc = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) acc += red[w2 * kRedStride + d * 16 + hh];
-        const size_t slot = part_slot(p, b, h0 + hh, c);
-        part_store(p, p.o_part + slot * kHeadDim + d, acc);
-    }
     if (wave == 0) {
         int f = 0;
         float l = 0.f;
@@ -448,20 +448,38 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
                 l += red[w2 * kRedStride + 2048 + lane];
                 f |= red[w2 * kRedStride + 2064 + lane] != 0.f;
             }
-            const size_t slot = part_slot(p, b, h0 + lane, c);
-            part_store(p, p.l_part + slot, l);
-            part_store(p, p.m_part + slot, p.phi);
-            part_store(p, p.cflag + slot, (uint8_t)f);
+            if (!direct) {
+                const size_t slot = part_slot(p, b, h0 + lane, c);
+                part_store(p, p.l_part + slot, l);
+                part_store(p, p.m_part + slot, p.phi);
+                part_store(p, p.cflag + slot, (uint8_t)f);
+            }
         }
         const uint64_t m = __ballot(f);
         if (lane == 0) flagged_heads = (int)(uint32_t)m;
     }
     __syncthreads();
     const int fmask = flagged_heads;
+    for (int idx = threadIdx.x; idx < GB * kHeadDim; idx += NW * 64) {
+        const int hh = idx >> 7, d = idx & 127;
+        float acc = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) acc += red[w2 * kRedStride + d * 16 + hh];
+        if (direct) {
+            if ((fmask >> hh) & 1) continue;          // written after the recompute
+            float l = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) l += red[w2 * kRedStride + 2048 + hh];
+            store_out(p, (row0 + hh) * kHeadDim + d, L > 0 ? acc * (vs / l) : 0.f);
+        } else {
+            const size_t slot = part_slot(p, b, h0 + hh, c);
+            part_store(p, p.o_part + slot * kHeadDim + d, acc);
+        }
+    }
 
     // ---- a score of this chunk left the safe band (FlashDecoding++ theory
     // page, section 3): redo the chunk with online softmax and replace the
-    // partials of the flagged heads
+    // partials (or outputs) of the flagged heads
     if (fmask != 0) {
         __syncthreads();   // everyone has read red[] before the ring is refilled
         run(std::true_type{});
@@ -471,17 +489,22 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
             float M = -INFINITY;
 #pragma unroll
             for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, red[w2 * kRedStride + 2064 + hh]);
-            float acc = 0.f;
+            float acc = 0.f, l = 0.f;
 #pragma unroll
             for (int w2 = 0; w2 < NW; ++w2) {
                 const float mw = red[w2 * kRedStride + 2064 + hh];
                 const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
                 acc += red[w2 * kRedStride + d * 16 + hh] * f;
+                l += red[w2 * kRedStride + 2048 + hh] * f;
             }
-            const size_t slot = part_slot(p, b, h0 + hh, c);
-            part_store(p, p.o_part + slot * kHeadDim + d, acc);
+            if (direct) {
+                store_out(p, (row0 + hh) * kHeadDim + d, acc * (vs / l));
+            } else {
+                const size_t slot = part_slot(p, b, h0 + hh, c);
+                part_store(p, p.o_part + slot * kHeadDim + d, acc);
+            }
         }
-        if (threadIdx.x < GB && ((fmask >> threadIdx.x) & 1)) {
+        if (!direct && threadIdx.x < GB && ((fmask >> threadIdx.x) & 1)) {
             const int hh = threadIdx.x;
             float M = -INFINITY;
 #pragma unroll
@@ -500,7 +523,12 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     }
 
     // ---- publish the unit; the last unit of the row group merges it
-    if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) merge_group<NW>(p, b, h0, GB, merged);
+    if (direct) {
+        if (threadIdx.x < GB) p.flags[row0 + threadIdx.x] = (uint8_t)((fmask >> threadIdx.x) & 1);
+        if (threadIdx.x == 0) finish_group(p, __popc(fmask));
+    } else if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) {
+        merge_group<NW>(p, b, h0, GB, merged);
+    }
 }
 
 }  // namespace chunk

@@ -451,29 +451,52 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
         else __builtin_nontemporal_store(o[dl], reinterpret_cast<f32x4 *>(orow + 16 * dl));
     };
 
+    // A row group whose sequence is this one chunk (or empty) needs no merge:
+    // in a fused call each wavefront writes its components of the rows'
+    // outputs itself, in the merge's arithmetic (the chunk's sum times
+    // v_scale over its weight sum; an empty row is zero), and no partial is
+    // stored.
+    const bool direct = p.fused && L <= p.chunk;
+    const float vs = FP8 ? p.v_scale[kvh] : 1.f;
+    const size_t row = (size_t)b * p.hq + h0 + (head_ok ? n : 0);
+    auto out_o = [&](int dl) {
+        store_out4(p, row * kHeadDim + 16 * DT * wave + 4 * g4 + 16 * dl,
+                   L > 0 ? o[dl] * (vs / lsum) : f32x4{0.f, 0.f, 0.f, 0.f});
+    };
+
     // ---- unified-max pass
     run(std::false_type{});
+    const uint64_t fmask = __ballot(g4 == 0 && bad != 0);   // the same in every wavefront
     if (head_ok) {
+        if (direct) {
+            if (!((fmask >> n) & 1)) {                         // flagged heads: after the recompute
 #pragma unroll
-        for (int dl = 0; dl < DT; ++dl) store_o(dl);
-        if (wave == 0 && g4 == 0) {
-            part_store(p, p.l_part + slot, lsum);
-            part_store(p, p.m_part + slot, p.phi);
-            part_store(p, p.cflag + slot, (uint8_t)(bad != 0));
+                for (int dl = 0; dl < DT; ++dl) out_o(dl);
+            }
+        } else {
+#pragma unroll
+            for (int dl = 0; dl < DT; ++dl) store_o(dl);
+            if (wave == 0 && g4 == 0) {
+                part_store(p, p.l_part + slot, lsum);
+                part_store(p, p.m_part + slot, p.phi);
+                part_store(p, p.cflag + slot, (uint8_t)(bad != 0));
+            }
         }
     }
-    const uint64_t fmask = __ballot(g4 == 0 && bad != 0);   // the same in every wavefront
 
     // ---- a score of this chunk left the safe band (FlashDecoding++ theory
     // page, section 3): redo the chunk with online softmax and replace the
-    // partials of the flagged heads
+    // partials (or outputs) of the flagged heads
     if (fmask != 0) {
         __builtin_amdgcn_s_barrier();   // everyone is done with the ring
         run(std::true_type{});
         if (head_ok && ((fmask >> n) & 1)) {
 #pragma unroll
-            for (int dl = 0; dl < DT; ++dl) store_o(dl);
-            if (wave == 0 && g4 == 0) {
+            for (int dl = 0; dl < DT; ++dl) {
+                if (direct) out_o(dl);
+                else store_o(dl);
+            }
+            if (!direct && wave == 0 && g4 == 0) {
                 part_store(p, p.l_part + slot, lsum);
                 part_store(p, p.m_part + slot, mrun);
             }
@@ -481,7 +504,12 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
     }
 
     // ---- publish the unit; the last unit of the row group merges it
-    if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) merge_group<S::waves, 1>(p, b, h0, GB, merged);
+    if (direct) {
+        if (head_ok && wave == 0 && g4 == 0) p.flags[row] = (uint8_t)((fmask >> n) & 1);
+        if (threadIdx.x == 0) finish_group(p, __popcll(fmask));
+    } else if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) {
+        merge_group<S::waves, 1>(p, b, h0, GB, merged);
+    }
 }
 
 }  // namespace coop

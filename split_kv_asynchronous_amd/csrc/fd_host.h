@@ -74,8 +74,11 @@ constexpr int kShapes[3] = {3, 3, 1};
 // a family takes every longer call): the chunk size for chunk_size == 0, the
 // kernel shape at that chunk size (other chunk sizes run shape 0), and the
 // largest chunk size whose calls merge inside the chunk launch (0: none).
-// Grids of at most kSmallGrid units (sequence x head block x chunk), one
-// round of workgroups, merge inside the launch whatever the row says.
+// Whatever the row says, a call merges inside the launch if its grid has at
+// most kSmallGrid units (sequence x head block x chunk), one round of
+// workgroups, or if its chunk covers max_seq_len: then every row is one
+// chunk, which the chunk kernel writes out itself, with no partials and no
+// merge.
 struct TableRow {
     int family, paged, max_len, chunk, shape, fused_chunk;
 };
@@ -86,11 +89,13 @@ constexpr int64_t kSmallGrid = 512;
 // chunk size 256 .. 4096 x every shape x both merge placements, on ragged
 // synthetic batches of each family, paging and length range (whole-call
 // TB/s of K/V; best against the runner-up):
-//   grouped bf16, 64/8 heads: 256 x U[256,2K] 5.76 (chunk 2048) ; 64 x
+//   grouped bf16, 64/8 heads: 256 x U[256,2K] 5.83 (chunk 2048, 4 waves x 3
+//     stages, rows written by the chunk kernel; with a merge launch 5.72) ; 64 x
 //     U[1K,8K] 6.12 (4096, 4 waves x 3 stages; 1024: 6.04) ; 32 x U[1K,32K]
 //     6.32 (2048; 1024: 6.17, merged in the launch 6.22) ; 4 x U[32K,128K]
-//     6.09 (1024; 2048: 5.91) ; paged: 5.56, 5.98, 6.28 (in the launch), 5.92
-//   grouped E4M3FN, 32/8 heads: 512 x U[256,2K] 5.32 (1024) ; 64 x
+//     6.09 (1024; 2048: 5.91) ; paged: 5.69 (as contiguous), 5.98, 6.28 (in
+//     the launch), 5.92
+//   grouped E4M3FN, 32/8 heads: 512 x U[256,2K] 5.30 (1024, either way) ; 64 x
 //     U[512,16K] 5.75 (1024, in the launch; 512 in the launch 5.64) ;
 //     16 x U[16K,64K] 5.75 (2048) ; paged: 5.16, 5.59 (in the launch), 5.69
 //   one query per KV head, 32 heads: 64 x 2K 6.77 (2048) ; 8 x 8K 6.66
@@ -103,18 +108,18 @@ constexpr int64_t kSmallGrid = 512;
 // the launch) and on short E4M3FN rows at chunks of 1024 and more; the
 // one-query-per-KV-head kernel was 3-60% behind at every chunk size.
 inline constexpr TableRow kTable[] = {
-    {kFamGroupedBf16, 0, 2048, 2048, 0, 0},
+    {kFamGroupedBf16, 0, 2048, 2048, 1, 0},
     {kFamGroupedBf16, 0, 8192, 4096, 1, 512},
     {kFamGroupedBf16, 0, 32768, 2048, 0, 1024},
     {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 0},
-    {kFamGroupedBf16, 1, 2048, 2048, 0, 0},
-    {kFamGroupedBf16, 1, 8192, 4096, 1, 512},
+    {kFamGroupedBf16, 1, 2048, 2048, 1, 0},
+    {kFamGroupedBf16, 1, 8192, 4096, 1, 1024},
     {kFamGroupedBf16, 1, 32768, 2048, 0, 2048},
     {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 0},
-    {kFamGroupedFp8, 0, 2048, 1024, 0, 512},
+    {kFamGroupedFp8, 0, 2048, 1024, 0, 1024},
     {kFamGroupedFp8, 0, 16384, 1024, 0, 1024},
     {kFamGroupedFp8, 0, 1 << 23, 2048, 0, 0},
-    {kFamGroupedFp8, 1, 2048, 1024, 0, 512},
+    {kFamGroupedFp8, 1, 2048, 1024, 0, 1024},
     {kFamGroupedFp8, 1, 16384, 1024, 0, 1024},
     {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 0},
     {kFamVector, 0, 2048, 2048, 0, 0},
@@ -167,7 +172,10 @@ inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
     const int blocks = pl->family == kFamVector ? d->num_q_heads
                                                 : d->num_q_heads / heads_per_block(d->num_q_heads / d->num_kv_heads);
     const int64_t units = maxch * blocks * d->batch;
-    pl->fused = place == FD_PLAN_FUSED ? 1 : place == FD_PLAN_SPLIT ? 0 : units <= kSmallGrid || pl->chunk <= r.fused_chunk;
+    pl->fused = place == FD_PLAN_FUSED   ? 1
+                : place == FD_PLAN_SPLIT ? 0
+                                         : units <= kSmallGrid || pl->chunk <= r.fused_chunk ||
+                                               pl->chunk >= d->max_seq_len;
     return FD_OK;
 }
 

@@ -144,6 +144,50 @@ FD_DEV bool publish_unit(const Params &p, int rg, int nunits, int &flag)
     return flag != 0;
 }
 
+// A row group of a fused call is complete (merged, or written directly as a
+// one-chunk row group), with `total` recomputed (row, chunk) pairs; in one
+// thread.  The pairs go into the call's fused count, then (once that add has
+// completed) one into the count of completed row groups; the last row group
+// publishes the call's count and zeroes both words for the next call (a
+// replay of the launch with the same epoch re-bases them).
+FD_DEV void finish_group(const Params &p, int total)
+{
+    if (total) {
+        epoch_add(p.fused_count, p.epoch, (uint32_t)total);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    const uint32_t n = epoch_add(p.fused_word, p.epoch, 1);
+    if ((int)n == p.ngroups) {
+        const unsigned long long c = get(p.fused_count);
+        const uint32_t cnt = (uint32_t)(c >> 32) == p.epoch ? (uint32_t)c : 0u;
+        put(p.count_word, ((unsigned long long)p.epoch << 32) | cnt);
+        put(p.fused_word, next_tag(p.epoch));
+        put(p.fused_count, next_tag(p.epoch));
+    }
+}
+
+// Output element `e` (row * 128 + component): fp32, or bf16 rounded to
+// nearest even (NaN stays NaN), as the merge writes it.
+FD_DEV uint32_t bf16_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (x != x) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+FD_DEV void store_out(const Params &p, size_t e, float x)
+{
+    if (p.out_bf16) static_cast<uint16_t *>(p.out)[e] = (uint16_t)bf16_bits(x);
+    else static_cast<float *>(p.out)[e] = x;
+}
+
+FD_DEV void store_out4(const Params &p, size_t e, f32x4 x)
+{
+    if (p.out_bf16)
+        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.out) + e) =
+            u32x2{bf16_bits(x[0]) | (bf16_bits(x[1]) << 16), bf16_bits(x[2]) | (bf16_bits(x[3]) << 16)};
+    else *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + e) = x;
+}
+
 // One wavefront merges up to R rows (b, h[0..nr-1]) at once: writes
 // out[b][h][:] and fallback_flags[b][h] and returns the rows' number of
 // recomputed chunks (in every lane).  Lane i holds components 2i and 2i + 1,
@@ -267,13 +311,7 @@ FD_DEV int merge_rows(const Params &p, int b, const int (&h)[R], int nr, int lan
         }
         const size_t row = (size_t)b * p.hq + h[r];
         if (p.out_bf16) {
-            uint32_t w[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t u = __float_as_uint(res[i]);
-                w[i] = (res[i] != res[i]) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-            }
-            reinterpret_cast<uint32_t *>(p.out)[row * (kHeadDim / 2) + lane] = w[0] | (w[1] << 16);
+            reinterpret_cast<uint32_t *>(p.out)[row * (kHeadDim / 2) + lane] = bf16_bits(res[0]) | (bf16_bits(res[1]) << 16);
         } else {
             reinterpret_cast<f32x2 *>(p.out)[row * (kHeadDim / 2) + lane] = res;
         }
@@ -302,24 +340,7 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
     }
     if (lane == 0 && mine) atomicAdd(&total, mine);
     __syncthreads();
-    // The row group's recomputed pairs go into the call's fused count, then
-    // (once that add has completed) one into the count of merged row groups;
-    // the last row group publishes the call's count and zeroes both words for
-    // the next call (a replay of the launch with the same epoch re-bases them).
-    if (threadIdx.x == 0) {
-        if (total) {
-            epoch_add(p.fused_count, p.epoch, (uint32_t)total);
-            __builtin_amdgcn_s_waitcnt(0);
-        }
-        const uint32_t n = epoch_add(p.fused_word, p.epoch, 1);
-        if ((int)n == p.ngroups) {
-            const unsigned long long c = get(p.fused_count);
-            const uint32_t cnt = (uint32_t)(c >> 32) == p.epoch ? (uint32_t)c : 0u;
-            put(p.count_word, ((unsigned long long)p.epoch << 32) | cnt);
-            put(p.fused_word, next_tag(p.epoch));
-            put(p.fused_count, next_tag(p.epoch));
-        }
-    }
+    if (threadIdx.x == 0) finish_group(p, total);
 }
 
 // Separate merge launch (large grids): RW wavefronts per row, 256 threads per
@@ -437,20 +458,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p)
         if (p.v_scale) vs = p.v_scale[h / p.group];
         r = acc * (vs / lacc);
     }
-    if (half == 0) {
-        if (p.out_bf16) {
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t u = __float_as_uint(r[i]);
-                w[i] = (r[i] != r[i]) ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-            }
-            reinterpret_cast<u32x2 *>(p.out)[(size_t)row * (kHeadDim / 4) + q4] =
-                u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-        } else {
-            reinterpret_cast<f32x4 *>(p.out)[(size_t)row * (kHeadDim / 4) + q4] = r;
-        }
-    }
+    if (half == 0) store_out4(p, (size_t)row * kHeadDim + 4 * q4, r);
     if (lane == 0) {
         p.flags[row] = any ? 1 : 0;
         if (nflag) epoch_add(p.count_word, p.epoch, (uint32_t)nflag);

@@ -23,8 +23,12 @@ namespace fd {
 //                   section, first formula, used by the fallback rule);
 //                   writes o, l and the chunk maximum m.
 // NW = wavefronts in the workgroup; `red` is LDS of at least NW * 132 floats.
+// direct: the row is this one chunk (or empty) in a fused call -- write its
+// output (the merge's arithmetic: the chunk's sum times v_scale over its
+// weight sum) instead of the partial; a unified pass that is flagged writes
+// nothing (the online pass does).
 template <int KV, int QT, bool PAGED, bool ONLINE, int NW>
-FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_end, float *red)
+FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_end, float *red, bool direct)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -122,8 +126,11 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w * 132 + 129]);
     }
+    bool flagged = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) flagged |= red[w * 132 + 130] != 0.f;
     if (threadIdx.x < kHeadDim) {
-        float acc = 0.f;
+        float acc = 0.f, lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             float f = 1.f;
@@ -132,10 +139,17 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
                 f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
             }
             acc += red[w * 132 + threadIdx.x] * f;
+            lsum += red[w * 132 + 128] * f;
         }
-        part_store(p, p.o_part + slot * kHeadDim + threadIdx.x, acc);
+        if (!direct) {
+            part_store(p, p.o_part + slot * kHeadDim + threadIdx.x, acc);
+        } else if (ONLINE || !flagged) {
+            float vs = 1.f;
+            if constexpr (KV == FD_FP8_E4M3FN) vs = p.v_scale[kvh];
+            store_out(p, ((size_t)b * p.hq + h) * kHeadDim + threadIdx.x, t_end > t_begin ? acc * (vs / lsum) : 0.f);
+        }
     }
-    if (threadIdx.x == 0) {
+    if (!direct && threadIdx.x == 0) {
         float lsum = 0.f;
         bool any = false;
 #pragma unroll
@@ -152,9 +166,6 @@ FD_DEV bool valu_chunk(const Params &p, int b, int h, int c, int t_begin, int t_
         part_store(p, p.m_part + slot, M);
         if constexpr (!ONLINE) part_store(p, p.cflag + slot, (uint8_t)(any ? 1 : 0));
     }
-    bool flagged = false;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) flagged |= red[w * 132 + 130] != 0.f;
     __syncthreads();   // `red` is reused by the caller
     return flagged;
 }
@@ -178,9 +189,19 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
     const int t1 = min(t0 + p.chunk, L);
     // a score left the safe band: this workgroup redoes its chunk with online
     // softmax and overwrites the partial (the chunk flag stays set)
-    if (valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, t1, red))
-        valu_chunk<KV, QT, PAGED, true, 4>(p, b, h, c, t0, t1, red);
-    if (publish_unit(p, b * p.hq + h, units_of(p, L), last_flag)) merge_group<4, 1>(p, b, h, 1, merged);
+    // A row whose sequence is this one chunk (or empty) needs no merge: in a
+    // fused call the workgroup writes its output and flag itself.
+    const bool direct = p.fused && L <= p.chunk;
+    const bool flagged = valu_chunk<KV, QT, PAGED, false, 4>(p, b, h, c, t0, t1, red, direct);
+    if (flagged) valu_chunk<KV, QT, PAGED, true, 4>(p, b, h, c, t0, t1, red, direct);
+    if (direct) {
+        if (threadIdx.x == 0) {
+            p.flags[(size_t)b * p.hq + h] = flagged ? 1 : 0;
+            finish_group(p, flagged ? 1 : 0);
+        }
+    } else if (publish_unit(p, b * p.hq + h, units_of(p, L), last_flag)) {
+        merge_group<4, 1>(p, b, h, 1, merged);
+    }
 }
 
 }  // namespace fd

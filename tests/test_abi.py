@@ -286,17 +286,18 @@ def test_flat_gemm_table_covers_the_7b_layers():
 # The plan table (measured on MI355X; the rows of fd_host.h): per kernel
 # family, paging and max_seq_len range, the chunk size for chunk_size = 0, the
 # kernel shape at that chunk, and the largest chunk size whose calls merge in
-# the launch (0: none; grids of one round of workgroups always do).
+# the launch (0: none; grids of one round of workgroups, and calls whose chunk
+# covers max_seq_len, always do).
 FAMILY_KW = {0: dict(), 1: dict(kv_dtype="e4m3fn"), 2: dict(num_kv_heads=64)}
 PLAN_ROWS = [
     # family, paged, max_seq_len probes, chunk, shape, largest chunk merged in the launch
-    (0, 0, (1, 2048), 2048, 0, 0), (0, 0, (2049, 8192), 4096, 1, 512),
+    (0, 0, (1, 2048), 2048, 1, 0), (0, 0, (2049, 8192), 4096, 1, 512),
     (0, 0, (8193, 32768), 2048, 0, 1024), (0, 0, (32769, 1 << 20), 1024, 0, 0),
-    (0, 1, (16, 2048), 2048, 0, 0), (0, 1, (2064, 8192), 4096, 1, 512),
+    (0, 1, (16, 2048), 2048, 1, 0), (0, 1, (2064, 8192), 4096, 1, 1024),
     (0, 1, (8208, 32768), 2048, 0, 2048), (0, 1, (32784, 1 << 20), 2048, 0, 0),
-    (1, 0, (1, 2048), 1024, 0, 512), (1, 0, (2049, 16384), 1024, 0, 1024),
+    (1, 0, (1, 2048), 1024, 0, 1024), (1, 0, (2049, 16384), 1024, 0, 1024),
     (1, 0, (16385, 1 << 20), 2048, 0, 0),
-    (1, 1, (16, 2048), 1024, 0, 512), (1, 1, (2064, 16384), 1024, 0, 1024),
+    (1, 1, (16, 2048), 1024, 0, 1024), (1, 1, (2064, 16384), 1024, 0, 1024),
     (1, 1, (16400, 1 << 20), 2048, 0, 0),
     (2, 0, (1, 2048), 2048, 0, 0), (2, 0, (2049, 8192), 2048, 0, 0),
     (2, 0, (8193, 1 << 20), 4096, 0, 0),
@@ -316,7 +317,8 @@ def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk):
         c = max(chunk, 16 if paged else 0)
         blocks = 8 if fam != 2 else 64
         big = -(-L // c) * 256 * blocks > 512
-        assert got == dict(chunk_size=c, family=fam, shape=shape, fused=int(c <= fused_chunk or not big)), (kw, got)
+        fused = c <= fused_chunk or not big or c >= L      # a chunk covering max_seq_len: one-chunk rows
+        assert got == dict(chunk_size=c, family=fam, shape=shape, fused=int(fused)), (kw, got)
         # the workspace follows the plan's chunk
         assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
         # an explicit chunk size other than the table's runs shape 0, and
@@ -326,7 +328,8 @@ def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk):
                 continue
             p = fd.fd_attn_plan(_desc(**dict(kw, chunk_size=other)))
             big = -(-L // other) * 256 * blocks > 512
-            assert p["shape"] == 0 and p["fused"] == int(other <= fused_chunk or not big), (kw, other, p)
+            fused = other <= fused_chunk or not big or other >= L
+            assert p["shape"] == 0 and p["fused"] == int(fused), (kw, other, p)
 
 
 def test_plan_small_grids_merge_in_the_launch_and_forced_plans():

@@ -288,6 +288,46 @@ def test_every_kernel_shape_and_merge_placement(g, kv, page, nshapes):
             assert dp.recomputed() > 0
 
 
+ONE_CHUNK_CASES = [
+    # group, kv dtype, page size, kernel shape, output dtype
+    (8, "bf16", 0, 0, "f32"), (8, "bf16", 16, 2, "bf16"), (4, "bf16", 0, 1, "f32"),
+    (4, "e4m3fn", 16, 0, "f32"), (8, "e4m3fn", 0, 2, "bf16"), (16, "e4m3fn", 32, 1, "f32"),
+    (1, "bf16", 0, 0, "f32"), (1, "e4m3fn", 16, 0, "bf16"), (1, "f32", 32, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("g,kv,page,shape,out_dtype", ONE_CHUNK_CASES)
+def test_one_chunk_rows_written_by_the_chunk_kernel(g, kv, page, shape, out_dtype):
+    # Every sequence fits in one chunk (some empty): with the merge in the
+    # chunk launch the chunk kernel writes those rows itself, in the merge's
+    # arithmetic, so outputs, flags and the recomputed count equal the
+    # two-launch call's bit for bit; a narrow band sends some chunks to the
+    # recompute.
+    import split_kv_asynchronous_amd as fd
+    lens = [0, 1, 17, 200, 511, 512, 300, 64] * 12
+    prob = synthetic.make_problem(batch=len(lens), num_q_heads=2 * g, num_kv_heads=2, seq_lens=lens,
+                                  kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", page_size=page,
+                                  chunk_size=512, phi=1.0, a=3.0, b=1.5, seed=1200 + g)
+    res = {}
+    for place in (fd.FD_PLAN_FUSED, fd.FD_PLAN_SPLIT):
+        print("case one-chunk g=%d kv=%s page=%d shape=%d out=%s place=%d" % (g, kv, page, shape, out_dtype, place),
+              flush=True)
+        dp = DeviceProblem(prob, out_dtype=out_dtype, plan=fd.FD_PLAN_SHAPE(shape) | place)
+        dp.run()
+        dp.run()                     # a second call on the same workspace (a new epoch)
+        res[place] = (dp.out.clone(), dp.flags.clone(), dp.recomputed())
+        if place == fd.FD_PLAN_FUSED and out_dtype == "f32":
+            out, flags = dp.results()
+            ref_out, ref_flags, margin = oracle.decode_exact(**prob.args())
+            sure = margin >= 1e-3
+            np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+            compare(prob, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
+    fo, ff, fc = res[fd.FD_PLAN_FUSED]
+    so, sf, sc = res[fd.FD_PLAN_SPLIT]
+    assert torch.equal(fo, so) and torch.equal(ff, sf)
+    assert fc == sc and fc > 0
+
+
 TABLE_CASES = [
     # one call per row of the plan table (chunk_size = 0): group, kv dtype,
     # page size, sequence lengths, max_seq_len (selects the row)
