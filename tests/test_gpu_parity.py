@@ -304,7 +304,7 @@ def test_one_chunk_rows_written_by_the_chunk_kernel(g, kv, page, shape, out_dtyp
     # two-launch call's bit for bit; a narrow band sends some chunks to the
     # recompute.
     import split_kv_asynchronous_amd as fd
-    lens = [0, 1, 17, 200, 511, 512, 300, 64] * 12
+    lens = [0, 1, 17, 200, 511, 512, 300, 64] * 40
     prob = synthetic.make_problem(batch=len(lens), num_q_heads=2 * g, num_kv_heads=2, seq_lens=lens,
                                   kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", page_size=page,
                                   chunk_size=512, phi=1.0, a=3.0, b=1.5, seed=1200 + g)
@@ -326,6 +326,16 @@ def test_one_chunk_rows_written_by_the_chunk_kernel(g, kv, page, shape, out_dtyp
     so, sf, sc = res[fd.FD_PLAN_SPLIT]
     assert torch.equal(fo, so) and torch.equal(ff, sf)
     assert fc == sc and fc > 0
+    # the library's own plan: a chunk that covers max_seq_len merges in the
+    # launch; against the two-launch call of the same kernel shape
+    dp = DeviceProblem(prob, out_dtype=out_dtype)
+    plan = fd.fd_attn_plan(dp.desc())
+    assert plan["fused"] == 1
+    dp.run()
+    sp = DeviceProblem(prob, out_dtype=out_dtype, plan=fd.FD_PLAN_SHAPE(plan["shape"]) | fd.FD_PLAN_SPLIT)
+    sp.run()
+    assert torch.equal(dp.out, sp.out) and torch.equal(dp.flags, sp.flags)
+    assert dp.recomputed() == sp.recomputed() == fc
 
 
 TABLE_CASES = [
