@@ -25,9 +25,10 @@
  * Ownership and threading: every pointer is device memory owned by the
  * caller.  The library never allocates, frees or synchronises; its only
  * global state is a call counter that gives every call a fresh epoch.  A call
- * enqueues its kernels on `stream` and returns (one kernel for small grids,
- * where the merge runs inside it; a chunk kernel and a merge kernel
- * otherwise).  out, fallback_flags and the
+ * enqueues its kernels on `stream` and returns (one kernel where the merge
+ * runs inside it -- small grids, the plan table's fused rows, balanced
+ * shares; a chunk kernel and a merge kernel otherwise).  out,
+ * fallback_flags and the
  * workspace are valid once the stream has completed the call.  Calls may run
  * concurrently on different streams as long as each has its own workspace
  * and outputs; calls that share a workspace must be ordered (one stream).
@@ -116,7 +117,23 @@ typedef struct {
     /* 0: the library's plan (see fd_attn_plan).  Otherwise, for tuning and
      * tests, FD_PLAN_SHAPE(k) forces kernel shape k of the call's family and
      * FD_PLAN_FUSED / FD_PLAN_SPLIT force the merge into the chunk launch or
-     * into a second launch (either bit alone; the results are the same). */
+     * into a second launch (either bit alone; the results are the same).
+     * FD_PLAN_SHARES forces balanced shares (grouped families only; with
+     * FD_PLAN_SPLIT, FD_ERR_SHAPE): instead of fixed chunks of chunk_size
+     * tokens, a persistent grid of workgroups splits the call's tokens --
+     * all row groups (sequence x block of query heads sharing a KV head)
+     * laid end to end, counted in 64-token quanta, an empty sequence
+     * counting one.  Calls of at least 4 quanta per workgroup put three
+     * quarters of the quanta in equal contiguous shares, one per workgroup,
+     * and the rest in 1024-token grains that workgroups claim in turn once
+     * their share is done; smaller calls are all shares.  The cut depends
+     * on the lengths only, so results do not depend on which workgroup
+     * computes what.  A row group's chunks are then its pieces in the
+     * shares and grains that touch it (cut at their edges, multiples of 64
+     * tokens), reduced and band-checked on their own and merged in the
+     * launch.  chunk_size still has to be valid but does not apply.  The
+     * library also picks balanced shares for some calls with chunk_size 0
+     * and nothing forced (fd_attn_plan). */
     int32_t plan;
 } fd_attn_desc_t;
 
@@ -124,14 +141,18 @@ typedef struct {
 #define FD_PLAN_SHAPE_MASK 0x0f
 #define FD_PLAN_FUSED 0x10
 #define FD_PLAN_SPLIT 0x20
+#define FD_PLAN_SHARES 0x40 /* balanced shares (see plan above) */
 
 /* Bytes of workspace a call with this descriptor needs (0 if desc is NULL or
- * its sizes are invalid).  The workspace holds per-(row, chunk) partial sums
- * and per-row-group completion counters; it needs no initialisation (the
- * counters are tagged with a per-call epoch) and its contents between calls
- * are the library's.  After a call completes, its first 4 bytes hold the
- * uint32 number of (row, chunk) pairs that call recomputed with online
- * softmax, and the next 4 bytes that call's epoch.  A call captured into a
+ * its sizes are invalid; it depends on the plan, see fd_attn_plan).  The
+ * workspace holds per-(row, chunk) partial sums (with balanced shares, per
+ * (row, piece): a row group's piece in one share or pool grain), the counter
+ * of claimed pool grains and per-row-group completion counters; it needs no
+ * initialisation (the counters are tagged with a per-call epoch) and its
+ * contents between calls are the library's.  After a call completes, its
+ * first 4 bytes hold the uint32 number of (row, chunk) pairs (balanced
+ * shares: (row, piece) pairs) that call recomputed with online softmax, and
+ * the next 4 bytes that call's epoch.  A call captured into a
  * graph keeps the epoch it was captured with; every replay still counts from
  * zero, so after each replay the first 4 bytes hold that replay's count. */
 size_t fd_attn_workspace_size(const fd_attn_desc_t *desc);
@@ -167,16 +188,20 @@ int fd_attn_decode_static(const fd_attn_desc_t *desc, const void *q, const void 
                           hipStream_t stream);
 
 /* The plan a call with this descriptor would run, from the library's table
- * of measured plans (or desc->plan where it forces one): the chunk size, the
+ * of measured plans (or desc->plan where it forces one; with chunk_size 0,
+ * the table may pick balanced shares, and does for calls of many row groups):
+ * the chunk size, the
  * kernel family (0: grouped bf16 queries over a bf16 cache; 1: grouped bf16
  * queries over an E4M3FN cache; 2: one query per KV head, or fp32 operands),
- * the kernel shape within the family, and whether the merge runs inside the
- * chunk launch (1) or in a second launch (0).  The table is keyed by family,
+ * the kernel shape within the family, whether the merge runs inside the
+ * chunk launch (1) or in a second launch (0), and the number of balanced
+ * shares (0: fixed chunks of the reported size; otherwise the workgroups
+ * that split the call, see FD_PLAN_SHARES).  The table is keyed by family,
  * paging and max_seq_len (the offline table of shapes of the FlashDecoding++
  * theory page, section 4).  Any output pointer may be NULL.  Returns FD_OK or
  * FD_ERR_NULL / FD_ERR_SHAPE for an invalid descriptor. */
 int fd_attn_plan(const fd_attn_desc_t *desc, int32_t *chunk_size, int32_t *family, int32_t *shape,
-                 int32_t *fused);
+                 int32_t *fused, int32_t *shares);
 
 /* Static text for a status code. */
 const char *fd_attn_status_string(int status);

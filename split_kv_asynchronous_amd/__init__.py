@@ -14,7 +14,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["fd_attn_decode", "fd_attn_decode_static", "fd_attn_plan", "FD_PLAN_SHAPE",
-           "FD_PLAN_FUSED", "FD_PLAN_SPLIT", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
+           "FD_PLAN_FUSED", "FD_PLAN_SPLIT", "FD_PLAN_SHARES", "prepare_decode", "DecodeCall", "fd_attn_prefill", "fd_attn_score_stats", "fd_attn_choose_band",
            "fd_attn_workspace_size", "fd_flat_gemm", "fd_flat_gemm_plan",
            "fd_flat_gemm_workspace_size", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
            "make_gemm_desc",
@@ -51,7 +51,7 @@ class FdAttnDesc(ctypes.Structure):
 
 
 # fd_attn_desc_t.plan bits (include/fd_attn.h)
-FD_PLAN_FUSED, FD_PLAN_SPLIT = 0x10, 0x20
+FD_PLAN_FUSED, FD_PLAN_SPLIT, FD_PLAN_SHARES = 0x10, 0x20, 0x40
 
 
 def FD_PLAN_SHAPE(k: int) -> int:
@@ -133,7 +133,7 @@ def _load():
         lib.fd_flat_gemm_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_void_p]
         lib.fd_flat_gemm_pack_weights.restype = ctypes.c_int
-        lib.fd_attn_plan.argtypes = [D, i32p, i32p, i32p, i32p]
+        lib.fd_attn_plan.argtypes = [D, i32p, i32p, i32p, i32p, i32p]
         lib.fd_attn_plan.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
@@ -161,12 +161,13 @@ def make_desc(*, batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: i
 
 def fd_attn_plan(desc: FdAttnDesc) -> dict:
     """The plan the library runs for this descriptor (fd_attn_plan): chunk
-    size, kernel family, kernel shape, and whether the merge is fused."""
-    vals = [ctypes.c_int32() for _ in range(4)]
+    size, kernel family, kernel shape, whether the merge is fused, and the
+    number of balanced shares (0: fixed chunks)."""
+    vals = [ctypes.c_int32() for _ in range(5)]
     rc = _load().fd_attn_plan(ctypes.byref(desc), *[ctypes.byref(v) for v in vals])
     if rc != 0:
         raise FdAttnError(rc, fd_attn_status_string(rc))
-    return dict(zip(("chunk_size", "family", "shape", "fused"), (v.value for v in vals)))
+    return dict(zip(("chunk_size", "family", "shape", "fused", "shares"), (v.value for v in vals)))
 
 
 def fd_attn_workspace_size(desc: FdAttnDesc) -> int:

@@ -24,6 +24,7 @@ using fd::host::check_shape;
 constexpr size_t kAlign = 256;
 constexpr size_t kFusedWordOffset = 64;   // header word counting a fused call's merged row groups
 constexpr size_t kFusedCountOffset = 128; // header word adding up a fused call's recomputed pairs
+constexpr size_t kClaimOffset = 192;      // header word counting a balanced-share call's claimed grains
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -31,17 +32,36 @@ struct Layout {
     size_t header, o_part, l_part, m_part, cflag, rg_count, total;
 };
 
-Layout layout_of(size_t rows, size_t maxch)
+// `slots` partials of one row each, and one counter per row.
+Layout layout_of(size_t rows, size_t slots)
 {
     Layout L;
     L.header = 0;
     L.o_part = kAlign;
-    L.l_part = align_up(L.o_part + rows * maxch * fd::kHeadDim * sizeof(float));
-    L.m_part = align_up(L.l_part + rows * maxch * sizeof(float));
-    L.cflag = align_up(L.m_part + rows * maxch * sizeof(float));
-    L.rg_count = align_up(L.cflag + rows * maxch);
+    L.l_part = align_up(L.o_part + slots * fd::kHeadDim * sizeof(float));
+    L.m_part = align_up(L.l_part + slots * sizeof(float));
+    L.cflag = align_up(L.m_part + slots * sizeof(float));
+    L.rg_count = align_up(L.cflag + slots);
     L.total = align_up(L.rg_count + rows * sizeof(unsigned long long));
     return L;
+}
+
+// Partial slots of a plan: one per (row, chunk) with fixed chunks; with
+// balanced shares GB per (segment, row group) piece, at (s + r) GB for
+// segment s and row group r (s + r grows strictly along the cut): at most
+// (segments + row groups) GB, segments being the shares plus the pool grains
+// of the largest call the descriptor allows (every length max_seq_len).
+size_t slots_of(const fd_attn_desc_t *d, const fd::host::Plan &pl)
+{
+    const size_t rows = (size_t)d->batch * d->num_q_heads;
+    if (pl.shares) {
+        const int gb = fd::host::heads_per_block(d->num_q_heads / d->num_kv_heads);
+        const uint64_t qmax = ((uint64_t)d->max_seq_len + fd::ring::kQuantum - 1) / fd::ring::kQuantum;
+        const uint64_t nmax = qmax * (uint64_t)d->batch * (uint64_t)(d->num_q_heads / gb);
+        return ((size_t)pl.shares + fd::ring::pool_grains(nmax, pl.shares)) * gb + rows;
+    }
+    const size_t maxch = ((size_t)d->max_seq_len + pl.chunk - 1) / pl.chunk;
+    return rows * maxch;
 }
 
 // A fresh nonzero epoch for every call (see fd_merge.h): the workspace's
@@ -92,6 +112,26 @@ int dispatch_grouped(const Params &p, int family, int shape, dim3 grid, hipStrea
     return launch_coop<CoopShape0, PAGED>(p, grid, s, e0, e1);
 }
 
+template <typename S, int KV, bool PAGED>
+int launch_shares(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    return fd::host::launch(fd::chunk::share_kernel<KV, PAGED, S>, grid, dim3(S::waves * 64), 0, s, e0, e1, p);
+}
+
+// Balanced shares run the ring kernel of fd_chunk.h for both cache formats.
+template <bool PAGED>
+int dispatch_shares(const Params &p, int family, int shape, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    if (family == fd::host::kFamGroupedBf16) {
+        if (shape == 1) return launch_shares<ChunkShape1, FD_BF16, PAGED>(p, grid, s, e0, e1);
+        if (shape == 2) return launch_shares<ChunkShape2, FD_BF16, PAGED>(p, grid, s, e0, e1);
+        return launch_shares<ChunkShape0, FD_BF16, PAGED>(p, grid, s, e0, e1);
+    }
+    if (shape == 1) return launch_shares<ChunkShape1, FD_FP8_E4M3FN, PAGED>(p, grid, s, e0, e1);
+    if (shape == 2) return launch_shares<ChunkShape2, FD_FP8_E4M3FN, PAGED>(p, grid, s, e0, e1);
+    return launch_shares<ChunkShape0, FD_FP8_E4M3FN, PAGED>(p, grid, s, e0, e1);
+}
+
 template <int KV, int QT, bool PAGED>
 int launch_valu(const Params &p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
@@ -119,13 +159,13 @@ int dispatch_valu(const Params &p, int kv, int qt, bool paged, dim3 grid, hipStr
 extern "C" size_t fd_attn_workspace_size(const fd_attn_desc_t *desc)
 {
     if (!desc || check_shape(desc) != FD_OK) return 0;
-    const size_t chunk = (size_t)fd::host::chunk_of(desc);
-    const size_t maxch = ((size_t)desc->max_seq_len + chunk - 1) / chunk;
-    return layout_of((size_t)desc->batch * desc->num_q_heads, maxch).total;
+    fd::host::Plan pl;
+    fd::host::plan_of(desc, &pl);
+    return layout_of((size_t)desc->batch * desc->num_q_heads, slots_of(desc, pl)).total;
 }
 
 extern "C" int fd_attn_plan(const fd_attn_desc_t *desc, int32_t *chunk_size, int32_t *family, int32_t *shape,
-                            int32_t *fused)
+                            int32_t *fused, int32_t *shares)
 {
     if (!desc) return FD_ERR_NULL;
     const int rc = check_shape(desc);
@@ -136,6 +176,7 @@ extern "C" int fd_attn_plan(const fd_attn_desc_t *desc, int32_t *chunk_size, int
     if (family) *family = pl.family;
     if (shape) *shape = pl.shape;
     if (fused) *fused = pl.fused;
+    if (shares) *shares = pl.shares;
     return FD_OK;
 }
 
@@ -192,7 +233,7 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     const int chunk = pl.chunk;
     const int maxch = (d->max_seq_len + chunk - 1) / chunk;
     const size_t rows = (size_t)d->batch * d->num_q_heads;
-    const Layout L = layout_of(rows, (size_t)maxch);
+    const Layout L = layout_of(rows, slots_of(d, pl));
     uint8_t *ws = static_cast<uint8_t *>(wsp);
 
     Params p;
@@ -209,6 +250,7 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     p.count_word = reinterpret_cast<unsigned long long *>(ws + L.header);
     p.fused_word = reinterpret_cast<unsigned long long *>(ws + L.header + kFusedWordOffset);
     p.fused_count = reinterpret_cast<unsigned long long *>(ws + L.header + kFusedCountOffset);
+    p.claim_word = reinterpret_cast<unsigned long long *>(ws + L.header + kClaimOffset);
     p.rg_count = reinterpret_cast<unsigned long long *>(ws + L.rg_count);
     p.epoch = next_epoch();
     p.o_part = reinterpret_cast<float *>(ws + L.o_part);
@@ -243,7 +285,13 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     // group merges it) or in a second launch, as the plan says
     p.fused = pl.fused;
 
-    if (use_mfma) {
+    if (use_mfma && pl.shares) {
+        // a persistent grid: workgroup w takes share w of the call
+        p.heads_per_block = heads_per_block(p.group);
+        p.ngroups = p.batch * (p.hq / p.heads_per_block);
+        rc = paged ? dispatch_shares<true>(p, pl.family, pl.shape, dim3((unsigned)pl.shares), stream, ev0, ev1)
+                   : dispatch_shares<false>(p, pl.family, pl.shape, dim3((unsigned)pl.shares), stream, ev0, ev1);
+    } else if (use_mfma) {
         p.heads_per_block = heads_per_block(p.group);
         // One workgroup per unit; workgroups past the real units exit at once.
         // The unit index is blockIdx.y * gridDim.x + blockIdx.x.

@@ -2,11 +2,13 @@
 // through a per-wave LDS ring filled by coalesced buffer->LDS DMA; both
 // contractions run on the matrix cores.
 //
-// Work decomposition.  A unit is (sequence b, head block hb, chunk c).  The
-// grid is an upper bound on the number of units; workgroup i takes the i-th
-// real unit of the list "all full chunks, then all partial last chunks", so
-// workgroups past the end exit at once and no launch slot in the middle of the
-// grid is wasted on a chunk beyond its sequence.
+// Work decomposition (chunk_kernel).  A unit is (sequence b, head block hb,
+// chunk c).  The grid is an upper bound on the number of units; workgroup i
+// takes the i-th real unit of the list "all full chunks, then all partial
+// last chunks", so workgroups past the end exit at once and no launch slot in
+// the middle of the grid is wasted on a chunk beyond its sequence.
+// share_kernel runs the same unit body over balanced shares of the call
+// instead (see there).
 //
 // Shape <NW, NSUB, NST>: NW wavefronts per workgroup, each owning an
 // NST-stage ring; a ring block holds NSUB compute groups of K and of V (a
@@ -55,8 +57,31 @@ struct Shape {
     static_assert(lds <= 160 * 1024, "LDS per workgroup");
 };
 
+// One unit of work: tokens [t_begin, t_end) of the row group (sequence b,
+// head block hb), whose partials are `parts` (this unit's index idx there).
+// A direct unit is the whole row group of a call that merges in the launch:
+// it writes the rows' outputs and flags and stores no partial.
+struct Seg {
+    int b, hb, L;          // L = the sequence's clamped length
+    int t_begin, t_end;
+    int idx;
+    bool direct;
+    Parts parts;
+};
+
+// Reduces one unit with the whole workgroup, stores its partials (or, for a
+// direct unit, the outputs), publishes it, and merges the row group if it
+// was the row group's last unit.  `lds` is the workgroup's ring (S::lds
+// bytes); the three ints are workgroup-shared.  Every thread must call it;
+// it leaves the ring and those ints in use until all threads have returned.
+// With `claim` set, thread 0 adds 1 to *claim with a fetch-and-add once its
+// wave has issued the unit's last ring refill, and leaves the returned word
+// in claim_v: issued there, the round trip is older than no DMA that a later
+// ring wait waits for (a wave's vector-memory counter counts returns in issue
+// order), so it delays none of them.
 template <int KV, bool PAGED, typename S>
-__global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
+FD_DEV void run_unit(const Params &p, const Seg &sg, uint8_t *lds, int &flagged_heads, int &last_flag, int &merged,
+                     unsigned long long *claim = nullptr, unsigned long long *claim_v = nullptr)
 {
     using F = Fmt<KV>;
     constexpr bool FP8 = KV == FD_FP8_E4M3FN;
@@ -69,26 +94,17 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     constexpr int RPI = 1024 / ROW;                // rows per DMA instruction
     constexpr int LPR = 64 / RPI;                  // lanes per row in a DMA instruction
     constexpr int DMA_TILE = S::tile / 1024;       // DMA instructions per K (or V) tile
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
-    __shared__ int flagged_heads, last_flag, merged;
-    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) begin_call(p);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int g4 = lane >> 4;
     const int GB = p.heads_per_block;
-    const int nhb = p.hq / GB;
-
-    const Unit U = find_unit(p, blockIdx.y * gridDim.x + blockIdx.x, nhb, lane);
-    if (!U.ok) return;
-    const int b = __builtin_amdgcn_readfirstlane(U.b);
-    const int hb = __builtin_amdgcn_readfirstlane(U.hb);
-    const int c = __builtin_amdgcn_readfirstlane(U.c);
-    const int L = __builtin_amdgcn_readfirstlane(U.L);
-    const int t_begin = c * p.chunk;
-    const int t_end = min(t_begin + p.chunk, L);
+    const int b = sg.b, hb = sg.hb, L = sg.L;
+    const int t_begin = sg.t_begin, t_end = sg.t_end;
     const int h0 = hb * GB;
+    // workspace slot of this unit's partial of head h0 + hh
+    auto slot_of = [&](int hh) { return sg.parts.base + (size_t)sg.idx * sg.parts.stride + hh; };
     const int kvh = h0 / p.group;
     const bool head_ok = n < GB;
 
@@ -221,6 +237,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     // ordinary running-maximum softmax, the maximum advanced once per compute
     // group.  Leaves this wave's O^T, weight sum, and band flag (or running
     // maximum) in red[wave].
+    bool claim_sent = false;
     auto run = [&](auto online_tag) {
         constexpr bool ONLINE = decltype(online_tag)::value;
         constexpr int NT = FP8 ? 2 : 1;            // S tiles per compute group
@@ -313,7 +330,12 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
                                "+v"(kraw[u][0]), "+v"(kraw[u][1]), "+v"(kraw[u][2]), "+v"(kraw[u][3])
                              :
                              : "memory");
-            if (j + NST * NW < nblk) issue(j + NST * NW, stage, pg_next);
+            if (j + NST * NW < nblk) {
+                issue(j + NST * NW, stage, pg_next);
+            } else if (!ONLINE && claim && !claim_sent) {
+                if (threadIdx.x == 0) *claim_v = fetch_add64(claim, 1);
+                claim_sent = true;
+            }
             load_pages(j + (NST + 1) * NW, pg_next);
             stage = stage + 1 == NST ? 0 : stage + 1;
 
@@ -433,12 +455,13 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     // in a fused call the unit writes its rows' outputs and flags itself, in
     // the merge's arithmetic (the chunk's sum times v_scale over its weight
     // sum; an empty row is zero), and stores no partial.
-    const bool direct = p.fused && L <= p.chunk;
+    const bool direct = sg.direct;
     const float vs = FP8 ? p.v_scale[kvh] : 1.f;
     const size_t row0 = (size_t)b * p.hq + h0;
 
     // ---- unified-max pass: plain sums over the waves
     run(std::false_type{});
+    if (claim && !claim_sent && threadIdx.x == 0) *claim_v = fetch_add64(claim, 1);   // no loop iteration
     if (wave == 0) {
         int f = 0;
         float l = 0.f;
@@ -449,7 +472,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
                 f |= red[w2 * kRedStride + 2064 + lane] != 0.f;
             }
             if (!direct) {
-                const size_t slot = part_slot(p, b, h0 + lane, c);
+                const size_t slot = slot_of(lane);
                 part_store(p, p.l_part + slot, l);
                 part_store(p, p.m_part + slot, p.phi);
                 part_store(p, p.cflag + slot, (uint8_t)f);
@@ -472,7 +495,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
             for (int w2 = 0; w2 < NW; ++w2) l += red[w2 * kRedStride + 2048 + hh];
             store_out(p, (row0 + hh) * kHeadDim + d, L > 0 ? acc * (vs / l) : 0.f);
         } else {
-            const size_t slot = part_slot(p, b, h0 + hh, c);
+            const size_t slot = slot_of(hh);
             part_store(p, p.o_part + slot * kHeadDim + d, acc);
         }
     }
@@ -500,7 +523,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
             if (direct) {
                 store_out(p, (row0 + hh) * kHeadDim + d, acc * (vs / l));
             } else {
-                const size_t slot = part_slot(p, b, h0 + hh, c);
+                const size_t slot = slot_of(hh);
                 part_store(p, p.o_part + slot * kHeadDim + d, acc);
             }
         }
@@ -516,7 +539,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
                 const float f = (mw == M) ? 1.f : exp2_hw((mw - M) * kLog2e);
                 l += red[w2 * kRedStride + 2048 + hh] * f;
             }
-            const size_t slot = part_slot(p, b, h0 + hh, c);
+            const size_t slot = slot_of(hh);
             part_store(p, p.l_part + slot, l);
             part_store(p, p.m_part + slot, M);
         }
@@ -526,8 +549,107 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
     if (direct) {
         if (threadIdx.x < GB) p.flags[row0 + threadIdx.x] = (uint8_t)((fmask >> threadIdx.x) & 1);
         if (threadIdx.x == 0) finish_group(p, __popc(fmask));
-    } else if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) {
-        merge_group<NW>(p, b, h0, GB, merged);
+    } else if (publish_unit(p, b * p.hq + h0, sg.parts.n, last_flag)) {
+        merge_group<NW>(p, b, h0, GB, merged, sg.parts);
+    }
+}
+
+template <int KV, bool PAGED, typename S>
+__global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
+    __shared__ int flagged_heads, last_flag, merged;
+    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) begin_call(p);
+    const int GB = p.heads_per_block;
+    const Unit U = find_unit(p, blockIdx.y * gridDim.x + blockIdx.x, p.hq / GB, threadIdx.x & 63);
+    if (!U.ok) return;
+    Seg sg;
+    sg.b = __builtin_amdgcn_readfirstlane(U.b);
+    sg.hb = __builtin_amdgcn_readfirstlane(U.hb);
+    sg.L = __builtin_amdgcn_readfirstlane(U.L);
+    const int c = __builtin_amdgcn_readfirstlane(U.c);
+    sg.t_begin = c * p.chunk;
+    sg.t_end = min(sg.t_begin + p.chunk, sg.L);
+    sg.idx = c;
+    sg.direct = p.fused && sg.L <= p.chunk;
+    sg.parts = chunk_parts(p, sg.b, sg.hb * GB, sg.L);
+    run_unit<KV, PAGED, S>(p, sg, lds, flagged_heads, last_flag, merged);
+}
+
+// Balanced shares (a persistent grid): the call's work -- every row group's
+// tokens, row groups in (sequence, head block) order, in quanta of kQuantum
+// tokens -- is cut into segments (cut_of: one static share per workgroup,
+// then pool grains that workgroups claim as they finish).  A workgroup walks
+// the row groups each of its segments touches and reduces its piece of each
+// as one unit.  The pieces of a row group are its chunks, merged in the
+// launch by the piece that completes last; a row group inside one segment is
+// written directly.  Piece (segment s, row group r) keeps its partials in
+// slots (s + r) GB ..: along the cut, s + r grows strictly from piece to
+// piece.
+template <int KV, bool PAGED, typename S>
+__global__ __launch_bounds__(S::waves * 64, 2) void share_kernel(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
+    __shared__ int flagged_heads, last_flag, merged;
+    __shared__ uint32_t claimed;
+    const int GB = p.heads_per_block;
+    const int nhb = p.hq / GB;
+    const int lane = threadIdx.x & 63;
+    const Cut cut = cut_of(call_quanta(p, nhb, lane), gridDim.x);
+    if ((int)blockIdx.x >= cut.W) return;
+    // Pool grains are claimed with one fetch-and-add (thread 0) on the call's
+    // epoch-tagged claim counter (fd_merge.h), issued in the segment's last
+    // piece once its ring is fully issued and settled after the piece, so the
+    // round trip overlaps the piece's last blocks and epilogue.  Every
+    // workgroup claims until it draws past the pool: the call makes exactly
+    // ngrains + W claims, and the last one resets the counter for the next
+    // call.
+    uint32_t seg = blockIdx.x;
+    unsigned long long pending = 0;
+    bool first = true;
+    for (;;) {
+        uint64_t lo, hi;
+        seg_range(cut, seg, lo, hi);
+        RowGroup g = seek(p, nhb, lane, lo);
+        while (g.A < hi) {
+            if (!first) __syncthreads();   // the last unit's epilogue is done with the ring
+            first = false;
+            const uint64_t plo = lo > g.A ? lo : g.A;
+            const uint64_t phi = hi < g.A + g.nq ? hi : g.A + g.nq;
+            const uint32_t sf = seg_of(cut, g.A), sl = seg_of(cut, g.A + g.nq - 1);
+            Seg sg;
+            sg.b = g.b;
+            sg.hb = g.hb;
+            sg.L = g.L;
+            sg.t_begin = (int)(plo - g.A) * kQuantum;
+            sg.t_end = min((int)(phi - g.A) * kQuantum, g.L);
+            sg.idx = (int)(seg - sf);
+            sg.direct = sf == sl;
+            sg.parts = Parts{((size_t)sf + (size_t)g.b * nhb + g.hb) * GB, GB, (int)(sl - sf + 1)};
+            // the segment's last piece claims the next grain
+            const bool last_piece = hi <= g.A + g.nq;
+            run_unit<KV, PAGED, S>(p, sg, lds, flagged_heads, last_flag, merged,
+                                   cut.ngrains && last_piece ? p.claim_word : nullptr, &pending);
+            // next row group
+            g.A += g.nq;
+            if (++g.hb == nhb) {
+                g.hb = 0;
+                if (++g.b == p.batch) break;
+                g.L = __builtin_amdgcn_readfirstlane(seq_len_of(p, g.b));
+                g.nq = quanta_of(g.L);
+            }
+        }
+        if (!cut.ngrains) break;
+        __syncthreads();   // every wave is past the last unit's use of the shared ints
+        if (threadIdx.x == 0) {
+            const uint32_t k = epoch_settle(p.claim_word, p.epoch, 1, pending) - 1;
+            if (k == cut.ngrains + (uint32_t)cut.W - 1) put(p.claim_word, next_tag(p.epoch));
+            claimed = k;
+        }
+        __syncthreads();
+        const uint32_t k = claimed;
+        if (k >= cut.ngrains) break;
+        seg = (uint32_t)cut.W + k;
     }
 }
 

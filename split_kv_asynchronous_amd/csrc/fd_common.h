@@ -7,6 +7,7 @@
 #include "fd_attn.h"
 
 #define FD_DEV __device__ __forceinline__
+#define FD_HOST_DEV __host__ __device__
 
 namespace fd {
 
@@ -34,6 +35,7 @@ struct Params {
     unsigned long long *count_word;   // {recomputed (row, chunk) pairs, epoch} of the call
     unsigned long long *fused_word;   // fused merge: {epoch | merged row groups}
     unsigned long long *fused_count;  // fused merge: {epoch | recomputed (row, chunk) pairs}
+    unsigned long long *claim_word;   // balanced shares: {epoch | pool grains claimed}
     unsigned long long *rg_count;     // [B][Hq] epoch-tagged unit counts per row group (first head)
     uint32_t epoch;                   // this call's epoch (never 0)
     int fused;                        // the last workgroup of a row group merges it (else a merge launch)

@@ -508,7 +508,7 @@ __global__ __launch_bounds__(S::waves * 64) void chunk_kernel(Params p)
         if (head_ok && wave == 0 && g4 == 0) p.flags[row] = (uint8_t)((fmask >> n) & 1);
         if (threadIdx.x == 0) finish_group(p, __popcll(fmask));
     } else if (publish_unit(p, b * p.hq + h0, units_of(p, L), last_flag)) {
-        merge_group<S::waves, 1>(p, b, h0, GB, merged);
+        merge_group<S::waves, 1>(p, b, h0, GB, merged, chunk_parts(p, b, h0, L));
     }
 }
 

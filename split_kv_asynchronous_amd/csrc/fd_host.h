@@ -81,9 +81,20 @@ constexpr int kShapes[3] = {3, 3, 1};
 // merge.
 struct TableRow {
     int family, paged, max_len, chunk, shape, fused_chunk;
+    int shares;   // chunk_size == 0: 0 = fixed chunks, k + 1 = balanced shares in shape k
 };
 
 constexpr int64_t kSmallGrid = 512;
+
+// With chunk_size == 0, calls of at least this many row groups (sequences x
+// query-head blocks) run balanced shares in shape 2 whatever their row says:
+// the fixed-chunk kernels locate every unit by scanning all the lengths, and
+// at serving batches that scan dominates (measured on MI355X, lengths
+// U[128, 2048], whole call, shares against the table's plan: grouped bf16,
+// 64/8 heads, batch 512 / 1024 / 2048 / 4096: 0.98-1.02 / 0.91-0.94 /
+// 0.80-0.82 / 0.68; grouped E4M3FN, 32/8 heads, paged: 1.03 / 1.01 / 0.94 /
+// 0.84).
+constexpr int64_t kServeGroups[2] = {8192, 16384};
 
 // Measured on MI355X: calls replayed back to back (best of 3 x 10), every
 // chunk size 256 .. 4096 x every shape x both merge placements, on ragged
@@ -107,27 +118,31 @@ constexpr int64_t kSmallGrid = 512;
 // the longest rows (64K-128K: more chunks per row to merge at the end of
 // the launch) and on short E4M3FN rows at chunks of 1024 and more; the
 // one-query-per-KV-head kernel was 3-60% behind at every chunk size.
+// Balanced shares against the plan above (whole call, shares in shape 0,
+// best of 3 x 10): grouped E4M3FN 64 x U[512,16K] 0.96 (paged 0.96), 16 x
+// U[16K,64K] 0.98 (0.97); grouped bf16 32 x U[1K,32K] 0.98-0.99 (paged
+// 1.00); shorter and longer bf16 rows and 2K E4M3FN rows 1.04-1.10.
 inline constexpr TableRow kTable[] = {
-    {kFamGroupedBf16, 0, 2048, 2048, 1, 0},
-    {kFamGroupedBf16, 0, 8192, 4096, 1, 512},
-    {kFamGroupedBf16, 0, 32768, 2048, 0, 1024},
-    {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 0},
-    {kFamGroupedBf16, 1, 2048, 2048, 1, 0},
-    {kFamGroupedBf16, 1, 8192, 4096, 1, 1024},
-    {kFamGroupedBf16, 1, 32768, 2048, 0, 2048},
-    {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 0},
-    {kFamGroupedFp8, 0, 2048, 1024, 0, 1024},
-    {kFamGroupedFp8, 0, 16384, 1024, 0, 1024},
-    {kFamGroupedFp8, 0, 1 << 23, 2048, 0, 0},
-    {kFamGroupedFp8, 1, 2048, 1024, 0, 1024},
-    {kFamGroupedFp8, 1, 16384, 1024, 0, 1024},
-    {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 0},
-    {kFamVector, 0, 2048, 2048, 0, 0},
-    {kFamVector, 0, 8192, 2048, 0, 0},
-    {kFamVector, 0, 1 << 23, 4096, 0, 0},
-    {kFamVector, 1, 2048, 2048, 0, 0},
-    {kFamVector, 1, 8192, 2048, 0, 0},
-    {kFamVector, 1, 1 << 23, 4096, 0, 0},
+    {kFamGroupedBf16, 0, 2048, 2048, 1, 0, 0},
+    {kFamGroupedBf16, 0, 8192, 4096, 1, 512, 0},
+    {kFamGroupedBf16, 0, 32768, 2048, 0, 1024, 1},
+    {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 0, 0},
+    {kFamGroupedBf16, 1, 2048, 2048, 1, 0, 0},
+    {kFamGroupedBf16, 1, 8192, 4096, 1, 1024, 0},
+    {kFamGroupedBf16, 1, 32768, 2048, 0, 2048, 0},
+    {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 0, 0},
+    {kFamGroupedFp8, 0, 2048, 1024, 0, 1024, 0},
+    {kFamGroupedFp8, 0, 16384, 1024, 0, 1024, 1},
+    {kFamGroupedFp8, 0, 1 << 23, 2048, 0, 0, 1},
+    {kFamGroupedFp8, 1, 2048, 1024, 0, 1024, 0},
+    {kFamGroupedFp8, 1, 16384, 1024, 0, 1024, 1},
+    {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 0, 1},
+    {kFamVector, 0, 2048, 2048, 0, 0, 0},
+    {kFamVector, 0, 8192, 2048, 0, 0, 0},
+    {kFamVector, 0, 1 << 23, 4096, 0, 0, 0},
+    {kFamVector, 1, 2048, 2048, 0, 0, 0},
+    {kFamVector, 1, 8192, 2048, 0, 0, 0},
+    {kFamVector, 1, 1 << 23, 4096, 0, 0, 0},
 };
 
 inline const TableRow &table_row(const fd_attn_desc_t *d)
@@ -151,8 +166,16 @@ inline int chunk_of(const fd_attn_desc_t *d)
     return d->page_size > c ? d->page_size : c;
 }
 
+// Workgroups of a balanced-share call, by kernel shape: the persistent grid
+// of share_kernel, as many per compute unit (256 on an MI355X) as the
+// shape's LDS ring lets be resident -- 64, 96 and 48 KiB -- so that every
+// share streams from the start.
+constexpr int kCUs = 256;
+constexpr int kSharesPerCU[3] = {2, 1, 3};
+
 struct Plan {
     int family, chunk, shape, fused;
+    int shares;   // balanced shares: the workgroups that split the call (0: fixed chunks)
 };
 
 // The plan of a call whose shape has passed check_shape(); FD_ERR_SHAPE for
@@ -166,8 +189,29 @@ inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
     if (forced_shape >= kShapes[pl->family]) return FD_ERR_SHAPE;
     pl->shape = forced_shape >= 0 ? forced_shape : (pl->chunk == r.chunk ? r.shape : 0);
     const int place = d->plan & (FD_PLAN_FUSED | FD_PLAN_SPLIT);
-    if (place == (FD_PLAN_FUSED | FD_PLAN_SPLIT) || (d->plan & ~(FD_PLAN_SHAPE_MASK | FD_PLAN_FUSED | FD_PLAN_SPLIT)))
+    if (place == (FD_PLAN_FUSED | FD_PLAN_SPLIT) ||
+        (d->plan & ~(FD_PLAN_SHAPE_MASK | FD_PLAN_FUSED | FD_PLAN_SPLIT | FD_PLAN_SHARES)))
         return FD_ERR_SHAPE;
+    // balanced shares: grouped families only, merged in the launch; forced,
+    // or the library's pick for chunk_size == 0 when nothing is forced
+    pl->shares = 0;
+    if (d->plan & FD_PLAN_SHARES) {
+        if (pl->family == kFamVector || place == FD_PLAN_SPLIT) return FD_ERR_SHAPE;
+        pl->shares = kCUs * kSharesPerCU[pl->shape];
+        pl->fused = 1;
+        return FD_OK;
+    }
+    if (d->chunk_size == 0 && d->plan == 0 && pl->family != kFamVector) {
+        const int64_t groups =
+            (int64_t)d->batch * (d->num_q_heads / heads_per_block(d->num_q_heads / d->num_kv_heads));
+        const int sh = r.shares ? r.shares - 1 : groups >= kServeGroups[pl->family] ? 2 : -1;
+        if (sh >= 0) {
+            pl->shape = sh;
+            pl->shares = kCUs * kSharesPerCU[sh];
+            pl->fused = 1;
+            return FD_OK;
+        }
+    }
     const int64_t maxch = ((int64_t)d->max_seq_len + pl->chunk - 1) / pl->chunk;
     const int blocks = pl->family == kFamVector ? d->num_q_heads
                                                 : d->num_q_heads / heads_per_block(d->num_q_heads / d->num_kv_heads);

@@ -48,10 +48,11 @@ namespace fd {
 // for them.)  A call that completes a counter leaves it at zero tagged with
 // the next epoch the host will hand out (next_tag), so that on the next call
 // on this workspace -- the usual case -- every add counts at once.
-FD_DEV uint32_t epoch_add(unsigned long long *w, uint32_t epoch, uint32_t add)
+//
+// epoch_settle() is the part after the fetch-and-add, given the word it
+// returned (so that a caller can issue the add early and use it later).
+FD_DEV uint32_t epoch_settle(unsigned long long *w, uint32_t epoch, uint32_t add, unsigned long long v)
 {
-    unsigned long long v = __hip_atomic_fetch_add(w, (unsigned long long)add, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(v >> 32) == epoch) return (uint32_t)v + add;
     v += add;                                      // the word as this void add left it
     for (;;) {
@@ -62,6 +63,16 @@ FD_DEV uint32_t epoch_add(unsigned long long *w, uint32_t epoch, uint32_t add)
                                                  __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             return add;
     }
+}
+
+FD_DEV unsigned long long fetch_add64(unsigned long long *w, uint32_t add)
+{
+    return __hip_atomic_fetch_add(w, (unsigned long long)add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+FD_DEV uint32_t epoch_add(unsigned long long *w, uint32_t epoch, uint32_t add)
+{
+    return epoch_settle(w, epoch, add, fetch_add64(w, add));
 }
 
 // A zero count tagged with the epoch the host hands out after `epoch` (it
@@ -120,6 +131,22 @@ FD_DEV void begin_call(const Params &p)
 FD_DEV int units_of(const Params &p, int L)
 {
     return L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
+}
+
+// Where the partials of one row group (query heads h0 .. h0 + GB - 1 of a
+// sequence) live: partial j of head h0 + i is workspace slot
+// base + j * stride + i, for j < n.  Fixed chunks: j is the chunk, the
+// partials of one chunk are contiguous over all heads of the sequence
+// (part_slot).  Balanced shares: j is the share's index among the row
+// group's shares, packed GB slots each.
+struct Parts {
+    size_t base;
+    int stride, n;
+};
+
+FD_DEV Parts chunk_parts(const Params &p, int b, int h0, int L)
+{
+    return Parts{part_slot(p, b, h0, 0), p.hq, units_of(p, L)};
 }
 
 // The calling workgroup has stored its partials of one unit of row group
@@ -203,15 +230,15 @@ FD_DEV void store_out4(const Params &p, size_t e, f32x4 x)
 constexpr int kMergePass = 16;
 
 template <int R>
-FD_DEV int merge_rows(const Params &p, int b, const int (&h)[R], int nr, int lane)
+FD_DEV int merge_rows(const Params &p, int b, const int (&h)[R], int nr, int lane, const Parts &pt, int h0)
 {
     constexpr int PC = kMergePass;
     const int L = seq_len_of(p, b);
-    const int nch = (L + p.chunk - 1) / p.chunk;
-    const size_t cs = p.hq;                      // chunk c of a row at its base + c * hq
+    const int nch = L > 0 ? pt.n : 0;            // an empty row merges to zeros
+    const size_t cs = pt.stride;                 // partial c of a row at its base + c * stride
     size_t base[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) base[r] = part_slot(p, b, h[r < nr ? r : 0], 0);
+    for (int r = 0; r < R; ++r) base[r] = pt.base + (h[r < nr ? r : 0] - h0);
 
     // one pass of partials: chunks c0 .. c0 + PC - 1 (clamped to the last
     // chunk: every load stays in the row, the extra ones are not added)
@@ -325,7 +352,7 @@ FD_DEV int merge_rows(const Params &p, int b, const int (&h)[R], int nr, int lan
 // group's recomputed chunks to the call's count.  `total` is a
 // workgroup-shared int.
 template <int NW, int R = 2>
-FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
+FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total, const Parts &pt)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -336,7 +363,7 @@ FD_DEV void merge_group(const Params &p, int b, int h0, int nrows, int &total)
         int h[R];
 #pragma unroll
         for (int k = 0; k < R; ++k) h[k] = h0 + r + k * NW;
-        mine += merge_rows<R>(p, b, h, min(R, (nrows - 1 - r) / NW + 1), lane);
+        mine += merge_rows<R>(p, b, h, min(R, (nrows - 1 - r) / NW + 1), lane, pt, h0);
     }
     if (lane == 0 && mine) atomicAdd(&total, mine);
     __syncthreads();

@@ -235,5 +235,137 @@ FD_DEV Unit find_unit(const Params &p, int u, int nhb, int lane)
     return r;
 }
 
+// ---- Balanced shares (share_kernel).  The call's work is counted in quanta
+// of kQuantum tokens: a row group (sequence b, head block hb) has
+// quanta_of(L_b) of them, row groups in (b, hb) order; N in all.  The axis of
+// quanta is cut into segments, in order: W static shares (workgroup w takes
+// share w), then pool grains of kGrainQuanta quanta each, which workgroups
+// claim in turn from a counter as they run out of work, so that the
+// workgroups that stream faster (the chip serves them unevenly) take more.
+// The cut depends only on the lengths, never on who computes what, so the
+// result is the same bits on every call.  A quantum is a multiple of the 16
+// tokens a page-table entry covers, so a piece never starts inside a DMA
+// instruction's rows.
+constexpr int kQuantum = 64;
+constexpr int kPoolNum = 1, kPoolDen = 4;    // pooled fraction of a call's quanta
+constexpr int kGrainQuanta = 16;             // quanta of a pool grain (1024 tokens)
+
+// Quanta of a row group of length L (an empty one counts one, so that some
+// workgroup writes its rows).
+FD_DEV int quanta_of(int L)
+{
+    return L > 0 ? (L + kQuantum - 1) / kQuantum : 1;
+}
+
+// The cut of a call of N quanta over a grid of `grid` workgroups.  Calls of
+// at least 4 quanta per workgroup pool kPoolNum / kPoolDen of their quanta,
+// in grains of kGrainQuanta, and keep the rest in the static shares; smaller
+// ones are all static, in min(grid, N) shares (every share nonempty).  The
+// host sizes the workspace for the grains of the largest N its descriptor
+// allows (pool_grains() grows with N).
+struct Cut {
+    uint64_t N, S;       // quanta in all, in the static shares
+    int W;               // static shares
+    uint32_t ngrains;    // pool grains
+};
+
+FD_HOST_DEV inline uint64_t pooled(uint64_t N, int grid)
+{
+    return N < 4 * (uint64_t)grid ? 0 : N * kPoolNum / kPoolDen;
+}
+
+FD_HOST_DEV inline uint32_t pool_grains(uint64_t N, int grid)
+{
+    return (uint32_t)((pooled(N, grid) + kGrainQuanta - 1) / kGrainQuanta);
+}
+
+FD_DEV Cut cut_of(uint64_t N, int grid)
+{
+    Cut c;
+    c.N = N;
+    c.ngrains = pool_grains(N, grid);
+    if (c.ngrains) {
+        c.S = N - pooled(N, grid);
+        c.W = grid;
+    } else {
+        c.S = N;
+        c.W = N < (uint64_t)grid ? (int)N : grid;
+    }
+    return c;
+}
+
+// Segment holding quantum x (static share w: floor(w S / W) <= x, the last
+// such w; pool grain k: segment W + k).
+FD_DEV uint32_t seg_of(const Cut &c, uint64_t x)
+{
+    if (x < c.S) return (uint32_t)(((x + 1) * (uint64_t)c.W - 1) / c.S);
+    return (uint32_t)c.W + (uint32_t)((x - c.S) / kGrainQuanta);
+}
+
+// Quanta [lo, hi) of segment s.
+FD_DEV void seg_range(const Cut &c, uint32_t s, uint64_t &lo, uint64_t &hi)
+{
+    if (s < (uint32_t)c.W) {
+        lo = (uint64_t)s * c.S / (uint64_t)c.W;
+        hi = (uint64_t)(s + 1) * c.S / (uint64_t)c.W;
+    } else {
+        lo = c.S + (uint64_t)(s - c.W) * kGrainQuanta;
+        hi = lo + kGrainQuanta < c.N ? lo + kGrainQuanta : c.N;
+    }
+}
+
+// Quanta of the call: the lengths summed 64 at a time on DPP scans (the same
+// in every wavefront).  Sequence-level sums of quanta_of(L) fit 32 bits per
+// 64 sequences and are carried in 64 bits.
+FD_DEV uint64_t call_quanta(const Params &p, int nhb, int lane)
+{
+    const int last = p.batch - 1;
+    uint64_t seqq = 0;
+#pragma unroll 1
+    for (int sb = 0; sb < p.batch; sb += 64) {
+        const int b = sb + lane;
+        const int q = b < p.batch ? quanta_of(seq_len_of(p, b < last ? b : last)) : 0;
+        seqq += (uint32_t)__builtin_amdgcn_readlane(wave_scan(q), 63);
+    }
+    return seqq * (uint64_t)nhb;
+}
+
+// The row group holding quantum x (x < N).  Row group (b, hb) starts at
+// nhb P_b + hb quanta_of(L_b), with P_b the quanta of the sequences before b,
+// so x lies in sequence b iff P_b <= floor(x / nhb) < P_b + quanta_of(L_b).
+struct RowGroup {
+    uint64_t A;          // its first quantum
+    int b, hb, L, nq;    // sequence, head block, clamped length, quanta
+};
+
+FD_DEV RowGroup seek(const Params &p, int nhb, int lane, uint64_t x)
+{
+    RowGroup g = {0, 0, 0, 0, 1};
+    const int last = p.batch - 1;
+    const uint64_t xq = x / (uint64_t)nhb;
+    uint64_t base = 0;
+#pragma unroll 1
+    for (int sb = 0; sb < p.batch; sb += 64) {
+        const int b = sb + lane;
+        const int L = seq_len_of(p, b < last ? b : last);
+        const int q = b < p.batch ? quanta_of(L) : 0;
+        const int incl = wave_scan(q);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+        if (xq < base + total) {
+            const uint64_t m = __ballot(base + (uint32_t)incl > xq);
+            const int hit = __builtin_ctzll(m);      // < 64: the last lane's sum exceeds xq
+            const uint64_t P = base + (uint32_t)__builtin_amdgcn_readlane(incl - q, hit);
+            g.b = sb + hit;
+            g.L = __builtin_amdgcn_readlane(L, hit);
+            g.nq = __builtin_amdgcn_readlane(q, hit);
+            g.hb = (int)((x - P * (uint64_t)nhb) / (uint64_t)g.nq);
+            g.A = P * (uint64_t)nhb + (uint64_t)g.hb * (uint64_t)g.nq;
+            return g;
+        }
+        base += total;
+    }
+    return g;
+}
+
 }  // namespace ring
 }  // namespace fd

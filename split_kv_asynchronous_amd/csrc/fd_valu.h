@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void partial_valu_kernel(Params p)
             finish_group(p, flagged ? 1 : 0);
         }
     } else if (publish_unit(p, b * p.hq + h, units_of(p, L), last_flag)) {
-        merge_group<4, 1>(p, b, h, 1, merged);
+        merge_group<4, 1>(p, b, h, 1, merged, chunk_parts(p, b, h, L));
     }
 }
 

@@ -290,24 +290,25 @@ def test_flat_gemm_table_covers_the_7b_layers():
 # covers max_seq_len, always do).
 FAMILY_KW = {0: dict(), 1: dict(kv_dtype="e4m3fn"), 2: dict(num_kv_heads=64)}
 PLAN_ROWS = [
-    # family, paged, max_seq_len probes, chunk, shape, largest chunk merged in the launch
-    (0, 0, (1, 2048), 2048, 1, 0), (0, 0, (2049, 8192), 4096, 1, 512),
-    (0, 0, (8193, 32768), 2048, 0, 1024), (0, 0, (32769, 1 << 20), 1024, 0, 0),
-    (0, 1, (16, 2048), 2048, 1, 0), (0, 1, (2064, 8192), 4096, 1, 1024),
-    (0, 1, (8208, 32768), 2048, 0, 2048), (0, 1, (32784, 1 << 20), 2048, 0, 0),
-    (1, 0, (1, 2048), 1024, 0, 1024), (1, 0, (2049, 16384), 1024, 0, 1024),
-    (1, 0, (16385, 1 << 20), 2048, 0, 0),
-    (1, 1, (16, 2048), 1024, 0, 1024), (1, 1, (2064, 16384), 1024, 0, 1024),
-    (1, 1, (16400, 1 << 20), 2048, 0, 0),
-    (2, 0, (1, 2048), 2048, 0, 0), (2, 0, (2049, 8192), 2048, 0, 0),
-    (2, 0, (8193, 1 << 20), 4096, 0, 0),
-    (2, 1, (16, 2048), 2048, 0, 0), (2, 1, (2064, 8192), 2048, 0, 0),
-    (2, 1, (8208, 1 << 20), 4096, 0, 0),
+    # family, paged, max_seq_len probes, chunk, shape, largest chunk merged in
+    # the launch, balanced shares for chunk_size 0 (shape + 1; 0: fixed chunks)
+    (0, 0, (1, 2048), 2048, 1, 0, 0), (0, 0, (2049, 8192), 4096, 1, 512, 0),
+    (0, 0, (8193, 32768), 2048, 0, 1024, 1), (0, 0, (32769, 1 << 20), 1024, 0, 0, 0),
+    (0, 1, (16, 2048), 2048, 1, 0, 0), (0, 1, (2064, 8192), 4096, 1, 1024, 0),
+    (0, 1, (8208, 32768), 2048, 0, 2048, 0), (0, 1, (32784, 1 << 20), 2048, 0, 0, 0),
+    (1, 0, (1, 2048), 1024, 0, 1024, 0), (1, 0, (2049, 16384), 1024, 0, 1024, 1),
+    (1, 0, (16385, 1 << 20), 2048, 0, 0, 1),
+    (1, 1, (16, 2048), 1024, 0, 1024, 0), (1, 1, (2064, 16384), 1024, 0, 1024, 1),
+    (1, 1, (16400, 1 << 20), 2048, 0, 0, 1),
+    (2, 0, (1, 2048), 2048, 0, 0, 0), (2, 0, (2049, 8192), 2048, 0, 0, 0),
+    (2, 0, (8193, 1 << 20), 4096, 0, 0, 0),
+    (2, 1, (16, 2048), 2048, 0, 0, 0), (2, 1, (2064, 8192), 2048, 0, 0, 0),
+    (2, 1, (8208, 1 << 20), 4096, 0, 0, 0),
 ]
 
 
-@pytest.mark.parametrize("fam,paged,lens,chunk,shape,fused_chunk", PLAN_ROWS)
-def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk):
+@pytest.mark.parametrize("fam,paged,lens,chunk,shape,fused_chunk,shares", PLAN_ROWS)
+def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk, shares):
     for L in lens:
         kw = dict(FAMILY_KW[fam], max_seq_len=L, chunk_size=0, batch=256)
         if paged:
@@ -316,11 +317,17 @@ def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk):
         got = fd.fd_attn_plan(d)
         c = max(chunk, 16 if paged else 0)
         blocks = 8 if fam != 2 else 64
-        big = -(-L // c) * 256 * blocks > 512
-        fused = c <= fused_chunk or not big or c >= L      # a chunk covering max_seq_len: one-chunk rows
-        assert got == dict(chunk_size=c, family=fam, shape=shape, fused=int(fused)), (kw, got)
-        # the workspace follows the plan's chunk
-        assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
+        if shares:
+            # shape k's persistent grid: 2, 1 or 3 workgroups per compute unit
+            assert got == dict(chunk_size=c, family=fam, shape=shares - 1, fused=1,
+                               shares=256 * (2, 1, 3)[shares - 1]), (kw, got)
+            assert fd.fd_attn_workspace_size(d) != fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
+        else:
+            big = -(-L // c) * 256 * blocks > 512
+            fused = c <= fused_chunk or not big or c >= L      # a chunk covering max_seq_len: one-chunk rows
+            assert got == dict(chunk_size=c, family=fam, shape=shape, fused=int(fused), shares=0), (kw, got)
+            # the workspace follows the plan's chunk
+            assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
         # an explicit chunk size other than the table's runs shape 0, and
         # merges in the launch up to the row's largest such chunk
         for other in (256, 512, 2048, 4096):
@@ -336,23 +343,67 @@ def test_plan_small_grids_merge_in_the_launch_and_forced_plans():
     small = _desc(batch=1, num_q_heads=8, num_kv_heads=1, max_seq_len=4096, chunk_size=1024)
     assert fd.fd_attn_plan(small)["fused"] == 1
     big = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=512)
-    assert fd.fd_attn_plan(big) == dict(chunk_size=512, family=1, shape=0, fused=1)
+    assert fd.fd_attn_plan(big) == dict(chunk_size=512, family=1, shape=0, fused=1, shares=0)
     big = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=2048)
-    assert fd.fd_attn_plan(big) == dict(chunk_size=2048, family=1, shape=0, fused=0)
+    assert fd.fd_attn_plan(big) == dict(chunk_size=2048, family=1, shape=0, fused=0, shares=0)
     forced = _desc(kv_dtype="e4m3fn", max_seq_len=16384, chunk_size=512,
                    plan=fd.FD_PLAN_SHAPE(2) | fd.FD_PLAN_FUSED)
-    assert fd.fd_attn_plan(forced) == dict(chunk_size=512, family=1, shape=2, fused=1)
+    assert fd.fd_attn_plan(forced) == dict(chunk_size=512, family=1, shape=2, fused=1, shares=0)
     split = _desc(batch=1, num_q_heads=8, num_kv_heads=1, max_seq_len=4096, chunk_size=1024,
                   plan=fd.FD_PLAN_SPLIT)
     assert fd.fd_attn_plan(split)["fused"] == 0
     # a shape the family does not have, both placements, unknown bits: rejected
-    for bad in (fd.FD_PLAN_SHAPE(3), fd.FD_PLAN_FUSED | fd.FD_PLAN_SPLIT, 0x40):
+    for bad in (fd.FD_PLAN_SHAPE(3), fd.FD_PLAN_FUSED | fd.FD_PLAN_SPLIT, 0x80):
         d = _desc(plan=bad)
         assert fd.fd_attn_workspace_size(d) == 0
         with pytest.raises(fd.FdAttnError):
             fd.fd_attn_plan(d)
         assert _call(_valid_desc(plan=bad)) == -2
     assert _call(_valid_desc(num_kv_heads=64, plan=fd.FD_PLAN_SHAPE(1))) == -2   # vector: one shape
+
+
+def test_serving_batches_run_balanced_shares():
+    # chunk_size 0 and at least 8192 (bf16) / 16384 (E4M3FN) row groups:
+    # balanced shares in shape 2 (3 workgroups per compute unit); fewer row
+    # groups, an explicit chunk size or a forced plan: the table's plan
+    for kw, groups_needed in ((dict(), 8192), (dict(kv_dtype="e4m3fn", num_q_heads=32), 16384)):
+        for batch in (groups_needed // 8 - 1, groups_needed // 8):
+            base = dict(kw, batch=batch, max_seq_len=2048, chunk_size=0)
+            got = fd.fd_attn_plan(_desc(**base))
+            if batch * 8 >= groups_needed:
+                assert got["shares"] == 768 and got["shape"] == 2 and got["fused"] == 1, (base, got)
+            else:
+                assert got["shares"] == 0, (base, got)
+            assert fd.fd_attn_plan(_desc(**dict(base, chunk_size=1024)))["shares"] == 0
+            assert fd.fd_attn_plan(_desc(**dict(base, plan=fd.FD_PLAN_SPLIT)))["shares"] == 0
+    # one query per KV head: never
+    assert fd.fd_attn_plan(_desc(batch=4096, num_kv_heads=64, max_seq_len=2048, chunk_size=0))["shares"] == 0
+
+
+def test_balanced_share_plans():
+    # FD_PLAN_SHARES: a persistent grid of as many workgroups per compute unit
+    # (256) as the shape's ring lets be resident, merged in the launch; the
+    # workspace holds one partial per (share, row group) piece -- at most
+    # shares * heads_per_block + rows -- instead of one per (row, chunk)
+    for kw in (dict(), dict(kv_dtype="e4m3fn"), dict(page_size=16, max_blocks_per_seq=2048, num_pages=9)):
+        for shape, per_cu in ((0, 2), (1, 1), (2, 3)):
+            d = _desc(**dict(kw, max_seq_len=32768, chunk_size=1024, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(shape)))
+            got = fd.fd_attn_plan(d)
+            assert got == dict(chunk_size=1024, family=1 if kw.get("kv_dtype") else 0, shape=shape, fused=1,
+                               shares=256 * per_cu), (kw, got)
+            rows = 32 * 64
+            # pool grains of the largest call: 64-token quanta, a quarter
+            # pooled in grains of 16 quanta (calls of at least 4 quanta per share)
+            W, nmax = 256 * per_cu, 512 * 32 * 8
+            grains = -(-(nmax // 4) // 16) if nmax >= 4 * W else 0
+            slots = (W + grains) * 8 + rows
+            assert slots * (128 * 4 + 9) <= fd.fd_attn_workspace_size(d) <= slots * (128 * 4 + 9) + 8 * rows + 2048
+        assert fd.fd_attn_plan(_desc(**dict(kw, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_FUSED)))["shares"] == 512
+    # no shares for the one-query-per-KV-head kernel, nor with a merge launch
+    for bad in (_valid_desc(num_kv_heads=64, plan=fd.FD_PLAN_SHARES),
+                _valid_desc(plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SPLIT)):
+        assert fd.fd_attn_workspace_size(bad) == 0
+        assert _call(bad) == -2
 
 
 def test_static_workspace_variant_checks_before_the_gpu():

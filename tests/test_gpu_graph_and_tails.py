@@ -34,6 +34,9 @@ REPLAY_CASES = [
     ("split-gqa-bf16", 4, "bf16", 0, [8192, 6000, 8192, 5000], 256, "split"),
     ("split-mha-bf16", 1, "bf16", 0, [3000] * 4, 64, "split"),
     ("split-gqa-e4m3fn-paged", 4, "e4m3fn", 16, [4096, 3000, 2500, 4000], 128, "split"),
+    # balanced shares with pool grains claimed from the workspace's counter
+    ("shares-gqa-bf16", 8, "bf16", 0, [20000, 9000, 15000, 30000], 256, "shares"),
+    ("shares-gqa-e4m3fn-paged", 4, "e4m3fn", 16, [30000, 20000, 25000, 12000], 256, "shares"),
 ]
 
 
@@ -46,8 +49,10 @@ def test_decode_replayed_from_a_captured_graph(name, g, kv, page, lens, chunk, p
                                   kv_dtype=kv, page_size=page, chunk_size=chunk, phi=1.0, a=3.0, b=1.5,
                                   seed=600 + g)
     print("case replay %s" % name, flush=True)
-    dp = DeviceProblem(prob, plan=fd.FD_PLAN_FUSED if place == "fused" else fd.FD_PLAN_SPLIT)
-    assert fd.fd_attn_plan(dp.desc())["fused"] == (place == "fused")
+    dp = DeviceProblem(prob, plan={"fused": fd.FD_PLAN_FUSED, "split": fd.FD_PLAN_SPLIT,
+                                   "shares": fd.FD_PLAN_SHARES}[place])
+    plan = fd.fd_attn_plan(dp.desc())
+    assert plan["fused"] == (place != "split") and (plan["shares"] > 0) == (place == "shares")
     dp.run()
     out0, flags0 = dp.results()
     count0 = dp.recomputed()
