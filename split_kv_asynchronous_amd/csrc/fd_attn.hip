@@ -54,7 +54,7 @@ Layout layout_of(size_t rows, size_t slots)
 size_t slots_of(const fd_attn_desc_t *d, const fd::host::Plan &pl)
 {
     const size_t rows = (size_t)d->batch * d->num_q_heads;
-    if (pl.shares) {
+    if (pl.shares && !pl.share_chunks) {
         const int gb = fd::host::heads_per_block(d->num_q_heads / d->num_kv_heads);
         const uint64_t qmax = ((uint64_t)d->max_seq_len + fd::ring::kQuantum - 1) / fd::ring::kQuantum;
         const uint64_t nmax = qmax * (uint64_t)d->batch * (uint64_t)(d->num_q_heads / gb);
@@ -230,7 +230,7 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     Plan pl;
     int rc = fd::host::plan_of(d, &pl);
     if (rc != FD_OK) return rc;
-    const int chunk = pl.chunk;
+    const int chunk = pl.chunk ? pl.chunk : fd::host::chunk_of(d);   // 0: pieces (p.chunk unused)
     const int maxch = (d->max_seq_len + chunk - 1) / chunk;
     const size_t rows = (size_t)d->batch * d->num_q_heads;
     const Layout L = layout_of(rows, slots_of(d, pl));
@@ -284,6 +284,7 @@ int enqueue(const fd_attn_desc_t *d, const void *q, const void *k_cache, const v
     // the merge runs inside the chunk launch (the last workgroup of each row
     // group merges it) or in a second launch, as the plan says
     p.fused = pl.fused;
+    p.share_chunks = pl.share_chunks;
 
     if (use_mfma && pl.shares) {
         // a persistent grid: workgroup w takes share w of the call

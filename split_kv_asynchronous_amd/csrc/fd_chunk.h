@@ -580,12 +580,17 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
 // tokens, row groups in (sequence, head block) order, in quanta of kQuantum
 // tokens -- is cut into segments (cut_of: one static share per workgroup,
 // then pool grains that workgroups claim as they finish).  A workgroup walks
-// the row groups each of its segments touches and reduces its piece of each
-// as one unit.  The pieces of a row group are its chunks, merged in the
-// launch by the piece that completes last; a row group inside one segment is
-// written directly.  Piece (segment s, row group r) keeps its partials in
-// slots (s + r) GB ..: along the cut, s + r grows strictly from piece to
-// piece.
+// the row groups each of its segments touches and reduces its units there,
+// each with the whole workgroup as in chunk_kernel.  Two kinds of unit:
+//  * pieces (p.share_chunks == 0): a row group's piece in a segment, cut at
+//    the segment's edges; the pieces are the row group's chunks, merged in
+//    the launch by the one that completes last (a row group inside one
+//    segment is written directly).  Piece (segment s, row group r) keeps its
+//    partials in slots (s + r) GB ..: along the cut, s + r grows strictly
+//    from piece to piece.
+//  * whole chunks of p.chunk tokens (p.share_chunks == 1, p.chunk a multiple
+//    of kQuantum): chunk c of a row group belongs to the segment holding its
+//    first quantum; partials, merge and one-chunk rows as in chunk_kernel.
 template <int KV, bool PAGED, typename S>
 __global__ __launch_bounds__(S::waves * 64, 2) void share_kernel(Params p)
 {
@@ -595,15 +600,18 @@ __global__ __launch_bounds__(S::waves * 64, 2) void share_kernel(Params p)
     const int GB = p.heads_per_block;
     const int nhb = p.hq / GB;
     const int lane = threadIdx.x & 63;
-    const Cut cut = cut_of(call_quanta(p, nhb, lane), gridDim.x);
+    if ((blockIdx.x | threadIdx.x) == 0) begin_call(p);
+    const int cq = p.share_chunks ? p.chunk / kQuantum : 0;       // quanta per chunk
+    const Cut cut = cut_of(call_quanta(p, nhb, lane), gridDim.x, cq > kGrainQuanta ? cq : kGrainQuanta);
     if ((int)blockIdx.x >= cut.W) return;
     // Pool grains are claimed with one fetch-and-add (thread 0) on the call's
     // epoch-tagged claim counter (fd_merge.h), issued in the segment's last
-    // piece once its ring is fully issued and settled after the piece, so the
-    // round trip overlaps the piece's last blocks and epilogue.  Every
-    // workgroup claims until it draws past the pool: the call makes exactly
-    // ngrains + W claims, and the last one resets the counter for the next
-    // call.
+    // unit once its ring is fully issued and settled after the unit, so the
+    // round trip overlaps the unit's last blocks and epilogue (a segment with
+    // no unit -- whole chunks, none starting in it -- claims at its end).
+    // Every workgroup claims until it draws past the pool: the call makes
+    // exactly ngrains + W claims, and the last one resets the counter for the
+    // next call.
     uint32_t seg = blockIdx.x;
     unsigned long long pending = 0;
     bool first = true;
@@ -611,25 +619,45 @@ __global__ __launch_bounds__(S::waves * 64, 2) void share_kernel(Params p)
         uint64_t lo, hi;
         seg_range(cut, seg, lo, hi);
         RowGroup g = seek(p, nhb, lane, lo);
+        bool sent = false;
         while (g.A < hi) {
-            if (!first) __syncthreads();   // the last unit's epilogue is done with the ring
-            first = false;
-            const uint64_t plo = lo > g.A ? lo : g.A;
-            const uint64_t phi = hi < g.A + g.nq ? hi : g.A + g.nq;
-            const uint32_t sf = seg_of(cut, g.A), sl = seg_of(cut, g.A + g.nq - 1);
+            const uint64_t end = hi < g.A + g.nq ? hi : g.A + g.nq;    // this segment's part of the row group
             Seg sg;
             sg.b = g.b;
             sg.hb = g.hb;
             sg.L = g.L;
-            sg.t_begin = (int)(plo - g.A) * kQuantum;
-            sg.t_end = min((int)(phi - g.A) * kQuantum, g.L);
-            sg.idx = (int)(seg - sf);
-            sg.direct = sf == sl;
-            sg.parts = Parts{((size_t)sf + (size_t)g.b * nhb + g.hb) * GB, GB, (int)(sl - sf + 1)};
-            // the segment's last piece claims the next grain
-            const bool last_piece = hi <= g.A + g.nq;
-            run_unit<KV, PAGED, S>(p, sg, lds, flagged_heads, last_flag, merged,
-                                   cut.ngrains && last_piece ? p.claim_word : nullptr, &pending);
+            if (cq) {
+                // chunks of the row group whose first quantum lies in [lo, end)
+                const uint64_t from = lo > g.A ? lo - g.A : 0;
+                const int nch = units_of(p, g.L);
+                for (int c = (int)((from + cq - 1) / cq); c < nch && (uint64_t)c * cq < end - g.A; ++c) {
+                    if (!first) __syncthreads();   // the last unit's epilogue is done with the ring
+                    first = false;
+                    sg.t_begin = c * p.chunk;
+                    sg.t_end = min(sg.t_begin + p.chunk, g.L);
+                    sg.idx = c;
+                    sg.direct = p.fused && g.L <= p.chunk;
+                    sg.parts = chunk_parts(p, g.b, g.hb * GB, g.L);
+                    const bool last_unit = (uint64_t)(c + 1) * cq >= end - g.A && g.A + g.nq >= hi;
+                    run_unit<KV, PAGED, S>(p, sg, lds, flagged_heads, last_flag, merged,
+                                           cut.ngrains && last_unit ? p.claim_word : nullptr, &pending);
+                    sent |= last_unit;
+                }
+            } else {
+                if (!first) __syncthreads();
+                first = false;
+                const uint64_t plo = lo > g.A ? lo : g.A;
+                const uint32_t sf = seg_of(cut, g.A), sl = seg_of(cut, g.A + g.nq - 1);
+                sg.t_begin = (int)(plo - g.A) * kQuantum;
+                sg.t_end = min((int)(end - g.A) * kQuantum, g.L);
+                sg.idx = (int)(seg - sf);
+                sg.direct = sf == sl;
+                sg.parts = Parts{((size_t)sf + (size_t)g.b * nhb + g.hb) * GB, GB, (int)(sl - sf + 1)};
+                const bool last_unit = hi <= g.A + g.nq;
+                run_unit<KV, PAGED, S>(p, sg, lds, flagged_heads, last_flag, merged,
+                                       cut.ngrains && last_unit ? p.claim_word : nullptr, &pending);
+                sent |= last_unit;
+            }
             // next row group
             g.A += g.nq;
             if (++g.hb == nhb) {
@@ -642,6 +670,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void share_kernel(Params p)
         if (!cut.ngrains) break;
         __syncthreads();   // every wave is past the last unit's use of the shared ints
         if (threadIdx.x == 0) {
+            if (!sent) pending = fetch_add64(p.claim_word, 1);
             const uint32_t k = epoch_settle(p.claim_word, p.epoch, 1, pending) - 1;
             if (k == cut.ngrains + (uint32_t)cut.W - 1) put(p.claim_word, next_tag(p.epoch));
             claimed = k;

@@ -39,6 +39,7 @@ struct Params {
     unsigned long long *rg_count;     // [B][Hq] epoch-tagged unit counts per row group (first head)
     uint32_t epoch;                   // this call's epoch (never 0)
     int fused;                        // the last workgroup of a row group merges it (else a merge launch)
+    int share_chunks;                 // balanced shares of whole chunks (else pieces cut at share edges)
     int ngroups;                      // row groups of the call (sequences x head blocks)
     int batch, hq, hkv, group;   // group = hq / hkv
     int heads_per_block;         // query heads one chunk workgroup serves (MFMA path)

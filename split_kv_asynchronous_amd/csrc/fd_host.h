@@ -86,14 +86,17 @@ struct TableRow {
 
 constexpr int64_t kSmallGrid = 512;
 
-// With chunk_size == 0, calls of at least this many row groups (sequences x
-// query-head blocks) run balanced shares in shape 2 whatever their row says:
-// the fixed-chunk kernels locate every unit by scanning all the lengths, and
-// at serving batches that scan dominates (measured on MI355X, lengths
-// U[128, 2048], whole call, shares against the table's plan: grouped bf16,
-// 64/8 heads, batch 512 / 1024 / 2048 / 4096: 0.98-1.02 / 0.91-0.94 /
-// 0.80-0.82 / 0.68; grouped E4M3FN, 32/8 heads, paged: 1.03 / 1.01 / 0.94 /
-// 0.84).
+// Calls of at least this many row groups (sequences x query-head blocks) run
+// balanced shares in shape 2 unless a plan is forced: pieces for chunk_size
+// 0, whole chunks of the given size otherwise (merged in a second launch
+// unless a chunk covers max_seq_len).  The fixed-chunk kernels locate every
+// unit by scanning all the lengths, and at serving batches that scan
+// dominates.  Measured on MI355X, lengths U[128, 2048], paged, whole call,
+// shares against fixed chunks: grouped bf16, 64/8 heads, chunk_size 0 (the
+// table's plan), batch 512 / 1024 / 2048 / 4096: 0.98-1.02 / 0.91-0.94 /
+// 0.80-0.82 / 0.68; chunk 512 at batch 1024 / 4096: 0.87 / 0.53, chunk 2048:
+// 0.90 / 0.64; grouped E4M3FN, 32/8 heads, chunk_size 0: 1.03 / 1.01 / 0.94
+// / 0.84, chunk 512 at batch 1024 / 4096: 0.97 / 0.67.
 constexpr int64_t kServeGroups[2] = {8192, 16384};
 
 // Measured on MI355X: calls replayed back to back (best of 3 x 10), every
@@ -175,7 +178,8 @@ constexpr int kSharesPerCU[3] = {2, 1, 3};
 
 struct Plan {
     int family, chunk, shape, fused;
-    int shares;   // balanced shares: the workgroups that split the call (0: fixed chunks)
+    int shares;         // balanced shares: the workgroups that split the call (0: fixed chunks)
+    int share_chunks;   // balanced shares of whole chunks (chunk_size given), else pieces
 };
 
 // The plan of a call whose shape has passed check_shape(); FD_ERR_SHAPE for
@@ -192,23 +196,43 @@ inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
     if (place == (FD_PLAN_FUSED | FD_PLAN_SPLIT) ||
         (d->plan & ~(FD_PLAN_SHAPE_MASK | FD_PLAN_FUSED | FD_PLAN_SPLIT | FD_PLAN_SHARES)))
         return FD_ERR_SHAPE;
-    // balanced shares: grouped families only, merged in the launch; forced,
-    // or the library's pick for chunk_size == 0 when nothing is forced
+    // balanced shares: grouped families only; forced, or the library's pick
+    // for chunk_size == 0 when nothing is forced.  With chunk_size 0 the
+    // units are pieces cut at the shares' edges (merged in the launch); with
+    // a chunk size (a multiple of 64) they are whole chunks, merged as with
+    // fixed chunks (in the launch unless a merge launch is forced).
     pl->shares = 0;
+    pl->share_chunks = 0;
     if (d->plan & FD_PLAN_SHARES) {
-        if (pl->family == kFamVector || place == FD_PLAN_SPLIT) return FD_ERR_SHAPE;
+        if (pl->family == kFamVector) return FD_ERR_SHAPE;
         pl->shares = kCUs * kSharesPerCU[pl->shape];
-        pl->fused = 1;
+        if (d->chunk_size) {
+            if (d->chunk_size % 64) return FD_ERR_SHAPE;
+            pl->share_chunks = 1;
+            pl->fused = place != FD_PLAN_SPLIT;
+        } else {
+            if (place == FD_PLAN_SPLIT) return FD_ERR_SHAPE;
+            pl->chunk = 0;
+            pl->fused = 1;
+        }
         return FD_OK;
     }
-    if (d->chunk_size == 0 && d->plan == 0 && pl->family != kFamVector) {
+    if (d->plan == 0 && pl->family != kFamVector) {
         const int64_t groups =
             (int64_t)d->batch * (d->num_q_heads / heads_per_block(d->num_q_heads / d->num_kv_heads));
-        const int sh = r.shares ? r.shares - 1 : groups >= kServeGroups[pl->family] ? 2 : -1;
-        if (sh >= 0) {
-            pl->shape = sh;
-            pl->shares = kCUs * kSharesPerCU[sh];
+        const bool serve = groups >= kServeGroups[pl->family];
+        if (d->chunk_size == 0 && (r.shares || serve)) {
+            pl->shape = r.shares ? r.shares - 1 : 2;
+            pl->shares = kCUs * kSharesPerCU[pl->shape];
+            pl->chunk = 0;
             pl->fused = 1;
+            return FD_OK;
+        }
+        if (d->chunk_size % 64 == 0 && serve) {
+            pl->shape = 2;
+            pl->shares = kCUs * kSharesPerCU[2];
+            pl->share_chunks = 1;
+            pl->fused = pl->chunk >= d->max_seq_len;
             return FD_OK;
         }
     }

@@ -267,6 +267,7 @@ struct Cut {
     uint64_t N, S;       // quanta in all, in the static shares
     int W;               // static shares
     uint32_t ngrains;    // pool grains
+    int G;               // quanta per grain
 };
 
 FD_HOST_DEV inline uint64_t pooled(uint64_t N, int grid)
@@ -274,16 +275,17 @@ FD_HOST_DEV inline uint64_t pooled(uint64_t N, int grid)
     return N < 4 * (uint64_t)grid ? 0 : N * kPoolNum / kPoolDen;
 }
 
-FD_HOST_DEV inline uint32_t pool_grains(uint64_t N, int grid)
+FD_HOST_DEV inline uint32_t pool_grains(uint64_t N, int grid, int G = kGrainQuanta)
 {
-    return (uint32_t)((pooled(N, grid) + kGrainQuanta - 1) / kGrainQuanta);
+    return (uint32_t)((pooled(N, grid) + G - 1) / G);
 }
 
-FD_DEV Cut cut_of(uint64_t N, int grid)
+FD_DEV Cut cut_of(uint64_t N, int grid, int G = kGrainQuanta)
 {
     Cut c;
     c.N = N;
-    c.ngrains = pool_grains(N, grid);
+    c.G = G;
+    c.ngrains = pool_grains(N, grid, G);
     if (c.ngrains) {
         c.S = N - pooled(N, grid);
         c.W = grid;
@@ -299,7 +301,7 @@ FD_DEV Cut cut_of(uint64_t N, int grid)
 FD_DEV uint32_t seg_of(const Cut &c, uint64_t x)
 {
     if (x < c.S) return (uint32_t)(((x + 1) * (uint64_t)c.W - 1) / c.S);
-    return (uint32_t)c.W + (uint32_t)((x - c.S) / kGrainQuanta);
+    return (uint32_t)c.W + (uint32_t)((x - c.S) / (uint64_t)c.G);
 }
 
 // Quanta [lo, hi) of segment s.
@@ -309,8 +311,8 @@ FD_DEV void seg_range(const Cut &c, uint32_t s, uint64_t &lo, uint64_t &hi)
         lo = (uint64_t)s * c.S / (uint64_t)c.W;
         hi = (uint64_t)(s + 1) * c.S / (uint64_t)c.W;
     } else {
-        lo = c.S + (uint64_t)(s - c.W) * kGrainQuanta;
-        hi = lo + kGrainQuanta < c.N ? lo + kGrainQuanta : c.N;
+        lo = c.S + (uint64_t)(s - c.W) * (uint64_t)c.G;
+        hi = lo + (uint64_t)c.G < c.N ? lo + (uint64_t)c.G : c.N;
     }
 }
 

@@ -319,7 +319,7 @@ def test_plan_table(fam, paged, lens, chunk, shape, fused_chunk, shares):
         blocks = 8 if fam != 2 else 64
         if shares:
             # shape k's persistent grid: 2, 1 or 3 workgroups per compute unit
-            assert got == dict(chunk_size=c, family=fam, shape=shares - 1, fused=1,
+            assert got == dict(chunk_size=0, family=fam, shape=shares - 1, fused=1,
                                shares=256 * (2, 1, 3)[shares - 1]), (kw, got)
             assert fd.fd_attn_workspace_size(d) != fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=chunk)))
         else:
@@ -363,18 +363,25 @@ def test_plan_small_grids_merge_in_the_launch_and_forced_plans():
 
 
 def test_serving_batches_run_balanced_shares():
-    # chunk_size 0 and at least 8192 (bf16) / 16384 (E4M3FN) row groups:
-    # balanced shares in shape 2 (3 workgroups per compute unit); fewer row
-    # groups, an explicit chunk size or a forced plan: the table's plan
+    # at least 8192 (bf16) / 16384 (E4M3FN) row groups: balanced shares in
+    # shape 2 (3 workgroups per compute unit) -- pieces for chunk_size 0,
+    # whole chunks for a chunk size that is a multiple of 64 (merged by a
+    # second launch unless a chunk covers max_seq_len); fewer row groups, a
+    # chunk size off the 64 grid or a forced plan: fixed chunks
     for kw, groups_needed in ((dict(), 8192), (dict(kv_dtype="e4m3fn", num_q_heads=32), 16384)):
         for batch in (groups_needed // 8 - 1, groups_needed // 8):
             base = dict(kw, batch=batch, max_seq_len=2048, chunk_size=0)
             got = fd.fd_attn_plan(_desc(**base))
+            whole = fd.fd_attn_plan(_desc(**dict(base, chunk_size=512)))
+            one = fd.fd_attn_plan(_desc(**dict(base, chunk_size=2048)))
             if batch * 8 >= groups_needed:
                 assert got["shares"] == 768 and got["shape"] == 2 and got["fused"] == 1, (base, got)
+                assert got["chunk_size"] == 0
+                assert whole == dict(chunk_size=512, family=whole["family"], shape=2, fused=0, shares=768)
+                assert one["shares"] == 768 and one["fused"] == 1
             else:
-                assert got["shares"] == 0, (base, got)
-            assert fd.fd_attn_plan(_desc(**dict(base, chunk_size=1024)))["shares"] == 0
+                assert got["shares"] == 0 and whole["shares"] == 0 and one["shares"] == 0, (base, got)
+            assert fd.fd_attn_plan(_desc(**dict(base, chunk_size=96)))["shares"] == 0
             assert fd.fd_attn_plan(_desc(**dict(base, plan=fd.FD_PLAN_SPLIT)))["shares"] == 0
     # one query per KV head: never
     assert fd.fd_attn_plan(_desc(batch=4096, num_kv_heads=64, max_seq_len=2048, chunk_size=0))["shares"] == 0
@@ -382,15 +389,19 @@ def test_serving_batches_run_balanced_shares():
 
 def test_balanced_share_plans():
     # FD_PLAN_SHARES: a persistent grid of as many workgroups per compute unit
-    # (256) as the shape's ring lets be resident, merged in the launch; the
-    # workspace holds one partial per (share, row group) piece -- at most
-    # shares * heads_per_block + rows -- instead of one per (row, chunk)
+    # (256) as the shape's ring lets be resident.  chunk_size 0: pieces cut at
+    # the shares' edges (reported chunk size 0), merged in the launch; the
+    # workspace holds one partial per (segment, row group) piece -- at most
+    # (shares + pool grains) * heads_per_block + rows.  A chunk size (a
+    # multiple of 64): whole chunks, the fixed-chunk workspace, either merge
+    # placement.
     for kw in (dict(), dict(kv_dtype="e4m3fn"), dict(page_size=16, max_blocks_per_seq=2048, num_pages=9)):
+        fam = 1 if kw.get("kv_dtype") else 0
         for shape, per_cu in ((0, 2), (1, 1), (2, 3)):
-            d = _desc(**dict(kw, max_seq_len=32768, chunk_size=1024, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(shape)))
+            plan = fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(shape)
+            d = _desc(**dict(kw, max_seq_len=32768, chunk_size=0, plan=plan))
             got = fd.fd_attn_plan(d)
-            assert got == dict(chunk_size=1024, family=1 if kw.get("kv_dtype") else 0, shape=shape, fused=1,
-                               shares=256 * per_cu), (kw, got)
+            assert got == dict(chunk_size=0, family=fam, shape=shape, fused=1, shares=256 * per_cu), (kw, got)
             rows = 32 * 64
             # pool grains of the largest call: 64-token quanta, a quarter
             # pooled in grains of 16 quanta (calls of at least 4 quanta per share)
@@ -398,10 +409,17 @@ def test_balanced_share_plans():
             grains = -(-(nmax // 4) // 16) if nmax >= 4 * W else 0
             slots = (W + grains) * 8 + rows
             assert slots * (128 * 4 + 9) <= fd.fd_attn_workspace_size(d) <= slots * (128 * 4 + 9) + 8 * rows + 2048
-        assert fd.fd_attn_plan(_desc(**dict(kw, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_FUSED)))["shares"] == 512
-    # no shares for the one-query-per-KV-head kernel, nor with a merge launch
+            for place, fused in ((0, 1), (fd.FD_PLAN_FUSED, 1), (fd.FD_PLAN_SPLIT, 0)):
+                d = _desc(**dict(kw, max_seq_len=32768, chunk_size=1024, plan=plan | place))
+                assert fd.fd_attn_plan(d) == dict(chunk_size=1024, family=fam, shape=shape, fused=fused,
+                                                  shares=256 * per_cu)
+                assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(
+                    _desc(**dict(kw, max_seq_len=32768, chunk_size=1024)))
+    # no shares for the one-query-per-KV-head kernel, nor pieces with a merge
+    # launch, nor whole chunks of a size that is not a multiple of 64
     for bad in (_valid_desc(num_kv_heads=64, plan=fd.FD_PLAN_SHARES),
-                _valid_desc(plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SPLIT)):
+                _valid_desc(chunk_size=0, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SPLIT),
+                _valid_desc(chunk_size=96, plan=fd.FD_PLAN_SHARES)):
         assert fd.fd_attn_workspace_size(bad) == 0
         assert _call(bad) == -2
 

@@ -34,7 +34,9 @@ REPLAY_CASES = [
     ("split-gqa-bf16", 4, "bf16", 0, [8192, 6000, 8192, 5000], 256, "split"),
     ("split-mha-bf16", 1, "bf16", 0, [3000] * 4, 64, "split"),
     ("split-gqa-e4m3fn-paged", 4, "e4m3fn", 16, [4096, 3000, 2500, 4000], 128, "split"),
-    # balanced shares with pool grains claimed from the workspace's counter
+    # balanced shares with pool grains claimed from the workspace's counter:
+    # pieces cut at segment edges (chunk 0) and whole chunks
+    ("shares-pieces-gqa-bf16", 8, "bf16", 0, [20000, 9000, 15000, 30000], 0, "shares"),
     ("shares-gqa-bf16", 8, "bf16", 0, [20000, 9000, 15000, 30000], 256, "shares"),
     ("shares-gqa-e4m3fn-paged", 4, "e4m3fn", 16, [30000, 20000, 25000, 12000], 256, "shares"),
 ]

@@ -369,17 +369,19 @@ def test_plan_table_rows(g, kv, page, lens, cap):
     compare(prob, *dp.results())
 
 
-def test_serving_batch_runs_balanced_shares():
-    # chunk_size 0 at a serving batch (4096 sequences x 2 KV heads = 8192 row
-    # groups): the library picks balanced shares
+@pytest.mark.parametrize("chunk,fused", [(0, 1), (512, 0), (2048, 1)])
+def test_serving_batch_runs_balanced_shares(chunk, fused):
+    # a serving batch (4096 sequences x 2 KV heads = 8192 row groups): the
+    # library picks balanced shares -- pieces for chunk_size 0, whole chunks
+    # otherwise (merged by a second launch unless a chunk covers max_seq_len)
     import split_kv_asynchronous_amd as fd
-    lens = np.random.default_rng(17).integers(0, 300, size=4096)
-    prob = synthetic.make_problem(batch=4096, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=0,
+    lens = np.random.default_rng(17).integers(0, 1500, size=4096)
+    prob = synthetic.make_problem(batch=4096, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=chunk,
                                   max_seq_len=2048, page_size=16, seed=1717)
     dp = DeviceProblem(prob)
     plan = fd.fd_attn_plan(dp.desc())
-    print("case serving batch -> %s" % plan, flush=True)
-    assert plan["shares"] == 768 and plan["shape"] == 2
+    print("case serving batch chunk %d -> %s" % (chunk, plan), flush=True)
+    assert plan["shares"] == 768 and plan["shape"] == 2 and plan["fused"] == fused and plan["chunk_size"] == chunk
     dp.run()
     compare(prob, *dp.results())
 
@@ -401,23 +403,31 @@ SHARE_CASES = [
 ]
 
 
+# units: pieces cut at the segments' edges (chunk_size 0), or whole chunks
+# of 512 tokens merged in the launch or of 2048 tokens merged by a second launch
+SHARE_UNITS = [(0, 0), (512, 0), (2048, 0x20)]
+
+
+@pytest.mark.parametrize("chunk,place", SHARE_UNITS, ids=["pieces", "chunks512", "chunks2048-split"])
 @pytest.mark.parametrize("name,g,kv,page,lens,shape,out_dtype,narrow", SHARE_CASES, ids=[c[0] for c in SHARE_CASES])
-def test_balanced_shares(name, g, kv, page, lens, shape, out_dtype, narrow):
-    # the persistent grid of equal shares: rows cut at share edges (a row
-    # group inside one share is written directly, one spread over many is
-    # merged from all its pieces), empty and short rows, more sequences than
-    # one 64-wide scan, and pieces recomputed with online softmax
+def test_balanced_shares(name, g, kv, page, lens, shape, out_dtype, narrow, chunk, place):
+    # the persistent grid of equal shares and claimed grains: rows cut at
+    # segment edges (a row group inside one segment is written directly, one
+    # spread over many is merged from all its pieces) or whole chunks, empty
+    # and short rows, more sequences than one 64-wide scan, and units
+    # recomputed with online softmax
     import split_kv_asynchronous_amd as fd
     if lens == "many":
         lens = list(np.random.default_rng(5).integers(0, 300, size=700))
     hkv = 2
     band = dict(phi=1.0, a=3.0, b=1.5) if narrow else {}
     prob = synthetic.make_problem(batch=len(lens), num_q_heads=g * hkv, num_kv_heads=hkv, seq_lens=lens,
-                                  kv_dtype=kv, page_size=page, chunk_size=512, seed=1300 + g, **band)
-    print("case shares %s" % name, flush=True)
-    dp = DeviceProblem(prob, out_dtype=out_dtype, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(shape))
+                                  kv_dtype=kv, page_size=page, chunk_size=chunk, seed=1300 + g, **band)
+    print("case shares %s chunk %d place %d" % (name, chunk, place), flush=True)
+    dp = DeviceProblem(prob, out_dtype=out_dtype, plan=fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(shape) | place)
     plan = fd.fd_attn_plan(dp.desc())
-    assert plan["shares"] > 0 and plan["fused"] == 1 and plan["shape"] == shape
+    assert plan["shares"] > 0 and plan["fused"] == (place == 0) and plan["shape"] == shape
+    assert plan["chunk_size"] == chunk
     dp.run()
     out, flags = dp.results()
     ref_out, ref_flags, margin = oracle.decode_exact(**prob.args())
