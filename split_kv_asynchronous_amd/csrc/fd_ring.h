@@ -316,18 +316,36 @@ FD_DEV void seg_range(const Cut &c, uint32_t s, uint64_t &lo, uint64_t &hi)
     }
 }
 
-// Quanta of the call: the lengths summed 64 at a time on DPP scans (the same
-// in every wavefront).  Sequence-level sums of quanta_of(L) fit 32 bits per
-// 64 sequences and are carried in 64 bits.
-FD_DEV uint64_t call_quanta(const Params &p, int nhb, int lane)
+// Lengths and quanta of sequences sb + 64 k + lane, k < kFindBlocks (quanta 0
+// past the batch): all loads issued at once (indices clamped into the array,
+// so no load is conditional), one memory round trip per 64 kFindBlocks
+// sequences.
+FD_DEV void load_quanta(const Params &p, int sb, int lane, int (&L)[kFindBlocks], int (&q)[kFindBlocks])
 {
     const int last = p.batch - 1;
+#pragma unroll
+    for (int k = 0; k < kFindBlocks; ++k) {
+        const int b = sb + 64 * k + lane;
+        L[k] = seq_len_of(p, b < last ? b : last);
+    }
+#pragma unroll
+    for (int k = 0; k < kFindBlocks; ++k) q[k] = sb + 64 * k + lane < p.batch ? quanta_of(L[k]) : 0;
+}
+
+// Quanta of the call (the same in every wavefront).  A lane's quanta over
+// kFindBlocks sequences fit 32 bits, and so does their sum over 64 lanes;
+// the running total is carried in 64 bits.
+FD_DEV uint64_t call_quanta(const Params &p, int nhb, int lane)
+{
     uint64_t seqq = 0;
 #pragma unroll 1
-    for (int sb = 0; sb < p.batch; sb += 64) {
-        const int b = sb + lane;
-        const int q = b < p.batch ? quanta_of(seq_len_of(p, b < last ? b : last)) : 0;
-        seqq += (uint32_t)__builtin_amdgcn_readlane(wave_scan(q), 63);
+    for (int sb = 0; sb < p.batch; sb += 64 * kFindBlocks) {
+        int L[kFindBlocks], q[kFindBlocks];
+        load_quanta(p, sb, lane, L, q);
+        int mine = 0;
+#pragma unroll
+        for (int k = 0; k < kFindBlocks; ++k) mine += q[k];
+        seqq += (uint32_t)__builtin_amdgcn_readlane(wave_scan(mine), 63);
     }
     return seqq * (uint64_t)nhb;
 }
@@ -335,6 +353,7 @@ FD_DEV uint64_t call_quanta(const Params &p, int nhb, int lane)
 // The row group holding quantum x (x < N).  Row group (b, hb) starts at
 // nhb P_b + hb quanta_of(L_b), with P_b the quanta of the sequences before b,
 // so x lies in sequence b iff P_b <= floor(x / nhb) < P_b + quanta_of(L_b).
+// The lengths are scanned 64 at a time on DPP prefix sums.
 struct RowGroup {
     uint64_t A;          // its first quantum
     int b, hb, L, nq;    // sequence, head block, clamped length, quanta
@@ -343,28 +362,30 @@ struct RowGroup {
 FD_DEV RowGroup seek(const Params &p, int nhb, int lane, uint64_t x)
 {
     RowGroup g = {0, 0, 0, 0, 1};
-    const int last = p.batch - 1;
     const uint64_t xq = x / (uint64_t)nhb;
     uint64_t base = 0;
 #pragma unroll 1
-    for (int sb = 0; sb < p.batch; sb += 64) {
-        const int b = sb + lane;
-        const int L = seq_len_of(p, b < last ? b : last);
-        const int q = b < p.batch ? quanta_of(L) : 0;
-        const int incl = wave_scan(q);
-        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane(incl, 63);
-        if (xq < base + total) {
-            const uint64_t m = __ballot(base + (uint32_t)incl > xq);
-            const int hit = __builtin_ctzll(m);      // < 64: the last lane's sum exceeds xq
-            const uint64_t P = base + (uint32_t)__builtin_amdgcn_readlane(incl - q, hit);
-            g.b = sb + hit;
-            g.L = __builtin_amdgcn_readlane(L, hit);
-            g.nq = __builtin_amdgcn_readlane(q, hit);
-            g.hb = (int)((x - P * (uint64_t)nhb) / (uint64_t)g.nq);
-            g.A = P * (uint64_t)nhb + (uint64_t)g.hb * (uint64_t)g.nq;
-            return g;
+    for (int sb = 0; sb < p.batch; sb += 64 * kFindBlocks) {
+        int L[kFindBlocks], q[kFindBlocks];
+        load_quanta(p, sb, lane, L, q);
+#pragma unroll
+        for (int k = 0; k < kFindBlocks; ++k) {
+            if (sb + 64 * k >= p.batch) break;
+            const int incl = wave_scan(q[k]);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+            if (xq < base + total) {
+                const uint64_t m = __ballot(base + (uint32_t)incl > xq);
+                const int hit = __builtin_ctzll(m);      // < 64: the last lane's sum exceeds xq
+                const uint64_t P = base + (uint32_t)__builtin_amdgcn_readlane(incl - q[k], hit);
+                g.b = sb + 64 * k + hit;
+                g.L = __builtin_amdgcn_readlane(L[k], hit);
+                g.nq = __builtin_amdgcn_readlane(q[k], hit);
+                g.hb = (int)((x - P * (uint64_t)nhb) / (uint64_t)g.nq);
+                g.A = P * (uint64_t)nhb + (uint64_t)g.hb * (uint64_t)g.nq;
+                return g;
+            }
+            base += total;
         }
-        base += total;
     }
     return g;
 }
