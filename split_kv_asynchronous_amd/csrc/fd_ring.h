@@ -319,7 +319,8 @@ FD_DEV void seg_range(const Cut &c, uint32_t s, uint64_t &lo, uint64_t &hi)
 // Lengths and quanta of sequences sb + 64 k + lane, k < kFindBlocks (quanta 0
 // past the batch): all loads issued at once (indices clamped into the array,
 // so no load is conditional), one memory round trip per 64 kFindBlocks
-// sequences.
+// sequences.  Callers use every value (no path leaves a load's register to
+// be reused while the load is in flight).
 FD_DEV void load_quanta(const Params &p, int sb, int lane, int (&L)[kFindBlocks], int (&q)[kFindBlocks])
 {
     const int last = p.batch - 1;
@@ -368,12 +369,14 @@ FD_DEV RowGroup seek(const Params &p, int nhb, int lane, uint64_t x)
     for (int sb = 0; sb < p.batch; sb += 64 * kFindBlocks) {
         int L[kFindBlocks], q[kFindBlocks];
         load_quanta(p, sb, lane, L, q);
+        // every block of the group is scanned (blocks past the batch add 0),
+        // the hit kept, so that each loaded value is used
+        bool found = false;
 #pragma unroll
         for (int k = 0; k < kFindBlocks; ++k) {
-            if (sb + 64 * k >= p.batch) break;
             const int incl = wave_scan(q[k]);
             const uint32_t total = (uint32_t)__builtin_amdgcn_readlane(incl, 63);
-            if (xq < base + total) {
+            if (!found && xq < base + total) {
                 const uint64_t m = __ballot(base + (uint32_t)incl > xq);
                 const int hit = __builtin_ctzll(m);      // < 64: the last lane's sum exceeds xq
                 const uint64_t P = base + (uint32_t)__builtin_amdgcn_readlane(incl - q[k], hit);
@@ -382,10 +385,11 @@ FD_DEV RowGroup seek(const Params &p, int nhb, int lane, uint64_t x)
                 g.nq = __builtin_amdgcn_readlane(q[k], hit);
                 g.hb = (int)((x - P * (uint64_t)nhb) / (uint64_t)g.nq);
                 g.A = P * (uint64_t)nhb + (uint64_t)g.hb * (uint64_t)g.nq;
-                return g;
+                found = true;
             }
             base += total;
         }
+        if (found) return g;
     }
     return g;
 }
