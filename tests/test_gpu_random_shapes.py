@@ -65,3 +65,30 @@ def test_random_shape(i):
     out2, flags2 = dp.results()
     np.testing.assert_array_equal(out2, out)
     np.testing.assert_array_equal(flags2, flags)
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_random_shape_balanced_shares(i):
+    # the same random cases through balanced shares, where the family has
+    # them (grouped bf16 queries over a bf16 or E4M3FN cache): pieces cut at
+    # the segments' edges (chunk_size 0) and, for a chunk size on the 64-token
+    # grid, whole chunks
+    import split_kv_asynchronous_amd as fd
+    kw = draw_case(i)
+    g = kw["num_q_heads"] // kw["num_kv_heads"]
+    if g == 1 or kw["q_dtype"] != "bf16" or kw["kv_dtype"] == "f32":
+        pytest.skip("no balanced shares for this family")
+    prob = synthetic.make_problem(**kw)
+    ref_out, ref_flags, margin = oracle.decode_exact(**prob.args())
+    sure = margin >= 1e-3
+    chunk = prob.chunk_size
+    for c in (0, chunk) if chunk % 64 == 0 else (0,):
+        prob.chunk_size = c
+        print("case %d shares chunk %d" % (i, c), flush=True)
+        dp = DeviceProblem(prob, plan=fd.FD_PLAN_SHARES)
+        assert fd.fd_attn_plan(dp.desc())["shares"] > 0
+        dp.run()
+        out, flags = dp.results()
+        np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+        compare(prob, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
+    prob.chunk_size = chunk
