@@ -55,6 +55,7 @@ struct Shape {
     static_assert(NST * dma_per_block < 64, "vmcnt cannot count that deep");
     static_assert(NW * kRedStride * 4 <= lds, "epilogue reduction must fit in the ring");
     static_assert(lds <= 160 * 1024, "LDS per workgroup");
+    static constexpr int per_cu = lds > 80 * 1024 ? 1 : 2;      // workgroups the LDS lets share a compute unit
 };
 
 // One unit of work: tokens [t_begin, t_end) of the row group (sequence b,
@@ -555,7 +556,7 @@ FD_DEV void run_unit(const Params &p, const Seg &sg, uint8_t *lds, int &flagged_
 }
 
 template <int KV, bool PAGED, typename S>
-__global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
+__global__ __launch_bounds__(S::waves * 64, S::per_cu) void chunk_kernel(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
     __shared__ int flagged_heads, last_flag, merged;
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(S::waves * 64, 2) void chunk_kernel(Params p)
 //    of kQuantum): chunk c of a row group belongs to the segment holding its
 //    first quantum; partials, merge and one-chunk rows as in chunk_kernel.
 template <int KV, bool PAGED, typename S>
-__global__ __launch_bounds__(S::waves * 64, 2) void share_kernel(Params p)
+__global__ __launch_bounds__(S::waves * 64, S::per_cu) void share_kernel(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S::lds];
     __shared__ int flagged_heads, last_flag, merged;
