@@ -75,6 +75,15 @@ __global__ __launch_bounds__(256) void stats_init_kernel(StatsParams p)
         for (int i = blockIdx.x * 256 + threadIdx.x; i < p.nbins + 2; i += gridDim.x * 256) p.hist[i] = 0u;
 }
 
+// One count into an LDS histogram bin, written out: the compiler cannot tell
+// the bin from the ring slots the DMA is still filling and would wait for
+// every DMA in flight before an atomic of its own (one drain per score).  The
+// bins and the ring are disjoint; the add returns nothing, so nothing waits.
+FD_DEV void lds_count(uint32_t *bin)
+{
+    asm volatile("ds_add_u32 %0, %1" : : "v"((uint32_t)(uintptr_t)bin), "v"(1u) : "memory");
+}
+
 // Histogram slot of a score: 0 below hist_lo (and NaN), 1 + i for bin i,
 // nbins + 1 at or above hist_hi.
 FD_DEV int hist_slot(const StatsParams &p, float s)
@@ -375,7 +384,7 @@ __global__ __launch_bounds__(kStatsWaves * 64, 2) void score_stats_dma_kernel(St
                 if (head_ok && t0 + r < t_end) {
                     mx = fmaxf(mx, x);
                     mn = fminf(mn, x);
-                    if (sp.hist) atomicAdd(&lhist[hist_slot(sp, x)], 1u);
+                    if (sp.hist) lds_count(&lhist[hist_slot(sp, x)]);
                 }
             }
         }
