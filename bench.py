@@ -8,8 +8,10 @@ lengths U{1024..32768}, bf16 cache, chunk 1024), inputs resident in HBM.
 Prints one JSON line: KV GB/s (valid K and V bytes / time per call over K
 uninstrumented calls), calls/s, the chunk kernel's roofline (algorithmic
 bytes / its average duration in a second pass of K calls, from start/stop
-events stamped by its own dispatch on its stream), and the float64 CPU
-oracle timed on a bounded sample as a reported baseline.
+events stamped by its own dispatch on its stream), the read ceiling of the
+same call's loads (its units streamed through the kernel's DMA ring with
+nothing computed, include/fd_probe.h) beside it, and the float64 CPU oracle
+timed on a bounded sample as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--config N]
 
@@ -539,6 +541,68 @@ def library_plan_line(fd, dp, prob, K, torch):
     return out
 
 
+def heads_per_block(g: int) -> int:
+    """Query heads per head block of the grouped-query kernels: the largest
+    divisor of the group size up to 16."""
+    return next((k for k in range(min(g, 16), 1, -1) if g % k == 0), 1)
+
+
+def probe_units(prob, chunk: int) -> np.ndarray:
+    """The chunk kernel's units of a contiguous grouped-query call as byte
+    ranges of the cache, in the kernel's order: every sequence's full chunks
+    (sequence-major, chunks outer, head blocks inner), then the partial last
+    chunks.  A unit of head block hb reads its KV head's slice."""
+    import split_kv_asynchronous_amd as fd
+    row = prob.head_dim * {"bf16": 2, "e4m3fn": 1, "f32": 4}[prob.kv_dtype]
+    G = prob.num_q_heads // prob.num_kv_heads
+    GB = heads_per_block(G)
+    nhb = prob.num_q_heads // GB
+    kvh = np.arange(nhb) * GB // G
+    S = prob.max_seq_len
+    recs = []
+    for b, L in enumerate(prob.seq_lens.tolist()):
+        base = (b * prob.num_kv_heads + kvh) * S
+        for c in range(L // chunk):
+            recs.append(np.stack([(base + c * chunk) * row, np.full(nhb, chunk * row)], 1))
+    for b, L in enumerate(prob.seq_lens.tolist()):
+        if L % chunk or L == 0:
+            c = L // chunk
+            base = (b * prob.num_kv_heads + kvh) * S
+            recs.append(np.stack([(base + c * chunk) * row, np.full(nhb, (L - c * chunk) * row)], 1))
+    r = np.concatenate(recs)
+    out = np.zeros(len(r), dtype=fd.PROBE_UNIT)
+    out["offset"], out["bytes"] = r[:, 0], r[:, 1]
+    return out
+
+
+def read_ceiling(fd, dp, prob, plan, K, torch):
+    """The decode call's loads alone (include/fd_probe.h): the chunk kernel's
+    units, in its order, streamed through its DMA ring shape with nothing
+    computed, K back-to-back launches timed by events.  For grouped bf16
+    queries over a contiguous cache in the 4-wavefront shapes (the headline
+    kernel); None otherwise."""
+    if plan["family"] != 0 or plan["shape"] not in (0, 1) or plan["shares"] or prob.page_size:
+        return None
+    units = probe_units(prob, plan["chunk_size"])
+    nbytes = 2 * int(units["bytes"].sum())
+    dev = torch.from_numpy(units.view(np.uint8).copy()).cuda()
+    stages = 2 if plan["shape"] == 0 else 3
+    sink = torch.empty(1, dtype=torch.int32, device="cuda")
+    for _ in range(5):
+        fd.fd_probe_read(dp.k, dp.v, dev, stages, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        fd.fd_probe_read(dp.k, dp.v, dev, stages, sink)
+    e1.record()
+    e1.synchronize()
+    per = e0.elapsed_time(e1) / K / 1e3
+    return {"value": round(nbytes / per / 1e9, 2), "unit": "GB/s", "ms_per_launch": round(per * 1e3, 5),
+            "bytes_per_launch": nbytes, "units": len(units),
+            "ring": "4 wavefronts x %d stages of 8 KiB, non-temporal 1 KiB DMA" % stages}
+
+
 def main_serving(args):
     """One JSON line per serving-batch case: whole-call and chunk-kernel TB/s
     of K/V over K back-to-back calls (a side measurement, not the bench line)."""
@@ -687,6 +751,9 @@ def main():
     # (chunk_size 0), K calls on the same inputs: reported beside the value,
     # which keeps the workload's stated chunk size
     lib = library_plan_line(fd, dp, prob, K, torch)
+    # the same call's loads with nothing computed: what its load pattern can
+    # reach on this device, beside the roofline's published peak
+    ceil = read_ceiling(fd, dp, prob, plan, K, torch)
 
     if args.copy_calibration:
         copy_calibration()
@@ -726,6 +793,7 @@ def main():
                      "traffic": load_traffic(prob.workload),
                      "kernel": "chunk kernel" + (" (with the merge)" if fused else ""),
                      "bytes_per_launch": nbytes},
+        "read_ceiling": None if ceil is None else dict(ceil, kernel_frac=round(achieved / ceil["value"], 4)),
         "source_hash": source_hash(),
         "library_plan": lib,
     }

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import numpy as np
 from typing import Optional, Sequence
 
 __all__ = ["fd_attn_decode", "fd_attn_decode_static", "fd_attn_plan", "FD_PLAN_SHAPE",
@@ -135,6 +136,9 @@ def _load():
         lib.fd_flat_gemm_pack_weights.restype = ctypes.c_int
         lib.fd_attn_plan.argtypes = [D, i32p, i32p, i32p, i32p, i32p]
         lib.fd_attn_plan.restype = ctypes.c_int
+        lib.fd_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        lib.fd_probe_read.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -614,6 +618,27 @@ def fd_flat_gemm(a, w, out=None, *, out_dtype: str = "f32", variant: int = 0, ks
     if rc != 0:
         raise FdAttnError(rc, fd_attn_status_string(rc))
     return out
+
+
+# numpy layout of fd_probe_unit_t (include/fd_probe.h)
+PROBE_UNIT = np.dtype([("offset", "<u8"), ("bytes", "<u4"), ("reserved", "<u4")])
+
+
+def fd_probe_read(k, v, units, stages: int = 2, sink=None, stream=None):
+    """Streams the byte ranges `units` (a device uint8 tensor holding
+    PROBE_UNIT records) of k and v through the decode kernels' DMA ring and
+    computes nothing (include/fd_probe.h): a read-bandwidth measurement."""
+    import torch
+    if units.dtype != torch.uint8 or units.numel() % PROBE_UNIT.itemsize or not units.is_contiguous():
+        raise ValueError("units must be a contiguous uint8 tensor of PROBE_UNIT records")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=k.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device).cuda_stream
+    rc = _load().fd_probe_read(k.data_ptr(), v.data_ptr(), units.data_ptr(),
+                               units.numel() // PROBE_UNIT.itemsize, stages, sink.data_ptr(), stream)
+    if rc != 0:
+        raise FdAttnError(rc, fd_attn_status_string(rc))
 
 
 def default_scale(head_dim: int = 128) -> float:

@@ -1,4 +1,4 @@
-"""Compiles the HIP sources under csrc/ (decode, prefill, calibration, flat GEMM) into libfd_attn.so (gfx950 only).
+"""Compiles the HIP sources under csrc/ (decode, prefill, calibration, flat GEMM, read probe) into libfd_attn.so (gfx950 only).
 
 Each source is compiled to an object file in its own hipcc process (in
 parallel), then the objects are linked into the shared library."""
@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", f)
-        for f in ("fd_attn.hip", "fd_prefill.hip", "fd_calib.hip", "fd_gemm.hip")]
+        for f in ("fd_attn.hip", "fd_prefill.hip", "fd_calib.hip", "fd_gemm.hip", "fd_probe.hip")]
 LIB = os.path.join(HERE, "libfd_attn.so")
 OBJDIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -18,7 +18,7 @@ def _declared_functions():
         if h.endswith(".h"):
             src = open(os.path.join(ROOT, "include", h)).read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names |= set(re.findall(r"\b(fd_(?:attn|flat_gemm)\w*)\s*\(", src))
+            names |= set(re.findall(r"\b(fd_(?:attn|flat_gemm|probe)\w*)\s*\(", src))
     return sorted(names)
 
 
@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
                      "fd_attn_prefill",
                      "fd_attn_score_stats", "fd_attn_status_string", "fd_attn_workspace_size",
                      "fd_flat_gemm", "fd_flat_gemm_pack_weights", "fd_flat_gemm_packed_bytes",
-                     "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size"]
+                     "fd_flat_gemm_plan", "fd_flat_gemm_workspace_size", "fd_probe_read"]
     lib = ctypes.CDLL(fd.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -441,3 +441,25 @@ def test_static_workspace_variant_checks_before_the_gpu():
     big = _valid_desc(batch=64, num_q_heads=64, num_kv_heads=8, max_seq_len=1 << 20, chunk_size=1024)
     assert fd.fd_attn_workspace_size(big) > (64 << 20)
     assert scall(big) == -6
+
+
+def test_read_probe_host_checks():
+    # the read probe (include/fd_probe.h) rejects its arguments before any
+    # launch: NULL buffers or sink, units NULL with units to read, a negative
+    # count, a ring depth other than 2 or 3, unaligned buffers; no units: OK,
+    # nothing enqueued
+    lib = ctypes.CDLL(fd.library_path())
+    lib.fd_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    k, v, u, sink = 0x10000, 0x20000, 0x30000, 0x40000
+    assert lib.fd_probe_read(None, v, u, 1, 2, sink, None) == -1
+    assert lib.fd_probe_read(k, None, u, 1, 2, sink, None) == -1
+    assert lib.fd_probe_read(k, v, u, 1, 2, None, None) == -1
+    assert lib.fd_probe_read(k, v, None, 1, 2, sink, None) == -1
+    assert lib.fd_probe_read(k, v, None, 0, 2, sink, None) == 0
+    assert lib.fd_probe_read(k, v, u, -1, 2, sink, None) == -2
+    for bad in (0, 1, 4):
+        assert lib.fd_probe_read(k, v, u, 1, bad, sink, None) == -2
+    assert lib.fd_probe_read(k + 8, v, u, 1, 2, sink, None) == -4
+    assert lib.fd_probe_read(k, v + 4, u, 1, 3, sink, None) == -4
+    assert fd.PROBE_UNIT.itemsize == 16
