@@ -547,60 +547,83 @@ def heads_per_block(g: int) -> int:
     return next((k for k in range(min(g, 16), 1, -1) if g % k == 0), 1)
 
 
-def probe_units(prob, chunk: int) -> np.ndarray:
-    """The chunk kernel's units of a contiguous grouped-query call as byte
-    ranges of the cache, in the kernel's order: every sequence's full chunks
-    (sequence-major, chunks outer, head blocks inner), then the partial last
-    chunks.  A unit of head block hb reads its KV head's slice."""
+def probe_units(prob, chunk: int):
+    """The chunk kernel's units of a grouped-query call, in the kernel's
+    order: every sequence's full chunks (sequence-major, chunks outer, head
+    blocks inner), then the partial last chunks.  A unit of head block hb
+    reads its KV head's tokens of the chunk.  Contiguous cache: (units as
+    byte ranges, None, 0).  Paged: (units indexing a page list, the page list
+    -- byte offsets of (page, KV head) pieces, as the block table gives them
+    --, page bytes)."""
     import split_kv_asynchronous_amd as fd
     row = prob.head_dim * {"bf16": 2, "e4m3fn": 1, "f32": 4}[prob.kv_dtype]
     G = prob.num_q_heads // prob.num_kv_heads
     GB = heads_per_block(G)
     nhb = prob.num_q_heads // GB
     kvh = np.arange(nhb) * GB // G
-    S = prob.max_seq_len
-    recs = []
+    P = prob.page_size
+    order = []   # (b, chunk, tokens)
     for b, L in enumerate(prob.seq_lens.tolist()):
-        base = (b * prob.num_kv_heads + kvh) * S
-        for c in range(L // chunk):
-            recs.append(np.stack([(base + c * chunk) * row, np.full(nhb, chunk * row)], 1))
+        order += [(b, c, chunk) for c in range(L // chunk)]
     for b, L in enumerate(prob.seq_lens.tolist()):
         if L % chunk or L == 0:
-            c = L // chunk
-            base = (b * prob.num_kv_heads + kvh) * S
-            recs.append(np.stack([(base + c * chunk) * row, np.full(nhb, (L - c * chunk) * row)], 1))
-    r = np.concatenate(recs)
-    out = np.zeros(len(r), dtype=fd.PROBE_UNIT)
-    out["offset"], out["bytes"] = r[:, 0], r[:, 1]
-    return out
+            order.append((b, L // chunk, L - L // chunk * chunk))
+    units = np.zeros(len(order) * nhb, dtype=fd.PROBE_UNIT)
+    if not P:
+        S = prob.max_seq_len
+        for n, (b, c, t) in enumerate(order):
+            units["offset"][n * nhb:(n + 1) * nhb] = ((b * prob.num_kv_heads + kvh) * S + c * chunk) * row
+            units["bytes"][n * nhb:(n + 1) * nhb] = t * row
+        return units, None, 0
+    assert chunk % P == 0
+    pages = []
+    for n, (b, c, t) in enumerate(order):
+        blocks = prob.block_table[b, c * chunk // P:c * chunk // P + -(-t // P)].astype(np.int64)
+        for i, h in enumerate(kvh.tolist()):
+            units["offset"][n * nhb + i] = len(pages)
+            units["bytes"][n * nhb + i] = t * row
+            pages += ((blocks * prob.num_kv_heads + h) * P * row).tolist()
+    return units, np.array(pages, dtype=np.int64), P * row
+
+
+# probe ring shape per (kernel family, kernel shape) of the plan: the grouped
+# bf16 kernel's 4 x 2 and 4 x 3 rings, the cooperative E4M3FN kernel's 2 x 3
+PROBE_SHAPES = {(0, 0): 0, (0, 1): 1, (1, 0): 2}
 
 
 def read_ceiling(fd, dp, prob, plan, K, torch):
     """The decode call's loads alone (include/fd_probe.h): the chunk kernel's
     units, in its order, streamed through its DMA ring shape with nothing
-    computed, K back-to-back launches timed by events.  For grouped bf16
-    queries over a contiguous cache in the 4-wavefront shapes (the headline
-    kernel); None otherwise."""
-    if plan["family"] != 0 or plan["shape"] not in (0, 1) or plan["shares"] or prob.page_size:
+    computed, K back-to-back launches timed by events.  For the grouped
+    kernels' fixed-chunk plans whose ring the probe has; None otherwise."""
+    shape = PROBE_SHAPES.get((plan["family"], plan["shape"]))
+    if shape is None or plan["shares"] or plan["chunk_size"] % max(prob.page_size, 1):
         return None
-    units = probe_units(prob, plan["chunk_size"])
+    units, pages, page_bytes = probe_units(prob, plan["chunk_size"])
+    if pages is not None and int(units["bytes"].max()) > 64 * page_bytes:
+        return None
     nbytes = 2 * int(units["bytes"].sum())
     dev = torch.from_numpy(units.view(np.uint8).copy()).cuda()
-    stages = 2 if plan["shape"] == 0 else 3
+    pg = None if pages is None else torch.from_numpy(pages).cuda()
     sink = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def run():
+        fd.fd_probe_read(dp.k, dp.v, dev, shape, pg, page_bytes, sink)
     for _ in range(5):
-        fd.fd_probe_read(dp.k, dp.v, dev, stages, sink)
+        run()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(K):
-        fd.fd_probe_read(dp.k, dp.v, dev, stages, sink)
+        run()
     e1.record()
     e1.synchronize()
     per = e0.elapsed_time(e1) / K / 1e3
+    ring = {0: "4 wavefronts x 2 stages of 8 KiB", 1: "4 wavefronts x 3 stages of 8 KiB",
+            2: "2 wavefronts x 3 stages of 4 KiB"}[shape]
     return {"value": round(nbytes / per / 1e9, 2), "unit": "GB/s", "ms_per_launch": round(per * 1e3, 5),
             "bytes_per_launch": nbytes, "units": len(units),
-            "ring": "4 wavefronts x %d stages of 8 KiB, non-temporal 1 KiB DMA" % stages}
+            "ring": ring + ", non-temporal 1 KiB DMA" + (", whole pages" if pages is not None else "")}
 
 
 def main_serving(args):

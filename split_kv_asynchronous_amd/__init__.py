@@ -137,7 +137,8 @@ def _load():
         lib.fd_attn_plan.argtypes = [D, i32p, i32p, i32p, i32p, i32p]
         lib.fd_attn_plan.restype = ctypes.c_int
         lib.fd_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
-                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
         lib.fd_probe_read.restype = ctypes.c_int
         lib.fd_attn_status_string.argtypes = [ctypes.c_int]
         lib.fd_attn_status_string.restype = ctypes.c_char_p
@@ -624,19 +625,24 @@ def fd_flat_gemm(a, w, out=None, *, out_dtype: str = "f32", variant: int = 0, ks
 PROBE_UNIT = np.dtype([("offset", "<u8"), ("bytes", "<u4"), ("reserved", "<u4")])
 
 
-def fd_probe_read(k, v, units, stages: int = 2, sink=None, stream=None):
-    """Streams the byte ranges `units` (a device uint8 tensor holding
-    PROBE_UNIT records) of k and v through the decode kernels' DMA ring and
+def fd_probe_read(k, v, units, shape: int = 0, pages=None, page_bytes: int = 0, sink=None, stream=None):
+    """Streams the units (a device uint8 tensor of PROBE_UNIT records) of k
+    and v -- byte ranges, or with `pages` (a device int64 tensor of page byte
+    offsets) whole pages -- through a decode kernel's DMA ring shape and
     computes nothing (include/fd_probe.h): a read-bandwidth measurement."""
     import torch
     if units.dtype != torch.uint8 or units.numel() % PROBE_UNIT.itemsize or not units.is_contiguous():
         raise ValueError("units must be a contiguous uint8 tensor of PROBE_UNIT records")
+    if pages is not None and (pages.dtype != torch.int64 or not pages.is_contiguous()):
+        raise ValueError("pages must be a contiguous int64 tensor of byte offsets")
     if sink is None:
         sink = torch.empty(1, dtype=torch.int32, device=k.device)
     if stream is None:
         stream = torch.cuda.current_stream(k.device).cuda_stream
     rc = _load().fd_probe_read(k.data_ptr(), v.data_ptr(), units.data_ptr(),
-                               units.numel() // PROBE_UNIT.itemsize, stages, sink.data_ptr(), stream)
+                               units.numel() // PROBE_UNIT.itemsize,
+                               None if pages is None else pages.data_ptr(), page_bytes, shape,
+                               sink.data_ptr(), stream)
     if rc != 0:
         raise FdAttnError(rc, fd_attn_status_string(rc))
 

@@ -446,20 +446,24 @@ def test_static_workspace_variant_checks_before_the_gpu():
 def test_read_probe_host_checks():
     # the read probe (include/fd_probe.h) rejects its arguments before any
     # launch: NULL buffers or sink, units NULL with units to read, a negative
-    # count, a ring depth other than 2 or 3, unaligned buffers; no units: OK,
-    # nothing enqueued
+    # count, a ring shape other than 0..2, with a page list a page size that
+    # is not a multiple of 1 KiB in [1 KiB, 1 MiB], unaligned buffers; no
+    # units: OK, nothing enqueued
     lib = ctypes.CDLL(fd.library_path())
     lib.fd_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
-                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    k, v, u, sink = 0x10000, 0x20000, 0x30000, 0x40000
-    assert lib.fd_probe_read(None, v, u, 1, 2, sink, None) == -1
-    assert lib.fd_probe_read(k, None, u, 1, 2, sink, None) == -1
-    assert lib.fd_probe_read(k, v, u, 1, 2, None, None) == -1
-    assert lib.fd_probe_read(k, v, None, 1, 2, sink, None) == -1
-    assert lib.fd_probe_read(k, v, None, 0, 2, sink, None) == 0
-    assert lib.fd_probe_read(k, v, u, -1, 2, sink, None) == -2
-    for bad in (0, 1, 4):
-        assert lib.fd_probe_read(k, v, u, 1, bad, sink, None) == -2
-    assert lib.fd_probe_read(k + 8, v, u, 1, 2, sink, None) == -4
-    assert lib.fd_probe_read(k, v + 4, u, 1, 3, sink, None) == -4
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    k, v, u, pg, sink = 0x10000, 0x20000, 0x30000, 0x50000, 0x40000
+
+    def call(k=k, v=v, u=u, n=1, pages=None, page_bytes=0, shape=0, sink=sink):
+        return lib.fd_probe_read(k, v, u, n, pages, page_bytes, shape, sink, None)
+    assert call(k=None) == -1 and call(v=None) == -1 and call(sink=None) == -1 and call(u=None) == -1
+    assert call(u=None, n=0) == 0
+    assert call(n=-1) == -2
+    for bad in (-1, 3, 4):
+        assert call(shape=bad) == -2
+    for bad in (0, 512, 1536, 2 << 20):
+        assert call(pages=pg, page_bytes=bad) == -2
+    assert call(pages=pg, page_bytes=2048, n=0) == 0
+    assert call(k=k + 8) == -4 and call(v=v + 4, shape=2) == -4
     assert fd.PROBE_UNIT.itemsize == 16
