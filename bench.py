@@ -455,6 +455,39 @@ def main_gemm(args):
         layers[name] = {"n": n, "k": k, "kernel_ms": round(ms, 5),
                         "kernel_GBps": round(algo / (ms / 1e3) / 1e9, 2), "plan": plans[li],
                         "bytes_per_launch": algo}
+    # each layer's weights read alone (include/fd_probe.h): one unit per
+    # 16-row block of the packed weights, its halves from the two halves of
+    # the buffer, through the 4 x 2 DMA ring with nothing computed, the
+    # copies rotated as in the step: what one launch reading that many bytes
+    # reaches on this device
+    sink = torch.empty(1, dtype=torch.int32, device="cuda")
+    for li, (name, n, k) in enumerate(cfg["layers"]):
+        nblk = -(-n // 16)
+        if nblk % 2:
+            layers[name]["read_ceiling_GBps"] = None
+            continue
+        ub = nblk // 2 * 32 * k // nblk          # bytes of a block in each half
+        units = np.zeros(nblk, dtype=fd.PROBE_UNIT)
+        units["offset"] = np.arange(nblk, dtype=np.uint64) * ub
+        units["bytes"] = ub
+        ud = torch.from_numpy(units.view(np.uint8).copy()).cuda()
+        half = nblk * ub
+
+        def probe(j):
+            raw = dev[j % copies][li][1].view(torch.uint8)
+            fd.fd_probe_read(raw[:half], raw[half:2 * half], ud, 0, None, 0, sink)
+        for j in range(copies):
+            probe(j)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            probe(W + i)
+        e1.record()
+        e1.synchronize()
+        ceil = 2 * half / (e0.elapsed_time(e1) / K / 1e3) / 1e9
+        layers[name]["read_ceiling_GBps"] = round(ceil, 2)
+        layers[name]["kernel_frac_of_ceiling"] = round(layers[name]["kernel_GBps"] / ceil, 4)
     # the dominant kernel: the partial-sum kernel of the largest layer
     big = max(layers, key=lambda x: layers[x]["n"] * layers[x]["k"])
     achieved = layers[big]["kernel_GBps"]
