@@ -150,7 +150,10 @@ extern "C" int fd_attn_score_stats(const fd_attn_desc_t *d, const void *q, const
     // grouped bf16 queries over a bf16 or E4M3FN cache: matrix-core kernel
     const bool use_mfma = p.group > 1 && qt == FD_BF16 && kv != FD_F32;
     const int heads = use_mfma ? fd::stats::kStatsMfmaHeads : fd::stats::kStatsHeads;
-    sp.nchunk = (d->max_seq_len + fd::stats::kStatsChunk - 1) / fd::stats::kStatsChunk;
+    sp.chunk = !use_mfma ? fd::stats::kStatsChunk
+               : kv == FD_FP8_E4M3FN ? fd::stats::stats_dma_chunk<FD_FP8_E4M3FN>()
+                                     : fd::stats::stats_dma_chunk<FD_BF16>();
+    sp.nchunk = (d->max_seq_len + sp.chunk - 1) / sp.chunk;
     sp.nhb = (p.group + heads - 1) / heads;
     const int64_t units = (int64_t)d->batch * d->num_kv_heads * sp.nhb * sp.nchunk;
     if (units >= ((int64_t)1 << 31)) return FD_ERR_SHAPE;
