@@ -97,7 +97,8 @@ typedef struct {
     int32_t head_dim;           /* must be 128 */
     int32_t max_seq_len;        /* 1 .. 2^23: contiguous capacity; seq_lens are clamped to it */
     int32_t chunk_size;         /* split size: a multiple of 32 (and of page_size), >= 32;
-                                   0 = the library's pick from its table (fd_attn_plan) */
+                                   0 = the library's pick from its table (fd_attn_plan),
+                                   halved for calls with few rows (see fd_attn_plan) */
     int32_t page_size;          /* 0 = contiguous; else a power of two in [16, 256] */
     int32_t max_blocks_per_seq; /* paged: >= ceil(max_seq_len / page_size) */
     int32_t num_pages;          /* paged: number of pages in the K/V pool (>= 1) */
@@ -189,7 +190,11 @@ int fd_attn_decode_static(const fd_attn_desc_t *desc, const void *q, const void 
 
 /* The plan a call with this descriptor would run, from the library's table
  * of measured plans (or desc->plan where it forces one; with chunk_size 0,
- * the table may pick balanced shares, and does for calls of many row groups):
+ * the table may pick balanced shares, and does for calls of many row groups,
+ * but only when each share gets at least 1024 tokens of work counted at
+ * max_seq_len; and a call with few rows gets the table's chunk size halved,
+ * down to 256 tokens, until it has 256 units -- the table was measured on
+ * full batches, where a small call would leave most of the chip idle):
  * the chunk size, the
  * kernel family (0: grouped bf16 queries over a bf16 cache; 1: grouped bf16
  * queries over an E4M3FN cache; 2: one query per KV head, or fp32 operands),

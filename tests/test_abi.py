@@ -467,3 +467,44 @@ def test_read_probe_host_checks():
     assert call(pages=pg, page_bytes=2048, n=0) == 0
     assert call(k=k + 8) == -4 and call(v=v + 4, shape=2) == -4
     assert fd.PROBE_UNIT.itemsize == 16
+
+
+def test_small_calls_plan_smaller_chunks_and_no_shares():
+    # chunk_size 0 on a call with few rows: the table's chunk (measured on
+    # full batches) is halved, down to 256 tokens, until the call has 256
+    # units (counted at max_seq_len); balanced shares need 16 quanta of 64
+    # tokens per share.  Full batches keep the table's pick.
+    def plan(**kw):
+        return fd.fd_attn_plan(_desc(**dict(kw, chunk_size=0)))
+
+    def units(p, kw):
+        g = kw["num_q_heads"] // kw["num_kv_heads"]
+        gb = kw["num_q_heads"] if p["family"] == 2 else kw["num_q_heads"] // max(
+            k for k in range(1, min(g, 16) + 1) if g % k == 0)
+        return -(-kw["max_seq_len"] // p["chunk_size"]) * gb * kw["batch"]
+
+    small = [dict(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=4096, q_dtype="f32", kv_dtype="f32"),
+             dict(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=131072),
+             dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=8192),
+             dict(batch=1, num_q_heads=64, num_kv_heads=8, max_seq_len=32768),
+             dict(batch=2, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn"),
+             dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn", page_size=16,
+                  max_blocks_per_seq=1024, num_pages=1024)]
+    want = [256, 512, 256, 1024, 1024, 512]
+    for kw, c in zip(small, want):
+        p = plan(**kw)
+        assert p["shares"] == 0 and p["chunk_size"] == c, (kw, p)
+        # the largest chunk (at least 256) that gives 256 units
+        assert c == 256 or units(p, kw) >= 256 > units(dict(p, chunk_size=2 * c), kw), (kw, p)
+        assert p["fused"] == 1       # a grid of at most 512 units merges in the launch
+        assert fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=0))) == \
+            fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=c)))
+    # full batches: the table's pick, balanced shares where the table takes them
+    assert plan(batch=32, num_q_heads=64, num_kv_heads=8, max_seq_len=32768)["shares"] == 512
+    assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn", page_size=16,
+                max_blocks_per_seq=1024, num_pages=40000)["shares"] == 512
+    assert plan(batch=8, num_q_heads=32, num_kv_heads=32, max_seq_len=8192)["chunk_size"] == 2048
+    assert plan(batch=1, num_q_heads=32, num_kv_heads=32, max_seq_len=131072)["chunk_size"] == 4096
+    # an explicit chunk size is kept as given
+    assert fd.fd_attn_plan(_desc(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=4096,
+                                 chunk_size=2048))["chunk_size"] == 2048
