@@ -98,6 +98,11 @@ constexpr int64_t kSmallGrid = 512;
 // 0.90 / 0.64; grouped E4M3FN, 32/8 heads, chunk_size 0: 1.03 / 1.01 / 0.94
 // / 0.84, chunk 512 at batch 1024 / 4096: 0.97 / 0.67.
 constexpr int64_t kServeGroups[2] = {8192, 16384};
+// The same threshold for pieces under chunk_size 0.  For bf16 it is higher:
+// against the best fixed plan (shape 0, below) rather than the table's first
+// one, pieces at 1024 sequences of up to 1K / 2K tokens lost 9% / 5% (465.6
+// against 424.2 µs, 845.9 against 804.7).
+constexpr int64_t kServeGroupsAuto[2] = {16384, 16384};
 
 // Measured on MI355X: calls replayed back to back (best of 3 x 10), every
 // chunk size 256 .. 4096 x every shape x both merge placements, on ragged
@@ -125,12 +130,16 @@ constexpr int64_t kServeGroups[2] = {8192, 16384};
 // best of 3 x 10): grouped E4M3FN 64 x U[512,16K] 0.96 (paged 0.96), 16 x
 // U[16K,64K] 0.98 (0.97); grouped bf16 32 x U[1K,32K] 0.98-0.99 (paged
 // 1.00); shorter and longer bf16 rows and 2K E4M3FN rows 1.04-1.10.
+// Rows of grouped bf16 up to 2K tokens run shape 0 (4 waves x 2 stages):
+// measured later over batch sizes, 64 / 256 / 1024 sequences of up to 1K
+// tokens 32.1 / 107.8 / 424.2 µs against 35.2 / 132.0 / 576.1 with 4 x 3,
+// and of 256-2K tokens 57.6 / 225.2 / 804.7 against 57.9 / 219.2 / 887.0.
 inline constexpr TableRow kTable[] = {
-    {kFamGroupedBf16, 0, 2048, 2048, 1, 0, 0},
+    {kFamGroupedBf16, 0, 2048, 2048, 0, 0, 0},
     {kFamGroupedBf16, 0, 8192, 4096, 1, 512, 0},
     {kFamGroupedBf16, 0, 32768, 2048, 0, 1024, 1},
     {kFamGroupedBf16, 0, 1 << 23, 1024, 0, 0, 0},
-    {kFamGroupedBf16, 1, 2048, 2048, 1, 0, 0},
+    {kFamGroupedBf16, 1, 2048, 2048, 0, 0, 0},
     {kFamGroupedBf16, 1, 8192, 4096, 1, 1024, 0},
     {kFamGroupedBf16, 1, 32768, 2048, 0, 2048, 0},
     {kFamGroupedBf16, 1, 1 << 23, 2048, 0, 0, 0},
@@ -173,18 +182,23 @@ inline int64_t units_at(const fd_attn_desc_t *d, int c)
 
 // The table's chunk sizes were measured on full batches.  A call with few
 // rows gets the table's chunk halved, down to kMinAutoChunk tokens, until it
-// has kMinAutoUnits units, so that it still spreads over the chip.  Measured
-// on MI355X, µs per call, table's chunk -> halved: 1 row x 4K fp32 20.9 ->
-// 8.4 (chunk 256); 1 row x 128K bf16 137 -> 44 (512); 1 x 32/8 heads x 8K
-// bf16 41.8 -> 14.6 (256); 8 rows x 4K bf16 26.9 -> 11.0 (256).
-constexpr int kMinAutoUnits = 256;
+// has kMinAutoUnits units of its family, so that it still spreads over the
+// chip: 256 for the one-wavefront-ring bf16 and the one-query-per-KV-head
+// kernels, 2048 for the E4M3FN kernel (six workgroups per compute unit).
+// Measured on MI355X, µs per call, table's chunk -> halved: 1 row x 4K fp32
+// 20.9 -> 8.4 (chunk 256); 1 row x 128K bf16 137 -> 44 (512); 1 x 32/8
+// heads x 8K bf16 41.8 -> 14.6 (256); 8 rows x 4K bf16 26.9 -> 11.0 (256);
+// E4M3FN 32/8 heads, 16 / 64 sequences of 256-2K tokens 32.0 / 44.1 -> 19.2
+// / 37.9 (256 / 512), 64 of 128-1K 36.6 -> 24.7 (256), 2 x 16K 31.8 -> 28.8
+// (256).
+constexpr int kMinAutoUnits[3] = {256, 2048, 256};
 constexpr int kMinAutoChunk = 256;
 
 inline int chunk_of(const fd_attn_desc_t *d)
 {
     if (d->chunk_size != 0) return d->chunk_size;
     int c = table_row(d).chunk;
-    while (c > kMinAutoChunk && units_at(d, c) < kMinAutoUnits) c /= 2;
+    while (c > kMinAutoChunk && units_at(d, c) < kMinAutoUnits[family_of(d)]) c /= 2;
     return d->page_size > c ? d->page_size : c;
 }
 
@@ -250,7 +264,7 @@ inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
         const bool serve = groups >= kServeGroups[pl->family];
         const int auto_shape = r.shares ? r.shares - 1 : 2;
         const int64_t quanta = groups * (((int64_t)d->max_seq_len + kQuantaTokens - 1) / kQuantaTokens);
-        if (d->chunk_size == 0 && (r.shares || serve) &&
+        if (d->chunk_size == 0 && (r.shares || groups >= kServeGroupsAuto[pl->family]) &&
             quanta >= (int64_t)kMinShareQuanta * kCUs * kSharesPerCU[auto_shape]) {
             pl->shape = auto_shape;
             pl->shares = kCUs * kSharesPerCU[pl->shape];
@@ -258,7 +272,7 @@ inline int plan_of(const fd_attn_desc_t *d, Plan *pl)
             pl->fused = 1;
             return FD_OK;
         }
-        if (d->chunk_size % 64 == 0 && serve) {
+        if (d->chunk_size != 0 && d->chunk_size % 64 == 0 && serve) {
             pl->shape = 2;
             pl->shares = kCUs * kSharesPerCU[2];
             pl->share_chunks = 1;

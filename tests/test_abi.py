@@ -292,9 +292,9 @@ FAMILY_KW = {0: dict(), 1: dict(kv_dtype="e4m3fn"), 2: dict(num_kv_heads=64)}
 PLAN_ROWS = [
     # family, paged, max_seq_len probes, chunk, shape, largest chunk merged in
     # the launch, balanced shares for chunk_size 0 (shape + 1; 0: fixed chunks)
-    (0, 0, (1, 2048), 2048, 1, 0, 0), (0, 0, (2049, 8192), 4096, 1, 512, 0),
+    (0, 0, (1, 2048), 2048, 0, 0, 0), (0, 0, (2049, 8192), 4096, 1, 512, 0),
     (0, 0, (8193, 32768), 2048, 0, 1024, 1), (0, 0, (32769, 1 << 20), 1024, 0, 0, 0),
-    (0, 1, (16, 2048), 2048, 1, 0, 0), (0, 1, (2064, 8192), 4096, 1, 1024, 0),
+    (0, 1, (16, 2048), 2048, 0, 0, 0), (0, 1, (2064, 8192), 4096, 1, 1024, 0),
     (0, 1, (8208, 32768), 2048, 0, 2048, 0), (0, 1, (32784, 1 << 20), 2048, 0, 0, 0),
     (1, 0, (1, 2048), 1024, 0, 1024, 0), (1, 0, (2049, 16384), 1024, 0, 1024, 1),
     (1, 0, (16385, 1 << 20), 2048, 0, 0, 1),
@@ -363,24 +363,28 @@ def test_plan_small_grids_merge_in_the_launch_and_forced_plans():
 
 
 def test_serving_batches_run_balanced_shares():
-    # at least 8192 (bf16) / 16384 (E4M3FN) row groups: balanced shares in
-    # shape 2 (3 workgroups per compute unit) -- pieces for chunk_size 0,
-    # whole chunks for a chunk size that is a multiple of 64 (merged by a
-    # second launch unless a chunk covers max_seq_len); fewer row groups, a
-    # chunk size off the 64 grid or a forced plan: fixed chunks
-    for kw, groups_needed in ((dict(), 8192), (dict(kv_dtype="e4m3fn", num_q_heads=32), 16384)):
-        for batch in (groups_needed // 8 - 1, groups_needed // 8):
+    # serving batches run balanced shares in shape 2 (3 workgroups per
+    # compute unit): whole chunks, for a chunk size that is a multiple of 64
+    # (merged by a second launch unless a chunk covers max_seq_len), from
+    # 8192 (bf16) / 16384 (E4M3FN) row groups; pieces, for chunk_size 0, from
+    # 16384 row groups in both families.  Fewer row groups, a chunk size off
+    # the 64 grid or a forced plan: fixed chunks
+    for kw, whole_needed in ((dict(), 8192), (dict(kv_dtype="e4m3fn", num_q_heads=32), 16384)):
+        for batch in sorted({whole_needed // 8 - 1, whole_needed // 8, 16384 // 8 - 1, 16384 // 8}):
             base = dict(kw, batch=batch, max_seq_len=2048, chunk_size=0)
             got = fd.fd_attn_plan(_desc(**base))
             whole = fd.fd_attn_plan(_desc(**dict(base, chunk_size=512)))
             one = fd.fd_attn_plan(_desc(**dict(base, chunk_size=2048)))
-            if batch * 8 >= groups_needed:
+            if batch * 8 >= 16384:
                 assert got["shares"] == 768 and got["shape"] == 2 and got["fused"] == 1, (base, got)
                 assert got["chunk_size"] == 0
+            else:
+                assert got["shares"] == 0 and got["chunk_size"] > 0, (base, got)
+            if batch * 8 >= whole_needed:
                 assert whole == dict(chunk_size=512, family=whole["family"], shape=2, fused=0, shares=768)
                 assert one["shares"] == 768 and one["fused"] == 1
             else:
-                assert got["shares"] == 0 and whole["shares"] == 0 and one["shares"] == 0, (base, got)
+                assert whole["shares"] == 0 and one["shares"] == 0, (base, whole, one)
             assert fd.fd_attn_plan(_desc(**dict(base, chunk_size=96)))["shares"] == 0
             assert fd.fd_attn_plan(_desc(**dict(base, plan=fd.FD_PLAN_SPLIT)))["shares"] == 0
     # one query per KV head: never
@@ -472,8 +476,9 @@ def test_read_probe_host_checks():
 def test_small_calls_plan_smaller_chunks_and_no_shares():
     # chunk_size 0 on a call with few rows: the table's chunk (measured on
     # full batches) is halved, down to 256 tokens, until the call has 256
-    # units (counted at max_seq_len); balanced shares need 16 quanta of 64
-    # tokens per share.  Full batches keep the table's pick.
+    # units (2048 for the E4M3FN family; counted at max_seq_len); balanced
+    # shares need 16 quanta of 64 tokens per share.  Full batches keep the
+    # table's pick.
     def plan(**kw):
         return fd.fd_attn_plan(_desc(**dict(kw, chunk_size=0)))
 
@@ -490,12 +495,13 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
              dict(batch=2, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn"),
              dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn", page_size=16,
                   max_blocks_per_seq=1024, num_pages=1024)]
-    want = [256, 512, 256, 1024, 1024, 512]
+    want = [256, 512, 256, 1024, 256, 256]
     for kw, c in zip(small, want):
         p = plan(**kw)
         assert p["shares"] == 0 and p["chunk_size"] == c, (kw, p)
-        # the largest chunk (at least 256) that gives 256 units
-        assert c == 256 or units(p, kw) >= 256 > units(dict(p, chunk_size=2 * c), kw), (kw, p)
+        # the largest chunk (at least 256) that gives the family's units
+        target = 2048 if p["family"] == 1 else 256
+        assert c == 256 or units(p, kw) >= target > units(dict(p, chunk_size=2 * c), kw), (kw, p)
         assert p["fused"] == 1       # a grid of at most 512 units merges in the launch
         assert fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=0))) == \
             fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=c)))

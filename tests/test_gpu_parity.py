@@ -371,13 +371,13 @@ def test_plan_table_rows(g, kv, page, lens, cap):
 
 @pytest.mark.parametrize("chunk,fused", [(0, 1), (512, 0), (2048, 1)])
 def test_serving_batch_runs_balanced_shares(chunk, fused):
-    # a serving batch (4096 sequences x 2 KV heads = 8192 row groups): the
+    # a serving batch (8192 sequences x 2 KV heads = 16384 row groups): the
     # library picks balanced shares -- pieces for chunk_size 0, whole chunks
     # otherwise (merged by a second launch unless a chunk covers max_seq_len)
     import split_kv_asynchronous_amd as fd
-    lens = np.random.default_rng(17).integers(0, 1500, size=4096)
-    prob = synthetic.make_problem(batch=4096, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=chunk,
-                                  max_seq_len=2048, page_size=16, seed=1717)
+    lens = np.random.default_rng(17).integers(0, 750, size=8192)
+    prob = synthetic.make_problem(batch=8192, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=chunk,
+                                  max_seq_len=1024, page_size=16, seed=1717)
     dp = DeviceProblem(prob)
     plan = fd.fd_attn_plan(dp.desc())
     print("case serving batch chunk %d -> %s" % (chunk, plan), flush=True)
