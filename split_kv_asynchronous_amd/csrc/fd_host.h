@@ -130,6 +130,15 @@ constexpr int64_t kServeGroupsAuto[2] = {16384, 16384};
 // best of 3 x 10): grouped E4M3FN 64 x U[512,16K] 0.96 (paged 0.96), 16 x
 // U[16K,64K] 0.98 (0.97); grouped bf16 32 x U[1K,32K] 0.98-0.99 (paged
 // 1.00); shorter and longer bf16 rows and 2K E4M3FN rows 1.04-1.10.
+// Rows of one query per KV head longer than 8K take chunks of 1024 too: a
+// flagged chunk is recomputed in place at the end of the launch, so the
+// chunk size sets the fallback's tail (1 x 32 heads x 128K with 1% of its
+// chunks flagged: 343 µs at 1024, 369 at 2048, 422 at 4096); without
+// fallback 1024 was within 1% of 4096 on that workload.
+// Rows of one query per KV head up to 2K tokens take chunks of 1024 (32
+// heads, µs, 1024 against 2048): ragged U[256, 2K] at 64 / 256 sequences
+// 185.6 / 737.7 against 215.6 / 835.6 (paged 200.4 / 779.6 against 218.8 /
+// 814.7); all rows of 2K 322.9 / 1261.5 against 314.7 / 1315.3.
 // Rows of grouped bf16 up to 2K tokens run shape 0 (4 waves x 2 stages):
 // measured later over batch sizes, 64 / 256 / 1024 sequences of up to 1K
 // tokens 32.1 / 107.8 / 424.2 µs against 35.2 / 132.0 / 576.1 with 4 x 3,
@@ -149,12 +158,12 @@ inline constexpr TableRow kTable[] = {
     {kFamGroupedFp8, 1, 2048, 1024, 0, 1024, 0},
     {kFamGroupedFp8, 1, 16384, 1024, 0, 1024, 1},
     {kFamGroupedFp8, 1, 1 << 23, 2048, 0, 0, 1},
-    {kFamVector, 0, 2048, 2048, 0, 0, 0},
+    {kFamVector, 0, 2048, 1024, 0, 0, 0},
     {kFamVector, 0, 8192, 2048, 0, 0, 0},
-    {kFamVector, 0, 1 << 23, 4096, 0, 0, 0},
-    {kFamVector, 1, 2048, 2048, 0, 0, 0},
+    {kFamVector, 0, 1 << 23, 1024, 0, 0, 0},
+    {kFamVector, 1, 2048, 1024, 0, 0, 0},
     {kFamVector, 1, 8192, 2048, 0, 0, 0},
-    {kFamVector, 1, 1 << 23, 4096, 0, 0, 0},
+    {kFamVector, 1, 1 << 23, 1024, 0, 0, 0},
 };
 
 inline const TableRow &table_row(const fd_attn_desc_t *d)
@@ -191,14 +200,25 @@ inline int64_t units_at(const fd_attn_desc_t *d, int c)
 // E4M3FN 32/8 heads, 16 / 64 sequences of 256-2K tokens 32.0 / 44.1 -> 19.2
 // / 37.9 (256 / 512), 64 of 128-1K 36.6 -> 24.7 (256), 2 x 16K 31.8 -> 28.8
 // (256).
-constexpr int kMinAutoUnits[3] = {256, 2048, 256};
+// The one-query-per-KV-head kernel aims at 1024 units (32 heads: 8 x
+// U[256, 2K] 68.3 -> 33.4 µs at chunk 512, 1 x U[4K, 32K] 97.7 -> 79.2 at
+// 1024; its table rows were measured on rows of one length, 8 x 8K stays at
+// 2048), and no family runs more than kMaxAutoChunksPerRow chunks per row
+// (the table's chunk is doubled for rows that long, and halving stops
+// there): one 128K row merges its chunks at the end of the launch, 61.2 µs
+// at chunk 256 against 43.9 at 512.
+constexpr int kMinAutoUnits[3] = {256, 2048, 1024};
 constexpr int kMinAutoChunk = 256;
+constexpr int kMaxAutoChunksPerRow = 256;
 
 inline int chunk_of(const fd_attn_desc_t *d)
 {
     if (d->chunk_size != 0) return d->chunk_size;
     int c = table_row(d).chunk;
-    while (c > kMinAutoChunk && units_at(d, c) < kMinAutoUnits[family_of(d)]) c /= 2;
+    while ((int64_t)c * kMaxAutoChunksPerRow < d->max_seq_len) c *= 2;
+    while (c > kMinAutoChunk && (int64_t)(c / 2) * kMaxAutoChunksPerRow >= d->max_seq_len &&
+           units_at(d, c) < kMinAutoUnits[family_of(d)])
+        c /= 2;
     return d->page_size > c ? d->page_size : c;
 }
 

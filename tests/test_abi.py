@@ -293,17 +293,17 @@ PLAN_ROWS = [
     # family, paged, max_seq_len probes, chunk, shape, largest chunk merged in
     # the launch, balanced shares for chunk_size 0 (shape + 1; 0: fixed chunks)
     (0, 0, (1, 2048), 2048, 0, 0, 0), (0, 0, (2049, 8192), 4096, 1, 512, 0),
-    (0, 0, (8193, 32768), 2048, 0, 1024, 1), (0, 0, (32769, 1 << 20), 1024, 0, 0, 0),
+    (0, 0, (8193, 32768), 2048, 0, 1024, 1), (0, 0, (32769, 1 << 18), 1024, 0, 0, 0),
     (0, 1, (16, 2048), 2048, 0, 0, 0), (0, 1, (2064, 8192), 4096, 1, 1024, 0),
-    (0, 1, (8208, 32768), 2048, 0, 2048, 0), (0, 1, (32784, 1 << 20), 2048, 0, 0, 0),
+    (0, 1, (8208, 32768), 2048, 0, 2048, 0), (0, 1, (32784, 1 << 18), 2048, 0, 0, 0),
     (1, 0, (1, 2048), 1024, 0, 1024, 0), (1, 0, (2049, 16384), 1024, 0, 1024, 1),
-    (1, 0, (16385, 1 << 20), 2048, 0, 0, 1),
+    (1, 0, (16385, 1 << 18), 2048, 0, 0, 1),
     (1, 1, (16, 2048), 1024, 0, 1024, 0), (1, 1, (2064, 16384), 1024, 0, 1024, 1),
-    (1, 1, (16400, 1 << 20), 2048, 0, 0, 1),
-    (2, 0, (1, 2048), 2048, 0, 0, 0), (2, 0, (2049, 8192), 2048, 0, 0, 0),
-    (2, 0, (8193, 1 << 20), 4096, 0, 0, 0),
-    (2, 1, (16, 2048), 2048, 0, 0, 0), (2, 1, (2064, 8192), 2048, 0, 0, 0),
-    (2, 1, (8208, 1 << 20), 4096, 0, 0, 0),
+    (1, 1, (16400, 1 << 18), 2048, 0, 0, 1),
+    (2, 0, (1, 2048), 1024, 0, 0, 0), (2, 0, (2049, 8192), 2048, 0, 0, 0),
+    (2, 0, (8193, 1 << 18), 1024, 0, 0, 0),
+    (2, 1, (16, 2048), 1024, 0, 0, 0), (2, 1, (2064, 8192), 2048, 0, 0, 0),
+    (2, 1, (8208, 1 << 18), 1024, 0, 0, 0),
 ]
 
 
@@ -475,10 +475,11 @@ def test_read_probe_host_checks():
 
 def test_small_calls_plan_smaller_chunks_and_no_shares():
     # chunk_size 0 on a call with few rows: the table's chunk (measured on
-    # full batches) is halved, down to 256 tokens, until the call has 256
-    # units (2048 for the E4M3FN family; counted at max_seq_len); balanced
-    # shares need 16 quanta of 64 tokens per share.  Full batches keep the
-    # table's pick.
+    # full batches) is halved, down to 256 tokens and to no more than 256
+    # chunks per row, until the call has 256 units (2048 for the E4M3FN
+    # family, 1024 for one query per KV head; counted at max_seq_len);
+    # balanced shares need 16 quanta of 64 tokens per share.  Full batches
+    # keep the table's pick.
     def plan(**kw):
         return fd.fd_attn_plan(_desc(**dict(kw, chunk_size=0)))
 
@@ -499,9 +500,11 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
     for kw, c in zip(small, want):
         p = plan(**kw)
         assert p["shares"] == 0 and p["chunk_size"] == c, (kw, p)
-        # the largest chunk (at least 256) that gives the family's units
-        target = 2048 if p["family"] == 1 else 256
-        assert c == 256 or units(p, kw) >= target > units(dict(p, chunk_size=2 * c), kw), (kw, p)
+        # the largest chunk (at least 256, at most 256 per row) that gives
+        # the family's units
+        target = (256, 2048, 1024)[p["family"]]
+        assert c == 256 or c * 256 < 2 * kw["max_seq_len"] or \
+            units(p, kw) >= target > units(dict(p, chunk_size=2 * c), kw), (kw, p)
         assert p["fused"] == 1       # a grid of at most 512 units merges in the launch
         assert fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=0))) == \
             fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=c)))
@@ -510,7 +513,15 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
     assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn", page_size=16,
                 max_blocks_per_seq=1024, num_pages=40000)["shares"] == 512
     assert plan(batch=8, num_q_heads=32, num_kv_heads=32, max_seq_len=8192)["chunk_size"] == 2048
-    assert plan(batch=1, num_q_heads=32, num_kv_heads=32, max_seq_len=131072)["chunk_size"] == 4096
+    assert plan(batch=1, num_q_heads=32, num_kv_heads=32, max_seq_len=131072)["chunk_size"] == 1024
+    # one query per KV head: 1024 units, but at most 256 chunks per row
+    assert plan(batch=8, num_q_heads=32, num_kv_heads=32, max_seq_len=2048)["chunk_size"] == 512
+    assert plan(batch=1, num_q_heads=32, num_kv_heads=32, max_seq_len=32768)["chunk_size"] == 1024
+    assert plan(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=131072)["chunk_size"] == 512
+    assert plan(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=1 << 20)["chunk_size"] == 4096
+    # at most 256 chunks per row: rows this long double the table's chunk
+    assert plan(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=1 << 20)["chunk_size"] == 4096
+    assert plan(batch=64, num_q_heads=32, num_kv_heads=32, max_seq_len=1 << 23)["chunk_size"] == 32768
     # an explicit chunk size is kept as given
     assert fd.fd_attn_plan(_desc(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=4096,
                                  chunk_size=2048))["chunk_size"] == 2048
