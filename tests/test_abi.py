@@ -525,3 +525,31 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
     # an explicit chunk size is kept as given
     assert fd.fd_attn_plan(_desc(batch=1, num_q_heads=1, num_kv_heads=1, max_seq_len=4096,
                                  chunk_size=2048))["chunk_size"] == 2048
+
+
+def test_automatic_plans_are_valid_on_random_calls():
+    # chunk_size 0 over random shapes: every plan is one the call accepts --
+    # a chunk of at least 256 tokens (a multiple of the page size) and at
+    # most 256 chunks per row, or balanced shares (grouped families only) --
+    # and sizes the same workspace as the call with that chunk stated
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    for _ in range(400):
+        hkv = int(rng.choice([1, 2, 4, 8, 32]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        kv = str(rng.choice(["bf16", "e4m3fn", "f32"]))
+        page = int(rng.choice([0, 0, 16, 32, 256]))
+        L = int(rng.choice([1, 17, 300, 2048, 5000, 32768, 200000, 1 << 23]))
+        kw = dict(batch=int(rng.choice([1, 3, 16, 200, 2048, 20000])), num_q_heads=g * hkv, num_kv_heads=hkv,
+                  max_seq_len=L, kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16")
+        if page:
+            kw.update(page_size=page, max_blocks_per_seq=-(-L // page), num_pages=4)
+        d = _desc(**dict(kw, chunk_size=0))
+        p = fd.fd_attn_plan(d)
+        if p["shares"]:
+            assert p["family"] in (0, 1) and p["chunk_size"] == 0 and p["fused"] == 1, (kw, p)
+            continue
+        c = p["chunk_size"]
+        assert c >= 256 and c % 32 == 0 and c % max(page, 1) == 0, (kw, p)
+        assert -(-L // c) <= 256 or c == 256, (kw, p)
+        assert fd.fd_attn_workspace_size(d) == fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=c))), (kw, p)
