@@ -191,7 +191,7 @@ int fd_attn_decode_static(const fd_attn_desc_t *desc, const void *q, const void 
 /* The plan a call with this descriptor would run, from the library's table
  * of measured plans (or desc->plan where it forces one; with chunk_size 0,
  * the table may pick balanced shares, and does for calls of many row groups,
- * but only when each share gets at least 1024 tokens of work counted at
+ * but only when each share gets at least 8192 tokens of work counted at
  * max_seq_len; and a call with few rows gets the table's chunk size halved,
  * down to 256 tokens, until it has 256 units -- the table was measured on
  * full batches, where a small call would leave most of the chip idle):

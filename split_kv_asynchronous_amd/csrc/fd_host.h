@@ -232,10 +232,13 @@ constexpr int kSharesPerCU[3] = {2, 1, 3};
 // The library picks balanced shares (chunk_size 0) only for calls with at
 // least kMinShareQuanta quanta of kQuantaTokens tokens per share (counted at
 // max_seq_len): on smaller calls every share holds a sliver and the pieces'
-// merges dominate (1 x 64/8 heads x 32K bf16: 54.3 µs on shares against
-// 31.1 at chunk 1024; 2 x 32/8 x 16K E4M3FN: 36.9 against 28.8-31.9).
+// merges dominate.  Measured, µs, shares against the fixed plan taken
+// instead: 1 x 64/8 heads x 32K bf16 (8 quanta per share) 54.3 against 31.1;
+// 8 x U[2K, 32K] bf16 (64) 114.8 against 103.3; 8 x U[512, 16K] E4M3FN (32)
+// 54.7 against 41.8; at 128 (32 x U[512, 16K] E4M3FN) shares tie the best
+// fixed plan, and the 32K GQA and paged 16K E4M3FN workloads (256) gain.
 constexpr int kQuantaTokens = 64;
-constexpr int kMinShareQuanta = 16;
+constexpr int kMinShareQuanta = 128;
 
 struct Plan {
     int family, chunk, shape, fused;

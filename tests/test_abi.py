@@ -478,7 +478,7 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
     # full batches) is halved, down to 256 tokens and to no more than 256
     # chunks per row, until the call has 256 units (2048 for the E4M3FN
     # family, 1024 for one query per KV head; counted at max_seq_len);
-    # balanced shares need 16 quanta of 64 tokens per share.  Full batches
+    # balanced shares need 128 quanta of 64 tokens per share.  Full batches
     # keep the table's pick.
     def plan(**kw):
         return fd.fd_attn_plan(_desc(**dict(kw, chunk_size=0)))
