@@ -92,3 +92,23 @@ def test_random_shape_balanced_shares(i):
         np.testing.assert_array_equal(flags[sure], ref_flags[sure])
         compare(prob, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
     prob.chunk_size = chunk
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_random_shape_library_plan(i):
+    # the same random cases under the library's own plan (chunk_size 0): the
+    # plan table refined by the call's size (smaller chunks for small calls,
+    # balanced shares only with enough work per share)
+    import split_kv_asynchronous_amd as fd
+    kw = dict(draw_case(i), chunk_size=0)
+    prob = synthetic.make_problem(**kw)
+    ref_out, ref_flags, margin = oracle.decode_exact(**prob.args())
+    sure = margin >= 1e-3
+    dp = DeviceProblem(prob)
+    plan = fd.fd_attn_plan(dp.desc())
+    print("case %d library plan %s" % (i, plan), flush=True)
+    assert plan["shares"] > 0 or plan["chunk_size"] >= 256
+    dp.run()
+    out, flags = dp.results()
+    np.testing.assert_array_equal(flags[sure], ref_flags[sure])
+    compare(prob, out, np.where(sure, flags, ref_flags), ref=(ref_out, ref_flags))
