@@ -92,7 +92,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            raise ImportError("libfd_attn.so is not built; run __graft_entry__.build() "
+            raise ImportError("libfd_attn.so is not built; run python split_kv_asynchronous_amd/build.py "
                               "(hipcc --offload-arch=gfx950)")
         lib = ctypes.CDLL(_LIB_PATH)
         D = ctypes.POINTER(FdAttnDesc)
