@@ -661,7 +661,9 @@ def read_ceiling(fd, dp, prob, plan, K, torch):
 
 def main_serving(args):
     """One JSON line per serving-batch case: whole-call and chunk-kernel TB/s
-    of K/V over K back-to-back calls (a side measurement, not the bench line)."""
+    of K/V over K back-to-back calls at the case's chunk size, and the same
+    batch under the library's own plan (a side measurement, not the bench
+    line)."""
     import torch
 
     import split_kv_asynchronous_amd as fd
@@ -692,10 +694,13 @@ def main_serving(args):
         torch.cuda.synchronize()
         kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
         kvb = prob.kv_bytes()
-        print(json.dumps({"workload": name, "batch": B, "kv_bytes_per_call": kvb,
-                          "ms_per_call": round(per_call * 1e3, 5), "call_tbs": round(kvb / per_call / 1e12, 3),
-                          "kernel_ms": round(kms, 5), "kernel_tbs": round(kvb / kms / 1e9, 3),
-                          "plan": fd.fd_attn_plan(dp.desc())}), flush=True)
+        line = {"workload": name, "batch": B, "kv_bytes_per_call": kvb,
+                "ms_per_call": round(per_call * 1e3, 5), "call_tbs": round(kvb / per_call / 1e12, 3),
+                "kernel_ms": round(kms, 5), "kernel_tbs": round(kvb / kms / 1e9, 3),
+                "plan": fd.fd_attn_plan(dp.desc())}
+        # the same batch under the library's own plan (chunk_size 0)
+        line["library_plan"] = library_plan_line(fd, dp, prob, args.steps, torch)
+        print(json.dumps(line), flush=True)
         del dp
         torch.cuda.empty_cache()
 

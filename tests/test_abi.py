@@ -366,9 +366,10 @@ def test_serving_batches_run_balanced_shares():
     # serving batches run balanced shares in shape 2 (3 workgroups per
     # compute unit): whole chunks, for a chunk size that is a multiple of 64
     # (merged by a second launch unless a chunk covers max_seq_len), from
-    # 8192 (bf16) / 16384 (E4M3FN) row groups; pieces, for chunk_size 0, from
-    # 16384 row groups in both families.  Fewer row groups, a chunk size off
-    # the 64 grid or a forced plan: fixed chunks
+    # 8192 (bf16) / 16384 (E4M3FN) row groups; for chunk_size 0, from 16384
+    # row groups in both families: whole chunks covering every row when rows
+    # are at most 2K tokens, pieces beyond.  Fewer row groups, a chunk size
+    # off the 64 grid or a forced plan: fixed chunks
     for kw, whole_needed in ((dict(), 8192), (dict(kv_dtype="e4m3fn", num_q_heads=32), 16384)):
         for batch in sorted({whole_needed // 8 - 1, whole_needed // 8, 16384 // 8 - 1, 16384 // 8}):
             base = dict(kw, batch=batch, max_seq_len=2048, chunk_size=0)
@@ -376,8 +377,10 @@ def test_serving_batches_run_balanced_shares():
             whole = fd.fd_attn_plan(_desc(**dict(base, chunk_size=512)))
             one = fd.fd_attn_plan(_desc(**dict(base, chunk_size=2048)))
             if batch * 8 >= 16384:
-                assert got["shares"] == 768 and got["shape"] == 2 and got["fused"] == 1, (base, got)
-                assert got["chunk_size"] == 0
+                # rows of up to 2K tokens: whole-chunk shares, one chunk per row
+                assert got == dict(chunk_size=2048, family=got["family"], shape=2, fused=1, shares=768), (base, got)
+                long_rows = fd.fd_attn_plan(_desc(**dict(base, max_seq_len=4096)))
+                assert long_rows["shares"] > 0 and long_rows["chunk_size"] == 0 and long_rows["fused"] == 1
             else:
                 assert got["shares"] == 0 and got["chunk_size"] > 0, (base, got)
             if batch * 8 >= whole_needed:
@@ -530,8 +533,9 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
 def test_automatic_plans_are_valid_on_random_calls():
     # chunk_size 0 over random shapes: every plan is one the call accepts --
     # a chunk of at least 256 tokens (a multiple of the page size) and at
-    # most 256 chunks per row, or balanced shares (grouped families only) --
-    # and sizes the same workspace as the call with that chunk stated
+    # most 256 chunks per row, or balanced shares (grouped families only;
+    # pieces, or whole chunks covering every row) -- and a fixed-chunk plan
+    # sizes the same workspace as the call with that chunk stated
     import numpy as np
     rng = np.random.default_rng(2024)
     for _ in range(400):
@@ -547,7 +551,10 @@ def test_automatic_plans_are_valid_on_random_calls():
         d = _desc(**dict(kw, chunk_size=0))
         p = fd.fd_attn_plan(d)
         if p["shares"]:
-            assert p["family"] in (0, 1) and p["chunk_size"] == 0 and p["fused"] == 1, (kw, p)
+            # pieces, or (serving batches of short rows) whole chunks covering every row
+            c = p["chunk_size"]
+            assert p["family"] in (0, 1) and p["fused"] == 1, (kw, p)
+            assert c == 0 or (c >= L and c % 64 == 0 and c % max(page, 1) == 0), (kw, p)
             continue
         c = p["chunk_size"]
         assert c >= 256 and c % 32 == 0 and c % max(page, 1) == 0, (kw, p)

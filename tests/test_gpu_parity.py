@@ -369,19 +369,22 @@ def test_plan_table_rows(g, kv, page, lens, cap):
     compare(prob, *dp.results())
 
 
-@pytest.mark.parametrize("chunk,fused", [(0, 1), (512, 0), (2048, 1)])
-def test_serving_batch_runs_balanced_shares(chunk, fused):
+@pytest.mark.parametrize("chunk,cap,fused,planned", [(0, 1024, 1, 1024), (0, 4096, 1, 0), (512, 1024, 0, 512),
+                                                     (2048, 1024, 1, 2048)])
+def test_serving_batch_runs_balanced_shares(chunk, cap, fused, planned):
     # a serving batch (8192 sequences x 2 KV heads = 16384 row groups): the
-    # library picks balanced shares -- pieces for chunk_size 0, whole chunks
-    # otherwise (merged by a second launch unless a chunk covers max_seq_len)
+    # library picks balanced shares -- for chunk_size 0 whole chunks covering
+    # every row when max_seq_len is at most 2K, pieces beyond; whole chunks of
+    # a stated size otherwise (merged by a second launch unless a chunk
+    # covers max_seq_len)
     import split_kv_asynchronous_amd as fd
     lens = np.random.default_rng(17).integers(0, 750, size=8192)
     prob = synthetic.make_problem(batch=8192, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=chunk,
-                                  max_seq_len=1024, page_size=16, seed=1717)
+                                  max_seq_len=cap, page_size=16, seed=1717)
     dp = DeviceProblem(prob)
     plan = fd.fd_attn_plan(dp.desc())
-    print("case serving batch chunk %d -> %s" % (chunk, plan), flush=True)
-    assert plan["shares"] == 768 and plan["shape"] == 2 and plan["fused"] == fused and plan["chunk_size"] == chunk
+    print("case serving batch chunk %d cap %d -> %s" % (chunk, cap, plan), flush=True)
+    assert plan["shares"] == 768 and plan["shape"] == 2 and plan["fused"] == fused and plan["chunk_size"] == planned
     dp.run()
     compare(prob, *dp.results())
 
