@@ -198,8 +198,9 @@ inline int64_t units_at(const fd_attn_desc_t *d, int c)
 // The table's chunk sizes were measured on full batches.  A call with few
 // rows gets the table's chunk halved, down to kMinAutoChunk tokens, until it
 // has kMinAutoUnits units of its family, so that it still spreads over the
-// chip: 256 for the one-wavefront-ring bf16 and the one-query-per-KV-head
-// kernels, 2048 for the E4M3FN kernel (six workgroups per compute unit).
+// chip: 256 for the grouped bf16 kernel (per-wavefront rings), 2048 for the
+// E4M3FN kernel (six workgroups per compute unit), 1024 for one query per KV
+// head (below).
 // Measured on MI355X, µs per call, table's chunk -> halved: 1 row x 4K fp32
 // 20.9 -> 8.4 (chunk 256); 1 row x 128K bf16 137 -> 44 (512); 1 x 32/8
 // heads x 8K bf16 41.8 -> 14.6 (256); 8 rows x 4K bf16 26.9 -> 11.0 (256);
