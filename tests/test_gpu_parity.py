@@ -371,20 +371,29 @@ def test_plan_table_rows(g, kv, page, lens, cap):
 
 @pytest.mark.parametrize("chunk,cap,fused,planned", [(0, 1024, 1, 1024), (0, 4096, 1, 0), (512, 1024, 0, 512),
                                                      (2048, 1024, 1, 2048)])
-def test_serving_batch_runs_balanced_shares(chunk, cap, fused, planned):
+@pytest.mark.parametrize("kv", ["bf16", "e4m3fn"])
+def test_serving_batch_runs_balanced_shares(kv, chunk, cap, fused, planned):
     # a serving batch (8192 sequences x 2 KV heads = 16384 row groups): the
     # library picks balanced shares -- for chunk_size 0 whole chunks covering
     # every row when max_seq_len is at most 2K, pieces beyond; whole chunks of
     # a stated size otherwise (merged by a second launch unless a chunk
     # covers max_seq_len)
+    # (E4M3FN: 2048 sequences x 8 KV heads of 4 query heads, also 16384 row
+    # groups; shares for its 4K rows take the table's shape 0)
     import split_kv_asynchronous_amd as fd
-    lens = np.random.default_rng(17).integers(0, 750, size=8192)
-    prob = synthetic.make_problem(batch=8192, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=chunk,
-                                  max_seq_len=cap, page_size=16, seed=1717)
+    if kv == "bf16":
+        lens = np.random.default_rng(17).integers(0, 750, size=8192)
+        prob = synthetic.make_problem(batch=8192, num_q_heads=8, num_kv_heads=2, seq_lens=lens, chunk_size=chunk,
+                                      max_seq_len=cap, page_size=16, seed=1717)
+    else:
+        lens = np.random.default_rng(18).integers(0, 750, size=2048)
+        prob = synthetic.make_problem(batch=2048, num_q_heads=32, num_kv_heads=8, seq_lens=lens, chunk_size=chunk,
+                                      max_seq_len=cap, page_size=16, kv_dtype="e4m3fn", seed=1818)
     dp = DeviceProblem(prob)
     plan = fd.fd_attn_plan(dp.desc())
-    print("case serving batch chunk %d cap %d -> %s" % (chunk, cap, plan), flush=True)
-    assert plan["shares"] == 768 and plan["shape"] == 2 and plan["fused"] == fused and plan["chunk_size"] == planned
+    print("case serving batch %s chunk %d cap %d -> %s" % (kv, chunk, cap, plan), flush=True)
+    assert plan["shares"] > 0 and plan["fused"] == fused and plan["chunk_size"] == planned
+    assert plan["shape"] == (0 if (kv, chunk, cap) == ("e4m3fn", 0, 4096) else 2)
     dp.run()
     compare(prob, *dp.results())
 
