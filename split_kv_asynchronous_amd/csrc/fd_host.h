@@ -214,17 +214,24 @@ inline int64_t units_at(const fd_attn_desc_t *d, int c)
 // (the table's chunk is doubled for rows that long, and halving stops
 // there): one 128K row merges its chunks at the end of the launch, 61.2 µs
 // at chunk 256 against 43.9 at 512.
+// The grouped families also stop halving at 32 chunks per row: their merge
+// of a row's chunks runs in the launch, and past 32 it costs more than the
+// extra units give (E4M3FN, 8 x U[512, 16K] / U[4K, 16K]: 46.4 / 50.6 µs at
+// chunk 256 against 41.9 / 44.1 at 512; bf16, 1 x 64/8 heads x 32K: 36.7 at
+// 512 against 31.1 at 1024).
 constexpr int kMinAutoUnits[3] = {256, 2048, 1024};
 constexpr int kMinAutoChunk = 256;
 constexpr int kMaxAutoChunksPerRow = 256;
+constexpr int kMaxHalvedChunksPerRow[3] = {32, 32, 256};
 
 inline int chunk_of(const fd_attn_desc_t *d)
 {
     if (d->chunk_size != 0) return d->chunk_size;
+    const int fam = family_of(d);
     int c = table_row(d).chunk;
     while ((int64_t)c * kMaxAutoChunksPerRow < d->max_seq_len) c *= 2;
-    while (c > kMinAutoChunk && (int64_t)(c / 2) * kMaxAutoChunksPerRow >= d->max_seq_len &&
-           units_at(d, c) < kMinAutoUnits[family_of(d)])
+    while (c > kMinAutoChunk && (int64_t)(c / 2) * kMaxHalvedChunksPerRow[fam] >= d->max_seq_len &&
+           units_at(d, c) < kMinAutoUnits[fam])
         c /= 2;
     return d->page_size > c ? d->page_size : c;
 }

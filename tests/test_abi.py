@@ -478,9 +478,10 @@ def test_read_probe_host_checks():
 
 def test_small_calls_plan_smaller_chunks_and_no_shares():
     # chunk_size 0 on a call with few rows: the table's chunk (measured on
-    # full batches) is halved, down to 256 tokens and to no more than 256
-    # chunks per row, until the call has 256 units (2048 for the E4M3FN
-    # family, 1024 for one query per KV head; counted at max_seq_len);
+    # full batches) is halved, down to 256 tokens and to no more than 32
+    # chunks per row (256 for one query per KV head), until the call has 256
+    # units (2048 for the E4M3FN family, 1024 for one query per KV head;
+    # counted at max_seq_len);
     # balanced shares need 128 quanta of 64 tokens per share.  Full batches
     # keep the table's pick.
     def plan(**kw):
@@ -499,15 +500,18 @@ def test_small_calls_plan_smaller_chunks_and_no_shares():
              dict(batch=2, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn"),
              dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=16384, kv_dtype="e4m3fn", page_size=16,
                   max_blocks_per_seq=1024, num_pages=1024)]
-    want = [256, 512, 256, 1024, 256, 256]
+    want = [256, 512, 256, 1024, 512, 512]
     for kw, c in zip(small, want):
         p = plan(**kw)
         assert p["shares"] == 0 and p["chunk_size"] == c, (kw, p)
-        # the largest chunk (at least 256, at most 256 per row) that gives
-        # the family's units
+        # the largest chunk (at least 256, and no more than 32 chunks per
+        # row in the grouped families, 256 for one query per KV head) that
+        # gives the family's units
         target = (256, 2048, 1024)[p["family"]]
-        assert c == 256 or c * 256 < 2 * kw["max_seq_len"] or \
+        per_row = 256 if p["family"] == 2 else 32
+        assert c == 256 or c * per_row < 2 * kw["max_seq_len"] or \
             units(p, kw) >= target > units(dict(p, chunk_size=2 * c), kw), (kw, p)
+        assert -(-kw["max_seq_len"] // c) <= per_row or c == 256, (kw, p)
         assert p["fused"] == 1       # a grid of at most 512 units merges in the launch
         assert fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=0))) == \
             fd.fd_attn_workspace_size(_desc(**dict(kw, chunk_size=c)))
