@@ -58,6 +58,33 @@ def test_full_configs(cfg):
     print("cfg%d rel err %.3e flagged %d" % (cfg, rel, int(flags.sum())))
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_configs_library_plan(cfg):
+    # the same workloads with chunk_size 0, as the bench times them beside
+    # the stated chunk: the library's own plan (balanced shares on some)
+    import split_kv_asynchronous_amd as fd
+    prob = synthetic.make_config(cfg)
+    prob.chunk_size = 0
+    dp = DeviceProblem(prob)
+    plan = fd.fd_attn_plan(dp.desc())
+    print("case full cfg%d library plan %s" % (cfg, plan), flush=True)
+    dp.run()
+    out, flags = dp.results()
+    rel, _, _ = compare(prob, out, flags)
+    if cfg == 4:
+        # one recomputed pair per chunk that holds a perturbed key
+        heads = sorted(set(int(h) for h in prob.perturbed[:, 0]))
+        assert np.nonzero(flags)[0].tolist() == heads
+        assert 0 < dp.recomputed() <= len(prob.perturbed)
+    else:
+        assert flags.sum() == 0 and dp.recomputed() == 0
+    out1 = dp.out.clone()
+    dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, dp.out)
+    print("cfg%d library plan rel err %.3e" % (cfg, rel))
+
+
 GQA_CASES = [
     # group, kv dtype, page size, chunk, lens
     (2, "bf16", 0, 64, [1, 31, 32, 33, 200]),
