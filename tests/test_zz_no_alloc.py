@@ -39,13 +39,13 @@ CASES = [
 ]
 
 
-def _static_call(dp, phi=None, a=None, b=None):
+def _static_call(dp, phi=None, a=None, b=None, plan=0):
     p = dp.prob
     return fd.fd_attn_decode_static(
         dp.q, dp.k, dp.v, dp.seq_lens, dp.block_table, p.phi if phi is None else phi,
         p.a if a is None else a, p.b if b is None else b, dp.out, dp.flags, chunk_size=p.chunk_size,
         max_seq_len=p.max_seq_len, num_kv_heads=p.num_kv_heads, page_size=p.page_size, scale=p.scale,
-        k_scale=dp.k_scale, v_scale=dp.v_scale, q_dtype=p.q_dtype, kv_dtype=p.kv_dtype)
+        k_scale=dp.k_scale, v_scale=dp.v_scale, q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, plan=plan)
 
 
 @pytest.mark.parametrize("first,second", CASES, ids=["gqa-bf16", "paged-e4m3fn", "mha-bf16"])
@@ -68,6 +68,38 @@ def test_static_workspace_equals_caller_workspace(first, second):
         if not i:
             out, flags = dp.results()
             compare(prob, out, flags)
+
+
+SHARE_CALLS = [
+    # balanced shares in pieces (a quarter of the work in claimed grains,
+    # narrow band: pieces recomputed), then whole 512-token chunks of a
+    # smaller paged E4M3FN call, then the first call again on what the
+    # second left in the array
+    dict(batch=4, num_q_heads=16, num_kv_heads=2, seq_lens=[40000, 30000, 50000, 2000], kv_dtype="bf16",
+         page_size=0, chunk_size=0, seed=808, phi=1.0, a=3.0, b=1.5),
+    dict(batch=4, num_q_heads=8, num_kv_heads=2, seq_lens=[5000, 700, 0, 3000], kv_dtype="e4m3fn",
+         page_size=16, chunk_size=512, seed=809),
+]
+
+
+def test_static_workspace_runs_balanced_shares():
+    plan = fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(0)
+    dps = [DeviceProblem(synthetic.make_problem(**kw), plan=plan) for kw in SHARE_CALLS]
+    for i in (0, 1, 0):
+        dp = dps[i]
+        got = fd.fd_attn_plan(dp.desc())
+        print("case no-alloc shares call %d: plan %s" % (i, got), flush=True)
+        assert got["shares"] > 0 and fd.fd_attn_workspace_size(dp.desc()) <= STATIC_BYTES
+        dp.run()
+        ref_out, ref_flags, ref_rec = dp.out.clone(), dp.flags.clone(), dp.recomputed()
+        if i == 0:
+            assert ref_rec > 0 and bool(ref_flags.any())
+        dp.out.fill_(float("nan"))
+        dp.flags.fill_(7)
+        _static_call(dp, plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(dp.out, ref_out), "output differs from fd_attn_decode"
+        assert torch.equal(dp.flags, ref_flags), "flags differ from fd_attn_decode"
 
 
 def test_static_workspace_refuses_oversized_calls():
