@@ -102,6 +102,42 @@ def test_static_workspace_runs_balanced_shares():
         assert torch.equal(dp.flags, ref_flags), "flags differ from fd_attn_decode"
 
 
+def test_static_entry_replayed_from_a_captured_graph():
+    # the callers it is for include code under graph capture: a captured
+    # static call (balanced shares, chunks recomputed) replayed with eager
+    # static calls of another, smaller problem between the replays, which
+    # rewrite the array the captured call uses
+    plan = fd.FD_PLAN_SHARES | fd.FD_PLAN_SHAPE(0)
+    dps = [DeviceProblem(synthetic.make_problem(**kw), plan=plan) for kw in SHARE_CALLS]
+    refs = []
+    for dp in dps:
+        dp.run()
+        refs.append((dp.out.clone(), dp.flags.clone()))
+        _static_call(dp, plan=plan)        # eager static calls first (the array's address is looked up)
+        torch.cuda.synchronize()
+        assert torch.equal(dp.out, refs[-1][0]) and torch.equal(dp.flags, refs[-1][1])
+    a, b = dps
+    print("case no-alloc graph replay", flush=True)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=stream):
+        _static_call(a, plan=plan)
+    torch.cuda.synchronize()
+    for i in range(5):
+        a.out.fill_(float("nan"))
+        a.flags.fill_(7)
+        if i % 2:
+            b.out.fill_(float("nan"))
+            _static_call(b, plan=plan)
+            torch.cuda.synchronize()
+            assert torch.equal(b.out, refs[1][0]) and torch.equal(b.flags, refs[1][1])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, refs[0][0]), "replay %d: output differs from fd_attn_decode" % i
+        assert torch.equal(a.flags, refs[0][1]), "replay %d: flags differ" % i
+
+
 def test_static_workspace_refuses_oversized_calls():
     prob = synthetic.make_problem(batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=[100, 50], chunk_size=32,
                                   seed=807)
